@@ -1,0 +1,325 @@
+// C ABI of libloopspec: argument validation, workspace carving and kernel orchestration for
+// ls_prelude / ls_loop_step / ls_readout / ls_verify (see include/loopspec.h).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/loopspec.h"
+#include "kernels.h"
+
+using namespace ls;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ls_status fail(ls_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+struct ls_model {
+  ls_model_desc d;
+  const void* emb = nullptr;
+  const float* g_final = nullptr;
+  std::vector<ls_layer_ptrs> pre, core, coda;
+  // bound workspace
+  char* ws = nullptr;
+  int max_rows = 0, max_keys = 0, max_jobs = 0, max_chunks = 0;
+  int* err = nullptr;
+  int32_t *slot_ok = nullptr, *dep_ok = nullptr, *row_ok = nullptr;
+  void *X = nullptr, *o = nullptr, *act = nullptr;
+  float *q = nullptr, *part = nullptr, *hc = nullptr, *logits = nullptr;
+  bool bf16() const { return d.dtype == LS_BF16; }
+  size_t esz() const { return bf16() ? 2 : 4; }
+  size_t entry() const { return (size_t)2 * d.d * esz(); }   // bytes of one KV entry
+};
+
+namespace {
+
+struct Carve {
+  int max_rows, max_keys, max_jobs, max_chunks;
+  size_t off_err, off_slot, off_dep, off_row, off_X, off_q, off_o, off_act, off_part, off_hc, off_logits, total;
+};
+
+Carve carve(const ls_model* m, int max_rows, int max_keys, int max_jobs) {
+  Carve c{};
+  c.max_rows = max_rows;
+  c.max_keys = max_keys;
+  c.max_jobs = max_jobs;
+  c.max_chunks = (max_keys + ATTN_CHUNK - 1) / ATTN_CHUNK;
+  const ls_model_desc& d = m->d;
+  const size_t R = (size_t)max_rows;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  c.off_err = take(256);
+  c.off_slot = take(R * 4);
+  c.off_dep = take(R * 4);
+  c.off_row = take(R * 4);
+  c.off_X = take(R * (size_t)std::max(d.d, d.F) * 4);
+  c.off_q = take(R * d.d * 4);
+  c.off_o = take(R * d.d * 4);
+  c.off_act = take(R * d.F * 4);
+  c.off_part = take(R * d.n_heads * (size_t)c.max_chunks * (d.head_dim + 2) * 4);
+  c.off_hc = take(R * d.d * 4);
+  c.off_logits = take(R * (size_t)d.V * 4);
+  c.total = off;
+  return c;
+}
+
+ls_status check_hip(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(LS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return LS_OK;
+}
+
+ls_status check_rows(const ls_model* m, const ls_rows* r, const char* who) {
+  if (!m || !r) return fail(LS_ERR_INVALID, "%s: null model or rows", who);
+  if (!m->ws) return fail(LS_ERR_INVALID, "%s: no workspace bound", who);
+  if (r->n < 0 || r->n_fin < 0 || r->max_anc < 0) return fail(LS_ERR_INVALID, "%s: negative sizes", who);
+  if (r->n > m->max_rows) return fail(LS_ERR_CAPACITY, "%s: %d rows > workspace max_rows %d", who, r->n, m->max_rows);
+  if ((long long)r->n_fin + r->max_anc + 1 > m->max_keys)
+    return fail(LS_ERR_CAPACITY, "%s: n_fin + max_anc + 1 = %lld > workspace max_keys %d", who,
+                (long long)r->n_fin + r->max_anc + 1, m->max_keys);
+  if (r->n > 0 && (!r->slot || !r->pos || !r->anc_off)) return fail(LS_ERR_INVALID, "%s: null row array", who);
+  if (r->n_fin > 0 && !r->fin_slots) return fail(LS_ERR_INVALID, "%s: null fin_slots", who);
+  if (r->max_anc > 0 && !r->anc_slots) return fail(LS_ERR_INVALID, "%s: null anc_slots", who);
+  return LS_OK;
+}
+
+// One transformer layer (pre-norm attention + SwiGLU MLP) on the rows' hidden states.
+void run_layer(ls_model* m, const ls_layer_ptrs& lw, float* H, const int32_t* hidx, const ls_rows* r, KvSel kv,
+               hipStream_t s) {
+  const ls_model_desc& d = m->d;
+  const bool b = m->bf16();
+  const int n = r->n;
+  launch_rmsnorm(b, H, hidx, d.d, lw.g1, n, d.d, d.norm_eps, m->X, s);
+
+  GemmArgs g{};
+  g.M = n;
+  g.d = d.d;
+  g.hd = d.head_dim;
+  g.theta = d.rope_theta;
+  g.err = m->err;
+  // q, k, v with rotary embedding; k, v into the KV slot of the row
+  g.W0 = lw.Wq; g.W1 = lw.Wk; g.W2 = lw.Wv;
+  g.N = d.d; g.K = d.d; g.X = m->X;
+  g.q = m->q; g.kv = kv; g.slot = m->slot_ok; g.pos = r->pos;
+  launch_gemm(b, EP_QKV, g, s);
+
+  AttnArgs a{};
+  a.q = m->q; a.kv = kv; a.slot = m->slot_ok; a.pos = r->pos; a.fin = r->fin_slots;
+  a.anc_off = r->anc_off; a.anc = r->anc_slots; a.n_fin = r->n_fin; a.M = n; a.d = d.d;
+  a.n_heads = d.n_heads; a.hd = d.head_dim; a.part = m->part; a.max_chunks = m->max_chunks;
+  a.grid_chunks = (r->n_fin + r->max_anc + 1 + ATTN_CHUNK - 1) / ATTN_CHUNK;
+  a.o = m->o; a.err = m->err;
+  launch_attention(b, a, s);
+
+  GemmArgs go{};
+  go.M = n; go.W0 = lw.Wo; go.N = d.d; go.K = d.d; go.X = m->o; go.H = H; go.hidx = hidx; go.ldh = d.d; go.err = m->err;
+  launch_gemm(b, EP_RESID, go, s);
+
+  launch_rmsnorm(b, H, hidx, d.d, lw.g2, n, d.d, d.norm_eps, m->X, s);
+  GemmArgs gu{};
+  gu.M = n; gu.W0 = lw.Wg; gu.W1 = lw.Wu; gu.K = d.d; gu.X = m->X; gu.act = m->act; gu.F = d.F; gu.err = m->err;
+  launch_gemm(b, EP_SWIGLU, gu, s);
+
+  GemmArgs gd{};
+  gd.M = n; gd.W0 = lw.Wd; gd.N = d.d; gd.K = d.F; gd.X = m->act; gd.H = H; gd.hidx = hidx; gd.ldh = d.d; gd.err = m->err;
+  launch_gemm(b, EP_RESID, gd, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ls_last_error(void) { return g_err; }
+
+ls_status ls_model_create(const ls_model_desc* desc, const ls_weight_ptrs* w, ls_model** out) {
+  if (!desc || !w || !out) return fail(LS_ERR_INVALID, "ls_model_create: null argument");
+  const ls_model_desc& d = *desc;
+  if (d.V <= 0 || d.d <= 0 || d.n_heads <= 0 || d.head_dim <= 0 || d.F <= 0 || d.L <= 0 || d.R <= 0 ||
+      d.L_pre < 0 || d.L_coda < 0 || d.slot_capacity <= 0)
+    return fail(LS_ERR_INVALID, "ls_model_create: non-positive shape");
+  if (d.n_heads * d.head_dim != d.d) return fail(LS_ERR_INVALID, "ls_model_create: n_heads * head_dim != d");
+  if (d.dtype != LS_F32 && d.dtype != LS_BF16) return fail(LS_ERR_INVALID, "ls_model_create: bad dtype");
+  if (d.head_dim % 16 || d.head_dim > 128) return fail(LS_ERR_UNSUPPORTED, "head_dim must be a multiple of 16, <= 128");
+  const int kmul = d.dtype == LS_BF16 ? 32 : 16;
+  if (d.d % kmul || d.F % kmul) return fail(LS_ERR_UNSUPPORTED, "d and F must be multiples of %d", kmul);
+  if (d.n_readout < 1 || d.n_readout > LS_MAX_READOUT_DEPTHS) return fail(LS_ERR_INVALID, "bad n_readout");
+  for (int i = 0; i < d.n_readout; ++i) {
+    if (d.readout_depths[i] < 1 || d.readout_depths[i] > d.R || (i && d.readout_depths[i] <= d.readout_depths[i - 1]))
+      return fail(LS_ERR_INVALID, "readout depths must be ascending within [1, R]");
+  }
+  if (d.readout_depths[d.n_readout - 1] != d.R) return fail(LS_ERR_INVALID, "last readout depth must be R");
+  if (!w->emb || !w->g_final || (d.L && !w->core) || (d.L_pre && !w->pre) || (d.L_coda && !w->coda))
+    return fail(LS_ERR_INVALID, "ls_model_create: null weight pointer");
+  auto check_layers = [&](const ls_layer_ptrs* p, int n) {
+    for (int i = 0; i < n; ++i)
+      if (!p[i].Wq || !p[i].Wk || !p[i].Wv || !p[i].Wo || !p[i].Wg || !p[i].Wu || !p[i].Wd || !p[i].g1 || !p[i].g2)
+        return false;
+    return true;
+  };
+  if (!check_layers(w->core, d.L) || !check_layers(w->pre, d.L_pre) || !check_layers(w->coda, d.L_coda))
+    return fail(LS_ERR_INVALID, "ls_model_create: null layer weight");
+  ls_model* m = new ls_model();
+  m->d = d;
+  m->emb = w->emb;
+  m->g_final = w->g_final;
+  m->core.assign(w->core, w->core + d.L);
+  if (d.L_pre) m->pre.assign(w->pre, w->pre + d.L_pre);
+  if (d.L_coda) m->coda.assign(w->coda, w->coda + d.L_coda);
+  *out = m;
+  return LS_OK;
+}
+
+void ls_model_destroy(ls_model* m) { delete m; }
+
+size_t ls_workspace_bytes(const ls_model* m, int max_rows, int max_keys, int max_jobs) {
+  if (!m || max_rows <= 0 || max_keys <= 0 || max_jobs < 0) return 0;
+  return carve(m, max_rows, max_keys, max_jobs).total;
+}
+
+ls_status ls_bind_workspace(ls_model* m, void* ws, int max_rows, int max_keys, int max_jobs, hipStream_t stream) {
+  if (!m || !ws) return fail(LS_ERR_INVALID, "ls_bind_workspace: null argument");
+  if (max_rows <= 0 || max_rows > LS_MAX_ROWS || max_keys <= 0 || max_jobs < 0)
+    return fail(LS_ERR_INVALID, "ls_bind_workspace: bad capacities (rows 1..%d)", LS_MAX_ROWS);
+  if ((uintptr_t)ws % 256) return fail(LS_ERR_INVALID, "ls_bind_workspace: workspace not 256-byte aligned");
+  const Carve c = carve(m, max_rows, max_keys, max_jobs);
+  char* b = (char*)ws;
+  m->ws = b;
+  m->max_rows = max_rows; m->max_keys = max_keys; m->max_jobs = max_jobs; m->max_chunks = c.max_chunks;
+  m->err = (int*)(b + c.off_err);
+  m->slot_ok = (int32_t*)(b + c.off_slot);
+  m->dep_ok = (int32_t*)(b + c.off_dep);
+  m->row_ok = (int32_t*)(b + c.off_row);
+  m->X = b + c.off_X;
+  m->q = (float*)(b + c.off_q);
+  m->o = b + c.off_o;
+  m->act = b + c.off_act;
+  m->part = (float*)(b + c.off_part);
+  m->hc = (float*)(b + c.off_hc);
+  m->logits = (float*)(b + c.off_logits);
+  launch_fill_i32(m->err, 1, 0, stream);
+  return check_hip("ls_bind_workspace");
+}
+
+ls_status ls_prelude(ls_model* m, const ls_rows* r, const int32_t* tokens, float* H, const ls_kv* kv, hipStream_t s) {
+  ls_status st = check_rows(m, r, "ls_prelude");
+  if (st) return st;
+  if (!H || !kv || (r->n && !tokens)) return fail(LS_ERR_INVALID, "ls_prelude: null argument");
+  if (m->d.L_pre && !kv->pre) return fail(LS_ERR_INVALID, "ls_prelude: prelude layers need kv->pre");
+  if (r->n == 0) return LS_OK;
+  const ls_model_desc& d = m->d;
+  launch_validate(r->n, r->slot, nullptr, 0, 0, r->pos, r->anc_off, r->n_fin, r->max_anc, d.slot_capacity, m->slot_ok,
+                  m->dep_ok, m->row_ok, m->err, s);
+  launch_embed(m->bf16(), m->emb, tokens, m->slot_ok, r->n, d.V, d.d, d.slot_capacity, H, m->err, s);
+  for (int l = 0; l < d.L_pre; ++l) {
+    KvSel kvs{kv->pre, nullptr, 0, 0, l, d.slot_capacity};
+    run_layer(m, m->pre[l], H, m->slot_ok, r, kvs, s);
+  }
+  return check_hip("ls_prelude");
+}
+
+ls_status ls_loop_step(ls_model* m, const ls_rows* r, float* H, const ls_kv* kv, hipStream_t s) {
+  ls_status st = check_rows(m, r, "ls_loop_step");
+  if (st) return st;
+  if (!H || !kv || !kv->core) return fail(LS_ERR_INVALID, "ls_loop_step: null argument");
+  if (r->n && !r->depth) return fail(LS_ERR_INVALID, "ls_loop_step: null depth");
+  if (r->n == 0) return LS_OK;
+  const ls_model_desc& d = m->d;
+  launch_validate(r->n, r->slot, r->depth, 1, d.R, r->pos, r->anc_off, r->n_fin, r->max_anc, d.slot_capacity,
+                  m->slot_ok, m->dep_ok, m->row_ok, m->err, s);
+  for (int l = 0; l < d.L; ++l) {
+    KvSel kvs{kv->core, m->dep_ok, -1, d.L, l, d.slot_capacity};
+    run_layer(m, m->core[l], H, m->slot_ok, r, kvs, s);
+  }
+  return check_hip("ls_loop_step");
+}
+
+ls_status ls_readout(ls_model* m, const ls_rows* r, const float* H, const ls_sampling* smp, float* probs,
+                     const int32_t* out_rows, int n_prob_rows, int32_t* argmax, float* logits, const ls_kv* kv,
+                     hipStream_t s) {
+  ls_status st = check_rows(m, r, "ls_readout");
+  if (st) return st;
+  if (!H || !smp || !probs || !kv) return fail(LS_ERR_INVALID, "ls_readout: null argument");
+  if (r->n && !r->depth) return fail(LS_ERR_INVALID, "ls_readout: null depth");
+  if (!smp->greedy && !(smp->temperature > 0.f)) return fail(LS_ERR_INVALID, "ls_readout: temperature must be > 0");
+  if (!smp->greedy && !(smp->top_p > 0.f)) return fail(LS_ERR_INVALID, "ls_readout: top_p must be > 0");
+  if (m->d.L_coda && !kv->coda) return fail(LS_ERR_INVALID, "ls_readout: coda layers need kv->coda");
+  if (!out_rows && n_prob_rows < r->n) return fail(LS_ERR_INVALID, "ls_readout: n_prob_rows < rows");
+  if (r->n == 0) return LS_OK;
+  const ls_model_desc& d = m->d;
+  launch_validate(r->n, r->slot, r->depth, 0, d.n_readout - 1, r->pos, r->anc_off, r->n_fin, r->max_anc,
+                  d.slot_capacity, m->slot_ok, m->dep_ok, m->row_ok, m->err, s);
+  const bool b = m->bf16();
+  if (d.L_coda) {
+    launch_gather(H, m->slot_ok, r->n, d.d, d.slot_capacity, m->hc, m->err, s);
+    for (int l = 0; l < d.L_coda; ++l) {
+      KvSel kvs{kv->coda, m->dep_ok, 0, d.L_coda, l, d.slot_capacity};
+      run_layer(m, m->coda[l], m->hc, m->row_ok, r, kvs, s);
+    }
+    launch_rmsnorm(b, m->hc, m->row_ok, d.d, m->g_final, r->n, d.d, d.norm_eps, m->X, s);
+  } else {
+    launch_rmsnorm(b, H, m->slot_ok, d.d, m->g_final, r->n, d.d, d.norm_eps, m->X, s);
+  }
+  float* lg = logits ? logits : m->logits;
+  GemmArgs g{};
+  g.M = r->n; g.W0 = m->emb; g.N = d.V; g.K = d.d; g.X = m->X; g.out = lg; g.ldo = d.V; g.err = m->err;
+  launch_gemm(b, EP_STORE, g, s);
+  launch_dist(lg, r->n, d.V, smp->greedy, smp->temperature, smp->top_p, probs, out_rows, n_prob_rows, argmax, m->err, s);
+  return check_hip("ls_readout");
+}
+
+ls_status ls_verify(ls_model* m, const ls_verify_job* jobs, int n_jobs, const float* probs, int n_prob_rows,
+                    const int32_t* cands, int n_cands, const uint32_t* uniforms, ls_verify_out* out, hipStream_t s) {
+  if (!m || !m->ws) return fail(LS_ERR_INVALID, "ls_verify: null model or no workspace");
+  if (n_jobs < 0 || n_prob_rows < 0) return fail(LS_ERR_INVALID, "ls_verify: negative count");
+  if (n_jobs == 0) return LS_OK;
+  if (n_jobs > m->max_jobs) return fail(LS_ERR_CAPACITY, "ls_verify: %d jobs > workspace max_jobs %d", n_jobs, m->max_jobs);
+  if (!jobs || !probs || !uniforms || !out) return fail(LS_ERR_INVALID, "ls_verify: null argument");
+  if (n_cands < 0 || (n_cands > 0 && !cands)) return fail(LS_ERR_INVALID, "ls_verify: bad candidate array");
+  launch_verify(jobs, n_jobs, probs, m->d.V, n_prob_rows, cands, n_cands, uniforms, out, m->err, s);
+  return check_hip("ls_verify");
+}
+
+ls_status ls_sync_status(ls_model* m, hipStream_t s) {
+  if (!m || !m->err) return fail(LS_ERR_INVALID, "ls_sync_status: no workspace bound");
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(LS_ERR_HIP, "stream: %s", hipGetErrorString(e));
+  int h = 0;
+  e = hipMemcpy(&h, m->err, sizeof(int), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(LS_ERR_HIP, "error word: %s", hipGetErrorString(e));
+  if (h) return fail((ls_status)h, "a kernel rejected a descriptor (device error word %d)", h);
+  return LS_OK;
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of
+// (c0,c1,c2,c3) -> (hi(M1*c2)^c1^k0, lo(M1*c2), hi(M0*c0)^c3^k1, lo(M0*c0)), key bumped by the
+// Weyl constants between rounds.
+void ls_philox_uniforms(uint64_t seed, int64_t pos, const int32_t* purposes, int n, uint32_t* out) {
+  for (int i = 0; i < n; ++i) {
+    uint32_t c0 = (uint32_t)pos, c1 = (uint32_t)purposes[i], c2 = 0, c3 = 0;
+    uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    for (int rnd = 0; rnd < 10; ++rnd) {
+      if (rnd) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+      const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+      const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n1 = (uint32_t)p1;
+      const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1, n3 = (uint32_t)p0;
+      c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[i] = c0;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,405 @@
+"""Host-side branch scheduler of pipelined self-speculative decoding.
+
+LoopSpec page, section 2.2-2.4.  A branch is a fixed prefix plus its current loop depth.
+After prefill the first token is committed from p_R and a root branch starts.  Every
+pipeline step advances every active branch by one loop iteration in one batched call of the
+shared block; a branch reaching d1 draws x1 from q1 = p_d1 and immediately spawns the child
+branch prefix+x1 while it keeps deepening; at d2 the gate p_d2(x1) < p_d1(x1) decides whether
+a second, residual proposal x2 ~ p_d2 (-) p_d1 is drawn and spawned; the root reaching R runs
+the cascade, commits a token, keeps the accepted child's subtree (re-rooting) and prunes the
+rest, or restarts from the committed token.  Children reuse the parent's KV by slot index;
+pruning only returns slots to the free list.
+
+Copy-suffix proposals (CopyLoop page) replace the draws: at the screening depth a branch
+reads p_s, keeps the copied candidates with p_s(c) >= tau, spawns one child per survivor, and
+the root verifies them with the point-mass cascade; with no survivor a single proposal is
+drawn from p_s.
+
+When the branch cap (or the slot pool) would be exceeded, a proposal is still drawn and
+verified but gets no precomputed child; if it is accepted a fresh branch starts at depth 0,
+so the committed tokens do not depend on the cap.
+
+One upload of row descriptors and job arrays and one read-back of the verification results
+per step are the only host<->device crossings.
+"""
+
+import ctypes
+import time
+
+import numpy as np
+import torch
+
+from . import _lib as L
+from . import copyprop
+
+PURPOSES = list(range(6)) + list(range(8, 24))   # uniform words per job (index = purpose)
+
+
+class Node:
+    __slots__ = ("slot", "pos", "token", "depth", "parent", "kids", "kind", "x1", "x2", "gate", "q1_row",
+                 "q2_row", "child1", "child2", "cands", "copy_kids", "qs_row", "alive")
+
+    def __init__(self, slot, pos, token, parent=None, kind="root"):
+        self.slot, self.pos, self.token = slot, pos, token
+        self.depth = 0
+        self.parent = parent
+        self.kids = []
+        self.kind = kind
+        self.x1, self.x2, self.gate = -1, -1, False
+        self.q1_row = self.q2_row = self.qs_row = -1
+        self.child1 = self.child2 = None
+        self.cands = []          # screened copy candidates (ordered)
+        self.copy_kids = {}      # token -> child
+        self.alive = True
+
+
+class CapacityError(RuntimeError):
+    pass
+
+
+class Decoder:
+    def __init__(self, engine, dec, mode="spec"):
+        """mode: "spec" (pipelined speculative decoding) or "ar" (plain full-depth decoding
+        on the same kernels, proposals off)."""
+        self.e = engine
+        self.cfg = engine.cfg
+        self.dec = dec
+        self.mode = mode
+        self.D = list(self.cfg.readout_depths)
+        self.didx = {r: j for j, r in enumerate(self.D)}
+        self.free_slots = list(range(engine.S - 1, -1, -1))
+        self.free_prob = list(range(engine.prob_rows - 1, -1, -1))
+        self.fin = []
+        self.fin_dev = torch.zeros(engine.S, dtype=torch.int32, device=engine.dev)
+        self.fin_ptr = ctypes.c_void_p(self.fin_dev.data_ptr())
+        self.tokens = []
+        self.records = []
+        self.rows_hist = []
+        self.steps = 0
+
+    # ---- bookkeeping ------------------------------------------------------------------
+    def _slot(self):
+        if not self.free_slots:
+            raise CapacityError("KV slot pool exhausted")
+        return self.free_slots.pop()
+
+    def _prob(self):
+        if not self.free_prob:
+            raise CapacityError("probability row pool exhausted")
+        return self.free_prob.pop()
+
+    def _release_probs(self, n):
+        for attr in ("q1_row", "q2_row", "qs_row"):
+            r = getattr(n, attr)
+            if r >= 0:
+                self.free_prob.append(r)
+                setattr(n, attr, -1)
+
+    def _prune(self, n):
+        """Free n and its whole subtree (slots and probability rows)."""
+        stack = [n]
+        while stack:
+            x = stack.pop()
+            x.alive = False
+            self._release_probs(x)
+            self.free_slots.append(x.slot)
+            stack.extend(x.kids)
+            x.kids = []
+
+    def _fin_append(self, slots):
+        a = len(self.fin)
+        self.fin.extend(slots)
+        src = torch.tensor(np.asarray(slots, np.int32))
+        if self.fin_dev.is_cuda:
+            src = src.pin_memory()
+        self.fin_dev[a:a + len(slots)].copy_(src, non_blocking=True)
+
+    def _path(self, n):
+        p = []
+        x = n.parent
+        while x is not None:
+            p.append(x.slot)
+            x = x.parent
+        return p[::-1]
+
+    def _nodes(self):
+        out, stack = [], [self.root]
+        while stack:
+            x = stack.pop()
+            out.append(x)
+            stack.extend(reversed(x.kids))
+        return out
+
+    def _uniforms(self, pos):
+        return L.philox_uniforms(self.dec.seed_s, pos, PURPOSES)
+
+    @staticmethod
+    def _urow(words):
+        u = np.zeros(L.LS_UNIFORMS_PER_JOB, np.uint32)
+        u[:6] = words[:6]
+        u[8:24] = words[6:22]
+        return u
+
+    # ---- prefill ----------------------------------------------------------------------
+    def prefill(self, prompt, chunk=None):
+        """Run the prompt through P, all R loops and the readouts, then commit the first new
+        token from p_R of the last prompt position.  Not part of the timed decode."""
+        cfg, e = self.cfg, self.e
+        prompt = [int(t) for t in prompt]
+        T0 = len(prompt)
+        chunk = chunk or e.max_rows
+        last_row = -1
+        for c0 in range(0, T0, chunk):
+            toks = prompt[c0:c0 + chunk]
+            n = len(toks)
+            slots = [self._slot() for _ in range(n)]
+            pos = list(range(c0, c0 + n))
+            anc = [slots[:i] for i in range(n)]
+            r0 = e.rows(slots, pos, [0] * n, c0, anc, self.fin_ptr, extra=[np.asarray(toks, np.int32)])
+            e.prelude(r0, r0.extra[0])
+            final = c0 + n == T0
+            for k in range(1, cfg.R + 1):
+                rk = e.rows(slots, pos, [k] * n, c0, anc, self.fin_ptr)
+                e.loop_step(rk)
+                if k in self.didx and (cfg.L_coda or (final and k == cfg.R)):
+                    out_rows = [-1] * n
+                    if final and k == cfg.R:
+                        last_row = self._prob()
+                        out_rows[-1] = last_row
+                    rr = e.rows(slots, pos, [self.didx[k]] * n, c0, anc, self.fin_ptr,
+                                extra=[np.asarray(out_rows, np.int32)])
+                    e.readout(rr, self.dec.greedy, self.dec.T, self.dec.top_p, rr.extra[0])
+            self._fin_append(slots)
+        self.prompt_len = T0
+        self.tokens = list(prompt)
+        job = np.zeros((1, 10), np.int32)
+        job[0, 0], job[0, 1] = L.LS_JOB_SAMPLE, last_row
+        out = e.verify(job, self._urow(self._uniforms(T0))[None, :])
+        self.free_prob.append(last_row)
+        x0 = int(out[0, 0])
+        st = e.sync_status()
+        if st != L.LS_OK:
+            raise L.LoopSpecError(st, "prefill")
+        self.tokens.append(x0)
+        self.records.append({"pos": T0, "token": x0, "outcome": L.LS_OUT_DRAWN, "x1": -1, "gate": False, "x2": -1})
+        self.root = Node(self._slot(), T0, x0)
+        self.pending = [self.root]
+        return x0
+
+    # ---- one pipeline step ------------------------------------------------------------
+    def _spawn(self, parent, token, kind, n_active):
+        if n_active >= self.dec.max_branches or not self.free_slots:
+            return None
+        c = Node(self._slot(), parent.pos + 1, token, parent, kind)
+        parent.kids.append(c)
+        self.pending.append(c)
+        return c
+
+    def step(self):
+        cfg, e, dec = self.cfg, self.e, self.dec
+        R = cfg.R
+        spec = self.mode == "spec"
+        n_fin = len(self.fin)
+        self.steps += 1
+        # 1. prelude of branches spawned last step
+        if self.pending:
+            pn = [x for x in self.pending if x.alive]
+            self.pending = []
+            if pn:
+                rp = e.rows([x.slot for x in pn], [x.pos for x in pn], [0] * len(pn), n_fin,
+                            [self._path(x) for x in pn], self.fin_ptr,
+                            extra=[np.asarray([x.token for x in pn], np.int32)])
+                e.prelude(rp, rp.extra[0])
+        # 2. one loop iteration for every active branch
+        act = [x for x in self._nodes() if x.depth < R]
+        paths = [self._path(x) for x in act]
+        rl = e.rows([x.slot for x in act], [x.pos for x in act], [x.depth + 1 for x in act], n_fin, paths,
+                    self.fin_ptr)
+        e.loop_step(rl)
+        self.rows_hist.append(len(act))
+        for x in act:
+            x.depth += 1
+        # 3. readouts at the depths in D
+        rd = [(x, p) for x, p in zip(act, paths) if x.depth in self.didx]
+        if not rd:
+            return
+        out_rows = []
+        for x, _ in rd:
+            out_rows.append(self._prob())
+        rr = e.rows([x.slot for x, _ in rd], [x.pos for x, _ in rd], [self.didx[x.depth] for x, _ in rd], n_fin,
+                    [p for _, p in rd], self.fin_ptr, extra=[np.asarray(out_rows, np.int32)])
+        e.readout(rr, dec.greedy, dec.T, dec.top_p, rr.extra[0])
+        # 4. verification / draw jobs
+        jobs, us, cands, tags = [], [], [], []
+        tmp_rows = []
+        for (x, _), prow in zip(rd, out_rows):
+            keep_row = False
+            if x.depth == R:
+                j = np.zeros(10, np.int32)
+                if not spec:
+                    j[0], j[1] = L.LS_JOB_SAMPLE, prow
+                elif dec.copy and x.cands:
+                    j[0], j[1], j[7], j[8] = L.LS_JOB_VERIFY_COPY, prow, len(cands), len(x.cands)
+                    cands.extend(x.cands)
+                else:
+                    j[0], j[1], j[2] = L.LS_JOB_VERIFY, prow, x.q1_row
+                    j[3] = x.q2_row if x.gate else -1
+                    j[4], j[5], j[6] = x.x1, x.x2 if x.gate else -1, int(x.gate)
+                jobs.append(j); tags.append(("verify", x)); us.append(self._urow(self._uniforms(x.pos + 1)))
+            elif spec and dec.copy and x.depth == dec.screen_depth:
+                x.qs_row = prow
+                keep_row = True
+                tags.append(("screen", x))
+            elif spec and not dec.copy and x.depth == dec.d1:
+                x.q1_row = prow
+                keep_row = True
+                j = np.zeros(10, np.int32)
+                j[0], j[2] = L.LS_JOB_DRAW1, prow
+                jobs.append(j); tags.append(("draw1", x)); us.append(self._urow(self._uniforms(x.pos + 1)))
+            elif spec and not dec.copy and dec.d2 is not None and x.depth == dec.d2:
+                x.q2_row = prow
+                keep_row = True
+                j = np.zeros(10, np.int32)
+                j[0], j[2], j[3], j[4], j[6] = L.LS_JOB_DRAW2, x.q1_row, prow, x.x1, int(dec.gate)
+                jobs.append(j); tags.append(("draw2", x)); us.append(self._urow(self._uniforms(x.pos + 1)))
+            if not keep_row:
+                tmp_rows.append(prow)
+        # copy-mode screening needs the screened distribution on the host side only for the
+        # threshold test, done below from the device probabilities of the candidates
+        screen = [x for t, x in tags if t == "screen"]
+        if screen:
+            self._screen(screen, jobs, tags, us)
+        res = e.verify(np.asarray(jobs, np.int32).reshape(-1, 10), np.asarray(us, np.uint32).reshape(-1, 24),
+                       np.asarray(cands, np.int32) if cands else None) if jobs else np.zeros((0, 4), np.int32)
+        for r in tmp_rows:
+            self.free_prob.append(r)
+        # 5. host updates: verification first (it decides which subtree survives)
+        results = list(zip([t for t in tags if t[0] != "screen"], res))
+        for (tag, x), o in results:
+            if tag == "verify":
+                self._commit(x, int(o[0]), int(o[1]), int(o[3]))
+        n_active = sum(1 for y in self._nodes() if y.depth < R) + len(self.pending)
+        spawn = []
+        for (tag, x), o in results:
+            if not x.alive:
+                continue
+            if tag == "draw1":
+                x.x1 = int(o[0])
+                spawn.append((-x.depth, 0, x, x.x1, "p1"))
+            elif tag == "draw2":
+                x.gate = bool(o[2])
+                if x.gate:
+                    x.x2 = int(o[0])
+                    spawn.append((-x.depth, 1, x, x.x2, "p2"))
+            elif tag == "drawc":
+                x.x1 = int(o[0])
+                spawn.append((-x.depth, 0, x, x.x1, "p1"))
+        for x in screen:
+            if x.alive:
+                for c in x.cands:
+                    spawn.append((-x.depth, 0, x, c, "copy"))
+        spawn.sort(key=lambda t: (t[0], t[1]))
+        for _, _, x, tok, kind in spawn:
+            c = self._spawn(x, tok, kind, n_active)
+            if c is not None:
+                n_active += 1
+            if kind == "p1":
+                x.child1 = c
+            elif kind == "p2":
+                x.child2 = c
+            elif c is not None:
+                x.copy_kids[tok] = c
+
+    def _screen(self, nodes, jobs, tags, us):
+        """Copy proposals: candidates from the committed prefix plus the branch path, kept
+        when their screened probability reaches tau; nodes without survivors draw one
+        proposal from p_s instead."""
+        rows = [x.qs_row for x in nodes]
+        P = self.e.probs[torch.tensor(rows, device=self.e.dev)].cpu().numpy()
+        for x, p in zip(nodes, P):
+            prefix = self.tokens + [y.token for y in self._ancestors_and_self(x)]
+            cands = copyprop.candidates(prefix, self.dec.copy_max_cands)
+            x.cands = copyprop.screen(cands, p, self.dec.tau)
+            if not x.cands:
+                j = np.zeros(10, np.int32)
+                j[0], j[2] = L.LS_JOB_DRAW1, x.qs_row
+                x.q1_row = x.qs_row
+                x.qs_row = -1
+                jobs.append(j)
+                tags.append(("drawc", x))
+                us.append(self._urow(self._uniforms(x.pos + 1)))
+
+    def _ancestors_and_self(self, x):
+        out = []
+        while x is not None and x is not self.root:
+            out.append(x)
+            x = x.parent
+        out = out[::-1]
+        # the root's token is already committed (it is the last entry of self.tokens)
+        return out
+
+    def _commit(self, root, token, outcome, aux):
+        """The root verified at depth R: commit, re-root onto the accepted child or restart."""
+        assert root is self.root
+        pos = root.pos + 1
+        self.tokens.append(token)
+        self.records.append({"pos": pos, "token": token, "outcome": outcome, "x1": root.x1, "gate": root.gate,
+                             "x2": root.x2 if root.gate else -1, "aux": aux})
+        nxt = None
+        if outcome == L.LS_OUT_ACC1:
+            nxt = root.child1
+        elif outcome == L.LS_OUT_ACC2:
+            nxt = root.child2
+        elif outcome == L.LS_OUT_ACC_COPY:
+            nxt = root.copy_kids.get(token)
+        for k in root.kids:
+            if k is not nxt:
+                self._prune(k)
+        root.kids = []
+        root.alive = False
+        self._release_probs(root)
+        self._fin_append([root.slot])
+        if nxt is None or not nxt.alive:
+            nxt = Node(self._slot(), pos, token)
+            self.pending.append(nxt)
+        nxt.parent = None
+        self.root = nxt
+
+    # ---- full decode ------------------------------------------------------------------
+    def decode(self, n_new):
+        """Steps until n_new tokens (including the one from prefill) are committed."""
+        while len(self.tokens) - self.prompt_len < n_new:
+            self.step()
+        st = self.e.sync_status()
+        if st != L.LS_OK:
+            raise L.LoopSpecError(st, "decode")
+        n = len(self.tokens) - self.prompt_len
+        return self.tokens[self.prompt_len:self.prompt_len + n_new]
+
+    def stats(self):
+        recs = self.records[1:]
+        cnt = lambda o: sum(1 for r in recs if r["outcome"] == o)
+        R, d1 = self.cfg.R, self.dec.d1
+        d2 = self.dec.d2 if self.dec.d2 is not None else R
+        N = len(recs)
+        n1, n2 = cnt(L.LS_OUT_ACC1) + cnt(L.LS_OUT_ACC_COPY), cnt(L.LS_OUT_ACC2)
+        gamma = N * R / max(1, n1 * d1 + n2 * d2 + (N - n1 - n2) * R) if N else 0.0
+        return {"steps": self.steps, "committed": N + 1, "accept1": n1, "accept2": n2,
+                "fallback": cnt(L.LS_OUT_RESAMPLED), "gate_open": sum(1 for r in recs if r["gate"]),
+                "gamma": gamma, "rows_mean": float(np.mean(self.rows_hist)) if self.rows_hist else 0.0,
+                "rows_max": int(max(self.rows_hist)) if self.rows_hist else 0}
+
+
+def generate(engine, prompt, n_new, dec, mode="spec"):
+    """Prefill + decode; returns (tokens, records, stats) with decode-only wall time."""
+    d = Decoder(engine, dec, mode)
+    d.prefill(prompt)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    toks = d.decode(n_new)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st = d.stats()
+    st["decode_seconds"] = dt
+    st["tokens_per_s"] = (n_new - 1) / dt if dt > 0 else 0.0
+    return toks, d.records[:n_new], st

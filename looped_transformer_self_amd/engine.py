@@ -1,0 +1,195 @@
+"""Device-resident model state and thin wrappers over the libloopspec calls.
+
+PyTorch provides device memory and the stream; every computation runs in the HIP kernels
+behind the C ABI.  Holds: weights (uploaded once), the depth-indexed KV caches, the
+slot-indexed hidden states H[S][d], a pool of probability rows, and the workspace.
+"""
+
+import ctypes as C
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
+
+
+class Uploader:
+    """Packs host int32/uint32 arrays into one pinned buffer and ships them with a single
+    host-to-device copy per call.  A ring of buffers guarded by events keeps a pending copy
+    from being overwritten."""
+
+    def __init__(self, dev, words=1 << 20, ring=4):
+        self.dev = dev
+        self.host = [torch.empty(words, dtype=torch.int32, pin_memory=True) for _ in range(ring)]
+        self.devb = [torch.empty(words, dtype=torch.int32, device=dev) for _ in range(ring)]
+        self.events = [None] * ring
+        self.i = 0
+
+    def pack(self, arrays):
+        k = self.i
+        self.i = (self.i + 1) % len(self.host)
+        if self.events[k] is not None:
+            self.events[k].synchronize()
+        offs, total = [], 0
+        for a in arrays:
+            offs.append(total)
+            total += (len(a) + 63) // 64 * 64          # 256-byte alignment per array
+        if total > self.host[k].numel():
+            raise ValueError("upload larger than the staging buffer")
+        hb = self.host[k].numpy()
+        for a, o in zip(arrays, offs):
+            if len(a):
+                hb[o:o + len(a)] = np.asarray(a).view(np.int32) if np.asarray(a).dtype != np.int32 else a
+        self.devb[k][:total].copy_(self.host[k][:total], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.events[k] = ev
+        base = self.devb[k].data_ptr()
+        return [C.c_void_p(base + 4 * o) for o in offs], self.devb[k]
+
+
+class Rows:
+    """An ls_rows descriptor whose arrays live in an uploaded device buffer."""
+
+    def __init__(self, struct, keep):
+        self.s = struct
+        self.keep = keep
+        self.n = struct.n
+
+
+class Engine:
+    def __init__(self, cfg, weights, slot_capacity, max_rows=16, max_keys=None, max_jobs=64, prob_rows=64,
+                 device="cuda"):
+        self.cfg = cfg
+        self.dev = torch.device(device)
+        self.S = int(slot_capacity)
+        self.max_rows = max_rows
+        self.max_keys = int(max_keys or slot_capacity)
+        self.max_jobs = max_jobs
+        self.prob_rows = prob_rows
+        bf16 = cfg.dtype == "bf16"
+        self.wdtype = torch.int16 if bf16 else torch.float32
+
+        def up(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to(self.dev)
+
+        self.w = {"emb": up(weights["emb"]), "g_final": up(weights["g_final"])}
+        self.layers = {}
+        for part in ("pre", "core", "coda"):
+            self.layers[part] = [{k: up(v) for k, v in lw.items()} for lw in weights[part]]
+
+        def lp(lw):
+            return L.ls_layer_ptrs(*[_ptr(lw[k]) for k in ("Wq", "Wk", "Wv", "Wo", "Wg", "Wu", "Wd", "g1", "g2")])
+
+        self._lp = {p: (L.ls_layer_ptrs * max(1, len(v)))(*[lp(x) for x in v]) for p, v in self.layers.items()}
+        wp = L.ls_weight_ptrs(_ptr(self.w["emb"]), _ptr(self.w["g_final"]), self._lp["pre"], self._lp["core"],
+                              self._lp["coda"])
+        desc = L.ls_model_desc()
+        desc.V, desc.d, desc.n_heads, desc.head_dim, desc.F = cfg.V, cfg.d, cfg.n_heads, cfg.head_dim, cfg.F
+        desc.L, desc.L_pre, desc.L_coda, desc.R = cfg.L, cfg.L_pre, cfg.L_coda, cfg.R
+        desc.n_readout = len(cfg.readout_depths)
+        for i, r in enumerate(cfg.readout_depths):
+            desc.readout_depths[i] = r
+        desc.dtype = L.LS_BF16 if bf16 else L.LS_F32
+        desc.rope_theta = cfg.rope_theta
+        desc.norm_eps = cfg.norm_eps
+        desc.slot_capacity = self.S
+        self.desc = desc
+        h = C.c_void_p()
+        L.check(L.lib.ls_model_create(C.byref(desc), C.byref(wp), C.byref(h)), "ls_model_create")
+        self.h = h
+
+        d = cfg.d
+        ent = 2 * d
+        self.kv_core = torch.zeros(cfg.R * cfg.L * self.S * ent, dtype=self.wdtype, device=self.dev)
+        self.kv_pre = (torch.zeros(cfg.L_pre * self.S * ent, dtype=self.wdtype, device=self.dev)
+                       if cfg.L_pre else None)
+        self.kv_coda = (torch.zeros(len(cfg.readout_depths) * cfg.L_coda * self.S * ent, dtype=self.wdtype,
+                                    device=self.dev) if cfg.L_coda else None)
+        self.kv = L.ls_kv(_ptr(self.kv_core), _ptr(self.kv_pre), _ptr(self.kv_coda))
+        self.H = torch.zeros(self.S, d, dtype=torch.float32, device=self.dev)
+        self.probs = torch.zeros(prob_rows, cfg.V, dtype=torch.float32, device=self.dev)
+        nb = L.lib.ls_workspace_bytes(h, max_rows, self.max_keys, max_jobs)
+        self.ws = torch.empty(nb + 256, dtype=torch.uint8, device=self.dev)
+        off = (-self.ws.data_ptr()) % 256
+        self.ws_ptr = C.c_void_p(self.ws.data_ptr() + off)
+        L.check(L.lib.ls_bind_workspace(h, self.ws_ptr, max_rows, self.max_keys, max_jobs, self.stream_ptr()),
+                "ls_bind_workspace")
+        self.up = Uploader(self.dev)
+        self.vout = torch.zeros(max_jobs * 4, dtype=torch.int32, device=self.dev)
+        self.vout_host = torch.zeros(max_jobs * 4, dtype=torch.int32, pin_memory=True)
+
+    def __del__(self):
+        try:
+            if getattr(self, "h", None):
+                L.lib.ls_model_destroy(self.h)
+                self.h = None
+        except Exception:
+            pass
+
+    @staticmethod
+    def stream_ptr():
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    # ---- descriptors -----------------------------------------------------------------
+    def rows(self, slots, pos, depth, n_fin, anc_lists, fin_ptr, extra=()):
+        """Build an ls_rows over uploaded arrays.  anc_lists: per row list of ancestor slots.
+        fin_ptr: device pointer (c_void_p) of the finished-prefix slot table.  `extra` arrays
+        ride along in the same upload; their device pointers are returned too."""
+        n = len(slots)
+        anc_off = np.zeros(n + 1, np.int32)
+        for i, a in enumerate(anc_lists):
+            anc_off[i + 1] = anc_off[i] + len(a)
+        anc = np.concatenate([np.asarray(a, np.int32) for a in anc_lists]) if anc_off[-1] else np.zeros(1, np.int32)
+        ptrs, keep = self.up.pack([np.asarray(slots, np.int32), np.asarray(pos, np.int32),
+                                   np.asarray(depth, np.int32), anc_off, anc, *extra])
+        s = L.ls_rows()
+        s.n, s.n_fin = n, int(n_fin)
+        s.max_anc = int(max((len(a) for a in anc_lists), default=0))
+        s.slot, s.pos, s.depth = ptrs[0], ptrs[1], ptrs[2]
+        s.fin_slots = fin_ptr
+        s.anc_off, s.anc_slots = ptrs[3], ptrs[4]
+        r = Rows(s, keep)
+        r.extra = ptrs[5:]
+        return r
+
+    # ---- calls ---------------------------------------------------------------------------
+    def prelude(self, rows, tokens_ptr):
+        L.check(L.lib.ls_prelude(self.h, C.byref(rows.s), tokens_ptr, _ptr(self.H), C.byref(self.kv),
+                                 self.stream_ptr()), "ls_prelude")
+
+    def loop_step(self, rows):
+        L.check(L.lib.ls_loop_step(self.h, C.byref(rows.s), _ptr(self.H), C.byref(self.kv), self.stream_ptr()),
+                "ls_loop_step")
+
+    def readout(self, rows, greedy, T, top_p, out_rows_ptr, argmax=None, logits=None):
+        smp = L.ls_sampling(int(bool(greedy)), float(T), float(top_p))
+        L.check(L.lib.ls_readout(self.h, C.byref(rows.s), _ptr(self.H), C.byref(smp), _ptr(self.probs),
+                                 out_rows_ptr, self.prob_rows, _ptr(argmax), _ptr(logits), C.byref(self.kv),
+                                 self.stream_ptr()), "ls_readout")
+
+    def verify(self, jobs, uniforms, cands=None):
+        """jobs: int32 array [n][10]; uniforms: uint32 [n][24]; cands: int32 array or None.
+        Returns an int32 numpy array [n][4] (token, outcome, gate, aux) after a stream sync."""
+        n = len(jobs)
+        arrays = [np.ascontiguousarray(jobs, np.int32).ravel(), np.ascontiguousarray(uniforms, np.uint32).ravel()]
+        if cands is not None and len(cands):
+            arrays.append(np.asarray(cands, np.int32))
+        ptrs, keep = self.up.pack(arrays)
+        cptr = ptrs[2] if len(ptrs) > 2 else C.c_void_p(0)
+        ncand = len(cands) if cands is not None else 0
+        L.check(L.lib.ls_verify(self.h, ptrs[0], n, _ptr(self.probs), self.prob_rows, cptr, ncand, ptrs[1],
+                                _ptr(self.vout), self.stream_ptr()), "ls_verify")
+        self.vout_host[:4 * n].copy_(self.vout[:4 * n], non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        return self.vout_host[:4 * n].numpy().reshape(n, 4).copy()
+
+    def sync_status(self):
+        return L.lib.ls_sync_status(self.h, self.stream_ptr())

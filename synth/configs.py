@@ -106,7 +106,8 @@ TINY_V8 = replace(TINY, name="tiny-v8", V=8)
 
 SMALL = {
     "tiny": Workload("tiny", TINY, DecodeCfg(greedy=True, d1=2, max_branches=4, prompt_len=16, new_tokens=24)),
-    "tiny-sample": Workload("tiny-sample", TINY, DecodeCfg(greedy=False, T=1.0, top_p=0.9, d1=2, d2=3,
+    "tiny-sample": Workload("tiny-sample", replace(TINY, readout_depths=(2, 3, 4)),
+                            DecodeCfg(greedy=False, T=1.0, top_p=0.9, d1=2, d2=3,
                                                            max_branches=8, prompt_len=16, new_tokens=24)),
     "mini-ouro": Workload("mini-ouro", MINI_OURO, DecodeCfg(greedy=False, T=1.0, top_p=0.9, d1=2, d2=3,
                                                             max_branches=8, prompt_len=24, new_tokens=24)),

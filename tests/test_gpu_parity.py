@@ -1,0 +1,253 @@
+"""GPU parity of the libloopspec calls against the CPU reference, through the C ABI.
+
+Every input is seeded and synthetic; the reference sees the same inputs, never a value the
+GPU produced.  Tolerances (per-row relative L2): 1e-5 for the fp32 model, 2e-2 for bf16
+models; verification outputs must be bit-identical.
+"""
+
+import ctypes as C
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import philox as ophilox
+from oracle import readout as oreadout
+from oracle import sampler as osampler
+from oracle.model import Model
+from synth import configs, inputs, weights
+from tests.gpu_helpers import as_f64, branch_rows, kv_values, oracle_row_block, rel_l2, to_dev, tol
+
+pytestmark = pytest.mark.gpu
+
+SMALL_CFGS = [configs.TINY, configs.MINI_OURO, configs.MINI_HUGINN]
+
+
+def _engine(cfg, w, S, max_rows=32, max_jobs=256, prob_rows=64):
+    from looped_transformer_self_amd.engine import Engine
+    return Engine(cfg, w, slot_capacity=S, max_rows=max_rows, max_keys=S, max_jobs=max_jobs, prob_rows=prob_rows)
+
+
+def _fill_cache(e, cfg, which, n_blocks, S, seed):
+    vals = kv_values(cfg, n_blocks, S, seed)
+    t = {"core": e.kv_core, "pre": e.kv_pre, "coda": e.kv_coda}[which]
+    t.copy_(to_dev(vals).reshape(-1))
+    return vals
+
+
+def _fin_table(fin, S):
+    t = torch.zeros(S, dtype=torch.int32, device="cuda")
+    if fin:
+        t[:len(fin)] = torch.tensor(fin, dtype=torch.int32, device="cuda")
+    return t
+
+
+@pytest.mark.parametrize("cfg", SMALL_CFGS, ids=lambda c: c.name)
+@pytest.mark.parametrize("M,n_fin", [(5, 300), (20, 37), (1, 0)])
+def test_loop_step_parity(cfg, M, n_fin):
+    print(f"[loop_step] {cfg.name} M={M} n_fin={n_fin}", flush=True)
+    S = 384
+    w = weights.make_weights(cfg, seed=0)
+    e = _engine(cfg, w, S)
+    m = Model(cfg, w)
+    kv = _fill_cache(e, cfg, "core", cfg.R * cfg.L, S, seed=11)
+    H0 = inputs.hidden_rows(S, cfg.d, seed=12)
+    e.H.copy_(torch.from_numpy(H0))
+    rng = np.random.Generator(np.random.PCG64(13 + M))
+    fin, slots, anc, pos, depth = branch_rows(M, n_fin, lambda i: 1 + (i * 3) % cfg.R, rng, S)
+    fin_t = _fin_table(fin, S)
+    rows = e.rows(slots, pos, depth, n_fin, anc, C.c_void_p(fin_t.data_ptr()))
+    e.loop_step(rows)
+    assert e.sync_status() == 0
+    Hg = e.H.cpu().numpy()
+    kvg = e.kv_core.view(cfg.R * cfg.L, S, 2, cfg.d).cpu().numpy()
+    if cfg.dtype == "bf16":
+        kvg = kvg.view(np.uint16)
+    for i in range(M):
+        k = depth[i]
+        blocks = [as_f64(kv[(k - 1) * cfg.L + l], cfg) for l in range(cfg.L)]
+        h_ref, kvs = oracle_row_block(m, m.core, H0[slots[i]][None].astype(np.float64), pos[i], fin + anc[i],
+                                      blocks, cfg)
+        assert rel_l2(Hg[slots[i]], h_ref[0]) <= tol(cfg), (i, rel_l2(Hg[slots[i]], h_ref[0]))
+        for l in range(cfg.L):
+            got = as_f64(kvg[(k - 1) * cfg.L + l, slots[i]], cfg)
+            assert rel_l2(got[0], kvs[l][0]) <= tol(cfg) and rel_l2(got[1], kvs[l][1]) <= tol(cfg), (i, l)
+    # rows not in the step keep their hidden state
+    others = sorted(set(range(S)) - set(slots))
+    assert np.array_equal(Hg[others], H0[others])
+
+
+def _readout_ref(m, cfg, w, h, pos, keys, coda_blocks, j):
+    """Oracle logits of C at readout index j for one hidden row."""
+    hh = h[None].astype(np.float64)
+    if cfg.L_coda:
+        hh, _ = oracle_row_block(m, m.coda, hh, pos, keys, coda_blocks, cfg)
+    a = m.rmsnorm(hh, m.g_final)
+    from oracle.numerics import round_f32, store
+    return round_f32(store(a, cfg.dtype) @ m.emb.T)[0]
+
+
+def _check_dist(pg, lg_ref, greedy, T, top_p, cfg):
+    pr = oreadout.distribution(lg_ref, greedy, T, top_p).astype(np.float64)
+    pg = pg.astype(np.float64)
+    assert abs(pg.sum() - 1) < 1e-5
+    if greedy:
+        top2 = np.sort(lg_ref)[-2:]
+        if top2[1] - top2[0] > 4 * tol(cfg) * np.abs(lg_ref).max():
+            assert np.array_equal(pg, pr)
+        return
+    both = (pg > 0) & (pr > 0)
+    rel = np.abs(pg[both] - pr[both]) / pr[both]
+    assert rel.max() <= (1e-4 if cfg.dtype == "f32" else 0.25), rel.max()
+    diff = np.nonzero((pg > 0) != (pr > 0))[0]
+    if len(diff):
+        p = oreadout.softmax_t(lg_ref, T)
+        order = np.lexsort((np.arange(len(p)), -p))
+        before = np.concatenate([[0.0], np.cumsum(p[order])[:-1]])
+        rank_before = np.empty(len(p)); rank_before[order] = before
+        slack = 1e-5 if cfg.dtype == "f32" else 2e-2
+        assert np.all(np.abs(rank_before[diff] - top_p) <= slack), (len(diff), rank_before[diff])
+
+
+@pytest.mark.parametrize("cfg", SMALL_CFGS, ids=lambda c: c.name)
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_readout_parity(cfg, mode):
+    print(f"[readout] {cfg.name} {mode}", flush=True)
+    S = 300
+    greedy, T, top_p = (True, 1.0, 1.0) if mode == "greedy" else (False, 0.8, 0.9)
+    w = weights.make_weights(cfg, seed=0)
+    e = _engine(cfg, w, S)
+    m = Model(cfg, w)
+    nD = len(cfg.readout_depths)
+    coda = _fill_cache(e, cfg, "coda", nD * cfg.L_coda, S, seed=21) if cfg.L_coda else None
+    H0 = inputs.hidden_rows(S, cfg.d, seed=22)
+    e.H.copy_(torch.from_numpy(H0))
+    M = 7
+    rng = np.random.Generator(np.random.PCG64(23))
+    fin, slots, anc, pos, depth = branch_rows(M, 260, lambda i: i % nD, rng, S)
+    fin_t = _fin_table(fin, S)
+    out_rows = np.arange(M, dtype=np.int32)[::-1].copy()
+    rows = e.rows(slots, pos, depth, 260, anc, C.c_void_p(fin_t.data_ptr()), extra=[out_rows])
+    lg = torch.zeros(M, cfg.V, device="cuda")
+    am = torch.zeros(M, dtype=torch.int32, device="cuda")
+    e.readout(rows, greedy, T, top_p, rows.extra[0], argmax=am, logits=lg)
+    assert e.sync_status() == 0
+    lg, am, pg = lg.cpu().numpy(), am.cpu().numpy(), e.probs.cpu().numpy()
+    for i in range(M):
+        blocks = [as_f64(coda[depth[i] * cfg.L_coda + l], cfg) for l in range(cfg.L_coda)] if cfg.L_coda else []
+        ref = _readout_ref(m, cfg, w, H0[slots[i]], pos[i], fin + anc[i], blocks, depth[i])
+        assert rel_l2(lg[i], ref) <= tol(cfg), (i, rel_l2(lg[i], ref))
+        assert am[i] == int(np.argmax(lg[i]))
+        _check_dist(pg[out_rows[i]], ref, greedy, T, top_p, cfg)
+
+
+def _py(P):
+    return [int(x) for x in P]
+
+
+@pytest.mark.parametrize("V", [37, 1000, 49152])
+def test_verify_bit_exact(V):
+    print(f"[verify] V={V}", flush=True)
+    cfg = replace(configs.TINY, V=V)
+    w = weights.make_weights(replace(cfg, V=16), seed=0)
+    w["emb"] = np.zeros((V, cfg.d), np.float32)
+    e = _engine(cfg, w, S=16, max_jobs=256, prob_rows=48)
+    n_rows = 48
+    P = np.concatenate([inputs.distributions(16, V, 31, sparsity=0.0, peaked=1.0),
+                        inputs.distributions(16, V, 32, sparsity=0.7, peaked=2.0),
+                        inputs.distributions(16, V, 33, sparsity=0.95, peaked=0.5)])
+    # a few one-hot rows (greedy readouts) and an exact copy (q == p)
+    P[3] = 0; P[3, 5 % V] = 1
+    P[4] = 0; P[4, 7 % V] = 1
+    P[5] = P[6]
+    e.probs.copy_(torch.from_numpy(P))
+    fx = [osampler.fixed(p) for p in P]
+    rng = np.random.Generator(np.random.PCG64(34))
+    n_jobs = 200 if V < 10000 else 40
+    jobs = np.zeros((n_jobs, 10), np.int32)
+    us = inputs.uniforms_u32((n_jobs, 24), 35)
+    cands_all = []
+    for k in range(n_jobs):
+        op = k % 5
+        p, q1, q2 = (int(x) for x in rng.integers(0, n_rows, 3))
+        if k % 17 == 0:
+            q1 = p
+        x1 = osampler.sample(fx[q1], int(us[k, 0]))
+        j = jobs[k]
+        j[0], j[1], j[2], j[3], j[4] = op, p, q1, q2, x1
+        if op == 2:
+            j[6] = k % 2
+        if op == 3:
+            g, x2 = osampler.draw2(fx[q1], fx[q2], x1, int(us[k, 1]))
+            j[6], j[5] = int(g), x2
+        if op == 4:
+            nc = int(rng.integers(0, 17))
+            c = rng.choice(V, size=min(nc, V), replace=False).tolist()
+            j[7], j[8] = len(cands_all), len(c)
+            cands_all.extend(c)
+    out = e.verify(jobs, us, np.asarray(cands_all, np.int32) if cands_all else None)
+    assert e.sync_status() == 0
+    for k in range(n_jobs):
+        op, p, q1, q2, x1, x2, g, co, nc = (int(v) for v in jobs[k][:9])
+        u = [int(v) for v in us[k]]
+        if op == 0:
+            want = (osampler.sample(fx[p], u[5]), osampler.DRAWN, 0)
+        elif op == 1:
+            want = (osampler.sample(fx[q1], u[0]), osampler.DRAWN, 0)
+        elif op == 2:
+            gate, t = osampler.draw2(fx[q1], fx[q2], x1, u[1], gated=bool(g))
+            want = (t, osampler.DRAWN, int(gate))
+        elif op == 3:
+            t, o = osampler.verify(fx[p], fx[q1], x1, u[2], u[4], bool(g), fx[q2], x2, u[3])
+            want = (t, o, 0)
+        else:
+            t, o, jj = osampler.verify_copy(fx[p], cands_all[co:co + nc], u[8:8 + nc], u[4])
+            want = (t, o, 0)
+            assert out[k, 3] == jj
+        assert tuple(int(v) for v in out[k, :3]) == want, (k, op, out[k], want)
+
+
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.MINI_HUGINN], ids=lambda c: c.name)
+def test_prelude_parity(cfg):
+    print(f"[prelude] {cfg.name}", flush=True)
+    S = 200
+    w = weights.make_weights(cfg, seed=0)
+    e = _engine(cfg, w, S)
+    m = Model(cfg, w)
+    pre = _fill_cache(e, cfg, "pre", cfg.L_pre, S, seed=41) if cfg.L_pre else None
+    rng = np.random.Generator(np.random.PCG64(42))
+    M = 6
+    fin, slots, anc, pos, depth = branch_rows(M, 150, lambda i: 0, rng, S)
+    toks = rng.integers(0, cfg.V, size=M).astype(np.int32)
+    fin_t = _fin_table(fin, S)
+    rows = e.rows(slots, pos, depth, 150, anc, C.c_void_p(fin_t.data_ptr()), extra=[toks])
+    e.prelude(rows, rows.extra[0])
+    assert e.sync_status() == 0
+    Hg = e.H.cpu().numpy()
+    for i in range(M):
+        h = m.r32(m.emb[toks[i]][None])
+        if cfg.L_pre:
+            h, _ = oracle_row_block(m, m.pre, h, pos[i], fin + anc[i], [as_f64(pre[l], cfg) for l in range(cfg.L_pre)],
+                                    cfg)
+        assert rel_l2(Hg[slots[i]], h[0]) <= tol(cfg)
+
+
+def test_descriptor_errors_are_reported_not_faulted():
+    cfg = configs.TINY
+    S = 64
+    w = weights.make_weights(cfg, seed=0)
+    e = _engine(cfg, w, S)
+    fin_t = _fin_table([], S)
+    from looped_transformer_self_amd import _lib as L
+    # empty call
+    rows = e.rows([], [], [], 0, [], C.c_void_p(fin_t.data_ptr()))
+    e.loop_step(rows)
+    assert e.sync_status() == L.LS_OK
+    # slot out of range and depth out of range are rejected on the device
+    rows = e.rows([S + 5, 3], [0, 0], [1, 9], 0, [[], []], C.c_void_p(fin_t.data_ptr()))
+    e.loop_step(rows)
+    assert e.sync_status() == L.LS_ERR_INVALID
+    # host-side capacity checks
+    with pytest.raises(L.LoopSpecError):
+        e.loop_step(e.rows(list(range(40)), [0] * 40, [1] * 40, 0, [[]] * 40, C.c_void_p(fin_t.data_ptr())))
