@@ -365,6 +365,25 @@ class Decoder:
         nxt.parent = None
         self.root = nxt
 
+    # ---- restart from the prefilled state ----------------------------------------------
+    def snapshot(self):
+        """Host state right after prefill.  Decoding never writes the prompt's slots, so
+        restoring this state replays the same decode on the same device caches."""
+        return {"free_slots": list(self.free_slots), "free_prob": list(self.free_prob), "fin": list(self.fin),
+                "tokens": list(self.tokens), "records": list(self.records), "root": (self.root.slot, self.root.pos,
+                                                                                      self.root.token)}
+
+    def restore(self, snap):
+        self.free_slots = list(snap["free_slots"])
+        self.free_prob = list(snap["free_prob"])
+        self.fin = list(snap["fin"])
+        self.tokens = list(snap["tokens"])
+        self.records = list(snap["records"])
+        self.root = Node(*snap["root"])
+        self.pending = [self.root]
+        self.steps = 0
+        self.rows_hist = []
+
     # ---- full decode ------------------------------------------------------------------
     def decode(self, n_new):
         """Steps until n_new tokens (including the one from prefill) are committed."""

@@ -125,6 +125,7 @@ class Engine:
         self.up = Uploader(self.dev)
         self.vout = torch.zeros(max_jobs * 4, dtype=torch.int32, device=self.dev)
         self.vout_host = torch.zeros(max_jobs * 4, dtype=torch.int32, pin_memory=True)
+        self.prof = None          # list of (start event, end event, row metadata) when profiling
 
     def __del__(self):
         try:
@@ -158,6 +159,7 @@ class Engine:
         s.anc_off, s.anc_slots = ptrs[3], ptrs[4]
         r = Rows(s, keep)
         r.extra = ptrs[5:]
+        r.host = (int(n_fin), list(slots), list(depth), anc_lists)
         return r
 
     # ---- calls ---------------------------------------------------------------------------
@@ -166,8 +168,33 @@ class Engine:
                                  self.stream_ptr()), "ls_prelude")
 
     def loop_step(self, rows):
+        if self.prof is not None and rows.n:
+            b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            b.record()
         L.check(L.lib.ls_loop_step(self.h, C.byref(rows.s), _ptr(self.H), C.byref(self.kv), self.stream_ptr()),
                 "ls_loop_step")
+        if self.prof is not None and rows.n:
+            e.record()
+            self.prof.append((b, e, rows.host))
+
+    def loop_step_bytes(self, host):
+        """Algorithmic HBM bytes of one ls_loop_step: block weights once, the unique KV
+        entries read (distinct (depth, slot) pairs over all rows' keys, for every layer), the
+        KV entries written, and the hidden rows read and written."""
+        cfg = self.cfg
+        n_fin, slots, depth, anc = host
+        es = 2 if cfg.dtype == "bf16" else 4
+        w = cfg.L * (4 * cfg.d * cfg.d + 3 * cfg.F * cfg.d) * es
+        keys = 0
+        for dep in set(depth):
+            extra = set()
+            for s_, d_, a in zip(slots, depth, anc):
+                if d_ == dep:
+                    extra.update(a)
+                    extra.add(s_)
+            keys += n_fin + len(extra)
+        ent = 2 * cfg.d * es
+        return w + keys * cfg.L * ent + len(slots) * cfg.L * ent + 2 * len(slots) * cfg.d * 4
 
     def readout(self, rows, greedy, T, top_p, out_rows_ptr, argmax=None, logits=None):
         smp = L.ls_sampling(int(bool(greedy)), float(T), float(top_p))
