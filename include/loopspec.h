@@ -212,6 +212,12 @@ ls_status ls_verify(ls_model *m, const ls_verify_job *jobs, int n_jobs, const fl
  * (LS_ERR_INVALID for a rejected descriptor) or LS_ERR_HIP for a runtime error. */
 ls_status ls_sync_status(ls_model *m, hipStream_t stream);
 
+/* Diagnostics: while dev_buf is non-NULL, each later layer-kernel launch writes wall-clock
+ * stamps (begin/end of each of the 6 phases, first 4 layers) per workgroup into dev_buf
+ * (device int64 [grid][4][6][2]); grid_out receives the grid size of the last launch.
+ * Pass NULL to stop.  Not needed for decoding. */
+ls_status ls_debug_trace(ls_model *m, long long *dev_buf, int *grid_out);
+
 /* Host-side Philox4x32-10 (Salmon et al., SC'11): word 0 of the block for key
  * (seed mod 2^32, seed >> 32) and counter (pos, purpose, 0, 0).  Fills out[i] for
  * purposes purposes[i]; used by the scheduler to build the uniform rows of ls_verify. */

@@ -20,7 +20,8 @@ LS_JOB_SAMPLE, LS_JOB_DRAW1, LS_JOB_DRAW2, LS_JOB_VERIFY, LS_JOB_VERIFY_COPY = r
 LS_OUT_ACC1, LS_OUT_ACC2, LS_OUT_RESAMPLED, LS_OUT_DRAWN, LS_OUT_ACC_COPY = 1, 2, 3, 4, 5
 
 EXPORTS = ("ls_last_error", "ls_model_create", "ls_model_destroy", "ls_workspace_bytes", "ls_bind_workspace",
-           "ls_prelude", "ls_loop_step", "ls_readout", "ls_verify", "ls_sync_status", "ls_philox_uniforms")
+           "ls_prelude", "ls_loop_step", "ls_readout", "ls_verify", "ls_sync_status", "ls_philox_uniforms",
+           "ls_debug_trace")
 
 
 class ls_model_desc(C.Structure):
@@ -81,6 +82,7 @@ def _load():
                                  C.POINTER(ls_kv), P]),
         "ls_verify": (C.c_int, [P, P, C.c_int, P, C.c_int, P, C.c_int, P, P, P]),
         "ls_sync_status": (C.c_int, [P, P]),
+        "ls_debug_trace": (C.c_int, [P, P, C.POINTER(C.c_int)]),
         "ls_philox_uniforms": (None, [C.c_uint64, C.c_int64, C.POINTER(C.c_int32), C.c_int,
                                       C.POINTER(C.c_uint32)]),
     }

@@ -43,6 +43,49 @@ struct AttnArgs {
 
 constexpr int ATTN_CHUNK = 256;
 
+struct LayerW {
+  const void *Wq, *Wk, *Wv, *Wo, *Wg, *Wu, *Wd;
+  const float *g1, *g2;
+};
+
+// Arguments of the persistent layer kernel (mega.hip).
+struct MegaArgs {
+  int M, d, F, hd, nh, V;
+  int KU;                       // reduction columns per weight unit
+  float theta, eps;
+  const LayerW* layers;         // device table of this call's layers
+  int n_layers;
+  const float* g_final;
+  const void* emb;
+  float* H;                     // working hidden rows H[hidx[m]] (stride d)
+  const int32_t* hidx;          // NULL: row m; negative: rejected row
+  float* Hb;                    // [M][d] second residual buffer
+  const int32_t *slot, *pos, *dep, *fin, *anc_off, *anc, *tokens;
+  int n_fin;
+  int att_chunks;               // 64-key chunks per (row, head)
+  void* kv;                     // cache tensor; block(i, l) = (dep[i] + dep_off) * blk_mul + layer0 + l
+  int dep_off, blk_mul, layer0;
+  long long S;
+  const double* inv_freq;       // rotary frequencies theta^(-2i/hd), i < hd/2
+  float* q;
+  void *o, *act;
+  float* logits;
+  int ldo;
+  float *pq, *po, *pgu, *pdown, *phead, *patt, *ssq;
+  int* cnt;
+  int* err;
+  int init_mode;                // 0 none, 1 embedding rows of tokens, 2 gather Hg[gather[m]]
+  const int32_t* gather;
+  const float* Hg;
+  int do_head;
+  long long* trace;             // optional: per-workgroup phase timestamps (wall clock)
+};
+
+size_t mega_counter_ints(int M, int d, int F, int nh, int V, int KU, int n_layers);
+size_t mega_smem_bytes(bool bf16, int M, int KU);
+int mega_occupancy(bool bf16, int M, int KU);
+hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s);
+
 void launch_gemm(bool bf16, int ep, const GemmArgs& a, hipStream_t s);
 void launch_rmsnorm(bool bf16, const float* H, const int32_t* hidx, int ldh, const float* g, int M, int d,
                     float eps, void* X, hipStream_t s);

@@ -40,6 +40,19 @@ struct ls_model {
   int32_t *slot_ok = nullptr, *dep_ok = nullptr, *row_ok = nullptr;
   void *X = nullptr, *o = nullptr, *act = nullptr;
   float *q = nullptr, *part = nullptr, *hc = nullptr, *logits = nullptr;
+  // persistent-kernel buffers
+  float* Hb = nullptr;
+  double* invf = nullptr;
+  std::vector<double> host_invf;
+  float *patt = nullptr, *ssq = nullptr;
+  int* cnt = nullptr;
+  LayerW *tab_pre = nullptr, *tab_core = nullptr, *tab_coda = nullptr;
+  std::vector<LayerW> host_tab;
+  int KU = 256;
+  int n_cu = 0;
+  int occ[9] = {0};      // resident workgroups per CU, by m-tile count
+  long long* trace = nullptr;   // optional phase timestamps of the next ls_loop_step
+  int last_grid = 0;
   bool bf16() const { return d.dtype == LS_BF16; }
   size_t esz() const { return bf16() ? 2 : 4; }
   size_t entry() const { return (size_t)2 * d.d * esz(); }   // bytes of one KV entry
@@ -49,7 +62,8 @@ namespace {
 
 struct Carve {
   int max_rows, max_keys, max_jobs, max_chunks;
-  size_t off_err, off_slot, off_dep, off_row, off_X, off_q, off_o, off_act, off_part, off_hc, off_logits, total;
+  size_t off_err, off_slot, off_dep, off_row, off_X, off_q, off_o, off_act, off_part, off_hc, off_logits;
+  size_t off_Hb, off_pq, off_po, off_pgu, off_pdown, off_phead, off_invf, off_patt, off_ssq, off_cnt, off_tab, total;
 };
 
 Carve carve(const ls_model* m, int max_rows, int max_keys, int max_jobs) {
@@ -73,6 +87,21 @@ Carve carve(const ls_model* m, int max_rows, int max_keys, int max_jobs) {
   c.off_part = take(R * d.n_heads * (size_t)c.max_chunks * (d.head_dim + 2) * 4);
   c.off_hc = take(R * d.d * 4);
   c.off_logits = take(R * (size_t)d.V * 4);
+  // persistent kernel: partial tiles of every K split, attention chunk partials, per-tile
+  // sums of squares, dependency counters, device layer tables
+  const int KU = d.dtype == LS_BF16 ? 256 : 128;
+  const size_t nksD = (d.d + KU - 1) / KU, nksF = (d.F + KU - 1) / KU;
+  const size_t RH = std::min<size_t>(R, 16);           // readouts run in chunks of <= 16 rows
+  const int nl = std::max(d.L, std::max(d.L_pre, d.L_coda));
+  const size_t att_chunks = (max_keys + 63) / 64;
+  (void)nksD; (void)nksF; (void)RH;
+  c.off_Hb = take(R * d.d * 4);
+  c.off_pq = c.off_po = c.off_pgu = c.off_pdown = c.off_phead = 0;
+  c.off_invf = take((size_t)d.head_dim / 2 * 8);
+  c.off_patt = take(R * d.n_heads * att_chunks * (d.head_dim + 2) * 4);
+  c.off_ssq = take((size_t)nl * 2 * (d.d / 16) * R * 4);
+  c.off_cnt = take(mega_counter_ints(max_rows, d.d, d.F, d.n_heads, d.V, KU, nl) * 4);
+  c.off_tab = take((size_t)(d.L + d.L_pre + d.L_coda) * sizeof(LayerW));
   c.total = off;
   return c;
 }
@@ -210,9 +239,90 @@ ls_status ls_bind_workspace(ls_model* m, void* ws, int max_rows, int max_keys, i
   m->part = (float*)(b + c.off_part);
   m->hc = (float*)(b + c.off_hc);
   m->logits = (float*)(b + c.off_logits);
+  m->Hb = (float*)(b + c.off_Hb);
+  m->invf = (double*)(b + c.off_invf);
+  m->patt = (float*)(b + c.off_patt);
+  m->ssq = (float*)(b + c.off_ssq);
+  m->cnt = (int*)(b + c.off_cnt);
+  m->KU = m->bf16() ? 256 : 128;
+  LayerW* tab = (LayerW*)(b + c.off_tab);
+  m->host_tab.clear();
+  auto add = [&](const std::vector<ls_layer_ptrs>& v) {
+    for (const auto& p : v) m->host_tab.push_back(LayerW{p.Wq, p.Wk, p.Wv, p.Wo, p.Wg, p.Wu, p.Wd, p.g1, p.g2});
+  };
+  add(m->pre); add(m->core); add(m->coda);
+  m->tab_pre = tab;
+  m->tab_core = tab + m->pre.size();
+  m->tab_coda = tab + m->pre.size() + m->core.size();
+  m->host_invf.resize(m->d.head_dim / 2);
+  for (int i = 0; i < m->d.head_dim / 2; ++i)
+    m->host_invf[i] = std::pow((double)m->d.rope_theta, -2.0 * (double)i / (double)m->d.head_dim);
+  {
+    hipError_t e = hipMemcpyAsync(m->invf, m->host_invf.data(), m->host_invf.size() * sizeof(double),
+                                  hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return fail(LS_ERR_HIP, "ls_bind_workspace: rotary table upload: %s", hipGetErrorString(e));
+  }
+  if (!m->host_tab.empty()) {
+    hipError_t e = hipMemcpyAsync(tab, m->host_tab.data(), m->host_tab.size() * sizeof(LayerW), hipMemcpyHostToDevice,
+                                  stream);
+    if (e != hipSuccess) return fail(LS_ERR_HIP, "ls_bind_workspace: layer table upload: %s", hipGetErrorString(e));
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(LS_ERR_HIP, "ls_bind_workspace: %s", hipGetErrorString(e));
+  }
+  int dev = 0;
+  hipGetDevice(&dev);
+  hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  for (int& o : m->occ) o = 0;
   launch_fill_i32(m->err, 1, 0, stream);
   return check_hip("ls_bind_workspace");
 }
+
+}  // extern "C"
+
+namespace {
+
+// One launch of the persistent layer kernel over rows [i0, i0 + mc) of `r`.
+ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, const int32_t* hidx, const LayerW* tab,
+                   int n_layers, void* kv, const int32_t* dep, int dep_off, int blk_mul, int init_mode,
+                   const int32_t* tokens, const int32_t* gather, const float* Hg, float* logits, hipStream_t s) {
+  const ls_model_desc& d = m->d;
+  MegaArgs a{};
+  a.M = mc; a.d = d.d; a.F = d.F; a.hd = d.head_dim; a.nh = d.n_heads; a.V = d.V; a.KU = m->KU;
+  a.theta = d.rope_theta; a.eps = d.norm_eps;
+  a.layers = tab; a.n_layers = n_layers;
+  a.g_final = m->g_final; a.emb = m->emb;
+  a.H = H; a.hidx = hidx ? hidx + i0 : nullptr; a.Hb = m->Hb;
+  a.slot = m->slot_ok + i0; a.pos = r->pos + i0; a.dep = dep ? dep + i0 : nullptr;
+  a.fin = r->fin_slots; a.anc_off = r->anc_off + i0; a.anc = r->anc_slots;
+  a.tokens = tokens ? tokens + i0 : nullptr;
+  a.n_fin = r->n_fin;
+  a.att_chunks = (r->n_fin + r->max_anc + 1 + 63) / 64;
+  a.kv = kv; a.dep_off = dep_off; a.blk_mul = blk_mul; a.layer0 = 0; a.S = d.slot_capacity;
+  a.q = m->q; a.o = m->o; a.act = m->act;
+  a.logits = logits; a.ldo = d.V;
+  a.inv_freq = m->invf;
+  a.patt = m->patt; a.ssq = m->ssq;
+  a.cnt = m->cnt; a.err = m->err;
+  a.init_mode = init_mode; a.gather = gather ? gather + i0 : nullptr; a.Hg = Hg;
+  a.do_head = logits != nullptr;
+  const int mt = (mc + 15) / 16;
+  int& occ = m->occ[mt];
+  if (!occ) {
+    occ = mega_occupancy(m->bf16(), 16 * mt, m->KU);
+    if (occ <= 0) return fail(LS_ERR_HIP, "persistent kernel: no resident workgroup fits (M=%d)", mc);
+    occ = std::min(occ, 4);
+  }
+  const int G = occ * m->n_cu;
+  a.trace = m->trace;
+  m->last_grid = G;
+  hipError_t e = launch_mega(m->bf16(), a, G, s);
+  if (e != hipSuccess) return fail(LS_ERR_HIP, "persistent kernel launch: %s", hipGetErrorString(e));
+  return LS_OK;
+}
+
+}  // namespace
+
+extern "C" {
 
 ls_status ls_prelude(ls_model* m, const ls_rows* r, const int32_t* tokens, float* H, const ls_kv* kv, hipStream_t s) {
   ls_status st = check_rows(m, r, "ls_prelude");
@@ -223,11 +333,9 @@ ls_status ls_prelude(ls_model* m, const ls_rows* r, const int32_t* tokens, float
   const ls_model_desc& d = m->d;
   launch_validate(r->n, r->slot, nullptr, 0, 0, r->pos, r->anc_off, r->n_fin, r->max_anc, d.slot_capacity, m->slot_ok,
                   m->dep_ok, m->row_ok, m->err, s);
-  launch_embed(m->bf16(), m->emb, tokens, m->slot_ok, r->n, d.V, d.d, d.slot_capacity, H, m->err, s);
-  for (int l = 0; l < d.L_pre; ++l) {
-    KvSel kvs{kv->pre, nullptr, 0, 0, l, d.slot_capacity};
-    run_layer(m, m->pre[l], H, m->slot_ok, r, kvs, s);
-  }
+  st = run_mega(m, r, 0, r->n, H, m->slot_ok, m->tab_pre, d.L_pre, kv->pre, nullptr, 0, 0, 1, tokens, nullptr, nullptr,
+                nullptr, s);
+  if (st) return st;
   return check_hip("ls_prelude");
 }
 
@@ -240,10 +348,9 @@ ls_status ls_loop_step(ls_model* m, const ls_rows* r, float* H, const ls_kv* kv,
   const ls_model_desc& d = m->d;
   launch_validate(r->n, r->slot, r->depth, 1, d.R, r->pos, r->anc_off, r->n_fin, r->max_anc, d.slot_capacity,
                   m->slot_ok, m->dep_ok, m->row_ok, m->err, s);
-  for (int l = 0; l < d.L; ++l) {
-    KvSel kvs{kv->core, m->dep_ok, -1, d.L, l, d.slot_capacity};
-    run_layer(m, m->core[l], H, m->slot_ok, r, kvs, s);
-  }
+  st = run_mega(m, r, 0, r->n, H, m->slot_ok, m->tab_core, d.L, kv->core, m->dep_ok, -1, d.L, 0, nullptr, nullptr,
+                nullptr, nullptr, s);
+  if (st) return st;
   return check_hip("ls_loop_step");
 }
 
@@ -262,21 +369,17 @@ ls_status ls_readout(ls_model* m, const ls_rows* r, const float* H, const ls_sam
   const ls_model_desc& d = m->d;
   launch_validate(r->n, r->slot, r->depth, 0, d.n_readout - 1, r->pos, r->anc_off, r->n_fin, r->max_anc,
                   d.slot_capacity, m->slot_ok, m->dep_ok, m->row_ok, m->err, s);
-  const bool b = m->bf16();
-  if (d.L_coda) {
-    launch_gather(H, m->slot_ok, r->n, d.d, d.slot_capacity, m->hc, m->err, s);
-    for (int l = 0; l < d.L_coda; ++l) {
-      KvSel kvs{kv->coda, m->dep_ok, 0, d.L_coda, l, d.slot_capacity};
-      run_layer(m, m->coda[l], m->hc, m->row_ok, r, kvs, s);
-    }
-    launch_rmsnorm(b, m->hc, m->row_ok, d.d, m->g_final, r->n, d.d, d.norm_eps, m->X, s);
-  } else {
-    launch_rmsnorm(b, H, m->slot_ok, d.d, m->g_final, r->n, d.d, d.norm_eps, m->X, s);
-  }
   float* lg = logits ? logits : m->logits;
-  GemmArgs g{};
-  g.M = r->n; g.W0 = m->emb; g.N = d.V; g.K = d.d; g.X = m->X; g.out = lg; g.ldo = d.V; g.err = m->err;
-  launch_gemm(b, EP_STORE, g, s);
+  for (int i0 = 0; i0 < r->n; i0 += 16) {
+    const int mc = std::min(16, r->n - i0);
+    if (d.L_coda)
+      st = run_mega(m, r, i0, mc, m->hc, m->row_ok, m->tab_coda, d.L_coda, kv->coda, m->dep_ok, 0, d.L_coda, 2,
+                    nullptr, m->slot_ok, H, lg + (size_t)i0 * d.V, s);
+    else
+      st = run_mega(m, r, i0, mc, (float*)H, m->slot_ok, nullptr, 0, nullptr, nullptr, 0, 0, 0, nullptr, nullptr,
+                    nullptr, lg + (size_t)i0 * d.V, s);
+    if (st) return st;
+  }
   launch_dist(lg, r->n, d.V, smp->greedy, smp->temperature, smp->top_p, probs, out_rows, n_prob_rows, argmax, m->err, s);
   return check_hip("ls_readout");
 }
@@ -300,7 +403,15 @@ ls_status ls_sync_status(ls_model* m, hipStream_t s) {
   int h = 0;
   e = hipMemcpy(&h, m->err, sizeof(int), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(LS_ERR_HIP, "error word: %s", hipGetErrorString(e));
+  if (h == 5) return fail(LS_ERR_HIP, "a device-side dependency wait timed out (error word 5)");
   if (h) return fail((ls_status)h, "a kernel rejected a descriptor (device error word %d)", h);
+  return LS_OK;
+}
+
+ls_status ls_debug_trace(ls_model* m, long long* dev_buf, int* grid_out) {
+  if (!m) return fail(LS_ERR_INVALID, "ls_debug_trace: null model");
+  m->trace = dev_buf;
+  if (grid_out) *grid_out = m->last_grid;
   return LS_OK;
 }
 
