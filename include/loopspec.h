@@ -213,8 +213,9 @@ ls_status ls_verify(ls_model *m, const ls_verify_job *jobs, int n_jobs, const fl
 ls_status ls_sync_status(ls_model *m, hipStream_t stream);
 
 /* Diagnostics: while dev_buf is non-NULL, each later layer-kernel launch writes wall-clock
- * stamps (begin/end of each of the 6 phases, first 4 layers) per workgroup into dev_buf
- * (device int64 [grid][4][6][2]); grid_out receives the grid size of the last launch.
+ * stamps (phase begin/end, dependency met, first chunk staged, first tile batch multiplied,
+ * first/last weight slab issued; first 4 layers) per workgroup into dev_buf (device int64
+ * [grid][4][8][8]); grid_out receives the grid size of the last launch.
  * Pass NULL to stop.  Not needed for decoding. */
 ls_status ls_debug_trace(ls_model *m, long long *dev_buf, int *grid_out);
 

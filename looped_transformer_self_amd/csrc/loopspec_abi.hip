@@ -35,20 +35,21 @@ struct ls_model {
   std::vector<ls_layer_ptrs> pre, core, coda;
   // bound workspace
   char* ws = nullptr;
-  int max_rows = 0, max_keys = 0, max_jobs = 0, max_chunks = 0;
+  int max_rows = 0, max_keys = 0, max_jobs = 0;
   int* err = nullptr;
   int32_t *slot_ok = nullptr, *dep_ok = nullptr, *row_ok = nullptr;
-  void *X = nullptr, *o = nullptr, *act = nullptr;
-  float *q = nullptr, *part = nullptr, *hc = nullptr, *logits = nullptr;
-  // persistent-kernel buffers
-  float* Hb = nullptr;
+  float *q = nullptr, *hc = nullptr, *logits = nullptr;
+  // persistent-kernel buffers: per-layer activations, rotary tables, attention partials,
+  // per-tile sums of squares, dependency counters
+  float *Xs = nullptr, *Ys = nullptr;
+  void *o = nullptr, *act = nullptr;
   double* invf = nullptr;
+  float* rope = nullptr;
   std::vector<double> host_invf;
   float *patt = nullptr, *ssq = nullptr;
   int* cnt = nullptr;
   LayerW *tab_pre = nullptr, *tab_core = nullptr, *tab_coda = nullptr;
   std::vector<LayerW> host_tab;
-  int KU = 256;
   int n_cu = 0;
   int occ[9] = {0};      // resident workgroups per CU, by m-tile count
   long long* trace = nullptr;   // optional phase timestamps of the next ls_loop_step
@@ -61,46 +62,44 @@ struct ls_model {
 namespace {
 
 struct Carve {
-  int max_rows, max_keys, max_jobs, max_chunks;
-  size_t off_err, off_slot, off_dep, off_row, off_X, off_q, off_o, off_act, off_part, off_hc, off_logits;
-  size_t off_Hb, off_pq, off_po, off_pgu, off_pdown, off_phead, off_invf, off_patt, off_ssq, off_cnt, off_tab, total;
+  int max_rows, max_keys, max_jobs;
+  size_t off_err, off_slot, off_dep, off_row, off_q, off_o, off_act, off_hc, off_logits;
+  size_t off_Xs, off_Ys, off_invf, off_rope, off_patt, off_ssq, off_cnt, off_tab, total;
 };
+
+// Elements of one layer's slice of a per-layer activation buffer: rows x width, rounded up so
+// that slices of different layers never share a 256-byte span (and hence a cache line).
+size_t layer_slice(size_t rows, size_t width) { return (rows * width + 127) / 128 * 128; }
 
 Carve carve(const ls_model* m, int max_rows, int max_keys, int max_jobs) {
   Carve c{};
   c.max_rows = max_rows;
   c.max_keys = max_keys;
   c.max_jobs = max_jobs;
-  c.max_chunks = (max_keys + ATTN_CHUNK - 1) / ATTN_CHUNK;
   const ls_model_desc& d = m->d;
   const size_t R = (size_t)max_rows;
+  const size_t es = d.dtype == LS_BF16 ? 2 : 4;
+  const size_t nl = (size_t)std::max(d.L, std::max(d.L_pre, d.L_coda));   // most layers in one launch
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   c.off_err = take(256);
   c.off_slot = take(R * 4);
   c.off_dep = take(R * 4);
   c.off_row = take(R * 4);
-  c.off_X = take(R * (size_t)std::max(d.d, d.F) * 4);
   c.off_q = take(R * d.d * 4);
-  c.off_o = take(R * d.d * 4);
-  c.off_act = take(R * d.F * 4);
-  c.off_part = take(R * d.n_heads * (size_t)c.max_chunks * (d.head_dim + 2) * 4);
   c.off_hc = take(R * d.d * 4);
   c.off_logits = take(R * (size_t)d.V * 4);
-  // persistent kernel: partial tiles of every K split, attention chunk partials, per-tile
-  // sums of squares, dependency counters, device layer tables
-  const int KU = d.dtype == LS_BF16 ? 256 : 128;
-  const size_t nksD = (d.d + KU - 1) / KU, nksF = (d.F + KU - 1) / KU;
-  const size_t RH = std::min<size_t>(R, 16);           // readouts run in chunks of <= 16 rows
-  const int nl = std::max(d.L, std::max(d.L_pre, d.L_coda));
-  const size_t att_chunks = (max_keys + 63) / 64;
-  (void)nksD; (void)nksF; (void)RH;
-  c.off_Hb = take(R * d.d * 4);
-  c.off_pq = c.off_po = c.off_pgu = c.off_pdown = c.off_phead = 0;
+  // per-layer activations of one launch (each written once per launch)
+  c.off_Xs = take((nl + 1) * layer_slice(R, d.d) * 4);
+  c.off_Ys = take(nl * layer_slice(R, d.d) * 4);
+  c.off_o = take(nl * layer_slice(R, d.d) * es);
+  c.off_act = take(nl * layer_slice(R, d.F) * es);
   c.off_invf = take((size_t)d.head_dim / 2 * 8);
+  c.off_rope = take(R * (size_t)d.head_dim * 4);
+  const size_t att_chunks = (max_keys + 63) / 64;
   c.off_patt = take(R * d.n_heads * att_chunks * (d.head_dim + 2) * 4);
-  c.off_ssq = take((size_t)nl * 2 * (d.d / 16) * R * 4);
-  c.off_cnt = take(mega_counter_ints(max_rows, d.d, d.F, d.n_heads, d.V, KU, nl) * 4);
+  c.off_ssq = take(nl * 2 * (d.d / 16) * R * 4);
+  c.off_cnt = take(mega_counter_ints(max_rows, d.d, d.F, d.n_heads, (int)nl) * 4);
   c.off_tab = take((size_t)(d.L + d.L_pre + d.L_coda) * sizeof(LayerW));
   c.total = off;
   return c;
@@ -124,48 +123,6 @@ ls_status check_rows(const ls_model* m, const ls_rows* r, const char* who) {
   if (r->n_fin > 0 && !r->fin_slots) return fail(LS_ERR_INVALID, "%s: null fin_slots", who);
   if (r->max_anc > 0 && !r->anc_slots) return fail(LS_ERR_INVALID, "%s: null anc_slots", who);
   return LS_OK;
-}
-
-// One transformer layer (pre-norm attention + SwiGLU MLP) on the rows' hidden states.
-void run_layer(ls_model* m, const ls_layer_ptrs& lw, float* H, const int32_t* hidx, const ls_rows* r, KvSel kv,
-               hipStream_t s) {
-  const ls_model_desc& d = m->d;
-  const bool b = m->bf16();
-  const int n = r->n;
-  launch_rmsnorm(b, H, hidx, d.d, lw.g1, n, d.d, d.norm_eps, m->X, s);
-
-  GemmArgs g{};
-  g.M = n;
-  g.d = d.d;
-  g.hd = d.head_dim;
-  g.theta = d.rope_theta;
-  g.err = m->err;
-  // q, k, v with rotary embedding; k, v into the KV slot of the row
-  g.W0 = lw.Wq; g.W1 = lw.Wk; g.W2 = lw.Wv;
-  g.N = d.d; g.K = d.d; g.X = m->X;
-  g.q = m->q; g.kv = kv; g.slot = m->slot_ok; g.pos = r->pos;
-  launch_gemm(b, EP_QKV, g, s);
-
-  AttnArgs a{};
-  a.q = m->q; a.kv = kv; a.slot = m->slot_ok; a.pos = r->pos; a.fin = r->fin_slots;
-  a.anc_off = r->anc_off; a.anc = r->anc_slots; a.n_fin = r->n_fin; a.M = n; a.d = d.d;
-  a.n_heads = d.n_heads; a.hd = d.head_dim; a.part = m->part; a.max_chunks = m->max_chunks;
-  a.grid_chunks = (r->n_fin + r->max_anc + 1 + ATTN_CHUNK - 1) / ATTN_CHUNK;
-  a.o = m->o; a.err = m->err;
-  launch_attention(b, a, s);
-
-  GemmArgs go{};
-  go.M = n; go.W0 = lw.Wo; go.N = d.d; go.K = d.d; go.X = m->o; go.H = H; go.hidx = hidx; go.ldh = d.d; go.err = m->err;
-  launch_gemm(b, EP_RESID, go, s);
-
-  launch_rmsnorm(b, H, hidx, d.d, lw.g2, n, d.d, d.norm_eps, m->X, s);
-  GemmArgs gu{};
-  gu.M = n; gu.W0 = lw.Wg; gu.W1 = lw.Wu; gu.K = d.d; gu.X = m->X; gu.act = m->act; gu.F = d.F; gu.err = m->err;
-  launch_gemm(b, EP_SWIGLU, gu, s);
-
-  GemmArgs gd{};
-  gd.M = n; gd.W0 = lw.Wd; gd.N = d.d; gd.K = d.F; gd.X = m->act; gd.H = H; gd.hidx = hidx; gd.ldh = d.d; gd.err = m->err;
-  launch_gemm(b, EP_RESID, gd, s);
 }
 
 }  // namespace
@@ -227,24 +184,23 @@ ls_status ls_bind_workspace(ls_model* m, void* ws, int max_rows, int max_keys, i
   const Carve c = carve(m, max_rows, max_keys, max_jobs);
   char* b = (char*)ws;
   m->ws = b;
-  m->max_rows = max_rows; m->max_keys = max_keys; m->max_jobs = max_jobs; m->max_chunks = c.max_chunks;
+  m->max_rows = max_rows; m->max_keys = max_keys; m->max_jobs = max_jobs;
   m->err = (int*)(b + c.off_err);
   m->slot_ok = (int32_t*)(b + c.off_slot);
   m->dep_ok = (int32_t*)(b + c.off_dep);
   m->row_ok = (int32_t*)(b + c.off_row);
-  m->X = b + c.off_X;
   m->q = (float*)(b + c.off_q);
-  m->o = b + c.off_o;
-  m->act = b + c.off_act;
-  m->part = (float*)(b + c.off_part);
   m->hc = (float*)(b + c.off_hc);
   m->logits = (float*)(b + c.off_logits);
-  m->Hb = (float*)(b + c.off_Hb);
+  m->Xs = (float*)(b + c.off_Xs);
+  m->Ys = (float*)(b + c.off_Ys);
+  m->o = b + c.off_o;
+  m->act = b + c.off_act;
   m->invf = (double*)(b + c.off_invf);
+  m->rope = (float*)(b + c.off_rope);
   m->patt = (float*)(b + c.off_patt);
   m->ssq = (float*)(b + c.off_ssq);
   m->cnt = (int*)(b + c.off_cnt);
-  m->KU = m->bf16() ? 256 : 128;
   LayerW* tab = (LayerW*)(b + c.off_tab);
   m->host_tab.clear();
   auto add = [&](const std::vector<ls_layer_ptrs>& v) {
@@ -287,11 +243,11 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
                    const int32_t* tokens, const int32_t* gather, const float* Hg, float* logits, hipStream_t s) {
   const ls_model_desc& d = m->d;
   MegaArgs a{};
-  a.M = mc; a.d = d.d; a.F = d.F; a.hd = d.head_dim; a.nh = d.n_heads; a.V = d.V; a.KU = m->KU;
+  a.M = mc; a.d = d.d; a.F = d.F; a.hd = d.head_dim; a.nh = d.n_heads; a.V = d.V;
   a.theta = d.rope_theta; a.eps = d.norm_eps;
   a.layers = tab; a.n_layers = n_layers;
   a.g_final = m->g_final; a.emb = m->emb;
-  a.H = H; a.hidx = hidx ? hidx + i0 : nullptr; a.Hb = m->Hb;
+  a.H = H; a.hidx = hidx ? hidx + i0 : nullptr; a.Xs = m->Xs; a.Ys = m->Ys;
   a.slot = m->slot_ok + i0; a.pos = r->pos + i0; a.dep = dep ? dep + i0 : nullptr;
   a.fin = r->fin_slots; a.anc_off = r->anc_off + i0; a.anc = r->anc_slots;
   a.tokens = tokens ? tokens + i0 : nullptr;
@@ -301,6 +257,7 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
   a.q = m->q; a.o = m->o; a.act = m->act;
   a.logits = logits; a.ldo = d.V;
   a.inv_freq = m->invf;
+  a.rope = m->rope;
   a.patt = m->patt; a.ssq = m->ssq;
   a.cnt = m->cnt; a.err = m->err;
   a.init_mode = init_mode; a.gather = gather ? gather + i0 : nullptr; a.Hg = Hg;
@@ -308,7 +265,7 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
   const int mt = (mc + 15) / 16;
   int& occ = m->occ[mt];
   if (!occ) {
-    occ = mega_occupancy(m->bf16(), 16 * mt, m->KU);
+    occ = mega_occupancy(m->bf16(), 16 * mt, d.d);
     if (occ <= 0) return fail(LS_ERR_HIP, "persistent kernel: no resident workgroup fits (M=%d)", mc);
     occ = std::min(occ, 4);
   }

@@ -49,6 +49,34 @@ LS_DEV unsigned long long ldc64(const void* p) {
   return __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16-byte coherent loads through a buffer descriptor: the SC1 cache-policy bit makes them the
+// same agent-coherent access as the atomic loads above, four words at a time.  A descriptor
+// covers n_bytes from base; the hardware range check returns zeros beyond it, so ragged row
+// ends and absent rows (n_bytes = 0) need no branches.
+constexpr int CPOL_SC1 = 16;
+LS_DEV __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int n_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n_bytes, 0x00020000);
+}
+LS_DEV u32x4_t ldc128(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CPOL_SC1);
+}
+// Plain (cached) 16-byte load.  Used for activations that every workgroup reads: each is
+// written exactly once per launch (per-layer buffers) and read only after its producers'
+// counters, so no cache can hold an older copy of it, and the workgroups of one XCD share
+// one L2 fill instead of each going to memory.
+LS_DEV u32x4_t ld128(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+// Per-layer activation buffers of one launch (rows m < M):
+//   layer input   l == 0: H[hidx[m]] (the caller's hidden rows), l > 0: Xs[l][m]
+//   after attention residual: Ys[l][m];  attention output o[l][m];  SwiGLU output act[l][m]
+// The last layer's output goes to H[hidx[m]] and, when the LM head follows, to Xs[n_layers].
+LS_DEV const float* layer_in(const MegaArgs& a, int l) { return l == 0 ? a.H : a.Xs + (size_t)l * a.M * a.d; }
+LS_DEV float* ys_of(const MegaArgs& a, int l) { return a.Ys + (size_t)l * a.M * a.d; }
+template <typename T> LS_DEV T* o_of(const MegaArgs& a, int l) { return (T*)a.o + (size_t)l * a.M * a.d; }
+template <typename T> LS_DEV T* act_of(const MegaArgs& a, int l) { return (T*)a.act + (size_t)l * a.M * a.F; }
+
 template <typename T> struct Coh;
 template <> struct Coh<uint16_t> {
   LS_DEV static void store(uint16_t* p, float v) { stc(p, f2bf(v)); }
@@ -100,6 +128,23 @@ LS_DEV void wait_ge(const int* c, int target, ConsBar& cb) {
   cb.sync();
 }
 
+// Consumer-side wait until base[i * stride] >= target for all i < n (n <= 64): lanes of the
+// first consumer wave poll one counter each, so n counters cost one round trip, not n.
+LS_DEV void wait_all_ge(const int* base, int stride, int n, int target, ConsBar& cb) {
+  if (threadIdx.x < 64) {
+    const int i = threadIdx.x;
+    int n_polls = 0;
+    bool done = i >= n;
+    while (true) {
+      if (!done) done = ld_acq(base + (size_t)i * stride) >= target;
+      if (__all(done)) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++n_polls > SPIN_LIMIT) { if (i == 0) ls_flag(cb.err, LS_TIMEOUT); break; }
+    }
+  }
+  cb.sync();
+}
+
 // ---- counter layout -----------------------------------------------------------------------------
 struct CntLayout {
   int per_layer, nchF;
@@ -124,40 +169,41 @@ __host__ __device__ inline CntLayout cnt_layout(int M, int F, int nh, int XC, in
   return c;
 }
 
-// LDS plan by row count and element size: ring depth, activation columns staged per chunk
-// (a multiple of every slab width), and single/double buffering of the tile reduction.
+// LDS plan by row count, element size and width d: ring depth, activation columns staged per
+// chunk (a multiple of every slab width; the whole row when it fits, so the normalised phases
+// need one staging pass) and how many tiles' partials the reduction holds at once.
 struct LdsPlan {
   int NS, XC, nred;
 };
+constexpr int LDS_BUDGET = 160 * 1024 - 512;
 __host__ __device__ inline size_t lds_bytes_for(int M, int esz, int NS, int XC, int nred) {
   size_t off = (size_t)NS * SLAB;
   off = (off + (size_t)M * (XC + 16 / esz) * esz + 15) & ~(size_t)15;
   off = (off + (size_t)nred * NCONS * M * 16 * 4 + 15) & ~(size_t)15;
   off = (off + (size_t)M * 4 + 15) & ~(size_t)15;
   off = (off + (4 * 128 + 64) * 4 + 15) & ~(size_t)15;
+  off = (off + (size_t)M * 4 + 15) & ~(size_t)15;
   off += (2 * NS + 8) * 4;
   return off;
 }
-__host__ __device__ inline LdsPlan lds_plan(int M, int esz) {
-  LdsPlan p;
-  p.NS = M <= 16 ? 12 : 6;
-  p.nred = M <= 64 ? 2 : 1;
+__host__ __device__ inline LdsPlan lds_plan(int M, int esz, int d) {
   const int sk = 512 / esz;
-  p.XC = 2048;
-  while (p.XC > sk && lds_bytes_for(M, esz, p.NS, p.XC, p.nred) > 160 * 1024 - 512) p.XC /= 2;
+  const int xfull = (d + sk - 1) / sk * sk;
+  const int ns_opts[5] = {16, 14, 12, 10, 8};
+  for (int i = 0; i < 5; ++i)
+    if (lds_bytes_for(M, esz, ns_opts[i], xfull, 2) <= LDS_BUDGET) return LdsPlan{ns_opts[i], xfull, 2};
+  LdsPlan p{8, xfull, M <= 64 ? 2 : 1};
+  while (p.XC > sk && lds_bytes_for(M, esz, p.NS, p.XC, p.nred) > LDS_BUDGET) p.XC = (p.XC / 2 + sk - 1) / sk * sk;
   return p;
 }
-__host__ __device__ inline int x_chunk_for(int M, int esz) { return lds_plan(M, esz).XC; }
+__host__ __device__ inline int x_chunk_for(int M, int esz, int d) { return lds_plan(M, esz, d).XC; }
 
-// accumulators of this many tiles stay in registers per consumer wave
-template <int MT> struct TileBatch { static constexpr int value = MT == 1 ? 16 : (MT == 2 ? 4 : (MT == 4 ? 2 : 1)); };
 
-size_t mega_counter_ints(int M, int d, int F, int nh, int V, int KU, int n_layers) {
-  (void)V; (void)KU; (void)d;
+size_t mega_counter_ints(int M, int d, int F, int nh, int n_layers) {
   size_t worst = 0;
   for (int m = 1; m <= M; ++m)
     for (int esz = 2; esz <= 4; esz += 2)
-      worst = std::max(worst, (size_t)cnt_layout(m, F, nh, x_chunk_for(m, esz), n_layers).total);
+      worst = std::max(worst, (size_t)cnt_layout(m, F, nh, x_chunk_for(m, esz, d), n_layers).total);
   return worst;
 }
 
@@ -168,6 +214,7 @@ struct Lds {
   float* red;        // nred x NCONS x M x 16: per-tile partials of the consumer waves
   float* rinv;       // M
   float* scr;        // attention scratch: 4*128 + 64 floats
+  int* hx;           // M: hidden-state row of each working row (-1: none)
   int* ints;         // [0..NS) full, [NS..2NS) empty, [2NS] consumer barrier, [2NS+1..] flags
   int xstride;       // elements
   int NS, XC, nred;
@@ -176,9 +223,9 @@ struct Lds {
 LS_DEV size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 template <typename T>
-LS_DEV Lds lds_carve(char* base, int M) {
+LS_DEV Lds lds_carve(char* base, int M, int d) {
   Lds s;
-  const LdsPlan pl = lds_plan(M, (int)sizeof(T));
+  const LdsPlan pl = lds_plan(M, (int)sizeof(T), d);
   s.NS = pl.NS;
   s.XC = pl.XC;
   s.nred = pl.nred;
@@ -189,14 +236,14 @@ LS_DEV Lds lds_carve(char* base, int M) {
   s.red = (float*)(base + off); off = align16(off + (size_t)s.nred * NCONS * M * 16 * 4);
   s.rinv = (float*)(base + off); off = align16(off + (size_t)M * 4);
   s.scr = (float*)(base + off); off = align16(off + (4 * 128 + 64) * 4);
+  s.hx = (int*)(base + off); off = align16(off + (size_t)M * 4);
   s.ints = (int*)(base + off);
   return s;
 }
 
-size_t mega_smem_bytes(bool bf16, int M, int KU) {
-  (void)KU;
+size_t mega_smem_bytes(bool bf16, int M, int d) {
   const int esz = bf16 ? 2 : 4;
-  const LdsPlan p = lds_plan(M, esz);
+  const LdsPlan p = lds_plan(M, esz, d);
   return lds_bytes_for(M, esz, p.NS, p.XC, p.nred);
 }
 
@@ -263,6 +310,16 @@ LS_DEV Share share_of(int n, int deal, int G, int b) {
   return s;
 }
 
+// LDS word read for the producer waves, from inline assembly with its wait in the same block:
+// a compiler-visible LDS read after direct-to-LDS loads gets a conservative wait for all of
+// them (vmcnt(0)), which would drain the prefetch pipeline at every ring-slot check.
+LS_DEV int lds_peek(const int* p) {
+  const unsigned addr = (unsigned)(size_t)(__attribute__((address_space(3))) const int*)p;
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
 // vmcnt-only wait with a compile-time count (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
 // lgkmcnt[11:8] | vmcnt[5:4] << 14; expcnt/lgkmcnt at their maxima = no wait).
 template <int N>
@@ -270,65 +327,122 @@ LS_DEV void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until at most n (a multiple of 8, run time) vector memory operations of this wave are in
+// flight.
+template <int N>
+LS_DEV void wait_vm_le8_impl(int n) {
+  if constexpr (N <= 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= N) wait_vm<N>();
+    else wait_vm_le8_impl<N - 8>(n);
+  }
+}
+LS_DEV void wait_vm_le8(int n) { wait_vm_le8_impl<56>(__builtin_amdgcn_readfirstlane(n)); }
+
 // =========================================== producer ===========================================
-template <typename T, int DP>
+// Every producer wave walks the workgroup's whole slab sequence and issues every NPROD-th slab
+// (slab j belongs to wave j mod NPROD) as eight 1 KB direct-to-LDS loads; a wave keeps at most
+// PFL of its slabs in flight.  A GCN/CDNA wave issues at most one instruction per four cycles,
+// so the per-slab instruction count is what bounds a wave's streaming rate: row addresses are
+// computed once per tile, and a slab costs a compare, eight address adds and eight loads.
+constexpr int PFL = 2;
+
+template <typename T>
 struct Producer {
   const MegaArgs& a;
   const Lds& s;
-  int p;           // producer index 0..3
+  int p;              // producer index 0..NPROD-1
   int lane;
-  int j = 0;       // slabs issued
-  int pub = 0;     // slabs published
+  int j = 0;          // position in the workgroup's slab sequence
+  int mine = 0;       // slabs issued by this wave (sequence positions p, p + NPROD, ...)
+  int pub = 0;        // of which published
+  int slot = 0, use = 0;          // ring slot and use count of this wave's next slab
+  int pslot = 0;                  // ring slot of this wave's oldest unpublished slab
+  const char* rp[8];  // this lane's source in load i of the current tile: row 2i + lane/32, swizzled chunk
+  int co[8];          // the swizzled chunk's byte offset within the 512-byte row segment
 
-  LS_DEV Producer(const MegaArgs& a_, const Lds& s_, int p_) : a(a_), s(s_), p(p_), lane(threadIdx.x & 63) {}
+  LS_DEV Producer(const MegaArgs& a_, const Lds& s_, int p_)
+      : a(a_), s(s_), p(p_), lane(threadIdx.x & 63), slot(p_), pslot(p_) {}
 
+  // Callers have waited (vmcnt retires in order) for the slab's loads to land in LDS.  The
+  // count is bumped by a non-returning ds_add issued from inline assembly: any compiler-visible
+  // LDS access here would get a conservative wait for every direct-to-LDS load still in flight,
+  // i.e. drain the prefetch pipeline at each slab.
   LS_DEV void publish_one() {
-    if (lane == 0) lds_add(s.ints + (pub % s.NS), 1);
+    if (lane == 0) {
+      const unsigned addr = (unsigned)(size_t)(__attribute__((address_space(3))) int*)(s.ints + pslot);
+      asm volatile("ds_add_u32 %0, %1" : : "v"(addr), "v"(1) : "memory");
+    }
     ++pub;
+    pslot += NPROD;
+    if (pslot >= s.NS) pslot -= s.NS;
   }
 
-  // Copy slab (t, k) of phase ph into the next ring slot: this producer's four rows, as two
-  // 1 KB direct-to-LDS loads.  Lane l of a load carries 16 bytes of row 4p + 2i + l/32; the
-  // 16-byte chunk index is XOR-swizzled with the row so consumers read conflict-free.
-  LS_DEV void issue(const LayerW& lw, int ph, int t, int k, const PhaseGeo& g) {
-    const int slot = j % s.NS, use = j / s.NS;
+  // Row addresses of tile t of phase ph for this lane's eight loads.
+  LS_DEV void begin_tile(const LayerW& lw, int ph, int t, const PhaseGeo& g) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rho = 2 * i + (lane >> 5);
+      co[i] = ((lane & 31) ^ rho) * 16;
+      rp[i] = wrow<T>(a, lw, ph, t, rho, g.K) + co[i];
+    }
+  }
+
+  // Slab k (512-byte column segment k) of the current tile.
+  LS_DEV void issue(int k, const PhaseGeo& g) {
+    const int jj = j++;
+    if ((jj & (NPROD - 1)) != p) return;
     if (use > 0) {
-      if (lane == 0) {
-        int n = 0;
-        while (lds_ld(s.ints + s.NS + slot) < use) {
+      // Wait for the consumers to release the slot.  Meanwhile publish, oldest first, every
+      // issued slab whose loads have landed, so a full ring never holds back ready slabs.
+      int n = 0;
+      while (lds_peek(s.ints + s.NS + slot) < use) {
+        if (pub < mine) {
+          wait_vm_le8(8 * (mine - pub - 1));
+          publish_one();
+        } else {
           __builtin_amdgcn_s_sleep(0);
-          if (++n > SPIN_LIMIT) { ls_flag(a.err, LS_TIMEOUT); break; }
+          if (++n > SPIN_LIMIT) {
+            if (lane == 0) ls_flag(a.err, LS_TIMEOUT);
+            break;
+          }
         }
       }
-      __builtin_amdgcn_wave_barrier();
     }
-    const int k0 = k * g.sk;
-    const int kn = min(g.sk, g.K - k0);
-    constexpr int E = 16 / (int)sizeof(T);
-    const int nch = kn / E;                         // valid 16-byte chunks in each row
-    char* dst = s.ring + (size_t)slot * SLAB;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rho = 4 * p + 2 * i + (lane >> 5);
-      const int pos = lane & 31;
-      int ch = pos ^ (rho & 31);
-      if (ch >= nch) ch = 0;
-      const char* src = wrow<T>(a, lw, ph, t, rho, g.K) + ((size_t)k0 + (size_t)ch * E) * sizeof(T);
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + (4 * p + 2 * i) * 512),
-                                       16, 0, 0);
-    }
-    ++j;
-    if (j - pub > DP) {
-      wait_vm<2 * DP>();
+    while (mine - pub >= PFL) {
+      wait_vm_le8(8 * (mine - pub - 1));
       publish_one();
     }
+    char* dst = s.ring + (size_t)slot * SLAB;
+    const int kb = k * 512;                           // byte offset of the segment in each row
+    const int vb = (g.K - k * g.sk) * (int)sizeof(T); // valid bytes of the segment (< 512: ragged tail)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const char* src = rp[i] + kb;
+      if (vb < 512 && co[i] >= vb) src -= co[i];      // chunk past the row end: any valid chunk will do
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+    }
+    ++mine;
+    slot += NPROD;
+    if (slot >= s.NS) { slot -= s.NS; ++use; }
   }
 
   LS_DEV void finish() {
     wait_vm<0>();
-    while (pub < j) publish_one();
+    while (pub < mine) publish_one();
   }
 };
+
+// Debug time stamps (wall clock, 100 MHz) of the first four layers: [grid][4][8 phases][8 events].
+LS_DEV void tstamp(const MegaArgs& a, int l, int ph, int e) {
+  if (a.trace && l < 4) a.trace[(((size_t)blockIdx.x * 4 + l) * 8 + ph) * 8 + e] = wall_clock64();
+}
+// Finer stamps of the first layer's QKV phase by thread 0, after the phase stamps: [grid][32].
+LS_DEV void dstamp(const MegaArgs& a, bool on, int e) {
+  if (on && a.trace && threadIdx.x == 0)
+    a.trace[(size_t)gridDim.x * 4 * 8 * 8 + (size_t)blockIdx.x * 32 + e] = wall_clock64();
+}
 
 // =========================================== consumer ===========================================
 template <typename T, int MT>
@@ -338,57 +452,142 @@ struct Consumer {
   ConsBar& cb;
   int c;            // consumer index 0..3
   int lane;
-  int j = 0;        // slabs passed in the sequence
-  int rinv_tag = -1;
+  int cslot = 0, cuse = 0;   // ring slot and use count of the next slab in the sequence
+  bool dbg = false; // fine stamps on (first layer's QKV phase)
 
   LS_DEV Consumer(const MegaArgs& a_, const Lds& s_, ConsBar& cb_, int c_)
       : a(a_), s(s_), cb(cb_), c(c_), lane(threadIdx.x & 63) {}
 
-  // RMSNorm factors for all rows, once per (layer, phase).
-  LS_DEV void compute_rinv(const float* ssq, const float* Hsrc, bool via_hidx, int tag) {
-    if (rinv_tag == tag) return;
+  // RMSNorm factor of every row from the per-tile sums of squares that the residual epilogues
+  // left (row m's d/16 tile sums are contiguous); one wave per row.
+  LS_DEV void rinv_from_ssq(const float* ssq) {
     const int nt = a.d / 16;
     for (int m = c; m < a.M; m += NCONS) {
+      const __amdgpu_buffer_rsrc_t R = rsrc_of(ssq + (size_t)m * nt, nt * 4);
       float acc = 0.f;
-      if (ssq) {
-        for (int t = lane; t < nt; t += 64) acc += ldc(ssq + (size_t)t * a.M + m);
-      } else {
-        const int hr = via_hidx ? (a.hidx ? a.hidx[m] : m) : m;
-        if (hr >= 0)
-          for (int k = lane; k < a.d; k += 64) {
-            const float x = ldc(Hsrc + (size_t)hr * a.d + k);
-            acc += x * x;
-          }
+      for (int p0 = 0; p0 < nt; p0 += 256) {
+        const u32x4_t v = ld128(R, (p0 + 4 * lane) * 4);
+        acc += (__uint_as_float(v.x) + __uint_as_float(v.y)) + (__uint_as_float(v.z) + __uint_as_float(v.w));
       }
       acc = warp_sum(acc);
       if (lane == 0) s.rinv[m] = 1.0f / sqrtf(acc / (float)a.d + a.eps);
     }
-    rinv_tag = tag;
     cb.sync();
   }
 
-  // Stage activation columns [x0, x0 + xn) of phase ph into LDS.
-  LS_DEV void stage_x(int ph, const LayerW& lw, int x0, int xn, int K) {
-    T* X = (T*)s.X;
-    const int tid = threadIdx.x;          // consumers are threads 0..255
-    if (ph == PH_QKV || ph == PH_GU || ph == PH_HEAD) {
-      const float* gain = ph == PH_QKV ? lw.g1 : (ph == PH_GU ? lw.g2 : a.g_final);
-      for (int idx = tid; idx < a.M * xn; idx += 64 * NCONS) {
-        const int m = idx / xn, kk = idx - m * xn;
-        float x;
-        if (ph == PH_GU) {
-          x = ldc(a.Hb + (size_t)m * a.d + x0 + kk);
-        } else {
-          const int hr = a.hidx ? a.hidx[m] : m;
-          x = hr >= 0 ? ldc(a.H + (size_t)hr * a.d + x0 + kk) : 0.f;
+  // RMSNorm factor of every row straight from the hidden rows (first layer of a call, where no
+  // residual epilogue has left tile sums).
+  LS_DEV void rinv_from_rows(const float* src) {
+    constexpr int NV = 8;
+    for (int m = c; m < a.M; m += NCONS) {
+      const int hr = __builtin_amdgcn_readfirstlane(s.hx[m]);
+      const __amdgpu_buffer_rsrc_t R = rsrc_of(src + (size_t)(hr >= 0 ? hr : 0) * a.d, hr >= 0 ? a.d * 4 : 0);
+      float acc = 0.f;
+      for (int p0 = 0; p0 < a.d; p0 += 256 * NV) {
+        u32x4_t v[NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) v[u] = ld128(R, (p0 + 4 * (lane + 64 * u)) * 4);
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const float f0 = __uint_as_float(v[u].x), f1 = __uint_as_float(v[u].y);
+          const float f2 = __uint_as_float(v[u].z), f3 = __uint_as_float(v[u].w);
+          acc += (f0 * f0 + f1 * f1) + (f2 * f2 + f3 * f3);
         }
-        Elem<T>::store(X + (size_t)m * s.xstride + kk, x * s.rinv[m] * gain[x0 + kk]);
       }
+      acc = warp_sum(acc);
+      if (lane == 0) s.rinv[m] = 1.0f / sqrtf(acc / (float)a.d + a.eps);
+    }
+    cb.sync();
+  }
+
+  // Stage columns [x0, x0 + xn) of the normalised rows, T(x * rinv * gain), into LDS; one
+  // wave per row, every load of a row pass in flight at once.  With fuse (the chunk is the
+  // whole row, d <= 64*4*NVF) the RMSNorm factor comes from the same loads.
+  static constexpr int NVF = 8;
+  LS_DEV void stage_norm(const float* src, bool via_hidx, const float* gain, int x0, int xn, bool fuse) {
+    T* X = (T*)s.X;
+    const __amdgpu_buffer_rsrc_t Rg = rsrc_of(gain + x0, xn * 4);
+    for (int m = c; m < a.M; m += NCONS) {
+      const int hv = __builtin_amdgcn_readfirstlane(s.hx[m]);   // negative: rejected row, stages zeros
+      const int hr = via_hidx ? hv : m;
+      const float* row = src + (size_t)(hv >= 0 ? hr : 0) * a.d + x0;
+      const __amdgpu_buffer_rsrc_t R = rsrc_of(row, hv >= 0 ? xn * 4 : 0);
+      T* xr = X + (size_t)m * s.xstride;
+      // row values and gains of a pass are all requested before any is used
+      if (fuse) {
+        u32x4_t v[NVF], gv[NVF];
+        dstamp(a, dbg && m == 0, 0);
+#pragma unroll
+        for (int u = 0; u < NVF; ++u) v[u] = ld128(R, (4 * (lane + 64 * u)) * 4);
+#pragma unroll
+        for (int u = 0; u < NVF; ++u) gv[u] = ld128(Rg, (4 * (lane + 64 * u)) * 4);
+        dstamp(a, dbg && m == 0, 1);
+        float ss = 0.f;
+#pragma unroll
+        for (int u = 0; u < NVF; ++u) {
+          const float f0 = __uint_as_float(v[u].x), f1 = __uint_as_float(v[u].y);
+          const float f2 = __uint_as_float(v[u].z), f3 = __uint_as_float(v[u].w);
+          ss += (f0 * f0 + f1 * f1) + (f2 * f2 + f3 * f3);
+        }
+        ss = warp_sum(ss);
+        dstamp(a, dbg && m == 0, 2);
+        const float ri = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+#pragma unroll
+        for (int u = 0; u < NVF; ++u) {
+          const int k = 4 * (lane + 64 * u);
+          if (k < xn) put4(xr + k, v[u], ri, gv[u]);
+        }
+        dstamp(a, dbg && m == 0, 3);
+      } else {
+        const float ri = s.rinv[m];
+        constexpr int NV = 8;
+        for (int p0 = 0; p0 < xn; p0 += 256 * NV) {
+          u32x4_t v[NV], gv[NV];
+#pragma unroll
+          for (int u = 0; u < NV; ++u) v[u] = ld128(R, (p0 + 4 * (lane + 64 * u)) * 4);
+#pragma unroll
+          for (int u = 0; u < NV; ++u) gv[u] = ld128(Rg, (p0 + 4 * (lane + 64 * u)) * 4);
+#pragma unroll
+          for (int u = 0; u < NV; ++u) {
+            const int k = p0 + 4 * (lane + 64 * u);
+            if (k < xn) put4(xr + k, v[u], ri, gv[u]);
+          }
+        }
+      }
+    }
+    cb.sync();
+  }
+
+  LS_DEV static void put4(T* dst, const u32x4_t& v, float ri, const u32x4_t& g) {
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = __uint_as_float(v[e]) * ri * __uint_as_float(g[e]);
+    if constexpr (sizeof(T) == 2) {
+      const unsigned lo = (unsigned)f2bf(y[0]) | ((unsigned)f2bf(y[1]) << 16);
+      const unsigned hi = (unsigned)f2bf(y[2]) | ((unsigned)f2bf(y[3]) << 16);
+      *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
     } else {
-      const T* src = (const T*)(ph == PH_O ? a.o : a.act);
-      for (int idx = tid; idx < a.M * xn; idx += 64 * NCONS) {
-        const int m = idx / xn, kk = idx - m * xn;
-        X[(size_t)m * s.xstride + kk] = Coh<T>::raw(src + (size_t)m * K + x0 + kk);
+      *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+    }
+  }
+
+  // Stage columns [x0, x0 + xn) of rows already in GEMM-input precision (attention output or
+  // SwiGLU activations, row stride K) into LDS, 16 bytes per lane.
+  LS_DEV void stage_raw(const T* src, int K, int x0, int xn) {
+    constexpr int E = 16 / (int)sizeof(T);
+    constexpr int NV = 8;
+    for (int m = c; m < a.M; m += NCONS) {
+      const __amdgpu_buffer_rsrc_t R = rsrc_of(src + (size_t)m * K + x0, xn * (int)sizeof(T));
+      char* xr = (char*)((T*)s.X + (size_t)m * s.xstride);
+      for (int p0 = 0; p0 < xn; p0 += 64 * E * NV) {
+        u32x4_t v[NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) v[u] = ld128(R, (p0 + E * (lane + 64 * u)) * (int)sizeof(T));
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int k = p0 + E * (lane + 64 * u);
+          if (k < xn) *reinterpret_cast<u32x4_t*>(xr + (size_t)k * sizeof(T)) = v[u];
+        }
       }
     }
     cb.sync();
@@ -396,18 +595,20 @@ struct Consumer {
 
   // Pass one slab of the sequence; if it is this consumer's (q mod 4 == c), multiply it.
   LS_DEV void slab(int q, int kn, f32x4_t* acc) {
-    const int slot = j % s.NS, use = j / s.NS;
-    ++j;
-    if (q % NCONS != c) return;
+    const int slot = cslot, use = cuse;
+    if (++cslot == s.NS) { cslot = 0; ++cuse; }
+    if ((q & (NCONS - 1)) != c) return;
     if (lane == 0) {
       int n = 0;
-      while (lds_ld(s.ints + slot) < (use + 1) * NPROD) {
+      while (lds_ld(s.ints + slot) < use + 1) {
         __builtin_amdgcn_s_sleep(0);
         if (++n > SPIN_LIMIT) { ls_flag(a.err, LS_TIMEOUT); break; }
       }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (dbg && a.trace && threadIdx.x == 0 && a.trace[(size_t)gridDim.x * 256 + (size_t)blockIdx.x * 32 + 6] == 0) dstamp(a, true, 6);
+    dstamp(a, dbg, 7);
     constexpr int E = 16 / (int)sizeof(T);
     const int r = lane & 15, g = lane >> 4;
     const char* base = s.ring + (size_t)slot * SLAB + r * 512;
@@ -431,13 +632,15 @@ struct Consumer {
     // ring reads are complete (their values fed the MFMAs) before the slot is released
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane == 0) lds_add(s.ints + s.NS + slot, 1);
+    dstamp(a, dbg, 8);
   }
 };
 
 // Epilogue of one finished tile (its sum over the four consumers is in Ts[m*16 + n]).
 template <typename T>
-LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, int ph, int l, int t, const float* Ts, int lane) {
-  int* C = a.cnt + (size_t)l * cl.per_layer;
+LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, const int* hx, int ph, int l, int t, const float* Ts,
+                     int lane) {
+  (void)cl;
   if (ph == PH_QKV) {
     const int tpm = a.d / 16, tph = a.hd / 16;
     const int mat = t / tpm, tl = t % tpm;
@@ -448,8 +651,7 @@ LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, int ph, int l, int 
       const int e0 = h * a.hd + i, e1 = e0 + a.hd / 2;
       float y0 = Ts[m * 16 + p], y1 = Ts[m * 16 + p + 8];
       if (mat < 2) {
-        const double ang = (double)a.pos[m] * a.inv_freq[i];
-        const float cs = (float)cos(ang), sn = (float)sin(ang);
+        const float cs = a.rope[((size_t)m * (a.hd / 2) + i) * 2], sn = a.rope[((size_t)m * (a.hd / 2) + i) * 2 + 1];
         const float r0 = y0 * cs - y1 * sn, r1 = y1 * cs + y0 * sn;
         y0 = r0; y1 = r1;
       }
@@ -465,48 +667,72 @@ LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, int ph, int l, int 
         Coh<T>::store(ent + e1, y1);
       }
     }
-    drain();
-    if (lane == 0) atomicAdd(C + cl.o_qkvh + h * PADC, 1);
   } else if (ph == PH_O || ph == PH_DOWN) {
-    float* ssq = a.ssq + ((size_t)l * 2 + (ph == PH_DOWN)) * (a.d / 16) * a.M;
-    for (int m = lane; m < a.M; m += 64) {
-      const int hr = a.hidx ? a.hidx[m] : m;
-      float sq = 0.f;
-      for (int nl = 0; nl < 16; ++nl) {
-        const int n = 16 * t + nl;
-        const float y = Ts[m * 16 + nl];
-        float nv = 0.f;
-        if (hr >= 0) {
-          if (ph == PH_O) {
-            nv = ldc(a.H + (size_t)hr * a.d + n) + y;
-            stc(a.Hb + (size_t)m * a.d + n, nv);
-          } else {
-            nv = ldc(a.Hb + (size_t)m * a.d + n) + y;
-            stc(a.H + (size_t)hr * a.d + n, nv);
-          }
-        } else if (ph == PH_O) {
-          stc(a.Hb + (size_t)m * a.d + n, 0.f);
-        }
-        sq += nv * nv;
+    // residual add: lane = (row group, column); the residual loads of up to 16 rows are in
+    // flight together, and the tile's sum of squares per row is reduced over its 16 lanes
+    const int nt = a.d / 16;
+    float* ssq = a.ssq + ((size_t)l * 2 + (ph == PH_DOWN)) * nt * a.M;
+    const int nl = lane & 15, n = 16 * t + nl;
+    const float* xin = layer_in(a, l);
+    float* yl = ys_of(a, l);
+    const bool last = l == a.n_layers - 1;
+    float* xout = (!last || a.do_head) ? a.Xs + (size_t)(l + 1) * a.M * a.d : nullptr;
+    for (int m0 = 0; m0 < a.M; m0 += 16) {
+      // residual inputs through one descriptor; rows that are absent read as zero (offset
+      // beyond the descriptor's range)
+      const __amdgpu_buffer_rsrc_t Rr = rsrc_of(ph == PH_O ? xin : yl, 0x7fffffff);
+      float res[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int m = m0 + 4 * u + (lane >> 4);
+        const int hr = m < a.M ? hx[m] : -1;
+        const int row = ph == PH_O && l == 0 ? hr : m;
+        const int off = hr >= 0 ? (row * a.d + n) * 4 : 0x7fffffff;
+        res[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(Rr, off, 0, 0));
       }
-      stc(ssq + (size_t)t * a.M + m, sq);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int m = m0 + 4 * u + (lane >> 4);
+        const int hr = m < a.M ? hx[m] : -1;
+        const float nv = hr >= 0 ? res[u] + Ts[m * 16 + nl] : 0.f;
+        if (m < a.M) {
+          if (ph == PH_O) {
+            stc(yl + (size_t)m * a.d + n, nv);
+          } else {
+            if (xout) stc(xout + (size_t)m * a.d + n, nv);
+            if (last && hr >= 0) stc(a.H + (size_t)hr * a.d + n, nv);
+          }
+        }
+        float sq = nv * nv;
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+        if (nl == 0 && m < a.M) stc(ssq + (size_t)m * nt + t, sq);
+      }
     }
-    drain();
-    if (lane == 0) atomicAdd(C + (ph == PH_O ? cl.o_o : cl.o_down), 1);
   } else if (ph == PH_GU) {
-    T* act = (T*)a.act;
+    T* act = act_of<T>(a, l);
     for (int idx = lane; idx < a.M * 8; idx += 64) {
       const int m = idx >> 3, p = idx & 7;
       const float gv = Ts[m * 16 + p], uv = Ts[m * 16 + p + 8];
       Coh<T>::store(act + (size_t)m * a.F + 8 * t + p, gv / (1.0f + expf(-gv)) * uv);
     }
-    drain();
-    if (lane == 0) atomicAdd(C + cl.o_gu + ((8 * t) / x_chunk_for(a.M, (int)sizeof(T))) * PADC, 1);
   } else {  // PH_HEAD
     for (int idx = lane; idx < a.M * 16; idx += 64) {
       const int m = idx >> 4, nl = idx & 15, n = 16 * t + nl;
       if (n < a.V) a.logits[(size_t)m * a.ldo + n] = Ts[idx];
     }
+  }
+}
+
+// Counter bump of a finished tile; the caller has drained the tile's stores.
+LS_DEV void tile_signal(const MegaArgs& a, const CntLayout& cl, int ph, int l, int t, int XC) {
+  int* C = a.cnt + (size_t)l * cl.per_layer;
+  if (ph == PH_QKV) {
+    atomicAdd(C + cl.o_qkvh + ((t % (a.d / 16)) / (a.hd / 16)) * PADC, 1);
+  } else if (ph == PH_O || ph == PH_DOWN) {
+    atomicAdd(C + (ph == PH_O ? cl.o_o : cl.o_down), 1);
+  } else if (ph == PH_GU) {
+    atomicAdd(C + cl.o_gu + ((8 * t) / XC) * PADC, 1);
   }
 }
 
@@ -545,7 +771,7 @@ LS_DEV void att_unit(const MegaArgs& a, const Lds& s, const CntLayout& cl, ConsB
     if (c == 0) {
       wait_ge(C + cl.o_qkvh + h * PADC, 3 * (a.hd / 16), cb);
       for (int dd = threadIdx.x; dd < a.hd; dd += 64 * NCONS)
-        Coh<T>::store((T*)a.o + (size_t)i * a.d + h * a.hd + dd, 0.f);
+        Coh<T>::store(o_of<T>(a, l) + (size_t)i * a.d + h * a.hd + dd, 0.f);
       drain();
       cb.sync();
       if (threadIdx.x == 0) atomicAdd(C + cl.o_att + h * PADC, 1);
@@ -588,8 +814,15 @@ LS_DEV void att_unit(const MegaArgs& a, const Lds& s, const CntLayout& cl, ConsB
   if (!early) load_kv();
   float q[8];
   const float scale = 1.0f / sqrtf((float)a.hd);
+  {
+    const __amdgpu_buffer_rsrc_t Rq = rsrc_of(a.q + (size_t)i * a.d + h * a.hd, a.hd * 4);
+    const u32x4_t q0 = ldc128(Rq, 32 * e), q1 = ldc128(Rq, 32 * e + 16);
 #pragma unroll
-  for (int t = 0; t < 8; ++t) q[t] = dim_ok ? ldc(a.q + (size_t)i * a.d + h * a.hd + 8 * e + t) * scale : 0.f;
+    for (int t = 0; t < 4; ++t) {
+      q[t] = __uint_as_float(q0[t]) * scale;
+      q[4 + t] = __uint_as_float(q1[t]) * scale;
+    }
+  }
   float sc[4];
   float mloc = -INFINITY;
 #pragma unroll
@@ -660,11 +893,18 @@ LS_DEV void att_unit(const MegaArgs& a, const Lds& s, const CntLayout& cl, ConsB
   for (int cc = 0; cc < nc; ++cc) den += (cmx[cc] == -INFINITY ? 0.f : __expf(cmx[cc] - M_)) * cmx[a.att_chunks + cc];
   for (int dd = threadIdx.x; dd < a.hd; dd += 64 * NCONS) {
     float num = 0.f;
-    for (int cc = 0; cc < nc; ++cc) {
-      const float wgt = cmx[cc] == -INFINITY ? 0.f : __expf(cmx[cc] - M_);
-      num += wgt * ldc(base + (size_t)cc * (a.hd + 2) + 2 + dd);
+    for (int c0 = 0; c0 < nc; c0 += 8) {       // eight chunk partials in flight per pass
+      float pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv[u] = ldc(base + (size_t)min(c0 + u, nc - 1) * (a.hd + 2) + 2 + dd);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int cc = c0 + u;
+        const float wgt = (cc >= nc || cmx[min(cc, nc - 1)] == -INFINITY) ? 0.f : __expf(cmx[min(cc, nc - 1)] - M_);
+        num += wgt * pv[u];
+      }
     }
-    Coh<T>::store((T*)a.o + (size_t)i * a.d + h * a.hd + dd, den > 0.f ? num / den : 0.f);
+    Coh<T>::store(o_of<T>(a, l) + (size_t)i * a.d + h * a.hd + dd, den > 0.f ? num / den : 0.f);
   }
   drain();
   cb.sync();
@@ -679,6 +919,7 @@ LS_DEV void init_unit(const MegaArgs& a, const CntLayout& cl, ConsBar& cb, int m
     if (a.init_mode == 1) {
       const int tok = a.tokens[m];
       if (tok >= 0 && tok < a.V) {
+#pragma unroll 8
         for (int k = threadIdx.x; k < a.d; k += 64 * NCONS)
           stc(a.H + (size_t)hr * a.d + k, Elem<T>::load((const T*)a.emb + (size_t)tok * a.d + k));
       } else if (threadIdx.x == 0) {
@@ -695,12 +936,15 @@ LS_DEV void init_unit(const MegaArgs& a, const CntLayout& cl, ConsBar& cb, int m
   if (threadIdx.x == 0) atomicAdd(a.cnt + cl.o_init, 1);
 }
 
+// Phase stamps: consumer wave 0: 0 phase begin, 1 phase end, 2 dependencies met, 3 first chunk
+// staged, 4 first tile batch multiplied.  Producer wave 0: 5 first slab issued, 6 last issued.
+
 // ---- the walk: the same slab sequence for producers and consumers ----------------------------------
-// Phase ph of layer l: the workgroup's tiles in batches of TB; within a batch, activation chunk
-// by chunk (XC columns); within a chunk, tile by tile, slab by slab.
-template <typename T, int MT, int DP, bool PROD>
+// Phase ph of layer l: the workgroup's tiles one by one; within a tile, activation chunk by
+// chunk (XC columns), slab by slab.
+template <typename T, int MT, bool PROD>
 LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int ph, int l, int& deal,
-                      Producer<T, DP>* pr, Consumer<T, MT>* co, ConsBar* cb) {
+                      Producer<T>* pr, Consumer<T, MT>* co, ConsBar* cb) {
   const int G = gridDim.x, b = blockIdx.x;
   const PhaseGeo g = phase_geo<T>(a, ph);
   const Share sh = share_of(g.n_tiles, deal, G, b);
@@ -709,176 +953,197 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
   const LayerW lw = ph == PH_HEAD ? LayerW{} : a.layers[l];
   const int nchunk = (g.K + s.XC - 1) / s.XC;
 
+  // normalised phases (QKV, GU, HEAD) read a whole row when one activation chunk covers it and
+  // then take the RMSNorm factor from the same loads; otherwise from the per-tile sums of squares
+  const bool fuse = nchunk == 1 && g.K <= 64 * 4 * Consumer<T, MT>::NVF;
+  const int lin = ph == PH_HEAD ? a.n_layers : l;              // layer whose input a normalised phase reads
+  const float* nsrc = ph == PH_GU ? ys_of(a, l) : layer_in(a, lin);
+  const bool nvia = ph != PH_GU && lin == 0;                   // rows addressed through hidx
+  const float* gain = ph == PH_QKV ? lw.g1 : (ph == PH_GU ? lw.g2 : a.g_final);
   if (!PROD) {
-    // dependencies of the normalised phases (full rows are needed for the RMSNorm factor)
+    co->dbg = l == 0 && ph == PH_QKV;
+    dstamp(a, co->dbg, 4);
     const int* C = a.cnt + (size_t)l * cl.per_layer;
-    if (ph == PH_QKV) {
-      if (l > 0) wait_ge(a.cnt + (size_t)(l - 1) * cl.per_layer + cl.o_down, a.d / 16, *cb);
-      else if (a.init_mode) wait_ge(a.cnt + cl.o_init, a.M, *cb);
-      const float* ssq = l > 0 ? a.ssq + ((size_t)(l - 1) * 2 + 1) * (a.d / 16) * a.M : nullptr;
-      co->compute_rinv(ssq, a.H, true, l * 8 + ph);
+    const int nt = a.d / 16;
+    const float* ssq = nullptr;
+    if (ph == PH_QKV || ph == PH_HEAD) {
+      const int lp = ph == PH_QKV ? l - 1 : a.n_layers - 1;    // layer whose output feeds this phase
+      if (lp >= 0) {
+        wait_ge(a.cnt + (size_t)lp * cl.per_layer + cl.o_down, nt, *cb);
+        ssq = a.ssq + ((size_t)lp * 2 + 1) * nt * a.M;
+      } else if (a.init_mode) {
+        wait_ge(a.cnt + cl.o_init, a.M, *cb);
+      }
+      if (!fuse) {
+        if (ssq) co->rinv_from_ssq(ssq);
+        else co->rinv_from_rows(a.H);            // first layer of the call: the caller's rows
+      }
     } else if (ph == PH_GU) {
-      wait_ge(C + cl.o_o, a.d / 16, *cb);
-      co->compute_rinv(a.ssq + ((size_t)l * 2) * (a.d / 16) * a.M, a.Hb, false, l * 8 + ph);
-    } else if (ph == PH_HEAD) {
-      if (a.n_layers > 0) wait_ge(a.cnt + (size_t)(a.n_layers - 1) * cl.per_layer + cl.o_down, a.d / 16, *cb);
-      else if (a.init_mode) wait_ge(a.cnt + cl.o_init, a.M, *cb);
-      const float* ssq = a.n_layers > 0 ? a.ssq + ((size_t)(a.n_layers - 1) * 2 + 1) * (a.d / 16) * a.M : nullptr;
-      co->compute_rinv(ssq, a.H, true, l * 8 + ph);
+      wait_ge(C + cl.o_o, nt, *cb);
+      if (!fuse) co->rinv_from_ssq(a.ssq + ((size_t)l * 2) * nt * a.M);
     }
+    if (threadIdx.x == 0) tstamp(a, l, ph, 2);
   }
 
-  constexpr int TBM = TileBatch<MT>::value;
-  for (int b0 = 0; b0 < sh.count; b0 += TBM) {
-    const int nb = min(TBM, sh.count - b0);
-    f32x4_t acc[TBM][MT];
-    if (!PROD) {
+  // One tile at a time.  With one activation chunk (the usual case) the chunk is staged once
+  // for all of the workgroup's tiles; with several, every tile re-stages its chunks.
+  const bool restage = nchunk > 1;
+  for (int i = 0; i < sh.count; ++i) {
+    const int t = sh.first + i * G;
+    f32x4_t acc[MT];
 #pragma unroll
-      for (int tb = 0; tb < TBM; ++tb)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[tb][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int ch = 0; ch < nchunk; ++ch) {
       const int x0 = ch * s.XC;
       const int xn = min(s.XC, g.K - x0);
-      if (!PROD) {
+      if (!PROD && (restage || i == 0)) {
         const int* C = a.cnt + (size_t)l * cl.per_layer;
         if (ph == PH_O) {
-          for (int h = x0 / a.hd; h <= (x0 + xn - 1) / a.hd; ++h) wait_ge(C + cl.o_att + h * PADC, a.M, *cb);
+          const int h0 = x0 / a.hd, h1 = (x0 + xn - 1) / a.hd;
+          for (int hb = h0; hb <= h1; hb += 64)
+            wait_all_ge(C + cl.o_att + hb * PADC, PADC, min(64, h1 + 1 - hb), a.M, *cb);
         } else if (ph == PH_DOWN) {
           wait_ge(C + cl.o_gu + ch * PADC, xn / 8, *cb);
         } else {
-          cb->sync();                     // previous chunk's readers are done with X
+          cb->sync();                     // earlier readers of the stage are done
         }
-        co->stage_x(ph, lw, x0, xn, g.K);
+        dstamp(a, co->dbg, 5);
+        if (ph == PH_O || ph == PH_DOWN) co->stage_raw(ph == PH_O ? o_of<T>(a, l) : act_of<T>(a, l), g.K, x0, xn);
+        else co->stage_norm(nsrc, nvia, gain, x0, xn, fuse);
+        if (threadIdx.x == 0 && i == 0 && ch == 0) tstamp(a, l, ph, 3);
       }
       const int k_first = x0 / g.sk;
       const int k_last = (x0 + xn + g.sk - 1) / g.sk;
-      for (int tb = 0; tb < nb; ++tb) {
-        const int t = sh.first + (b0 + tb) * G;
-        for (int k = k_first; k < k_last; ++k) {
-          if (PROD) {
-            pr->issue(lw, ph, t, k, g);
-          } else {
-            const int kn = min(g.sk, g.K - k * g.sk);
-            // constant-index accumulator selection keeps acc in registers
-#pragma unroll
-            for (int tt = 0; tt < TBM; ++tt)
-              if (tt == tb) co->slab(k - k_first, kn, acc[tt]);
-          }
+      if (PROD && ch == 0) pr->begin_tile(lw, ph, t, g);
+      for (int k = k_first; k < k_last; ++k) {
+        if (PROD) {
+          if (threadIdx.x == 64 * NCONS && i == 0 && ch == 0 && k == k_first) tstamp(a, l, ph, 5);
+          pr->issue(k, g);
+        } else {
+          co->slab(k - k_first, min(g.sk, g.K - k * g.sk), acc);
         }
       }
     }
     if (!PROD) {
-      // per tile: the four consumer partials meet in LDS and are summed in consumer order by
-      // consumer (tile mod 4), which then runs the epilogue
+      if (threadIdx.x == 0 && i == 0) tstamp(a, l, ph, 4);
+      // The four consumer partials meet in LDS (s.nred rotating buffers); consumer (tile mod 4)
+      // sums them in consumer order, runs the epilogue, drains its stores and bumps the tile's
+      // counter while the other consumers go on with the next tile.
       const int lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
-      for (int tb = 0; tb < nb; ++tb) {
-        float* buf = s.red + (size_t)(tb % s.nred) * NCONS * a.M * 16;
+      float* buf = s.red + (size_t)(i % s.nred) * NCONS * a.M * 16;
 #pragma unroll
-        for (int tt = 0; tt < TBM; ++tt) {
-          if (tt == tb) {
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + r;
+        if (m < a.M) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              const int m = mt * 16 + r;
-              if (m < a.M) {
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) buf[((size_t)co->c * a.M + m) * 16 + 4 * gq + jj] = acc[tt][mt][jj];
-              }
-            }
-          }
+          for (int jj = 0; jj < 4; ++jj) buf[((size_t)co->c * a.M + m) * 16 + 4 * gq + jj] = acc[mt][jj];
         }
-        cb->sync();
-        if (tb % NCONS == co->c) {
-          for (int idx = lane; idx < a.M * 16; idx += 64) {
-            float y = 0.f;
-#pragma unroll
-            for (int cc = 0; cc < NCONS; ++cc) y += buf[(size_t)cc * a.M * 16 + idx];
-            buf[idx] = y;                 // consumer 0's slot now holds the tile sum
-          }
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-          epilogue<T>(a, cl, ph, l, sh.first + (b0 + tb) * G, buf, lane);
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        }
-        if (s.nred == 1) cb->sync();      // single buffer: the sum is read before the next tile
       }
-      cb->sync();                         // reduction buffers reusable
+      dstamp(a, co->dbg, 9);
+      cb->sync();
+      dstamp(a, co->dbg, 10);
+      if (i % NCONS == co->c) {
+        for (int idx = lane; idx < a.M * 16; idx += 64) {
+          float y = 0.f;
+#pragma unroll
+          for (int cc = 0; cc < NCONS; ++cc) y += buf[(size_t)cc * a.M * 16 + idx];
+          buf[idx] = y;                   // consumer 0's slot now holds the tile sum
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        epilogue<T>(a, cl, s.hx, ph, l, t, buf, lane);
+        dstamp(a, co->dbg, 11);
+        if (ph != PH_HEAD) {
+          drain();
+          dstamp(a, co->dbg, 12);
+          if (lane == 0) tile_signal(a, cl, ph, l, t, s.XC);
+          dstamp(a, co->dbg, 13);
+        }
+      }
+      if (s.nred == 1) cb->sync();        // single buffer: read before the next tile's partials
     }
+    if (PROD && threadIdx.x == 64 * NCONS && i == sh.count - 1) tstamp(a, l, ph, 6);
   }
 }
 
-template <typename T, int MT, int DP>
+// Step st of a call's phase sequence: per layer QKV, attention, O, GU, DOWN; then the LM head.
+struct Step {
+  int ph, l;
+};
+LS_DEV Step step_of(const MegaArgs& a, int st) {
+  if (st >= 5 * a.n_layers) return Step{PH_HEAD, a.n_layers};
+  const int k = st % 5;
+  return Step{k == 0 ? PH_QKV : (k == 1 ? PH_ATT : (k == 2 ? PH_O : (k == 3 ? PH_GU : PH_DOWN))), st / 5};
+}
+
+template <typename T, int MT>
 __global__ __launch_bounds__(MEGA_THREADS) void k_mega(MegaArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  const Lds s = lds_carve<T>(smem_raw, a.M);
-  const CntLayout cl = cnt_layout(a.M, a.F, a.nh, x_chunk_for(a.M, (int)sizeof(T)), a.n_layers);
+  const Lds s = lds_carve<T>(smem_raw, a.M, a.d);
+  const CntLayout cl = cnt_layout(a.M, a.F, a.nh, x_chunk_for(a.M, (int)sizeof(T), a.d), a.n_layers);
   const int G = gridDim.x, b = blockIdx.x;
   const int wv = threadIdx.x >> 6;
   // ring counters and the consumer barrier start at zero
   for (int i = threadIdx.x; i < 2 * s.NS + 8; i += MEGA_THREADS) s.ints[i] = 0;
+  for (int i = threadIdx.x; i < a.M; i += MEGA_THREADS) s.hx[i] = a.hidx ? a.hidx[i] : i;
   __syncthreads();
   int deal = 0;
+  const int n_steps = 5 * a.n_layers + (a.do_head ? 1 : 0);
   if (wv >= NCONS) {
     // ------------------------------ producer waves ------------------------------
-    Producer<T, DP> pr(a, s, wv - NCONS);
-    for (int l = 0; l < a.n_layers; ++l) {
-      walk_gemm<T, MT, DP, true>(a, s, cl, PH_QKV, l, deal, &pr, nullptr, nullptr);
-      walk_gemm<T, MT, DP, true>(a, s, cl, PH_O, l, deal, &pr, nullptr, nullptr);
-      walk_gemm<T, MT, DP, true>(a, s, cl, PH_GU, l, deal, &pr, nullptr, nullptr);
-      walk_gemm<T, MT, DP, true>(a, s, cl, PH_DOWN, l, deal, &pr, nullptr, nullptr);
+    Producer<T> pr(a, s, wv - NCONS);
+#pragma unroll 1
+    for (int st = 0; st < n_steps; ++st) {
+      const Step sp = step_of(a, st);
+      if (sp.ph != PH_ATT) walk_gemm<T, MT, true>(a, s, cl, sp.ph, sp.l, deal, &pr, nullptr, nullptr);
     }
-    if (a.do_head) walk_gemm<T, MT, DP, true>(a, s, cl, PH_HEAD, a.n_layers, deal, &pr, nullptr, nullptr);
     pr.finish();
     return;
   }
   // ------------------------------ consumer waves ------------------------------
   ConsBar cb{s.ints + 2 * s.NS, 0, a.err};
   Consumer<T, MT> co(a, s, cb, wv);
-  auto stamp = [&](int l, int ph, int e) {
-    if (a.trace && l < 4 && threadIdx.x == 0) a.trace[(((size_t)b * 4 + l) * 6 + ph) * 2 + e] = wall_clock64();
-  };
   if (a.init_mode)
     for (int u = b; u < a.M; u += G) init_unit<T>(a, cl, cb, u);
   int att_deal = 0;
-  for (int l = 0; l < a.n_layers; ++l) {
-    stamp(l, 1, 0);
-    walk_gemm<T, MT, DP, false>(a, s, cl, PH_QKV, l, deal, nullptr, &co, &cb);
-    stamp(l, 1, 1);
-    stamp(l, 2, 0);
-    const int natt = a.M * a.nh * a.att_chunks;
-    const Share sa = share_of(natt, att_deal, G, b);
-    att_deal = (att_deal + natt) % G;
-    for (int k = 0; k < sa.count; ++k) {
-      const int u = sa.first + k * G;
-      const int cch = u % a.att_chunks, ih = u / a.att_chunks;
-      att_unit<T>(a, s, cl, cb, l, ih / a.nh, ih % a.nh, cch);
+#pragma unroll 1
+  for (int st = 0; st < n_steps; ++st) {
+    const Step sp = step_of(a, st);
+    if (threadIdx.x == 0) tstamp(a, sp.l, sp.ph, 0);
+    if (sp.ph == PH_ATT) {
+      const int natt = a.M * a.nh * a.att_chunks;
+      const Share sa = share_of(natt, att_deal, G, b);
+      att_deal = (att_deal + natt) % G;
+      for (int k = 0; k < sa.count; ++k) {
+        const int u = sa.first + k * G;
+        const int cch = u % a.att_chunks, ih = u / a.att_chunks;
+        att_unit<T>(a, s, cl, cb, sp.l, ih / a.nh, ih % a.nh, cch);
+      }
+    } else {
+      walk_gemm<T, MT, false>(a, s, cl, sp.ph, sp.l, deal, nullptr, &co, &cb);
     }
-    stamp(l, 2, 1);
-    stamp(l, 3, 0);
-    walk_gemm<T, MT, DP, false>(a, s, cl, PH_O, l, deal, nullptr, &co, &cb);
-    stamp(l, 3, 1);
-    stamp(l, 4, 0);
-    walk_gemm<T, MT, DP, false>(a, s, cl, PH_GU, l, deal, nullptr, &co, &cb);
-    stamp(l, 4, 1);
-    stamp(l, 5, 0);
-    walk_gemm<T, MT, DP, false>(a, s, cl, PH_DOWN, l, deal, nullptr, &co, &cb);
-    stamp(l, 5, 1);
+    if (threadIdx.x == 0) tstamp(a, sp.l, sp.ph, 1);
   }
-  if (a.do_head) walk_gemm<T, MT, DP, false>(a, s, cl, PH_HEAD, a.n_layers, deal, nullptr, &co, &cb);
 }
 
-__global__ void k_zero_i32(int* p, long long n) {
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
-    p[i] = 0;
+__global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, const double* inv_freq, int M, int half) {
+  const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x, str = (long long)gridDim.x * blockDim.x;
+  for (long long i = tid; i < n; i += str) cnt[i] = 0;
+  for (long long i = tid; i < (long long)M * half; i += str) {
+    const int m = (int)(i / half), f = (int)(i % half);
+    double sn, cs;
+    sincos((double)pos[m] * inv_freq[f], &sn, &cs);
+    rope[2 * i] = (float)cs;
+    rope[2 * i + 1] = (float)sn;
+  }
 }
 
 template <typename T>
 static const void* pick_t(int mt) {
-  if (mt <= 1) return reinterpret_cast<const void*>(&k_mega<T, 1, 8>);
-  if (mt <= 2) return reinterpret_cast<const void*>(&k_mega<T, 2, 4>);
-  if (mt <= 4) return reinterpret_cast<const void*>(&k_mega<T, 4, 4>);
-  return reinterpret_cast<const void*>(&k_mega<T, 8, 4>);
+  if (mt <= 1) return reinterpret_cast<const void*>(&k_mega<T, 1>);
+  if (mt <= 2) return reinterpret_cast<const void*>(&k_mega<T, 2>);
+  if (mt <= 4) return reinterpret_cast<const void*>(&k_mega<T, 4>);
+  return reinterpret_cast<const void*>(&k_mega<T, 8>);
 }
 
 static const void* pick(bool bf16, int M) {
@@ -886,18 +1151,19 @@ static const void* pick(bool bf16, int M) {
   return bf16 ? pick_t<uint16_t>(mt) : pick_t<float>(mt);
 }
 
-int mega_occupancy(bool bf16, int M, int KU) {
-  const size_t smem = mega_smem_bytes(bf16, M, KU);
+int mega_occupancy(bool bf16, int M, int d) {
+  const size_t smem = mega_smem_bytes(bf16, M, d);
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick(bf16, M), MEGA_THREADS, smem) != hipSuccess) return 0;
   return n;
 }
 
 hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s) {
-  const CntLayout cl = cnt_layout(a.M, a.F, a.nh, x_chunk_for(a.M, bf16 ? 2 : 4), a.n_layers);
-  hipLaunchKernelGGL(k_zero_i32, dim3(std::min(1024, (cl.total + 255) / 256)), dim3(256), 0, s, a.cnt,
-                     (long long)cl.total);
-  const size_t smem = mega_smem_bytes(bf16, a.M, a.KU);
+  const CntLayout cl = cnt_layout(a.M, a.F, a.nh, x_chunk_for(a.M, bf16 ? 2 : 4, a.d), a.n_layers);
+  const long long n_prep = std::max<long long>(cl.total, (long long)a.M * (a.hd / 2));
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<long long>(1024, (n_prep + 255) / 256)), dim3(256), 0, s, a.cnt,
+                     (long long)cl.total, a.rope, a.pos, a.inv_freq, a.M, a.hd / 2);
+  const size_t smem = mega_smem_bytes(bf16, a.M, a.d);
   void* args[] = {(void*)&a};
   return hipLaunchCooperativeKernel(pick(bf16, a.M), dim3(G), dim3(MEGA_THREADS), args, (unsigned)smem, s);
 }

@@ -1,45 +1,6 @@
-// Embedding gather (the prelude P of Ouro-like models, LoopSpec page section 2.1) and row
-// gathers of the hidden states.
+// Small helper kernels: fills and row validation.
 #include "common.h"
 #include "kernels.h"
-
-namespace ls {
-
-template <typename T>
-__global__ __launch_bounds__(256) void k_embed(const T* emb, const int32_t* tokens, const int32_t* slot, int V, int d,
-                                               long long S, float* H, int* err) {
-  const int m = blockIdx.x;
-  const int tok = tokens[m], sl = slot[m];
-  if (sl < 0) return;                             // row rejected by validation
-  if (tok < 0 || tok >= V || sl >= S) {
-    if (threadIdx.x == 0) ls_flag(err, 1);
-    return;
-  }
-  for (int i = threadIdx.x; i < d; i += 256) H[(size_t)sl * d + i] = Elem<T>::load(emb + (size_t)tok * d + i);
-}
-
-void launch_embed(bool bf16, const void* emb, const int32_t* tokens, const int32_t* slot, int M, int V, int d,
-                  long long S, float* H, int* err, hipStream_t s) {
-  if (bf16) hipLaunchKernelGGL(k_embed<uint16_t>, dim3(M), dim3(256), 0, s, (const uint16_t*)emb, tokens, slot, V, d, S, H, err);
-  else hipLaunchKernelGGL(k_embed<float>, dim3(M), dim3(256), 0, s, (const float*)emb, tokens, slot, V, d, S, H, err);
-}
-
-__global__ __launch_bounds__(256) void k_gather(const float* H, const int32_t* slot, int d, long long S, float* out, int* err) {
-  const int m = blockIdx.x;
-  const int sl = slot[m];
-  if (sl < 0 || sl >= S) {
-    if (threadIdx.x == 0) ls_flag(err, 1);
-    for (int i = threadIdx.x; i < d; i += 256) out[(size_t)m * d + i] = 0.f;
-    return;
-  }
-  for (int i = threadIdx.x; i < d; i += 256) out[(size_t)m * d + i] = H[(size_t)sl * d + i];
-}
-
-void launch_gather(const float* H, const int32_t* slot, int M, int d, long long S, float* out, int* err, hipStream_t s) {
-  hipLaunchKernelGGL(k_gather, dim3(M), dim3(256), 0, s, H, slot, d, S, out, err);
-}
-
-}  // namespace ls
 
 namespace ls {
 
