@@ -1,0 +1,65 @@
+"""Host-side checks of libloopspec that need no GPU: the shared library loads, exports every
+function include/loopspec.h declares, the Python binding names the same set, and the
+host-only Philox generator agrees with the oracle's (and with the published known answers,
+through the oracle's own pinned test)."""
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "loopspec.h")
+LIB = os.path.join(ROOT, "looped_transformer_self_amd", "libloopspec.so")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    pat = re.compile(r"(?:ls_status|void|size_t|const\s+char\s*\*)\s*\*?\s*(ls_[a-z0-9_]+)\s*\(")
+    return sorted(set(pat.findall(text)))
+
+
+def _lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libloopspec.so is not built (run __graft_entry__.build())")
+    return C.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("ls_prelude", "ls_loop_step", "ls_readout", "ls_verify", "ls_model_create", "ls_model_destroy",
+              "ls_workspace_bytes", "ls_bind_workspace", "ls_sync_status", "ls_last_error"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib()
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"declared in loopspec.h but not exported: {missing}"
+
+
+def test_binding_names_match_header():
+    from looped_transformer_self_amd import _lib as binding
+    assert sorted(binding.EXPORTS) == _declared_functions()
+
+
+def test_last_error_is_callable_without_gpu():
+    lib = _lib()
+    lib.ls_last_error.restype = C.c_char_p
+    assert isinstance(lib.ls_last_error(), bytes)
+
+
+@pytest.mark.parametrize("seed,pos", [(2, 0), (2, 511), (0xDEADBEEFCAFEF00D, 123456789), (7, 2 ** 33 + 5)])
+def test_host_philox_matches_oracle(seed, pos):
+    from oracle import philox
+    lib = _lib()
+    purposes = np.array([0, 1, 2, 3, 4, 5, 8, 9, 23], dtype=np.int32)
+    out = np.zeros(len(purposes), dtype=np.uint32)
+    lib.ls_philox_uniforms(C.c_uint64(seed), C.c_int64(pos), purposes.ctypes.data_as(C.c_void_p),
+                           C.c_int(len(purposes)), out.ctypes.data_as(C.c_void_p))
+    want = [philox.uniform(seed, pos, int(p)) for p in purposes]
+    assert out.tolist() == want
