@@ -26,7 +26,7 @@ struct MegaArgs {
   float* Ys;                    // per-layer attention-residual outputs at Ys + l*M*d
   const int32_t *slot, *pos, *dep, *fin, *anc_off, *anc, *tokens;
   int n_fin;
-  int att_chunks;               // 64-key chunks per (row, head)
+  int att_chunks;               // 64-key chunks of the finished prefix (>= 1)
   void* kv;                     // cache tensor; block(i, l) = (dep[i] + dep_off) * blk_mul + layer0 + l
   int dep_off, blk_mul, layer0;
   long long S;

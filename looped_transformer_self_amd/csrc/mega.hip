@@ -33,10 +33,16 @@ namespace ls {
 
 enum Phase { PH_INIT = 0, PH_QKV = 1, PH_ATT = 2, PH_O = 3, PH_GU = 4, PH_DOWN = 5, PH_HEAD = 6 };
 constexpr int ATT_CH = 64;              // keys per attention unit
-constexpr int NCONS = 4, NPROD = 4;
+constexpr int ATT_RB = 8;               // rows of a group an attention unit handles per pass
+constexpr int NCONS = 4, NPROD = 2;
 constexpr int MEGA_THREADS = 64 * (NCONS + NPROD);
 constexpr int SLAB = 8192;              // bytes: 16 rows x 512 bytes
 constexpr int PADC = 64;                // counters that are polled get their own 256-byte line
+
+// Wave index within the workgroup, known to the compiler to be wave-uniform (kept in SGPRs;
+// values derived from threadIdx.x are otherwise treated as divergent, which turns the walk's
+// bookkeeping into VGPR arithmetic under exec masks).
+LS_DEV int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 // ---- coherent (agent-scope) accesses ---------------------------------------------------------
 LS_DEV void drain() { __builtin_amdgcn_s_waitcnt(0); }
@@ -94,9 +100,24 @@ constexpr int SPIN_LIMIT = 1 << 25;
 constexpr int LS_TIMEOUT = 5;
 
 // ---- LDS synchronisation among the consumer waves only -----------------------------------------
-LS_DEV int lds_ld(const int* p) { return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); }
-LS_DEV void lds_add(int* p, int v) { __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); }
 
+// LDS signalling from inline assembly.  A compiler-visible LDS access after direct-to-LDS
+// loads (producers) gets a conservative wait for every one still in flight, and release or
+// acquire orderings make a wave wait for all of its outstanding global stores (consumers);
+// neither is needed for LDS-to-LDS signalling, where a wave's LDS operations complete in order.
+LS_DEV int lds_peek(const int* p) {
+  const unsigned addr = (unsigned)(size_t)(__attribute__((address_space(3))) const int*)p;
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return __builtin_amdgcn_readfirstlane(v);      // every lane read the same word
+}
+LS_DEV void lds_bump(int* p) {
+  const unsigned addr = (unsigned)(size_t)(__attribute__((address_space(3))) int*)p;
+  asm volatile("s_waitcnt lgkmcnt(0)\n\tds_add_u32 %0, %1" : : "v"(addr), "v"(1) : "memory");
+}
+
+// Barrier among the consumer waves (an LDS counter; the producer waves never take part).  It
+// orders LDS accesses only: global stores that other waves must see are drained explicitly.
 struct ConsBar {
   int* ctr;
   int gen;
@@ -104,15 +125,15 @@ struct ConsBar {
   LS_DEV void sync() {
     gen += NCONS;
     if ((threadIdx.x & 63) == 0) {
-      lds_add(ctr, 1);
+      lds_bump(ctr);
       int n = 0;
-      while (lds_ld(ctr) < gen) {
+      while (lds_peek(ctr) < gen) {
         __builtin_amdgcn_s_sleep(0);
         if (++n > SPIN_LIMIT) { ls_flag(err, LS_TIMEOUT); break; }
       }
     }
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    asm volatile("" : : : "memory");
   }
 };
 
@@ -176,12 +197,22 @@ struct LdsPlan {
   int NS, XC, nred;
 };
 constexpr int LDS_BUDGET = 160 * 1024 - 512;
+// The activation stage doubles as the attention scratch (queries, per-wave maxima, sums and
+// partial outputs of up to ATT_RB rows with head_dim <= 128).
+__host__ __device__ inline size_t x_region_bytes(int M, int esz, int XC) {
+  const size_t stage = (size_t)M * (XC + 16 / esz) * esz;
+  const size_t att = (size_t)(M < ATT_RB ? M : ATT_RB) * (5 * 128 + 8) * 4;
+  return stage > att ? stage : att;
+}
+// Per-launch row tables in LDS: rows by group [M], depth histogram [64], group offsets and
+// count [65], and copies of the rows' slot [M], depth [M] and ancestor offsets [M + 1].
+__host__ __device__ inline int row_table_ints(int M) { return M + 64 + 65 + M + M + M + 1; }
 __host__ __device__ inline size_t lds_bytes_for(int M, int esz, int NS, int XC, int nred) {
   size_t off = (size_t)NS * SLAB;
-  off = (off + (size_t)M * (XC + 16 / esz) * esz + 15) & ~(size_t)15;
+  off = (off + x_region_bytes(M, esz, XC) + 15) & ~(size_t)15;
+  off = (off + (size_t)row_table_ints(M) * 4 + 15) & ~(size_t)15;
   off = (off + (size_t)nred * NCONS * M * 16 * 4 + 15) & ~(size_t)15;
   off = (off + (size_t)M * 4 + 15) & ~(size_t)15;
-  off = (off + (4 * 128 + 64) * 4 + 15) & ~(size_t)15;
   off = (off + (size_t)M * 4 + 15) & ~(size_t)15;
   off += (2 * NS + 8) * 4;
   return off;
@@ -213,8 +244,10 @@ struct Lds {
   char* X;           // M x (XC + pad) elements
   float* red;        // nred x NCONS x M x 16: per-tile partials of the consumer waves
   float* rinv;       // M
-  float* scr;        // attention scratch: 4*128 + 64 floats
   int* hx;           // M: hidden-state row of each working row (-1: none)
+  int* grow;         // M: rows ordered by KV depth group (attention shares a group's keys)
+  int* goff;         // group g's rows: grow[goff[g] .. goff[g+1]); goff[64] = group count
+  int *rslot, *rdep, *raoff;   // the rows' validated slot, depth (0 without depths), ancestor offsets
   int* ints;         // [0..NS) full, [NS..2NS) empty, [2NS] consumer barrier, [2NS+1..] flags
   int xstride;       // elements
   int NS, XC, nred;
@@ -232,10 +265,15 @@ LS_DEV Lds lds_carve(char* base, int M, int d) {
   s.xstride = s.XC + 16 / (int)sizeof(T);
   size_t off = 0;
   s.ring = base; off += (size_t)s.NS * SLAB;
-  s.X = base + off; off = align16(off + (size_t)M * s.xstride * sizeof(T));
+  s.X = base + off; off = align16(off + x_region_bytes(M, (int)sizeof(T), s.XC));
+  s.grow = (int*)(base + off);
+  s.goff = s.grow + M + 64;
+  s.rslot = s.goff + 65;
+  s.rdep = s.rslot + M;
+  s.raoff = s.rdep + M;
+  off = align16(off + (size_t)row_table_ints(M) * 4);
   s.red = (float*)(base + off); off = align16(off + (size_t)s.nred * NCONS * M * 16 * 4);
   s.rinv = (float*)(base + off); off = align16(off + (size_t)M * 4);
-  s.scr = (float*)(base + off); off = align16(off + (4 * 128 + 64) * 4);
   s.hx = (int*)(base + off); off = align16(off + (size_t)M * 4);
   s.ints = (int*)(base + off);
   return s;
@@ -310,15 +348,8 @@ LS_DEV Share share_of(int n, int deal, int G, int b) {
   return s;
 }
 
-// LDS word read for the producer waves, from inline assembly with its wait in the same block:
-// a compiler-visible LDS read after direct-to-LDS loads gets a conservative wait for all of
-// them (vmcnt(0)), which would drain the prefetch pipeline at every ring-slot check.
-LS_DEV int lds_peek(const int* p) {
-  const unsigned addr = (unsigned)(size_t)(__attribute__((address_space(3))) const int*)p;
-  int v;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
-  return v;
-}
+// Wait for this wave's LDS (and scalar memory) operations only.
+LS_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
 // vmcnt-only wait with a compile-time count (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
 // lgkmcnt[11:8] | vmcnt[5:4] << 14; expcnt/lgkmcnt at their maxima = no wait).
@@ -370,10 +401,7 @@ struct Producer {
   // LDS access here would get a conservative wait for every direct-to-LDS load still in flight,
   // i.e. drain the prefetch pipeline at each slab.
   LS_DEV void publish_one() {
-    if (lane == 0) {
-      const unsigned addr = (unsigned)(size_t)(__attribute__((address_space(3))) int*)(s.ints + pslot);
-      asm volatile("ds_add_u32 %0, %1" : : "v"(addr), "v"(1) : "memory");
-    }
+    if (lane == 0) lds_bump(s.ints + pslot);
     ++pub;
     pslot += NPROD;
     if (pslot >= s.NS) pslot -= s.NS;
@@ -600,13 +628,13 @@ struct Consumer {
     if ((q & (NCONS - 1)) != c) return;
     if (lane == 0) {
       int n = 0;
-      while (lds_ld(s.ints + slot) < use + 1) {
+      while (lds_peek(s.ints + slot) < use + 1) {
         __builtin_amdgcn_s_sleep(0);
         if (++n > SPIN_LIMIT) { ls_flag(a.err, LS_TIMEOUT); break; }
       }
     }
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    asm volatile("" : : : "memory");
     if (dbg && a.trace && threadIdx.x == 0 && a.trace[(size_t)gridDim.x * 256 + (size_t)blockIdx.x * 32 + 6] == 0) dstamp(a, true, 6);
     dstamp(a, dbg, 7);
     constexpr int E = 16 / (int)sizeof(T);
@@ -630,15 +658,14 @@ struct Consumer {
       }
     }
     // ring reads are complete (their values fed the MFMAs) before the slot is released
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    if (lane == 0) lds_add(s.ints + s.NS + slot, 1);
+    if (lane == 0) lds_bump(s.ints + s.NS + slot);
     dstamp(a, dbg, 8);
   }
 };
 
 // Epilogue of one finished tile (its sum over the four consumers is in Ts[m*16 + n]).
 template <typename T>
-LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, const int* hx, int ph, int l, int t, const float* Ts,
+LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, const Lds& s, int ph, int l, int t, const float* Ts,
                      int lane) {
   (void)cl;
   if (ph == PH_QKV) {
@@ -659,9 +686,9 @@ LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, const int* hx, int 
         stc(a.q + (size_t)m * a.d + e0, y0);
         stc(a.q + (size_t)m * a.d + e1, y1);
       } else {
-        const int sl = a.slot[m];
+        const int sl = s.rslot[m];
         if (sl < 0) continue;
-        const int blk = (a.dep ? a.dep[m] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
+        const int blk = (a.dep ? s.rdep[m] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
         T* ent = (T*)a.kv + ((size_t)blk * a.S + sl) * 2 * a.d + (mat == 2 ? a.d : 0);
         Coh<T>::store(ent + e0, y0);
         Coh<T>::store(ent + e1, y1);
@@ -685,7 +712,7 @@ LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, const int* hx, int 
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int m = m0 + 4 * u + (lane >> 4);
-        const int hr = m < a.M ? hx[m] : -1;
+        const int hr = m < a.M ? s.hx[m] : -1;
         const int row = ph == PH_O && l == 0 ? hr : m;
         const int off = hr >= 0 ? (row * a.d + n) * 4 : 0x7fffffff;
         res[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(Rr, off, 0, 0));
@@ -693,7 +720,7 @@ LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, const int* hx, int 
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int m = m0 + 4 * u + (lane >> 4);
-        const int hr = m < a.M ? hx[m] : -1;
+        const int hr = m < a.M ? s.hx[m] : -1;
         const float nv = hr >= 0 ? res[u] + Ts[m * 16 + nl] : 0.f;
         if (m < a.M) {
           if (ph == PH_O) {
@@ -736,175 +763,347 @@ LS_DEV void tile_signal(const MegaArgs& a, const CntLayout& cl, int ph, int l, i
   }
 }
 
-// ---- attention unit (consumer waves) -----------------------------------------------------------------
-template <typename T>
-LS_DEV void load8f(const T* p, float* v);
-template <>
-LS_DEV void load8f<uint16_t>(const uint16_t* p, float* v) {
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-    const unsigned long long x = ldc64(p + 4 * h2);
-    const unsigned lo = (unsigned)x, hi = (unsigned)(x >> 32);
-    v[4 * h2 + 0] = __uint_as_float(lo << 16);
-    v[4 * h2 + 1] = __uint_as_float(lo & 0xffff0000u);
-    v[4 * h2 + 2] = __uint_as_float(hi << 16);
-    v[4 * h2 + 3] = __uint_as_float(hi & 0xffff0000u);
-  }
-}
-template <>
-LS_DEV void load8f<float>(const float* p, float* v) {
-#pragma unroll
-  for (int h2 = 0; h2 < 4; ++h2) {
-    const unsigned long long x = ldc64(p + 2 * h2);
-    v[2 * h2] = __uint_as_float((unsigned)x);
-    v[2 * h2 + 1] = __uint_as_float((unsigned)(x >> 32));
-  }
-}
+// ---- attention (consumer waves) -------------------------------------------------------------------
+// Causal decode attention of layer l, split over keys and merged with the log-sum-exp rule.
+// Rows are grouped by KV depth (a row at loop iteration k reads the depth-k cache, LoopSpec
+// section 2.1 and 2.4), and rows of one group share the finished prefix's keys:
+//  1. unit (group g, head h, chunk c): the prefix keys [64c, 64c + 64), for every row of the
+//     group at once, so those keys are read once per unit.  Wave w takes keys 16w..16w+15;
+//     lane = (key kk + 4rr, dims 8e..8e+7).  Partial (max, sum, acc[hd]) per row.
+//  2. the workgroup that finishes the group's last unit of head h merges, per row, those
+//     partials with the row's own keys (its speculative ancestors and itself, written by this
+//     launch) and stores o[l][row][h].
 
 template <typename T>
-LS_DEV void att_unit(const MegaArgs& a, const Lds& s, const CntLayout& cl, ConsBar& cb, int l, int i, int h, int c) {
-  int* C = a.cnt + (size_t)l * cl.per_layer;
-  const int self = a.slot[i];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;     // wv = consumer 0..3
-  const int kk = lane >> 4, e = lane & 15;
-  if (self < 0) {                               // rejected row: zero output, still counted
-    if (c == 0) {
-      wait_ge(C + cl.o_qkvh + h * PADC, 3 * (a.hd / 16), cb);
-      for (int dd = threadIdx.x; dd < a.hd; dd += 64 * NCONS)
-        Coh<T>::store(o_of<T>(a, l) + (size_t)i * a.d + h * a.hd + dd, 0.f);
-      drain();
-      cb.sync();
-      if (threadIdx.x == 0) atomicAdd(C + cl.o_att + h * PADC, 1);
+LS_DEV void load8_plain(const T* p, float* v);
+template <>
+LS_DEV void load8_plain<uint16_t>(const uint16_t* p, float* v) {
+  const uint4 x = *reinterpret_cast<const uint4*>(p);
+  const unsigned w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <>
+LS_DEV void load8_plain<float>(const float* p, float* v) {
+  const float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+  v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+}
+
+// Two adjacent elements of a K/V entry written by this launch (agent-coherent load).
+template <typename T>
+LS_DEV float2 load2_coh(const T* p);
+template <>
+LS_DEV float2 load2_coh<uint16_t>(const uint16_t* p) {
+  const unsigned w = __hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+template <>
+LS_DEV float2 load2_coh<float>(const float* p) {
+  const unsigned long long w = ldc64(p);
+  return make_float2(__uint_as_float((unsigned)w), __uint_as_float((unsigned)(w >> 32)));
+}
+template <typename T>
+LS_DEV void store2_coh(T* p, float x, float y);
+template <>
+LS_DEV void store2_coh<uint16_t>(uint16_t* p, float x, float y) {
+  const unsigned w = (unsigned)f2bf(x) | ((unsigned)f2bf(y) << 16);
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <>
+LS_DEV void store2_coh<float>(float* p, float x, float y) {
+  const unsigned long long w = (unsigned long long)__float_as_uint(x) | ((unsigned long long)__float_as_uint(y) << 32);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Group the call's rows by KV depth (at kernel start, all threads).  Depth values index a
+// 64-bin histogram; rows with no depth array form one group.
+LS_DEV void group_rows(const MegaArgs& a, const Lds& s) {
+  int* hist = s.grow + a.M;
+  for (int i = threadIdx.x; i < 64; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  for (int m = threadIdx.x; m < a.M; m += blockDim.x) {
+    const int dv = min(max(s.rdep[m], 0), 63);
+    atomicAdd(hist + dv, 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int cnt = hist[lane];
+    // exclusive prefix of the counts and of the non-empty bins, in bin order
+    int pre = cnt, ne = cnt > 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int x = __shfl_up(pre, o, 64), y = __shfl_up(ne, o, 64);
+      if (lane >= o) { pre += x; ne += y; }
     }
-    return;
+    const int start = pre - cnt, gidx = ne - (cnt > 0);
+    if (cnt > 0) s.goff[gidx] = start;
+    if (lane == 63) { s.goff[ne] = pre; s.goff[64] = ne; }
+    hist[lane] = start;                          // fill cursor of the bin
   }
-  const int a0 = a.anc_off[i], na = a.anc_off[i + 1] - a0;
-  const int nk = a.n_fin + na + 1;
-  const int nc = (nk + ATT_CH - 1) / ATT_CH;
-  if (c >= nc) return;
-  const int k0 = c * ATT_CH;
-  const int kn = min(ATT_CH, nk - k0);
-  const int blk = (a.dep ? a.dep[i] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
-  const T* cache = (const T*)a.kv + (size_t)blk * a.S * 2 * a.d;
-  const bool dim_ok = 8 * e < a.hd;
+  __syncthreads();
+  for (int m = threadIdx.x; m < a.M; m += blockDim.x) {
+    const int dv = min(max(s.rdep[m], 0), 63);
+    s.grow[atomicAdd(hist + dv, 1)] = m;         // order inside a group does not affect results
+  }
+  __syncthreads();
+}
 
+template <typename T>
+LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, ConsBar& cb, int l, int g, int h, int nu);
+
+template <typename T>
+LS_DEV void att_chunk(const MegaArgs& a, const Lds& s, const CntLayout& cl, ConsBar& cb, int l, int g, int h, int c,
+                      int nu) {
+  int* C = a.cnt + (size_t)l * cl.per_layer;
+  const int lane = threadIdx.x & 63, wv = wave_id();     // wv = consumer 0..3
+  const int kk = lane >> 4, e = lane & 15;
+  const int hd = a.hd;
+  const bool dim_ok = 8 * e < hd;
+  const int g0 = s.goff[g], ng = s.goff[g + 1] - g0;
+  const int rep = s.grow[g0];
+  const int blk = (a.dep ? s.rdep[rep] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
+  const T* cache = (const T*)a.kv + (size_t)blk * a.S * 2 * a.d;
+  const int k0 = c * ATT_CH;
+  const int kn = max(0, min(ATT_CH, a.n_fin - k0));
+  const bool dbg = l == 0 && a.trace && a.trace[(size_t)gridDim.x * 256 + (size_t)blockIdx.x * 32 + 16] == 0;
+  dstamp(a, dbg, 16);
+
+  // prefix keys were written by earlier launches: plain loads, issued before the wait
+  // all slot indices first, then all K/V loads (a load behind a branch with a side effect
+  // would wait for the one before it)
   int sl[4];
+  float kf[4][8], vf[4][8];
+  bool bad = false;
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int jk = wv * 16 + kk + 4 * rr;
-    sl[rr] = -1;
-    if (jk < kn) {
-      const int x = key_slot(k0 + jk, a.n_fin, a.fin, a.anc, a0, na, self);
-      sl[rr] = (x >= 0 && x < a.S) ? x : -1;
-      if (x < 0 || x >= a.S) ls_flag(a.err, 1);
+    sl[rr] = jk < kn ? a.fin[k0 + min(jk, kn - 1)] : -1;
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int jk = wv * 16 + kk + 4 * rr;
+    if (jk < kn && (sl[rr] < 0 || sl[rr] >= a.S)) { bad = true; sl[rr] = -1; }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) kf[rr][t] = vf[rr][t] = 0.f;
+    if (sl[rr] >= 0 && dim_ok) {
+      load8_plain<T>(cache + (size_t)sl[rr] * 2 * a.d + h * hd + 8 * e, kf[rr]);
+      load8_plain<T>(cache + (size_t)sl[rr] * 2 * a.d + a.d + h * hd + 8 * e, vf[rr]);
     }
   }
-  float kf[4][8], vf[4][8];
-  const bool early = k0 + kn <= a.n_fin;     // keys written by earlier calls only
-  auto load_kv = [&]() {
+  if (bad) ls_flag(a.err, 1);
+  dstamp(a, dbg, 17);
+  wait_ge(C + cl.o_qkvh + h * PADC, 3 * (hd / 16), cb);
+  dstamp(a, dbg, 18);
+
+  const float scale = 1.0f / sqrtf((float)hd);
+  const __amdgpu_buffer_rsrc_t Rq = rsrc_of(a.q, a.M * a.d * 4);
+  auto scores = [&](const float* qs, int r, float* sc) {
+    float q8[8];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      if (sl[rr] >= 0 && dim_ok) {
-        load8f<T>(cache + (size_t)sl[rr] * 2 * a.d + h * a.hd + 8 * e, kf[rr]);
-        load8f<T>(cache + (size_t)sl[rr] * 2 * a.d + a.d + h * a.hd + 8 * e, vf[rr]);
-      }
+    for (int t = 0; t < 8; ++t) q8[t] = dim_ok ? qs[r * hd + 8 * e + t] : 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float part = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) part += q8[t] * kf[rr][t];
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+      sc[rr] = sl[rr] >= 0 ? part : -INFINITY;
+    }
   };
-  if (early) load_kv();
-  wait_ge(C + cl.o_qkvh + h * PADC, 3 * (a.hd / 16), cb);
-  if (!early) load_kv();
-  float q[8];
-  const float scale = 1.0f / sqrtf((float)a.hd);
-  {
-    const __amdgpu_buffer_rsrc_t Rq = rsrc_of(a.q + (size_t)i * a.d + h * a.hd, a.hd * 4);
-    const u32x4_t q0 = ldc128(Rq, 32 * e), q1 = ldc128(Rq, 32 * e + 16);
+  // the group's rows, ATT_RB at a time
+  for (int rb = 0; rb < ng; rb += ATT_RB) {
+    const int nb = min(ATT_RB, ng - rb);
+    float* qs = (float*)s.X;                 // [nb][hd] scaled queries
+    float* wmx = qs + nb * hd;               // [nb][4] per-wave maxima
+    float* wsm = wmx + 4 * nb;               // [nb][4] per-wave sums
+    float* wac = wsm + 4 * nb;               // [nb][4][hd] per-wave partial outputs
+    if (rb > 0) cb.sync();                   // previous pass's readers are done with the scratch
+    for (int idx = threadIdx.x; idx < nb * (hd / 4); idx += 64 * NCONS) {
+      const int r = idx / (hd / 4), q4 = idx - r * (hd / 4);
+      const int i = s.grow[g0 + rb + r];
+      const u32x4_t v = ldc128(Rq, (i * a.d + h * hd + 4 * q4) * 4);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      q[t] = __uint_as_float(q0[t]) * scale;
-      q[4 + t] = __uint_as_float(q1[t]) * scale;
+      for (int t = 0; t < 4; ++t) qs[r * hd + 4 * q4 + t] = __uint_as_float(v[t]) * scale;
+    }
+    cb.sync();
+    dstamp(a, dbg, 19);
+    // pass 1: this wave's maximum per row
+    for (int r = 0; r < nb; ++r) {
+      float sc[4];
+      scores(qs, r, sc);
+      float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      if (lane == 0) wmx[r * 4 + wv] = mloc;
+    }
+    cb.sync();
+    dstamp(a, dbg, 20);
+    // pass 2: weights against the unit's maximum, partial sums and P.V
+    for (int r = 0; r < nb; ++r) {
+      const float mx = fmaxf(fmaxf(wmx[r * 4], wmx[r * 4 + 1]), fmaxf(wmx[r * 4 + 2], wmx[r * 4 + 3]));
+      float sc[4];
+      scores(qs, r, sc);
+      float lsum = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float pw = sl[rr] >= 0 ? __expf(sc[rr] - mx) : 0.f;
+        lsum += pw;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] += pw * vf[rr][t];
+      }
+      lsum += __shfl_xor(lsum, 16, 64);
+      lsum += __shfl_xor(lsum, 32, 64);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        acc[t] += __shfl_xor(acc[t], 16, 64);
+        acc[t] += __shfl_xor(acc[t], 32, 64);
+      }
+      if (lane == 0) wsm[r * 4 + wv] = lsum;
+      if (kk == 0 && dim_ok) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) wac[(r * 4 + wv) * hd + 8 * e + t] = acc[t];
+      }
+    }
+    cb.sync();
+    dstamp(a, dbg, 21);
+    // the unit's partial per row: (max, sum, acc[hd]), waves combined in fixed order
+    for (int idx = threadIdx.x; idx < nb * (hd + 2); idx += 64 * NCONS) {
+      const int r = idx / (hd + 2), dd = idx - r * (hd + 2);
+      const int i = s.grow[g0 + rb + r];
+      float* out = a.patt + (((size_t)i * a.nh + h) * a.att_chunks + c) * (hd + 2);
+      float v;
+      if (dd == 0) v = fmaxf(fmaxf(wmx[r * 4], wmx[r * 4 + 1]), fmaxf(wmx[r * 4 + 2], wmx[r * 4 + 3]));
+      else if (dd == 1) v = (wsm[r * 4] + wsm[r * 4 + 1]) + (wsm[r * 4 + 2] + wsm[r * 4 + 3]);
+      else {
+        const int x = dd - 2;
+        v = (wac[(r * 4) * hd + x] + wac[(r * 4 + 1) * hd + x]) + (wac[(r * 4 + 2) * hd + x] + wac[(r * 4 + 3) * hd + x]);
+      }
+      stc(out + dd, v);
     }
   }
-  float sc[4];
-  float mloc = -INFINITY;
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    float part = 0.f;
-    if (sl[rr] >= 0 && dim_ok) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) part += q[t] * kf[rr][t];
-    }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-    sc[rr] = sl[rr] >= 0 ? part : -INFINITY;
-    mloc = fmaxf(mloc, sc[rr]);
-  }
-  float* red = s.scr + 4 * 128;
-  mloc = warp_max(mloc);
-  if (lane == 0) red[wv] = mloc;
-  cb.sync();
-  const float mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float lsum = 0.f;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const float p = sc[rr] == -INFINITY ? 0.f : __expf(sc[rr] - mx);
-    if (e == 0) lsum += p;
-    if (sl[rr] >= 0 && dim_ok) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] += p * vf[rr][t];
-    }
-  }
-  lsum = warp_sum(lsum);
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    acc[t] += __shfl_xor(acc[t], 16, 64);
-    acc[t] += __shfl_xor(acc[t], 32, 64);
-  }
-  cb.sync();                                    // red[] reuse
-  if (lane == 0) red[4 + wv] = lsum;
-  if (kk == 0 && dim_ok) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) s.scr[wv * 128 + 8 * e + t] = acc[t];
-  }
-  cb.sync();
-  float* out = a.patt + (((size_t)i * a.nh + h) * a.att_chunks + c) * (a.hd + 2);
-  for (int dd = threadIdx.x; dd < a.hd; dd += 64 * NCONS)
-    stc(out + 2 + dd, s.scr[dd] + s.scr[128 + dd] + s.scr[256 + dd] + s.scr[384 + dd]);
-  if (threadIdx.x == 0) { stc(out, mx); stc(out + 1, red[4] + red[5] + red[6] + red[7]); }
+  dstamp(a, dbg, 22);
   drain();
   cb.sync();
+  dstamp(a, dbg, 23);
   int* flag = s.ints + 2 * s.NS + 1;
-  if (threadIdx.x == 0) *flag = atomicAdd(C + cl.o_fa + i * a.nh + h, 1);
+  if (threadIdx.x == 0) *flag = atomicAdd(C + cl.o_fa + g * a.nh + h, 1);
   cb.sync();
+  dstamp(a, dbg, 24);
   const int arrived = *flag;
-  cb.sync();
-  if (arrived != nc - 1) return;
-  // the last chunk merges all chunks of (row, head) in chunk order; the per-chunk maxima and
-  // sums are staged in LDS first so every output loads its partials independently
-  const float* base = a.patt + ((size_t)i * a.nh + h) * a.att_chunks * (a.hd + 2);
-  float* cmx = (float*)s.X;                          // the activation stage is free during attention
-  for (int cc = threadIdx.x; cc < nc; cc += 64 * NCONS) {
-    cmx[cc] = ldc(base + (size_t)cc * (a.hd + 2));
-    cmx[a.att_chunks + cc] = ldc(base + (size_t)cc * (a.hd + 2) + 1);
+  if (arrived == nu - 1) {
+    att_merge<T>(a, s, cl, cb, l, g, h, nu);
+    dstamp(a, dbg, 25);
   }
-  cb.sync();
-  float M_ = -INFINITY;
-  for (int cc = 0; cc < nc; ++cc) M_ = fmaxf(M_, cmx[cc]);
-  float den = 0.f;
-  for (int cc = 0; cc < nc; ++cc) den += (cmx[cc] == -INFINITY ? 0.f : __expf(cmx[cc] - M_)) * cmx[a.att_chunks + cc];
-  for (int dd = threadIdx.x; dd < a.hd; dd += 64 * NCONS) {
-    float num = 0.f;
-    for (int c0 = 0; c0 < nc; c0 += 8) {       // eight chunk partials in flight per pass
-      float pv[8];
+}
+
+// Merge of head h for the rows of group g: one wave per row, lane = dims 2*lane, 2*lane + 1.
+// Online log-sum-exp over batches of (16 prefix-chunk partials, 8 own keys); every load of a
+// batch is issued before any is used, so a batch costs one memory round trip.
+template <typename T>
+LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, ConsBar& cb, int l, int g, int h, int nu) {
+  int* C = a.cnt + (size_t)l * cl.per_layer;
+  const int lane = threadIdx.x & 63, wv = wave_id();
+  const int hd = a.hd;
+  const bool dok = 2 * lane < hd;
+  const int g0 = s.goff[g], ng = s.goff[g + 1] - g0;
+  const int rep = s.grow[g0];
+  const int blk = (a.dep ? s.rdep[rep] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
+  const T* cache = (const T*)a.kv + (size_t)blk * a.S * 2 * a.d;
+  const float scale = 1.0f / sqrtf((float)hd);
+  for (int r = wv; r < ng; r += NCONS) {
+    const int i = s.grow[g0 + r];
+    T* orow = o_of<T>(a, l) + (size_t)i * a.d + h * hd;
+    const int self = s.rslot[i];
+    if (self < 0) {                                  // rejected row: zero output
+      if (dok) store2_coh<T>(orow + 2 * lane, 0.f, 0.f);
+      continue;
+    }
+    const int a0 = s.raoff[i], na = s.raoff[i + 1] - a0;
+    const int nt = na + 1;                           // the row's own keys: ancestors, then itself
+    const float* base = a.patt + ((size_t)i * a.nh + h) * a.att_chunks * (hd + 2);
+    float q0 = 0.f, q1 = 0.f;
+    if (dok) {
+      const unsigned long long qw = ldc64(a.q + (size_t)i * a.d + h * hd + 2 * lane);
+      q0 = __uint_as_float((unsigned)qw) * scale;
+      q1 = __uint_as_float((unsigned)(qw >> 32)) * scale;
+    }
+    float run_m = -INFINITY, den = 0.f, num0 = 0.f, num1 = 0.f;
+    const int nbat = max((nu + 15) / 16, (nt + 7) / 8);
+    for (int bt = 0; bt < nbat; ++bt) {
+      const int c0 = bt * 16, j0 = bt * 8;
+      // ---- issue the batch's loads
+      const int cl_ = c0 + lane;                     // chunk whose statistics this lane holds
+      float mxc = -INFINITY, smc = 0.f;
+      if (lane < 16 && cl_ < nu) {
+        mxc = ldc(base + (size_t)cl_ * (hd + 2));
+        smc = ldc(base + (size_t)cl_ * (hd + 2) + 1);
+      }
+      float2 ac[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) pv[u] = ldc(base + (size_t)min(c0 + u, nc - 1) * (a.hd + 2) + 2 + dd);
+      for (int u = 0; u < 16; ++u) {
+        const int cc = min(c0 + u, nu - 1);
+        ac[u] = make_float2(0.f, 0.f);
+        if (dok && c0 + u < nu) {
+          const unsigned long long w = ldc64(base + (size_t)cc * (hd + 2) + 2 + 2 * lane);
+          ac[u] = make_float2(__uint_as_float((unsigned)w), __uint_as_float((unsigned)(w >> 32)));
+        }
+      }
+      float2 k2[8], v2[8];
+      int xs[8];
+      bool bad = false;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int cc = c0 + u;
-        const float wgt = (cc >= nc || cmx[min(cc, nc - 1)] == -INFINITY) ? 0.f : __expf(cmx[min(cc, nc - 1)] - M_);
-        num += wgt * pv[u];
+        const int j = min(j0 + u, nt - 1);
+        xs[u] = j < na ? a.anc[a0 + j] : self;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (xs[u] < 0 || xs[u] >= a.S) { bad = bad || j0 + u < nt; xs[u] = self; }
+        const T* ent = cache + (size_t)xs[u] * 2 * a.d + h * hd + 2 * lane;
+        k2[u] = v2[u] = make_float2(0.f, 0.f);
+        if (dok && j0 + u < nt) {
+          k2[u] = load2_coh<T>(ent);
+          v2[u] = load2_coh<T>(ent + a.d);
+        }
+      }
+      if (bad) ls_flag(a.err, 1);
+      // ---- the batch's scores and its maximum
+      float sc[8];
+      float bm = warp_max(mxc);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        sc[u] = warp_sum(q0 * k2[u].x + q1 * k2[u].y);
+        if (j0 + u < nt) bm = fmaxf(bm, sc[u]);
+      }
+      const float nm = fmaxf(run_m, bm);
+      if (nm == -INFINITY) continue;                 // nothing in this batch or before
+      const float rs = run_m == -INFINITY ? 0.f : __expf(run_m - nm);
+      den *= rs; num0 *= rs; num1 *= rs;
+      run_m = nm;
+      // prefix chunks: weight w_c = exp(mx_c - m) held by lane c - c0
+      const float wl = mxc == -INFINITY ? 0.f : __expf(mxc - nm);
+      den += warp_sum(wl * smc);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float w = __shfl(wl, u, 64);
+        num0 += w * ac[u].x;
+        num1 += w * ac[u].y;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = j0 + u < nt ? __expf(sc[u] - nm) : 0.f;
+        den += w;
+        num0 += w * v2[u].x;
+        num1 += w * v2[u].y;
       }
     }
-    Coh<T>::store(o_of<T>(a, l) + (size_t)i * a.d + h * a.hd + dd, den > 0.f ? num / den : 0.f);
+    if (dok) store2_coh<T>(orow + 2 * lane, den > 0.f ? num0 / den : 0.f, den > 0.f ? num1 / den : 0.f);
   }
   drain();
   cb.sync();
@@ -1001,7 +1200,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
         if (ph == PH_O) {
           const int h0 = x0 / a.hd, h1 = (x0 + xn - 1) / a.hd;
           for (int hb = h0; hb <= h1; hb += 64)
-            wait_all_ge(C + cl.o_att + hb * PADC, PADC, min(64, h1 + 1 - hb), a.M, *cb);
+            wait_all_ge(C + cl.o_att + hb * PADC, PADC, min(64, h1 + 1 - hb), s.goff[64], *cb);
         } else if (ph == PH_DOWN) {
           wait_ge(C + cl.o_gu + ch * PADC, xn / 8, *cb);
         } else {
@@ -1050,8 +1249,8 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
           buf[idx] = y;                   // consumer 0's slot now holds the tile sum
         }
         __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        epilogue<T>(a, cl, s.hx, ph, l, t, buf, lane);
+        wait_lgkm0();                      // the sums are visible to every lane
+        epilogue<T>(a, cl, s, ph, l, t, buf, lane);
         dstamp(a, co->dbg, 11);
         if (ph != PH_HEAD) {
           drain();
@@ -1082,10 +1281,17 @@ __global__ __launch_bounds__(MEGA_THREADS) void k_mega(MegaArgs a) {
   const Lds s = lds_carve<T>(smem_raw, a.M, a.d);
   const CntLayout cl = cnt_layout(a.M, a.F, a.nh, x_chunk_for(a.M, (int)sizeof(T), a.d), a.n_layers);
   const int G = gridDim.x, b = blockIdx.x;
-  const int wv = threadIdx.x >> 6;
+  const int wv = wave_id();
   // ring counters and the consumer barrier start at zero
   for (int i = threadIdx.x; i < 2 * s.NS + 8; i += MEGA_THREADS) s.ints[i] = 0;
-  for (int i = threadIdx.x; i < a.M; i += MEGA_THREADS) s.hx[i] = a.hidx ? a.hidx[i] : i;
+  for (int i = threadIdx.x; i < a.M; i += MEGA_THREADS) {
+    s.hx[i] = a.hidx ? a.hidx[i] : i;
+    s.rslot[i] = a.slot[i];
+    s.rdep[i] = a.dep ? a.dep[i] : 0;
+  }
+  for (int i = threadIdx.x; i <= a.M; i += MEGA_THREADS) s.raoff[i] = a.anc_off ? a.anc_off[i] : 0;
+  __syncthreads();
+  group_rows(a, s);
   __syncthreads();
   int deal = 0;
   const int n_steps = 5 * a.n_layers + (a.do_head ? 1 : 0);
@@ -1111,13 +1317,14 @@ __global__ __launch_bounds__(MEGA_THREADS) void k_mega(MegaArgs a) {
     const Step sp = step_of(a, st);
     if (threadIdx.x == 0) tstamp(a, sp.l, sp.ph, 0);
     if (sp.ph == PH_ATT) {
-      const int natt = a.M * a.nh * a.att_chunks;
+      const int nu = a.att_chunks;                 // prefix chunks per (group, head), >= 1
+      const int natt = s.goff[64] * a.nh * nu;
       const Share sa = share_of(natt, att_deal, G, b);
       att_deal = (att_deal + natt) % G;
       for (int k = 0; k < sa.count; ++k) {
         const int u = sa.first + k * G;
-        const int cch = u % a.att_chunks, ih = u / a.att_chunks;
-        att_unit<T>(a, s, cl, cb, sp.l, ih / a.nh, ih % a.nh, cch);
+        const int cch = u % nu, gh = u / nu;
+        att_chunk<T>(a, s, cl, cb, sp.l, gh / a.nh, gh % a.nh, cch, nu);
       }
     } else {
       walk_gemm<T, MT, false>(a, s, cl, sp.ph, sp.l, deal, nullptr, &co, &cb);
