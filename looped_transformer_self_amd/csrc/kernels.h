@@ -26,7 +26,7 @@ struct MegaArgs {
   float* Ys;                    // per-layer attention-residual outputs at Ys + l*M*d
   const int32_t *slot, *pos, *dep, *fin, *anc_off, *anc, *tokens;
   int n_fin;
-  int att_chunks;               // 64-key chunks of the finished prefix (>= 1)
+  int att_chunks;               // attention units per (group, head): ceil(n_fin / att_unit_keys), >= 1
   void* kv;                     // cache tensor; block(i, l) = (dep[i] + dep_off) * blk_mul + layer0 + l
   int dep_off, blk_mul, layer0;
   long long S;
@@ -49,6 +49,7 @@ struct MegaArgs {
 size_t mega_counter_ints(int M, int d, int F, int nh, int n_layers);
 size_t mega_smem_bytes(bool bf16, int M, int d);
 int mega_occupancy(bool bf16, int M, int d);
+int att_unit_keys(bool bf16);   // prefix keys per attention unit
 hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s);
 
 void launch_validate(int n, const int32_t* slot, const int32_t* dep, int dep_lo, int dep_hi, const int32_t* pos,

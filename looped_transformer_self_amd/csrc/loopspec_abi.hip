@@ -96,7 +96,8 @@ Carve carve(const ls_model* m, int max_rows, int max_keys, int max_jobs) {
   c.off_act = take(nl * layer_slice(R, d.F) * es);
   c.off_invf = take((size_t)d.head_dim / 2 * 8);
   c.off_rope = take(R * (size_t)d.head_dim * 4);
-  const size_t att_chunks = std::max(1, (max_keys + 63) / 64);
+  const int uk = att_unit_keys(d.dtype == LS_BF16);
+  const size_t att_chunks = std::max(1, (max_keys + uk - 1) / uk);
   c.off_patt = take(R * d.n_heads * att_chunks * (d.head_dim + 2) * 4);
   c.off_ssq = take(nl * 2 * (d.d / 16) * R * 4);
   c.off_cnt = take(mega_counter_ints(max_rows, d.d, d.F, d.n_heads, (int)nl) * 4);
@@ -252,7 +253,8 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
   a.fin = r->fin_slots; a.anc_off = r->anc_off + i0; a.anc = r->anc_slots;
   a.tokens = tokens ? tokens + i0 : nullptr;
   a.n_fin = r->n_fin;
-  a.att_chunks = std::max(1, (r->n_fin + 63) / 64);   // 64-key chunks of the finished prefix
+  const int uk = att_unit_keys(m->bf16());
+  a.att_chunks = std::max(1, (r->n_fin + uk - 1) / uk);   // attention units of the finished prefix
   a.kv = kv; a.dep_off = dep_off; a.blk_mul = blk_mul; a.layer0 = 0; a.S = d.slot_capacity;
   a.q = m->q; a.o = m->o; a.act = m->act;
   a.logits = logits; a.ldo = d.V;

@@ -32,8 +32,6 @@
 namespace ls {
 
 enum Phase { PH_INIT = 0, PH_QKV = 1, PH_ATT = 2, PH_O = 3, PH_GU = 4, PH_DOWN = 5, PH_HEAD = 6 };
-constexpr int ATT_CH = 64;              // keys per attention unit
-constexpr int ATT_RB = 8;               // rows of a group an attention unit handles per pass
 constexpr int NCONS = 4, NPROD = 2;
 constexpr int MEGA_THREADS = 64 * (NCONS + NPROD);
 constexpr int SLAB = 8192;              // bytes: 16 rows x 512 bytes
@@ -97,6 +95,13 @@ template <> struct Coh<float> {
 // records LS_TIMEOUT in the error word, so a broken dependency ends the kernel with an error
 // instead of hanging the device.
 constexpr int SPIN_LIMIT = 1 << 25;
+// Global counters are polled by up to every workgroup at once; each poll is a memory access
+// to the same line, so polls are spaced (s_sleep units of 64 cycles) to leave that line's
+// bandwidth to the atomics that move the counter.
+#ifndef LS_POLL_SLEEP
+#define LS_POLL_SLEEP 8
+#endif
+constexpr int POLL_SLEEP = LS_POLL_SLEEP;
 constexpr int LS_TIMEOUT = 5;
 
 // ---- LDS synchronisation among the consumer waves only -----------------------------------------
@@ -142,7 +147,7 @@ LS_DEV void wait_ge(const int* c, int target, ConsBar& cb) {
   if (threadIdx.x == 0) {
     int n = 0;
     while (ld_acq(c) < target) {
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(POLL_SLEEP);
       if (++n > SPIN_LIMIT) { ls_flag(cb.err, LS_TIMEOUT); break; }
     }
   }
@@ -159,7 +164,7 @@ LS_DEV void wait_all_ge(const int* base, int stride, int n, int target, ConsBar&
     while (true) {
       if (!done) done = ld_acq(base + (size_t)i * stride) >= target;
       if (__all(done)) break;
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(POLL_SLEEP);
       if (++n_polls > SPIN_LIMIT) { if (i == 0) ls_flag(cb.err, LS_TIMEOUT); break; }
     }
   }
@@ -197,13 +202,7 @@ struct LdsPlan {
   int NS, XC, nred;
 };
 constexpr int LDS_BUDGET = 160 * 1024 - 512;
-// The activation stage doubles as the attention scratch (queries, per-wave maxima, sums and
-// partial outputs of up to ATT_RB rows with head_dim <= 128).
-__host__ __device__ inline size_t x_region_bytes(int M, int esz, int XC) {
-  const size_t stage = (size_t)M * (XC + 16 / esz) * esz;
-  const size_t att = (size_t)(M < ATT_RB ? M : ATT_RB) * (5 * 128 + 8) * 4;
-  return stage > att ? stage : att;
-}
+__host__ __device__ inline size_t x_region_bytes(int M, int esz, int XC) { return (size_t)M * (XC + 16 / esz) * esz; }
 // Per-launch row tables in LDS: rows by group [M], depth histogram [64], group offsets and
 // count [65], and copies of the rows' slot [M], depth [M] and ancestor offsets [M + 1].
 __host__ __device__ inline int row_table_ints(int M) { return M + 64 + 65 + M + M + M + 1; }
@@ -853,162 +852,197 @@ LS_DEV void group_rows(const MegaArgs& a, const Lds& s) {
   __syncthreads();
 }
 
+// Keys of the finished prefix one attention unit covers: NPASS passes, each giving every lane
+// RR keys (for its 8 head dims); lanes hold one pass in registers while the next is in flight.
 template <typename T>
-LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, ConsBar& cb, int l, int g, int h, int nu);
+struct AttUnit {
+  static constexpr int RR = sizeof(T) == 2 ? 2 : 1;     // keys per lane per pass
+  static constexpr int NPASS = 8;
+  static constexpr int KEYS = 4 * RR * NPASS;             // 64 (bf16) / 32 (fp32)
+};
+int att_unit_keys(bool bf16) { return bf16 ? AttUnit<uint16_t>::KEYS : AttUnit<float>::KEYS; }
+
+// 8 consecutive elements of a K or V entry as raw storage words.
+template <typename T>
+struct Raw8 {
+  u32x4_t w[sizeof(T) / 2];
+  LS_DEV void load(const T* p) {
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 2); ++i) w[i] = *reinterpret_cast<const u32x4_t*>(p + i * (16 / sizeof(T)));
+  }
+  LS_DEV void zero() {
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 2); ++i) w[i] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+  LS_DEV void unpack(float* f) const {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[0][i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[0][i] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[i] = __uint_as_float(w[0][i]);
+        f[4 + i] = __uint_as_float(w[1][i]);
+      }
+    }
+  }
+};
 
 template <typename T>
-LS_DEV void att_chunk(const MegaArgs& a, const Lds& s, const CntLayout& cl, ConsBar& cb, int l, int g, int h, int c,
-                      int nu) {
+LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, int l, int g, int h, int nu);
+
+// One wave processes unit (g, h, c): prefix keys [KEYS*c, KEYS*c + KEYS) for every row of
+// group g, with no workgroup synchronisation.  Lane = (key kk of each group of four, dims
+// 8e..8e+7); key j of pass p = 4*RR*p + kk + 4*rr.  Online log-sum-exp over the passes;
+// partial (max, sum, acc[hd]) per row to the partial buffer; the wave that completes the last
+// unit of (g, h) merges.
+template <typename T>
+LS_DEV void att_unit_wave(const MegaArgs& a, const Lds& s, const CntLayout& cl, int l, int g, int h, int c, int nu) {
+  constexpr int RR = AttUnit<T>::RR, NPASS = AttUnit<T>::NPASS, KEYS = AttUnit<T>::KEYS;
   int* C = a.cnt + (size_t)l * cl.per_layer;
-  const int lane = threadIdx.x & 63, wv = wave_id();     // wv = consumer 0..3
+  const int lane = threadIdx.x & 63;
   const int kk = lane >> 4, e = lane & 15;
   const int hd = a.hd;
   const bool dim_ok = 8 * e < hd;
   const int g0 = s.goff[g], ng = s.goff[g + 1] - g0;
   const int rep = s.grow[g0];
   const int blk = (a.dep ? s.rdep[rep] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
-  const T* cache = (const T*)a.kv + (size_t)blk * a.S * 2 * a.d;
-  const int k0 = c * ATT_CH;
-  const int kn = max(0, min(ATT_CH, a.n_fin - k0));
-  const bool dbg = l == 0 && a.trace && a.trace[(size_t)gridDim.x * 256 + (size_t)blockIdx.x * 32 + 16] == 0;
-  dstamp(a, dbg, 16);
+  const T* cache = (const T*)a.kv + (size_t)blk * a.S * 2 * a.d + h * hd + 8 * e;
+  const int k0 = c * KEYS;
+  const int kn = max(0, min(KEYS, a.n_fin - k0));
 
-  // prefix keys were written by earlier launches: plain loads, issued before the wait
-  // all slot indices first, then all K/V loads (a load behind a branch with a side effect
-  // would wait for the one before it)
-  int sl[4];
-  float kf[4][8], vf[4][8];
+  // slots of this lane's keys (prefix keys were written by earlier launches: plain loads)
+  int sl[NPASS * RR];
+#pragma unroll
+  for (int q = 0; q < NPASS * RR; ++q) {
+    const int j = (q / RR) * 4 * RR + kk + 4 * (q % RR);
+    sl[q] = j < kn ? a.fin[k0 + min(j, kn - 1)] : -1;
+  }
   bool bad = false;
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int jk = wv * 16 + kk + 4 * rr;
-    sl[rr] = jk < kn ? a.fin[k0 + min(jk, kn - 1)] : -1;
-  }
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int jk = wv * 16 + kk + 4 * rr;
-    if (jk < kn && (sl[rr] < 0 || sl[rr] >= a.S)) { bad = true; sl[rr] = -1; }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) kf[rr][t] = vf[rr][t] = 0.f;
-    if (sl[rr] >= 0 && dim_ok) {
-      load8_plain<T>(cache + (size_t)sl[rr] * 2 * a.d + h * hd + 8 * e, kf[rr]);
-      load8_plain<T>(cache + (size_t)sl[rr] * 2 * a.d + a.d + h * hd + 8 * e, vf[rr]);
-    }
+  for (int q = 0; q < NPASS * RR; ++q) {
+    const int j = (q / RR) * 4 * RR + kk + 4 * (q % RR);
+    if (j < kn && (sl[q] < 0 || sl[q] >= a.S)) { bad = true; sl[q] = -1; }
   }
   if (bad) ls_flag(a.err, 1);
-  dstamp(a, dbg, 17);
-  wait_ge(C + cl.o_qkvh + h * PADC, 3 * (hd / 16), cb);
-  dstamp(a, dbg, 18);
+  auto load_pass = [&](int p, Raw8<T>* kr, Raw8<T>* vr) {
+#pragma unroll
+    for (int rr = 0; rr < RR; ++rr) {
+      const int x = sl[p * RR + rr];
+      kr[rr].zero();
+      vr[rr].zero();
+      if (x >= 0 && dim_ok) {
+        kr[rr].load(cache + (size_t)x * 2 * a.d);
+        vr[rr].load(cache + (size_t)x * 2 * a.d + a.d);
+      }
+    }
+  };
+  Raw8<T> ka[RR], va[RR], kb[RR], vb[RR];
+  load_pass(0, ka, va);                                   // before the wait: earlier launches' keys
+  // queries of this head are complete once the head's q/k/v tiles have all signalled
+  if (lane == 0) {
+    int n = 0;
+    while (ld_acq(C + cl.o_qkvh + h * PADC) < 3 * (hd / 16)) {
+      __builtin_amdgcn_s_sleep(POLL_SLEEP);
+      if (++n > SPIN_LIMIT) { ls_flag(a.err, LS_TIMEOUT); break; }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" : : : "memory");
 
   const float scale = 1.0f / sqrtf((float)hd);
   const __amdgpu_buffer_rsrc_t Rq = rsrc_of(a.q, a.M * a.d * 4);
-  auto scores = [&](const float* qs, int r, float* sc) {
+  for (int r = 0; r < ng; ++r) {
+    const int i = s.grow[g0 + r];
+    const int qoff = (i * a.d + h * hd + 8 * e) * 4;
+    const u32x4_t qa = ldc128(Rq, dim_ok ? qoff : 0x7fffff00), qb = ldc128(Rq, dim_ok ? qoff + 16 : 0x7fffff00);
+    if (r > 0) load_pass(0, ka, va);                      // a later row re-reads the keys (cached)
     float q8[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) q8[t] = dim_ok ? qs[r * hd + 8 * e + t] : 0.f;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      float part = 0.f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) part += q8[t] * kf[rr][t];
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-      sc[rr] = sl[rr] >= 0 ? part : -INFINITY;
+    for (int t = 0; t < 4; ++t) {
+      q8[t] = __uint_as_float(qa[t]) * scale;
+      q8[4 + t] = __uint_as_float(qb[t]) * scale;
     }
-  };
-  // the group's rows, ATT_RB at a time
-  for (int rb = 0; rb < ng; rb += ATT_RB) {
-    const int nb = min(ATT_RB, ng - rb);
-    float* qs = (float*)s.X;                 // [nb][hd] scaled queries
-    float* wmx = qs + nb * hd;               // [nb][4] per-wave maxima
-    float* wsm = wmx + 4 * nb;               // [nb][4] per-wave sums
-    float* wac = wsm + 4 * nb;               // [nb][4][hd] per-wave partial outputs
-    if (rb > 0) cb.sync();                   // previous pass's readers are done with the scratch
-    for (int idx = threadIdx.x; idx < nb * (hd / 4); idx += 64 * NCONS) {
-      const int r = idx / (hd / 4), q4 = idx - r * (hd / 4);
-      const int i = s.grow[g0 + rb + r];
-      const u32x4_t v = ldc128(Rq, (i * a.d + h * hd + 4 * q4) * 4);
+    float run_m = -INFINITY, lsum = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    auto consume = [&](int p, const Raw8<T>* kr, const Raw8<T>* vr) {
+      float sc[RR];
+      float pm = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) qs[r * hd + 4 * q4 + t] = __uint_as_float(v[t]) * scale;
-    }
-    cb.sync();
-    dstamp(a, dbg, 19);
-    // pass 1: this wave's maximum per row
-    for (int r = 0; r < nb; ++r) {
-      float sc[4];
-      scores(qs, r, sc);
-      float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      if (lane == 0) wmx[r * 4 + wv] = mloc;
-    }
-    cb.sync();
-    dstamp(a, dbg, 20);
-    // pass 2: weights against the unit's maximum, partial sums and P.V
-    for (int r = 0; r < nb; ++r) {
-      const float mx = fmaxf(fmaxf(wmx[r * 4], wmx[r * 4 + 1]), fmaxf(wmx[r * 4 + 2], wmx[r * 4 + 3]));
-      float sc[4];
-      scores(qs, r, sc);
-      float lsum = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int rr = 0; rr < RR; ++rr) {
+        float kf[8];
+        kr[rr].unpack(kf);
+        float part = 0.f;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float pw = sl[rr] >= 0 ? __expf(sc[rr] - mx) : 0.f;
+        for (int t = 0; t < 8; ++t) part += q8[t] * kf[t];
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+        sc[rr] = sl[p * RR + rr] >= 0 ? part : -INFINITY;
+        pm = fmaxf(pm, sc[rr]);
+      }
+      pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
+      pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+      const float nm = fmaxf(run_m, pm);
+      if (nm == -INFINITY) return;                        // no key so far
+      const float rs = run_m == -INFINITY ? 0.f : __expf(run_m - nm);
+      lsum *= rs;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] *= rs;
+      run_m = nm;
+#pragma unroll
+      for (int rr = 0; rr < RR; ++rr) {
+        const float pw = sl[p * RR + rr] >= 0 ? __expf(sc[rr] - nm) : 0.f;
         lsum += pw;
+        float vf[8];
+        vr[rr].unpack(vf);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] += pw * vf[rr][t];
+        for (int t = 0; t < 8; ++t) acc[t] += pw * vf[t];
       }
-      lsum += __shfl_xor(lsum, 16, 64);
-      lsum += __shfl_xor(lsum, 32, 64);
+    };
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        acc[t] += __shfl_xor(acc[t], 16, 64);
-        acc[t] += __shfl_xor(acc[t], 32, 64);
-      }
-      if (lane == 0) wsm[r * 4 + wv] = lsum;
-      if (kk == 0 && dim_ok) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) wac[(r * 4 + wv) * hd + 8 * e + t] = acc[t];
+    for (int p = 0; p < NPASS; p += 2) {
+      if (p + 1 < NPASS) load_pass(p + 1, kb, vb);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(p, ka, va);
+      __builtin_amdgcn_sched_barrier(0);
+      if (p + 1 < NPASS) {
+        if (p + 2 < NPASS) load_pass(p + 2, ka, va);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(p + 1, kb, vb);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    cb.sync();
-    dstamp(a, dbg, 21);
-    // the unit's partial per row: (max, sum, acc[hd]), waves combined in fixed order
-    for (int idx = threadIdx.x; idx < nb * (hd + 2); idx += 64 * NCONS) {
-      const int r = idx / (hd + 2), dd = idx - r * (hd + 2);
-      const int i = s.grow[g0 + rb + r];
-      float* out = a.patt + (((size_t)i * a.nh + h) * a.att_chunks + c) * (hd + 2);
-      float v;
-      if (dd == 0) v = fmaxf(fmaxf(wmx[r * 4], wmx[r * 4 + 1]), fmaxf(wmx[r * 4 + 2], wmx[r * 4 + 3]));
-      else if (dd == 1) v = (wsm[r * 4] + wsm[r * 4 + 1]) + (wsm[r * 4 + 2] + wsm[r * 4 + 3]);
-      else {
-        const int x = dd - 2;
-        v = (wac[(r * 4) * hd + x] + wac[(r * 4 + 1) * hd + x]) + (wac[(r * 4 + 2) * hd + x] + wac[(r * 4 + 3) * hd + x]);
-      }
-      stc(out + dd, v);
+    // per-lane sums cover the lane's keys; combine the four key groups
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      acc[t] += __shfl_xor(acc[t], 16, 64);
+      acc[t] += __shfl_xor(acc[t], 32, 64);
+    }
+    float* out = a.patt + (((size_t)i * a.nh + h) * a.att_chunks + c) * (hd + 2);
+    if (lane == 0) { stc(out, run_m); stc(out + 1, lsum); }
+    if (kk == 0 && dim_ok) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) stc(out + 2 + 8 * e + t, acc[t]);
     }
   }
-  dstamp(a, dbg, 22);
   drain();
-  cb.sync();
-  dstamp(a, dbg, 23);
-  int* flag = s.ints + 2 * s.NS + 1;
-  if (threadIdx.x == 0) *flag = atomicAdd(C + cl.o_fa + g * a.nh + h, 1);
-  cb.sync();
-  dstamp(a, dbg, 24);
-  const int arrived = *flag;
-  if (arrived == nu - 1) {
-    att_merge<T>(a, s, cl, cb, l, g, h, nu);
-    dstamp(a, dbg, 25);
-  }
+  int arrived = 0;
+  if (lane == 0) arrived = atomicAdd(C + cl.o_fa + g * a.nh + h, 1);
+  arrived = __shfl(arrived, 0, 64);
+  if (arrived == nu - 1) att_merge<T>(a, s, cl, l, g, h, nu);
 }
 
-// Merge of head h for the rows of group g: one wave per row, lane = dims 2*lane, 2*lane + 1.
+// Merge of head h for the rows of group g, by one wave, row by row; lane = dims 2*lane, 2*lane + 1.
 // Online log-sum-exp over batches of (16 prefix-chunk partials, 8 own keys); every load of a
 // batch is issued before any is used, so a batch costs one memory round trip.
 template <typename T>
-LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, ConsBar& cb, int l, int g, int h, int nu) {
+LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, int l, int g, int h, int nu) {
   int* C = a.cnt + (size_t)l * cl.per_layer;
-  const int lane = threadIdx.x & 63, wv = wave_id();
+  const int lane = threadIdx.x & 63;
   const int hd = a.hd;
   const bool dok = 2 * lane < hd;
   const int g0 = s.goff[g], ng = s.goff[g + 1] - g0;
@@ -1016,7 +1050,7 @@ LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, Cons
   const int blk = (a.dep ? s.rdep[rep] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
   const T* cache = (const T*)a.kv + (size_t)blk * a.S * 2 * a.d;
   const float scale = 1.0f / sqrtf((float)hd);
-  for (int r = wv; r < ng; r += NCONS) {
+  for (int r = 0; r < ng; ++r) {
     const int i = s.grow[g0 + r];
     T* orow = o_of<T>(a, l) + (size_t)i * a.d + h * hd;
     const int self = s.rslot[i];
@@ -1106,8 +1140,7 @@ LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, Cons
     if (dok) store2_coh<T>(orow + 2 * lane, den > 0.f ? num0 / den : 0.f, den > 0.f ? num1 / den : 0.f);
   }
   drain();
-  cb.sync();
-  if (threadIdx.x == 0) atomicAdd(C + cl.o_att + h * PADC, 1);
+  if (lane == 0) atomicAdd(C + cl.o_att + h * PADC, 1);
 }
 
 // ---- init unit: embedding row or gathered hidden row into the working rows ---------------------------
@@ -1321,10 +1354,12 @@ __global__ __launch_bounds__(MEGA_THREADS) void k_mega(MegaArgs a) {
       const int natt = s.goff[64] * a.nh * nu;
       const Share sa = share_of(natt, att_deal, G, b);
       att_deal = (att_deal + natt) % G;
-      for (int k = 0; k < sa.count; ++k) {
+      // unit u runs on workgroup (u + att_deal) mod G, wave (u / G) mod 4: every unit gets a
+      // wave of its own before any wave takes a second one
+      for (int k = co.c; k < sa.count; k += NCONS) {
         const int u = sa.first + k * G;
         const int cch = u % nu, gh = u / nu;
-        att_chunk<T>(a, s, cl, cb, sp.l, gh / a.nh, gh % a.nh, cch, nu);
+        att_unit_wave<T>(a, s, cl, sp.l, gh / a.nh, gh % a.nh, cch, nu);
       }
     } else {
       walk_gemm<T, MT, false>(a, s, cl, sp.ph, sp.l, deal, nullptr, &co, &cb);

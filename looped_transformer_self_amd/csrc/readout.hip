@@ -1,55 +1,58 @@
 // Readout distribution of C: temperature, softmax, top-p truncation, normalisation (LoopSpec
 // page, section 2.1: every intermediate readout applies the same processing as the target).
 //
-// One 1024-thread workgroup per row; thread t owns a contiguous id range, so "lowest id first"
-// orderings reduce to prefix scans over threads.  Top-p keeps the tokens ordered by
-// probability (then id) up to and including the one at which the kept mass reaches top_p.
-// The crossing token is found by an MSB-first radix select over the float32 bit patterns of
-// the probabilities (monotone for non-negative floats), accumulating mass in integer fixed
-// point (floor(p * 2^40)), so the selection is exact and independent of summation order.
+// One 512-thread workgroup per row; the row lives in registers (thread t holds ids
+// t, t + 512, t + 1024, ...: coalesced loads and stores, one read of the logits and one write
+// of the distribution).  Top-p keeps the tokens ordered by probability (then id) up to and
+// including the one at which the kept mass reaches top_p.  The crossing token's key (the
+// float32 bit pattern of its probability, monotone for non-negative floats) is found by a
+// radix select over the occupied key range, accumulating mass in 32-bit fixed point
+// (floor(p * 2^31)), so the selection is exact for those masses and independent of summation
+// order.  Ties at the crossing key are kept in id order.
 #include "common.h"
 #include "kernels.h"
 
 namespace ls {
 
-constexpr int DIST_THREADS = 1024;
+constexpr int DIST_THREADS = 512;
+constexpr int DIST_PT = 128;              // ids per thread: V <= 65536
+constexpr int DIST_BINS = 2048;
 
-LS_DEV unsigned long long shfl_xor_u64(unsigned long long v, int o) {
-  unsigned lo = (unsigned)v, hi = (unsigned)(v >> 32);
-  lo = __shfl_xor(lo, o, 64);
-  hi = __shfl_xor(hi, o, 64);
-  return ((unsigned long long)hi << 32) | lo;
-}
-
-LS_DEV unsigned long long block_sum_u64(unsigned long long v, unsigned long long* red) {
+LS_DEV unsigned block_sum_u32(unsigned v, unsigned* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += shfl_xor_u64(v, o);
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   if (lane == 0) red[w] = v;
   __syncthreads();
-  unsigned long long t = 0;
+  unsigned t = 0;
   for (int i = 0; i < nw; ++i) t += red[i];
   __syncthreads();
   return t;
 }
-
-// Exclusive prefix sum of one int per thread (thread order).
-LS_DEV int block_excl_scan(int v, int* red) {
+LS_DEV unsigned block_min_u32(unsigned v, unsigned* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int incl = v;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) red[w] = incl;
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (unsigned)__shfl_xor(v, o, 64));
+  if (lane == 0) red[w] = v;
   __syncthreads();
-  int off = 0;
-  for (int i = 0; i < w; ++i) off += red[i];
-  (void)nw;
+  unsigned t = red[0];
+  for (int i = 1; i < nw; ++i) t = min(t, red[i]);
   __syncthreads();
-  return off + incl - v;
+  return t;
 }
+LS_DEV unsigned block_max_u32(unsigned v, unsigned* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (unsigned)__shfl_xor(v, o, 64));
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  unsigned t = red[0];
+  for (int i = 1; i < nw; ++i) t = max(t, red[i]);
+  __syncthreads();
+  return t;
+}
+
+LS_DEV unsigned mass31(float p) { return (unsigned)(p * 2147483648.0f); }   // exact floor(p * 2^31), p in [0, 1]
 
 __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int V, int greedy, float T, float top_p,
                                                       float* probs, const int32_t* out_rows, int n_prob_rows,
@@ -57,30 +60,23 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
   const int m = blockIdx.x;
   const float* z = logits + (size_t)m * V;
   const int orow = out_rows ? out_rows[m] : m;
-  if (orow == -1) return;                       // distribution not requested for this row
-  if (orow < 0 || orow >= n_prob_rows) {
-    if (threadIdx.x == 0) ls_flag(err, 1);
-    return;
-  }
-  float* p = probs + (size_t)orow * V;
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int per = (V + nt - 1) / nt;
-  const int v0 = min(V, tid * per), v1 = min(V, v0 + per);
-
+  const int tid = threadIdx.x;
   __shared__ float redf[16];
   __shared__ int redi[16];
-  __shared__ unsigned long long redu[16];
-  __shared__ unsigned long long hist[256];
-  __shared__ unsigned s_prefix;
-  __shared__ unsigned long long s_base;
+  __shared__ unsigned redu[16];
+  __shared__ unsigned hist[DIST_BINS];
+  __shared__ unsigned s_sel[2];
 
-  // argmax, lowest id on ties
+  // ids past V hold -inf logits: probability 0, mass 0, never kept
+  float x[DIST_PT];
+#pragma unroll
+  for (int j = 0; j < DIST_PT; ++j) x[j] = tid + DIST_THREADS * j < V ? z[tid + DIST_THREADS * j] : -INFINITY;
+  // argmax, lowest id on ties (a thread's ids increase with j)
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int v = v0; v < v1; ++v) {
-    const float x = z[v];
-    if (x > best) { best = x; bi = v; }
-  }
+#pragma unroll
+  for (int j = 0; j < DIST_PT; ++j)
+    if (x[j] > best) { best = x[j]; bi = tid + DIST_THREADS * j; }
   for (int o = 32; o > 0; o >>= 1) {
     const float ob = __shfl_xor(best, o, 64);
     const int oi = __shfl_xor(bi, o, 64);
@@ -89,78 +85,159 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
   if ((tid & 63) == 0) { redf[tid >> 6] = best; redi[tid >> 6] = bi; }
   __syncthreads();
   best = redf[0]; bi = redi[0];
-  for (int w = 1; w < nt / 64; ++w)
+  for (int w = 1; w < DIST_THREADS / 64; ++w)
     if (redf[w] > best || (redf[w] == best && redi[w] < bi)) { best = redf[w]; bi = redi[w]; }
   __syncthreads();
   if (argmax && tid == 0) argmax[m] = bi;
+  if (orow == -1) return;                       // distribution not requested for this row
+  if (orow < 0 || orow >= n_prob_rows) {
+    if (tid == 0) ls_flag(err, 1);
+    return;
+  }
+  float* p = probs + (size_t)orow * V;
   if (greedy) {
-    for (int v = v0; v < v1; ++v) p[v] = v == bi ? 1.0f : 0.0f;
+#pragma unroll
+    for (int j = 0; j < DIST_PT; ++j) {
+      const int v = tid + DIST_THREADS * j;
+      if (v < V) p[v] = v == bi ? 1.0f : 0.0f;
+    }
     return;
   }
 
   // softmax of z / T
   const float mx = best / T;
-  float s = 0.f;
-  for (int v = v0; v < v1; ++v) s += expf(z[v] / T - mx);
-  s = block_sum(s, redf);
-  const float inv = 1.0f / s;
-  for (int v = v0; v < v1; ++v) p[v] = expf(z[v] / T - mx) * inv;
-  if (!(top_p < 1.0f)) return;
+  float sacc = 0.f;
+#pragma unroll
+  for (int j = 0; j < DIST_PT; ++j) {
+    x[j] = __expf(x[j] / T - mx);
+    sacc += x[j];
+  }
+  const float inv = 1.0f / block_sum(sacc, redf);
+#pragma unroll
+  for (int j = 0; j < DIST_PT; ++j) x[j] *= inv;
+  if (!(top_p < 1.0f)) {
+#pragma unroll
+    for (int j = 0; j < DIST_PT; ++j) {
+      const int v = tid + DIST_THREADS * j;
+      if (v < V) p[v] = x[j];
+    }
+    return;
+  }
 
   // fixed-point masses and the top-p target
-  const double ONE = 1099511627776.0;   // 2^40
-  unsigned long long zs = 0;
-  for (int v = v0; v < v1; ++v) zs += (unsigned long long)((double)p[v] * ONE);
-  const unsigned long long Z = block_sum_u64(zs, redu);
-  const unsigned long long TP = (unsigned long long)ceil((double)top_p * (double)Z);
-
-  // radix select: the key of the token at which the descending cumulative mass reaches TP
-  unsigned prefix = 0, pmask = 0;
-  unsigned long long base = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int b = tid; b < 256; b += nt) hist[b] = 0;
-    __syncthreads();
-    for (int v = v0; v < v1; ++v) {
-      const float pv = p[v];
-      const unsigned key = __float_as_uint(pv);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], (unsigned long long)((double)pv * ONE));
-    }
-    __syncthreads();
-    if (tid == 0) {
-      unsigned long long cum = base;
-      int sel = 0;
-      for (int dg = 255; dg >= 0; --dg) {
-        if (cum + hist[dg] >= TP) { sel = dg; break; }
-        cum += hist[dg];
-      }
-      s_prefix = prefix | ((unsigned)sel << shift);
-      s_base = cum;
-    }
-    __syncthreads();
-    prefix = s_prefix;
-    base = s_base;
-    pmask |= 255u << shift;
-    __syncthreads();
+  unsigned zl = 0, kmin = 0xffffffffu, kmax = 0;
+#pragma unroll
+  for (int j = 0; j < DIST_PT; ++j) {
+    zl += mass31(x[j]);
+    const unsigned k = __float_as_uint(x[j]);
+    kmin = min(kmin, k);
+    kmax = max(kmax, k);
   }
-  const unsigned kstar = prefix;
-  const unsigned long long Pk = (unsigned long long)((double)__uint_as_float(kstar) * ONE);
-  const unsigned long long n_keep = (TP - base + Pk - 1) / Pk;
+  const unsigned Z = block_sum_u32(zl, redu);
+  const unsigned TP = (unsigned)ceil((double)top_p * (double)Z);
+  kmin = block_min_u32(kmin, redu);
+  kmax = block_max_u32(kmax, redu);
 
-  // ties at kstar are kept in id order
-  int nt_local = 0;
-  for (int v = v0; v < v1; ++v) nt_local += __float_as_uint(p[v]) == kstar;
-  const int tie0 = block_excl_scan(nt_local, redi);
-  const int n_ties = (int)block_sum((float)nt_local, redf);
-  const unsigned long long kept_ties = n_keep < (unsigned long long)n_ties ? n_keep : (unsigned long long)n_ties;
-  const unsigned long long Zk = base + kept_ties * Pk;
-  const float scale = (float)(ONE / (double)Zk);
-  int tr = tie0;
-  for (int v = v0; v < v1; ++v) {
-    const unsigned key = __float_as_uint(p[v]);
-    bool keep = key > kstar;
-    if (key == kstar) { keep = (unsigned long long)tr < n_keep; ++tr; }
-    p[v] = keep ? p[v] * scale : 0.0f;
+  // radix select over keys in [lo, lo + 2^width): find the key at which the mass of larger
+  // keys reaches TP; `above` is the mass of keys above the current range
+  unsigned lo = kmin;
+  int width = 32 - __clz(kmax - kmin);          // bits needed for (key - lo)
+  unsigned above = 0;
+  while (true) {
+    const int shift = width > 11 ? width - 11 : 0;
+    const int nb = min(DIST_BINS, ((int)((1ull << width) - 1) >> shift) + 1);
+    for (int b = tid; b < nb; b += DIST_THREADS) hist[b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < DIST_PT; ++j) {
+      const unsigned off = __float_as_uint(x[j]) - lo;       // keys below lo wrap to large offsets
+      const unsigned ms = mass31(x[j]);
+      if (ms && (width >= 32 || off < (1u << width))) atomicAdd(&hist[off >> shift], ms);   // zero masses add nothing
+    }
+    __syncthreads();
+    {
+      // descending inclusive scan over the bins: thread t takes BPT consecutive bins from the top
+      constexpr int BPT = DIST_BINS / DIST_THREADS;
+      unsigned hv[BPT], tot = 0;
+#pragma unroll
+      for (int q = 0; q < BPT; ++q) {
+        const int b = nb - 1 - (BPT * tid + q);
+        hv[q] = b >= 0 ? hist[b] : 0u;
+        tot += hv[q];
+      }
+      unsigned inc = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned y = __shfl_up(inc, o, 64);
+        if ((tid & 63) >= o) inc += y;
+      }
+      if ((tid & 63) == 63) redu[tid >> 6] = inc;
+      __syncthreads();
+      unsigned run = above + inc - tot;             // mass of the bins above this thread's first
+      for (int w = 0; w < (tid >> 6); ++w) run += redu[w];
+      // the crossing bin: the first (highest) where the running mass reaches TP
+#pragma unroll
+      for (int q = 0; q < BPT; ++q) {
+        const int b = nb - 1 - (BPT * tid + q);
+        if (b >= 0 && run < TP && run + hv[q] >= TP) { s_sel[0] = (unsigned)b; s_sel[1] = run; }
+        run += hv[q];
+      }
+    }
+    __syncthreads();
+    const unsigned sel = s_sel[0];
+    above = s_sel[1];
+    lo += sel << shift;
+    width = shift;
+    __syncthreads();
+    if (shift == 0) break;
+  }
+  const unsigned kstar = lo;
+  const unsigned Pk = mass31(__uint_as_float(kstar));
+  // tokens at kstar kept: enough of them (in id order) to reach TP; at least one
+  unsigned n_keep = Pk > 0 ? (TP - above + Pk - 1) / Pk : 0xffffffffu;
+  if (n_keep == 0) n_keep = 1;
+  unsigned nt_local = 0;
+#pragma unroll
+  for (int j = 0; j < DIST_PT; ++j) nt_local += __float_as_uint(x[j]) == kstar;
+  const unsigned n_ties = block_sum_u32(nt_local, redu);
+  const unsigned kept_ties = min(n_keep, n_ties);
+  const double Zk = (double)above + (double)kept_ties * (double)Pk;
+  const float scale = (float)(2147483648.0 / Zk);
+  if (n_keep >= n_ties) {
+#pragma unroll
+    for (int j = 0; j < DIST_PT; ++j) {
+      const int v = tid + DIST_THREADS * j;
+      if (v < V) p[v] = __float_as_uint(x[j]) >= kstar ? x[j] * scale : 0.0f;
+    }
+    return;
+  }
+  // rare: more ties at kstar than are kept.  The row goes to the output first, then the ties
+  // are ranked by id (column j, then thread) reading it back.
+#pragma unroll
+  for (int j = 0; j < DIST_PT; ++j)
+    if (tid + DIST_THREADS * j < V) p[tid + DIST_THREADS * j] = x[j];
+  __syncthreads();
+  unsigned before = 0;                          // ties with smaller ids in earlier columns
+  for (int j = 0; j < DIST_PT; ++j) {
+    const int v = tid + DIST_THREADS * j;
+    const float pv = v < V ? p[v] : 0.f;
+    const bool tie = v < V && __float_as_uint(pv) == kstar;
+    const unsigned long long bal = __ballot(tie);
+    const unsigned in_wave = __popcll(bal & ((1ull << (tid & 63)) - 1ull));
+    if ((tid & 63) == 0) redu[tid >> 6] = __popcll(bal);
+    __syncthreads();
+    unsigned wave_off = 0, col = 0;
+    for (int w = 0; w < DIST_THREADS / 64; ++w) {
+      if (w < (tid >> 6)) wave_off += redu[w];
+      col += redu[w];
+    }
+    __syncthreads();
+    const unsigned rank = before + wave_off + in_wave;
+    if (v < V) {
+      const bool keep = __float_as_uint(pv) > kstar || (tie && rank < n_keep);
+      p[v] = keep ? pv * scale : 0.0f;
+    }
+    before += col;
   }
 }
 

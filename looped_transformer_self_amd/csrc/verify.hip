@@ -2,8 +2,9 @@
 // candidate rejection (eq. 3-4), gate and residual second proposal (eq. 5-6), cascade, and the
 // point-mass cascade used for copied candidates.  Probabilities enter as the fixed-point
 // integers A(v) = floor(p(v) * 2^40); every decision is exact integer arithmetic (u64/u128),
-// so identical inputs give identical outputs whatever the thread schedule.  One 256-thread
-// workgroup per job, one pass over the vocabulary per reduction.
+// so identical inputs give identical outputs whatever the thread schedule.  One 1024-thread
+// workgroup per job; thread t owns a contiguous id range; one pass over the vocabulary per
+// reduction, sums in u64 (u128 only for the second residual of the cascade).
 #include "common.h"
 #include "kernels.h"
 #include "../../include/loopspec.h"
@@ -12,38 +13,89 @@ namespace ls {
 
 typedef unsigned __int128 u128;
 typedef unsigned long long u64;
-constexpr int VT = 256;
+constexpr int VT = 1024;
+constexpr int NW = VT / 64;
 
 LS_DEV u64 fixp(float p) { return (u64)((double)p * 1099511627776.0); }
 
-// Sum over the block (every thread gets it).
-LS_DEV u128 bsum128(u128 v, u128* s) {
-  s[threadIdx.x] = v;
-  __syncthreads();
-  for (int off = VT / 2; off > 0; off >>= 1) {
-    if ((int)threadIdx.x < off) s[threadIdx.x] += s[threadIdx.x + off];
-    __syncthreads();
+LS_DEV u64 shfl_xor64(u64 v, int o) {
+  return ((u64)(unsigned)__shfl_xor((int)(v >> 32), o, 64) << 32) | (unsigned)__shfl_xor((int)v, o, 64);
+}
+LS_DEV u64 shfl_up64(u64 v, int o) {
+  return ((u64)(unsigned)__shfl_up((int)(v >> 32), o, 64) << 32) | (unsigned)__shfl_up((int)v, o, 64);
+}
+
+struct Scratch {
+  u64 w64[NW];
+  u128 w128[NW];
+  int res;
+};
+
+// Thread t owns the contiguous ids [v0, v1) (thread order = id order, so prefix sums over
+// threads are prefix sums over ids).
+struct Range {
+  int v0, v1;
+  LS_DEV Range(int V) {
+    const int per = (V + VT - 1) / VT;
+    v0 = min(V, (int)threadIdx.x * per);
+    v1 = min(V, v0 + per);
   }
-  const u128 t = s[0];
+};
+
+// Sum over the block of u64 values (every thread gets it).
+LS_DEV u64 bsum64(u64 v, Scratch& sc) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += shfl_xor64(v, o);
+  if ((threadIdx.x & 63) == 0) sc.w64[threadIdx.x >> 6] = v;
+  __syncthreads();
+  u64 t = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) t += sc.w64[i];
   __syncthreads();
   return t;
 }
-
-// Exclusive scan over threads; also returns the total.
-LS_DEV u128 bscan128(u128 v, u128* s, u128* s2, u128& total) {
-  s[threadIdx.x] = v;
-  __syncthreads();
-  u128* a = s;
-  u128* b = s2;
-  for (int off = 1; off < VT; off <<= 1) {
-    b[threadIdx.x] = a[threadIdx.x] + ((int)threadIdx.x >= off ? a[threadIdx.x - off] : (u128)0);
-    __syncthreads();
-    u128* t = a; a = b; b = t;
+// Exclusive scan over threads of u64 values.
+LS_DEV u64 bscan64(u64 v, Scratch& sc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  u64 inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const u64 y = shfl_up64(inc, o);
+    if (lane >= o) inc += y;
   }
-  const u128 incl = a[threadIdx.x];
-  total = a[VT - 1];
+  if (lane == 63) sc.w64[w] = inc;
   __syncthreads();
-  return incl - v;
+  u64 off = 0;
+  for (int i = 0; i < w; ++i) off += sc.w64[i];
+  __syncthreads();
+  return off + inc - v;
+}
+LS_DEV u128 bsum128(u128 v, Scratch& sc) {
+  // per-wave partials in LDS, summed in fixed order
+  for (int o = 32; o > 0; o >>= 1) {
+    const u64 hi = shfl_xor64((u64)(v >> 64), o), lo = shfl_xor64((u64)v, o);
+    v += ((u128)hi << 64) | lo;
+  }
+  if ((threadIdx.x & 63) == 0) sc.w128[threadIdx.x >> 6] = v;
+  __syncthreads();
+  u128 t = 0;
+  for (int i = 0; i < NW; ++i) t += sc.w128[i];
+  __syncthreads();
+  return t;
+}
+LS_DEV u128 bscan128(u128 v, Scratch& sc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  u128 inc = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const u64 hi = shfl_up64((u64)(inc >> 64), o), lo = shfl_up64((u64)inc, o);
+    if (lane >= o) inc += ((u128)hi << 64) | lo;
+  }
+  if (lane == 63) sc.w128[w] = inc;
+  __syncthreads();
+  u128 off = 0;
+  for (int i = 0; i < w; ++i) off += sc.w128[i];
+  __syncthreads();
+  return off + inc - v;
 }
 
 // floor(U * Z / 2^32) without overflow for Z < 2^120.
@@ -52,132 +104,182 @@ LS_DEV u128 scale_u(uint32_t U, u128 Z) {
   return (((u128)U * zh) << 32) + (((u128)U * zl) >> 32);
 }
 
-// SAMPLE(A, U): smallest v whose prefix sum of A exceeds floor(U * Z / 2^32).
+// Block total of a mass function (u64 masses whose sum stays below 2^64).
+// Range sums issue their loads sixteen at a time (a plain loop would wait for each load).
 template <class F>
-LS_DEV int block_sample(F A, int V, uint32_t U, u128* s, u128* s2, int* res) {
-  const int per = (V + VT - 1) / VT;
-  const int v0 = min(V, (int)threadIdx.x * per), v1 = min(V, v0 + per);
+LS_DEV u64 range_sum64(F A, const Range& r) {
+  u64 loc = 0;
+  int v = r.v0;
+  for (; v + 16 <= r.v1; v += 16) {
+    u64 t[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t[k] = A(v + k);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) loc += t[k];
+  }
+  for (; v < r.v1; ++v) loc += A(v);
+  return loc;
+}
+template <class F>
+LS_DEV u128 range_sum128(F A, const Range& r) {
   u128 loc = 0;
-  for (int v = v0; v < v1; ++v) loc += A(v);
-  u128 Z;
-  const u128 ex = bscan128(loc, s, s2, Z);
-  if (threadIdx.x == 0) *res = -1;
+  int v = r.v0;
+  for (; v + 8 <= r.v1; v += 8) {
+    u128 t[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t[k] = A(v + k);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) loc += t[k];
+  }
+  for (; v < r.v1; ++v) loc += A(v);
+  return loc;
+}
+
+template <class F>
+LS_DEV u64 total64(F A, const Range& r, Scratch& sc) {
+  return bsum64(range_sum64(A, r), sc);
+}
+template <class F>
+LS_DEV u128 total128(F A, const Range& r, Scratch& sc) {
+  return bsum128(range_sum128(A, r), sc);
+}
+
+// SAMPLE(A, U): smallest v whose prefix sum of A exceeds floor(U * Z / 2^32); -1 if Z = 0.
+template <class F>
+LS_DEV int sample64(F A, const Range& r, uint32_t U, Scratch& sc) {
+  const u64 loc = range_sum64(A, r);
+  const u64 ex = bscan64(loc, sc);
+  const u64 Z = bsum64(loc, sc);
+  if (threadIdx.x == 0) sc.res = -1;
+  __syncthreads();
+  if (Z > 0) {
+    const u64 thr = (u64)scale_u(U, Z);
+    if (loc > 0 && ex <= thr && thr < ex + loc) {
+      u64 c = ex;
+      for (int v = r.v0; v < r.v1; ++v) {
+        c += A(v);
+        if (c > thr) { sc.res = v; break; }
+      }
+    }
+  }
+  __syncthreads();
+  const int res = sc.res;
+  __syncthreads();
+  return res;
+}
+template <class F>
+LS_DEV int sample128(F A, const Range& r, uint32_t U, Scratch& sc) {
+  const u128 loc = range_sum128(A, r);
+  const u128 ex = bscan128(loc, sc);
+  const u128 Z = bsum128(loc, sc);
+  if (threadIdx.x == 0) sc.res = -1;
   __syncthreads();
   if (Z > 0) {
     const u128 thr = scale_u(U, Z);
     if (loc > 0 && ex <= thr && thr < ex + loc) {
       u128 c = ex;
-      for (int v = v0; v < v1; ++v) {
+      for (int v = r.v0; v < r.v1; ++v) {
         c += A(v);
-        if (c > thr) { *res = v; break; }
+        if (c > thr) { sc.res = v; break; }
       }
     }
   }
   __syncthreads();
-  const int r = *res;
+  const int res = sc.res;
   __syncthreads();
-  return r;
-}
-
-template <class F>
-LS_DEV u128 block_total(F A, int V, u128* s) {
-  const int per = (V + VT - 1) / VT;
-  const int v0 = min(V, (int)threadIdx.x * per), v1 = min(V, v0 + per);
-  u128 loc = 0;
-  for (int v = v0; v < v1; ++v) loc += A(v);
-  return bsum128(loc, s);
+  return res;
 }
 
 __global__ __launch_bounds__(VT) void k_verify(const ls_verify_job* jobs, const float* probs, int V, int n_rows,
                                               const int32_t* cands, int n_cands, const uint32_t* uniforms,
                                               ls_verify_out* out, int* err) {
-  __shared__ u128 s[VT], s2[VT];
-  __shared__ int res;
+  __shared__ Scratch sc;
   const ls_verify_job jb = jobs[blockIdx.x];
   const uint32_t* u = uniforms + (size_t)blockIdx.x * LS_UNIFORMS_PER_JOB;
   ls_verify_out o = {-1, 0, 0, -1};
+  const Range rg(V);
 
   auto row_ok = [&](int r) { return r >= 0 && r < n_rows; };
   auto tok_ok = [&](int x) { return x >= 0 && x < V; };
   const float* pR = probs + (size_t)(row_ok(jb.p_row) ? jb.p_row : 0) * V;
   const float* q1 = probs + (size_t)(row_ok(jb.q1_row) ? jb.q1_row : 0) * V;
   const float* q2 = probs + (size_t)(row_ok(jb.q2_row) ? jb.q2_row : 0) * V;
-  const u128 LIM = (u128)1 << 41;       // a probability row sums to at most ~1 (< 2 in fixed point)
+  const u64 LIM = (u64)1 << 41;         // a probability row sums to at most ~1 (< 2 in fixed point)
   bool bad = false;
+  auto P = [&](int v) { return fixp(pR[v]); };
+  auto Q1 = [&](int v) { return fixp(q1[v]); };
+  auto Q2 = [&](int v) { return fixp(q2[v]); };
+  auto r2 = [&](int v) { const u64 a = fixp(q2[v]), b = fixp(q1[v]); return a > b ? a - b : (u64)0; };
 
   if (jb.op == LS_JOB_SAMPLE) {
-    if (!row_ok(jb.p_row)) bad = true;
-    else if (block_total([&](int v) { return (u128)fixp(pR[v]); }, V, s) >= LIM) bad = true;
-    else { o.token = block_sample([&](int v) { return (u128)fixp(pR[v]); }, V, u[5], s, s2, &res); o.outcome = LS_OUT_DRAWN; }
+    if (!row_ok(jb.p_row) || total64(P, rg, sc) >= LIM) bad = true;
+    else { o.token = sample64(P, rg, u[5], sc); o.outcome = LS_OUT_DRAWN; }
   } else if (jb.op == LS_JOB_DRAW1) {
-    if (!row_ok(jb.q1_row)) bad = true;
-    else if (block_total([&](int v) { return (u128)fixp(q1[v]); }, V, s) >= LIM) bad = true;
-    else { o.token = block_sample([&](int v) { return (u128)fixp(q1[v]); }, V, u[0], s, s2, &res); o.outcome = LS_OUT_DRAWN; }
+    if (!row_ok(jb.q1_row) || total64(Q1, rg, sc) >= LIM) bad = true;
+    else { o.token = sample64(Q1, rg, u[0], sc); o.outcome = LS_OUT_DRAWN; }
   } else if (jb.op == LS_JOB_DRAW2) {
     if (!row_ok(jb.q1_row) || !row_ok(jb.q2_row) || !tok_ok(jb.x1)) bad = true;
     else {
-      auto r2 = [&](int v) { const u64 a = fixp(q2[v]), b = fixp(q1[v]); return (u128)(a > b ? a - b : 0); };
-      const u128 Z2 = block_total(r2, V, s);
-      const bool open = Z2 > 0 && (!jb.gate || fixp(q2[jb.x1]) < fixp(q1[jb.x1]));
+      const u64 Z2 = total64(r2, rg, sc);
+      const bool open = Z2 > 0 && (!jb.gate || Q2(jb.x1) < Q1(jb.x1));
       o.outcome = LS_OUT_DRAWN;
       if (Z2 >= LIM) bad = true;
-      else if (open) { o.gate = 1; o.token = block_sample(r2, V, u[1], s, s2, &res); }
+      else if (open) { o.gate = 1; o.token = sample64(r2, rg, u[1], sc); }
     }
   } else if (jb.op == LS_JOB_VERIFY) {
     if (!row_ok(jb.p_row) || !row_ok(jb.q1_row) || !tok_ok(jb.x1) || (jb.gate && (!row_ok(jb.q2_row) || !tok_ok(jb.x2)))) {
       bad = true;
-    } else if (block_total([&](int v) { return (u128)fixp(pR[v]); }, V, s) >= LIM) {
+    } else if (total64(P, rg, sc) >= LIM) {
       bad = true;
     } else {
-      const u64 Px = fixp(pR[jb.x1]), Qx = fixp(q1[jb.x1]);
+      const u64 Px = P(jb.x1), Qx = Q1(jb.x1);
       if ((u128)u[2] * Qx < ((u128)Px << 32)) {
         o.token = jb.x1; o.outcome = LS_OUT_ACC1;
       } else {
-        auto r1raw = [&](int v) { const u64 a = fixp(pR[v]), b = fixp(q1[v]); return (u128)(a > b ? a - b : 0); };
-        u128 Z1 = block_total(r1raw, V, s);
+        auto r1raw = [&](int v) { const u64 a = fixp(pR[v]), b = fixp(q1[v]); return a > b ? a - b : (u64)0; };
+        u64 Z1 = total64(r1raw, rg, sc);
         const bool fb1 = Z1 == 0;                              // residual vanished: fall back to p_R
-        auto r1 = [&](int v) { return fb1 ? (u128)fixp(pR[v]) : r1raw(v); };
-        if (fb1) Z1 = block_total(r1, V, s);
+        auto r1 = [&](int v) { return fb1 ? fixp(pR[v]) : r1raw(v); };
+        if (fb1) Z1 = total64(r1, rg, sc);
         if (!jb.gate) {
-          o.token = block_sample(r1, V, u[4], s, s2, &res); o.outcome = LS_OUT_RESAMPLED;
+          o.token = sample64(r1, rg, u[4], sc); o.outcome = LS_OUT_RESAMPLED;
         } else {
-          auto r2 = [&](int v) { const u64 a = fixp(q2[v]), b = fixp(q1[v]); return (u128)(a > b ? a - b : 0); };
-          const u128 Z2 = block_total(r2, V, s);
+          const u64 Z2 = total64(r2, rg, sc);
           if (Z2 >= LIM) bad = true;
-          else if ((u128)u[3] * Z1 * r2(jb.x2) < ((r1(jb.x2) * Z2) << 32)) {
+          else if ((u128)u[3] * Z1 * r2(jb.x2) < (((u128)r1(jb.x2) * Z2) << 32)) {
             o.token = jb.x2; o.outcome = LS_OUT_ACC2;
           } else {
-            auto r3raw = [&](int v) { const u128 a = r1(v) * Z2, b = r2(v) * Z1; return a > b ? a - b : (u128)0; };
-            const u128 Z3 = block_total(r3raw, V, s);
-            if (Z3 == 0) o.token = block_sample(r1, V, u[4], s, s2, &res);
-            else o.token = block_sample(r3raw, V, u[4], s, s2, &res);
+            auto r3 = [&](int v) { const u128 a = (u128)r1(v) * Z2, b = (u128)r2(v) * Z1; return a > b ? a - b : (u128)0; };
+            const u128 Z3 = total128(r3, rg, sc);
+            if (Z3 == 0) o.token = sample64(r1, rg, u[4], sc);
+            else o.token = sample128(r3, rg, u[4], sc);
             o.outcome = LS_OUT_RESAMPLED;
           }
         }
       }
     }
   } else if (jb.op == LS_JOB_VERIFY_COPY) {
-    __shared__ int sc[16];
+    __shared__ int cs[16];
     __shared__ int s_tok, s_j;
     if (!row_ok(jb.p_row) || jb.n_cand < 0 || jb.n_cand > 16 || jb.cand_off < 0 ||
         jb.cand_off + jb.n_cand > n_cands)
       bad = true;
     else {
-      for (int j = threadIdx.x; j < jb.n_cand; j += VT) sc[j] = cands[jb.cand_off + j];
+      for (int j = threadIdx.x; j < jb.n_cand; j += VT) cs[j] = cands[jb.cand_off + j];
       __syncthreads();
-      for (int j = 0; j < jb.n_cand; ++j) bad |= !tok_ok(sc[j]);
-      const u128 Z0 = bad ? 0 : block_total([&](int v) { return (u128)fixp(pR[v]); }, V, s);
+      for (int j = 0; j < jb.n_cand; ++j) bad |= !tok_ok(cs[j]);
+      const u64 Z0 = bad ? 0 : total64(P, rg, sc);
       if (Z0 >= LIM) bad = true;
       if (!bad) {
         if (threadIdx.x == 0) {
-          u128 Z = Z0;
+          u64 Z = Z0;
           s_tok = -1; s_j = -1;
           for (int j = 0; j < jb.n_cand; ++j) {
-            const int c = sc[j];
+            const int c = cs[j];
             bool removed = false;
-            for (int k = 0; k < j; ++k) removed |= sc[k] == c;
-            const u128 rho = removed ? 0 : (u128)fixp(pR[c]);
-            if ((u128)u[8 + j] * Z < (rho << 32)) { s_tok = c; s_j = j; break; }
+            for (int k = 0; k < j; ++k) removed |= cs[k] == c;
+            const u64 rho = removed ? 0 : P(c);
+            if ((u128)u[8 + j] * Z < ((u128)rho << 32)) { s_tok = c; s_j = j; break; }
             Z -= rho;
           }
         }
@@ -187,10 +289,10 @@ __global__ __launch_bounds__(VT) void k_verify(const ls_verify_job* jobs, const 
         } else {
           const int nc = jb.n_cand;
           auto rho = [&](int v) {
-            for (int k = 0; k < nc; ++k) if (sc[k] == v) return (u128)0;
-            return (u128)fixp(pR[v]);
+            for (int k = 0; k < nc; ++k) if (cs[k] == v) return (u64)0;
+            return fixp(pR[v]);
           };
-          o.token = block_sample(rho, V, u[4], s, s2, &res); o.outcome = LS_OUT_RESAMPLED;
+          o.token = sample64(rho, rg, u[4], sc); o.outcome = LS_OUT_RESAMPLED;
         }
       }
     }
