@@ -67,6 +67,19 @@ def _cpu_model():
     return "unknown"
 
 
+class _Progress:
+    """Prints '[bench] <what> done/total' to stderr at most every `every` seconds."""
+
+    def __init__(self, what, every=20.0):
+        self.what, self.every, self.last = what, every, time.perf_counter()
+
+    def __call__(self, done, total):
+        now = time.perf_counter()
+        if now - self.last >= self.every or done >= total:
+            self.last = now
+            print(f"[bench] {self.what} {done}/{total}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,12 +112,12 @@ def main():
                prob_rows=4 * dec.max_branches + 16)
     d = Decoder(e, dec, args.mode)
     print("[bench] prefill", file=sys.stderr, flush=True)
-    d.prefill(prompt)
+    d.prefill(prompt, progress=_Progress("prefill"))
     snap = d.snapshot()
     torch.cuda.synchronize()
     for i in range(args.warmup):
         d.restore(snap)
-        d.decode(n_new)
+        d.decode(n_new, progress=_Progress(f"warmup {i}"))
         print(f"[bench] warmup {i} done", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     e.prof = []
@@ -112,7 +125,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         d.restore(snap)
-        toks = d.decode(n_new)
+        toks = d.decode(n_new, progress=_Progress(f"step {i}", every=60.0))
         stats.append(d.stats())
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0

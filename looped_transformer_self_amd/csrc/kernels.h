@@ -50,7 +50,8 @@ size_t mega_counter_ints(int M, int d, int F, int nh, int n_layers);
 size_t mega_smem_bytes(bool bf16, int M, int d);
 int mega_occupancy(bool bf16, int M, int d);
 int att_unit_keys(bool bf16);   // prefix keys per attention unit
-hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s);
+// loop_block: launch under the k_mega symbol (shared block B) rather than k_mega_aux
+hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool loop_block);
 
 void launch_validate(int n, const int32_t* slot, const int32_t* dep, int dep_lo, int dep_hi, const int32_t* pos,
                      const int32_t* anc_off, int n_fin, int max_anc, long long S, int32_t* slot_ok, int32_t* dep_ok,

@@ -241,7 +241,8 @@ namespace {
 // One launch of the persistent layer kernel over rows [i0, i0 + mc) of `r`.
 ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, const int32_t* hidx, const LayerW* tab,
                    int n_layers, void* kv, const int32_t* dep, int dep_off, int blk_mul, int init_mode,
-                   const int32_t* tokens, const int32_t* gather, const float* Hg, float* logits, hipStream_t s) {
+                   const int32_t* tokens, const int32_t* gather, const float* Hg, float* logits, hipStream_t s,
+                   bool loop_block = false) {
   const ls_model_desc& d = m->d;
   MegaArgs a{};
   a.M = mc; a.d = d.d; a.F = d.F; a.hd = d.head_dim; a.nh = d.n_heads; a.V = d.V;
@@ -274,7 +275,7 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
   const int G = occ * m->n_cu;
   a.trace = m->trace;
   m->last_grid = G;
-  hipError_t e = launch_mega(m->bf16(), a, G, s);
+  hipError_t e = launch_mega(m->bf16(), a, G, s, loop_block);
   if (e != hipSuccess) return fail(LS_ERR_HIP, "persistent kernel launch: %s", hipGetErrorString(e));
   return LS_OK;
 }
@@ -308,7 +309,7 @@ ls_status ls_loop_step(ls_model* m, const ls_rows* r, float* H, const ls_kv* kv,
   launch_validate(r->n, r->slot, r->depth, 1, d.R, r->pos, r->anc_off, r->n_fin, r->max_anc, d.slot_capacity,
                   m->slot_ok, m->dep_ok, m->row_ok, m->err, s);
   st = run_mega(m, r, 0, r->n, H, m->slot_ok, m->tab_core, d.L, kv->core, m->dep_ok, -1, d.L, 0, nullptr, nullptr,
-                nullptr, nullptr, s);
+                nullptr, nullptr, s, true);
   if (st) return st;
   return check_hip("ls_loop_step");
 }

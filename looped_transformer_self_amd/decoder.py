@@ -141,9 +141,10 @@ class Decoder:
         return u
 
     # ---- prefill ----------------------------------------------------------------------
-    def prefill(self, prompt, chunk=None):
+    def prefill(self, prompt, chunk=None, progress=None):
         """Run the prompt through P, all R loops and the readouts, then commit the first new
-        token from p_R of the last prompt position.  Not part of the timed decode."""
+        token from p_R of the last prompt position.  Not part of the timed decode.
+        `progress(done, total)`, if given, is called after each chunk of prompt positions."""
         cfg, e = self.cfg, self.e
         prompt = [int(t) for t in prompt]
         T0 = len(prompt)
@@ -170,6 +171,8 @@ class Decoder:
                                 extra=[np.asarray(out_rows, np.int32)])
                     e.readout(rr, self.dec.greedy, self.dec.T, self.dec.top_p, rr.extra[0])
             self._fin_append(slots)
+            if progress is not None:
+                progress(c0 + n, T0)
         self.prompt_len = T0
         self.tokens = list(prompt)
         job = np.zeros((1, 10), np.int32)
@@ -385,10 +388,13 @@ class Decoder:
         self.rows_hist = []
 
     # ---- full decode ------------------------------------------------------------------
-    def decode(self, n_new):
-        """Steps until n_new tokens (including the one from prefill) are committed."""
+    def decode(self, n_new, progress=None):
+        """Steps until n_new tokens (including the one from prefill) are committed.
+        `progress(committed, n_new)`, if given, is called after each pipeline step."""
         while len(self.tokens) - self.prompt_len < n_new:
             self.step()
+            if progress is not None:
+                progress(len(self.tokens) - self.prompt_len, n_new)
         st = self.e.sync_status()
         if st != L.LS_OK:
             raise L.LoopSpecError(st, "decode")
