@@ -67,6 +67,128 @@ def _cpu_model():
     return "unknown"
 
 
+COPY_BYTES = 1 << 30            # size of the plain device copy that calibrates the HBM byte counters
+LOOP_KERNEL = "void ls::k_mega<"  # profile name prefix of the loop-block launches (ls_loop_step)
+TRAFFIC_SOURCES = ["mega.hip", "common.h", "kernels.h", "loopspec_abi.hip"]
+
+
+def _kernel_source_sha():
+    """sha256 over the sources that define the loop-block kernel and its launch."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "looped_transformer_self_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _measured_traffic(workload):
+    """HBM bytes per ls_loop_step launch from the committed counter summary of this workload,
+    if it was taken on the current kernel sources; else None."""
+    import glob
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
+        with open(path) as f:
+            for line in f:
+                line = line.strip()
+                if line.startswith('{"kernel": "k_mega"'):
+                    rec = json.loads(line)
+                    if rec.get("workload") == workload and rec.get("source_sha256") == _kernel_source_sha():
+                        return rec
+    return None
+
+
+def copy_calibration():
+    """One plain device-to-device copy of COPY_BYTES, the reference for the byte counters."""
+    import torch
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
+
+
+def _db(d):
+    """The rocpd SQLite database rocprofv3 wrote under directory d."""
+    import glob
+    import sqlite3
+    hits = sorted(glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no rocprofv3 database under {d}")
+    return sqlite3.connect(hits[0])
+
+
+def _counter_per_dispatch(d, counter, prefix):
+    rows = _db(d).execute("select dispatch_id, value from counters_collection where counter_name = ? and "
+                          "substr(kernel_name, 1, ?) = ? order by dispatch_id", (counter, len(prefix), prefix))
+    return [float(v) for _, v in rows]
+
+
+def pmc_summary(a):
+    """Digest of the rocprofv3 runs of one benchmark command: the loop-block kernel's
+    per-launch duration (kernel trace) and HBM bytes (FETCH_SIZE / WRITE_SIZE runs, scaled
+    by the same counters on a plain copy of known size), over the launches of the timed
+    region.  Prints a markdown summary with one machine-readable JSON line."""
+    import re
+    log = open(a.bench_log).read()
+    m = re.search(r"ls_loop_step launches: (\d+) before the timed region, (\d+) in it", log)
+    nb, nt = int(m.group(1)), int(m.group(2))
+    alg = float(re.search(r"algorithmic bytes per ls_loop_step launch: ([0-9.]+)", log).group(1))
+    ev_us = float(re.search(r"event-timed us per ls_loop_step launch: ([0-9.]+)", log).group(1))
+    bench_line = json.loads([l for l in log.splitlines() if l.startswith('{"metric"')][-1])
+    db = _db(a.trace_dir)
+    dur = [(e - b) / 1e3 for b, e in db.execute(
+        "select start, end from kernels where substr(name, 1, ?) = ? order by dispatch_id",
+        (len(LOOP_KERNEL), LOOP_KERNEL))]
+    st = [avg for name, avg in db.execute("select name, average from top_kernels") if name.startswith(LOOP_KERNEL)]
+    fe = _counter_per_dispatch(a.fetch_dir, "FETCH_SIZE", LOOP_KERNEL)
+    wr = _counter_per_dispatch(a.write_dir, "WRITE_SIZE", LOOP_KERNEL)
+    for name, v in (("kernel trace", dur), ("FETCH_SIZE run", fe), ("WRITE_SIZE run", wr)):
+        if len(v) != nb + nt:
+            raise SystemExit(f"{name}: {len(v)} loop-block launches, the bench log says {nb} + {nt}")
+    cf = max(_counter_per_dispatch(a.copy_fetch_dir, "FETCH_SIZE", "__amd_rocclr_copyBuffer"))
+    cw = max(_counter_per_dispatch(a.copy_write_dir, "WRITE_SIZE", "__amd_rocclr_copyBuffer"))
+    kf, kw = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    sl = slice(nb, nb + nt)
+    mean = lambda v: sum(v) / len(v)
+    f_b, w_b = mean(fe[sl]) * 1024 * kf, mean(wr[sl]) * 1024 * kw
+    rec = {"kernel": "k_mega", "workload": a.workload, "source_sha256": _kernel_source_sha(),
+           "launches": nt, "fetch_bytes_per_launch": round(f_b), "write_bytes_per_launch": round(w_b),
+           "traffic_bytes_per_launch": round(f_b + w_b), "algorithmic_bytes_per_launch": round(alg),
+           "copy_scale_fetch": round(kf, 4), "copy_scale_write": round(kw, 4),
+           "trace_us_per_launch": round(mean(dur[sl]), 2), "event_us_per_launch": ev_us}
+    out = [f"# k_mega (ls_loop_step) on workload {a.workload}: duration and HBM traffic per launch", "",
+           "Commands (repo root, MI355X, one GPU), in this order:", ""]
+    out += [f"    {c}" for c in a.commands]
+    out += ["", f"Timed region: launches {nb}..{nb + nt - 1} of the loop-block kernel (the {nb} before it are "
+            "the untimed prefill/warmup); the decode is deterministic, so every run makes the same launches.", "",
+            "| quantity | value |", "|---|---|",
+            f"| launches in the timed region | {nt} |",
+            f"| kernel-trace mean duration, timed launches (us) | {mean(dur[sl]):.1f} |",
+            f"| kernel-trace mean duration, all {nb + nt} launches (us) | {mean(dur):.1f} |",
+            f"| rocprofv3 top_kernels average, all launches (us) | {st[0] if st else float('nan'):.1f} |",
+            f"| HIP-event mean duration in bench.py, timed launches (us) | {ev_us:.1f} |",
+            f"| copy calibration: FETCH_SIZE / WRITE_SIZE of a {COPY_BYTES >> 20} MiB copy (KiB) | {cf:.0f} / {cw:.0f} |",
+            f"| scale to bytes (fetch, write) | {kf:.4f}, {kw:.4f} |",
+            f"| HBM bytes fetched per launch | {f_b / 1e9:.4f} GB |",
+            f"| HBM bytes written per launch | {w_b / 1e9:.4f} GB |",
+            f"| algorithmic bytes per launch | {alg / 1e9:.4f} GB |",
+            f"| traffic / algorithmic | {(f_b + w_b) / alg:.3f} |",
+            f"| bench line | {bench_line['value']} {bench_line['unit']}, frac {bench_line['roofline']['frac']} |",
+            "", "All kernels of the kernel-trace run (rocprofv3 top_kernels; prefill and decode):", "",
+            "| kernel | calls | total us | avg us | % |", "|---|---|---|---|---|"]
+    for name, calls, tot, avg, pct in db.execute(
+            "select name, total_calls, total_duration, average, percentage from top_kernels"):
+        out.append(f"| `{name[:90]}` | {calls} | {tot:.0f} | {avg:.1f} | {pct:.2f} |")
+    out += ["", "Machine-readable (read by bench.py while the kernel sources are unchanged):", "",
+            json.dumps(rec), ""]
+    text = "\n".join(out)
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
 class _Progress:
     """Prints '[bench] <what> done/total' to stderr at most every `every` seconds."""
 
@@ -88,11 +210,29 @@ def main():
     ap.add_argument("--workload", default="C2")
     ap.add_argument("--mode", default="spec", choices=["spec", "ar"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run one plain device copy of 1 GiB (byte-counter calibration)")
+    ap.add_argument("--pmc-summary", action="store_true",
+                    help="summarise rocprofv3 outputs of a benchmark run (no GPU)")
+    ap.add_argument("--bench-log")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--copy-fetch-dir")
+    ap.add_argument("--copy-write-dir")
+    ap.add_argument("--out")
+    ap.add_argument("--commands", nargs="*", default=[])
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not supported "
                                    f"(asked for --gpus {args.gpus})"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
@@ -121,6 +261,7 @@ def main():
         print(f"[bench] warmup {i} done", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     e.prof = []
+    n_before = e.n_loop_calls
     stats = []
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -137,8 +278,10 @@ def main():
     n_calls = len(e.prof)
     e.prof = None
     achieved = by / (t_ms * 1e-3) / 1e9 if t_ms > 0 else 0.0
-    print(f"[bench] {n_calls} ls_loop_step calls, {by / n_calls / 1e9:.3f} GB/call, "
-          f"{t_ms / n_calls * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+    print(f"[bench] ls_loop_step launches: {n_before} before the timed region, {n_calls} in it", file=sys.stderr)
+    print(f"[bench] algorithmic bytes per ls_loop_step launch: {by / n_calls:.1f}", file=sys.stderr)
+    print(f"[bench] event-timed us per ls_loop_step launch: {t_ms / n_calls * 1e3:.2f}", file=sys.stderr, flush=True)
+    traffic = _measured_traffic(wl.key)
     st = stats[-1]
     out = {
         "metric": "committed tokens/s at batch 1",
@@ -157,8 +300,11 @@ def main():
                    "mode": args.mode, "batch": 1},
         "roofline": {"kernel": "ls_loop_step (one call: all layers of the shared block, all active rows)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_call": round(by / n_calls), "us_per_call": round(t_ms / n_calls * 1e3, 2)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "bytes_per_call": round(by / n_calls), "us_per_call": round(t_ms / n_calls * 1e3, 2),
+                     "launches": n_calls},
         "decode_stats": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in st.items()},
     }
     if not args.no_cpu_baseline:

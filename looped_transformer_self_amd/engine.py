@@ -126,6 +126,7 @@ class Engine:
         self.vout = torch.zeros(max_jobs * 4, dtype=torch.int32, device=self.dev)
         self.vout_host = torch.zeros(max_jobs * 4, dtype=torch.int32, pin_memory=True)
         self.prof = None          # list of (start event, end event, row metadata) when profiling
+        self.n_loop_calls = 0     # ls_loop_step launches with at least one row, since creation
 
     def __del__(self):
         try:
@@ -173,6 +174,7 @@ class Engine:
             b.record()
         L.check(L.lib.ls_loop_step(self.h, C.byref(rows.s), _ptr(self.H), C.byref(self.kv), self.stream_ptr()),
                 "ls_loop_step")
+        self.n_loop_calls += rows.n > 0
         if self.prof is not None and rows.n:
             e.record()
             self.prof.append((b, e, rows.host))
