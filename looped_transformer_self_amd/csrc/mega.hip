@@ -641,20 +641,38 @@ struct Consumer {
     constexpr int E = 16 / (int)sizeof(T);
     const int r = lane & 15, g = lane >> 4;
     const char* base = s.ring + (size_t)slot * SLAB + r * 512;
-    const int nst = kn / (4 * E);
+    const int nst = kn / (4 * E);                    // 64-byte steps holding data (8 but for a ragged tail)
     const int xoff = q * (512 / (int)sizeof(T));     // element offset of this slab in the staged chunk
+    // Straight-line LDS traffic: every ring and activation read of a group is issued before the
+    // first MFMA consumes one, so a slab costs one LDS round trip per group rather than one per
+    // step.  Rows m >= M and steps past a ragged tail multiply zeros (their ring bytes are
+    // finite weights, their activation reads stay inside the row's staged chunk).
+    constexpr int VG = MT == 1 ? 8 : (MT == 2 ? 4 : (MT == 4 ? 2 : 1));
+    const T* xrow[MT];
+    bool mok[MT];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      if (v < nst) {
-        const int ch = 4 * v + g;
-        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(base + ((ch ^ (r & 31)) * 16));
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r;
+      mok[mt] = m < a.M;
+      xrow[mt] = (const T*)s.X + (size_t)(mok[mt] ? m : 0) * s.xstride + xoff;
+    }
+#pragma unroll
+    for (int v0 = 0; v0 < 8; v0 += VG) {
+      u32x4_t w[VG], x[VG][MT];
+#pragma unroll
+      for (int u = 0; u < VG; ++u) {
+        const int ch = 4 * (v0 + u) + g;
+        w[u] = *reinterpret_cast<const u32x4_t*>(base + ((ch ^ r) * 16));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) x[u][mt] = *reinterpret_cast<const u32x4_t*>(xrow[mt] + ch * E);
+      }
+#pragma unroll
+      for (int u = 0; u < VG; ++u) {
+        const bool live = v0 + u < nst;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const int m = mt * 16 + r;
-          u32x4_t x = u32x4_t{0u, 0u, 0u, 0u};
-          if (m < a.M)
-            x = *reinterpret_cast<const u32x4_t*>((const T*)s.X + (size_t)m * s.xstride + xoff + ch * E);
-          Mma<T>::run(acc[mt], w, x);
+          const u32x4_t xv = (live && mok[mt]) ? x[u][mt] : u32x4_t{0u, 0u, 0u, 0u};
+          Mma<T>::run(acc[mt], w[u], xv);
         }
       }
     }
