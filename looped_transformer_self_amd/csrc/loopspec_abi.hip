@@ -51,7 +51,7 @@ struct ls_model {
   LayerW *tab_pre = nullptr, *tab_core = nullptr, *tab_coda = nullptr;
   std::vector<LayerW> host_tab;
   int n_cu = 0;
-  int occ[9] = {0};      // resident workgroups per CU, by m-tile count
+  int occ[LS_MAX_ROWS + 1] = {0};   // resident workgroups per CU, by rows per launch
   long long* trace = nullptr;   // optional phase timestamps of the next ls_loop_step
   int last_grid = 0;
   bool bf16() const { return d.dtype == LS_BF16; }
@@ -265,10 +265,9 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
   a.cnt = m->cnt; a.err = m->err;
   a.init_mode = init_mode; a.gather = gather ? gather + i0 : nullptr; a.Hg = Hg;
   a.do_head = logits != nullptr;
-  const int mt = (mc + 15) / 16;
-  int& occ = m->occ[mt];
+  int& occ = m->occ[mc];
   if (!occ) {
-    occ = mega_occupancy(m->bf16(), 16 * mt, d.d);
+    occ = mega_occupancy(m->bf16(), mc, d.d);
     if (occ <= 0) return fail(LS_ERR_HIP, "persistent kernel: no resident workgroup fits (M=%d)", mc);
     occ = std::min(occ, 4);
   }

@@ -34,8 +34,9 @@
 namespace ls {
 
 enum Phase { PH_INIT = 0, PH_QKV = 1, PH_ATT = 2, PH_O = 3, PH_GU = 4, PH_DOWN = 5, PH_HEAD = 6 };
-constexpr int NCONS = 4, NPROD = 2;
-constexpr int MEGA_THREADS = 64 * (NCONS + NPROD);
+constexpr int NCONS = 4, NPROD = 2, NEPI = 1;
+constexpr int MEGA_THREADS = 64 * (NCONS + NPROD + NEPI);
+constexpr int EPI_WAVE = NCONS + NPROD;  // wave index of the epilogue wave
 constexpr int SLAB = 8192;              // bytes: 16 rows x 512 bytes
 constexpr int PADC = 64;                // counters that are polled get their own 256-byte line
 
@@ -249,7 +250,8 @@ struct Lds {
   int* grow;         // M: rows ordered by KV depth group (attention shares a group's keys)
   int* goff;         // group g's rows: grow[goff[g] .. goff[g+1]); goff[64] = group count
   int *rslot, *rdep, *raoff;   // the rows' validated slot, depth (0 without depths), ancestor offsets
-  int* ints;         // [0..NS) full, [NS..2NS) empty, [2NS] consumer barrier, [2NS+1..] flags
+  int* ints;         // [0..NS) full, [NS..2NS) empty, [2NS] consumer barrier, [2NS+1] partials
+                     // posted (4 per tile), [2NS+2] partial buffers released by the epilogue wave
   int xstride;       // elements
   int NS, XC, nred;
 };
@@ -304,15 +306,26 @@ LS_DEV PhaseGeo phase_geo(const MegaArgs& a, int ph) {
   return g;
 }
 
+// QKV tiles are numbered head-major: tile t holds 16 output features (8 rotary pairs) of matrix
+// mat (0 Q, 1 K, 2 V) of head h, pair block jj.  With round-robin dealing the first round of
+// tiles then completes whole heads, whose attention can start while later rounds run.
+struct QkvTile {
+  int mat, h, jj;
+};
+LS_DEV QkvTile qkv_tile(const MegaArgs& a, int t) {
+  const int tph = a.hd / 16;
+  const int h = t / (3 * tph), r = t % (3 * tph);
+  return QkvTile{r / tph, h, r % tph};
+}
+
 // Weight row r (0..15) of tile t: byte pointer of the row start.
 template <typename T>
 LS_DEV const char* wrow(const MegaArgs& a, const LayerW& lw, int ph, int t, int r, int K) {
   const size_t rb = (size_t)K * sizeof(T);
   if (ph == PH_QKV) {
-    const int tpm = a.d / 16, tph = a.hd / 16;
-    const int mat = t / tpm, tl = t % tpm;
-    const int h = tl / tph, jj = tl % tph;
-    const int n = h * a.hd + 8 * jj + (r & 7) + (r < 8 ? 0 : a.hd / 2);
+    const QkvTile q = qkv_tile(a, t);
+    const int mat = q.mat;
+    const int n = q.h * a.hd + 8 * q.jj + (r & 7) + (r < 8 ? 0 : a.hd / 2);
     const void* W = mat == 0 ? lw.Wq : (mat == 1 ? lw.Wk : lw.Wv);
     return (const char*)W + (size_t)n * rb;
   }
@@ -482,6 +495,7 @@ struct Consumer {
   int c;            // consumer index 0..3
   int lane;
   int cslot = 0, cuse = 0;   // ring slot and use count of the next slab in the sequence
+  int seq = 0;               // GEMM tiles of the launch whose partials this consumer has posted
   bool dbg = false; // fine stamps on (first layer's QKV phase)
 
   LS_DEV Consumer(const MegaArgs& a_, const Lds& s_, ConsBar& cb_, int c_)
@@ -688,9 +702,8 @@ LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, const Lds& s, int p
                      int lane) {
   (void)cl;
   if (ph == PH_QKV) {
-    const int tpm = a.d / 16, tph = a.hd / 16;
-    const int mat = t / tpm, tl = t % tpm;
-    const int h = tl / tph, jj = tl % tph;
+    const QkvTile qt = qkv_tile(a, t);
+    const int mat = qt.mat, h = qt.h, jj = qt.jj;
     for (int idx = lane; idx < a.M * 8; idx += 64) {
       const int m = idx >> 3, p = idx & 7;
       const int i = 8 * jj + p;
@@ -774,7 +787,7 @@ LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, const Lds& s, int p
 LS_DEV void tile_signal(const MegaArgs& a, const CntLayout& cl, int ph, int l, int t, int XC) {
   int* C = a.cnt + (size_t)l * cl.per_layer;
   if (ph == PH_QKV) {
-    atomicAdd(C + cl.o_qkvh + ((t % (a.d / 16)) / (a.hd / 16)) * PADC, 1);
+    atomicAdd(C + cl.o_qkvh + qkv_tile(a, t).h * PADC, 1);
   } else if (ph == PH_O || ph == PH_DOWN) {
     atomicAdd(C + (ph == PH_O ? cl.o_o : cl.o_down), 1);
   } else if (ph == PH_GU) {
@@ -960,8 +973,13 @@ LS_DEV void att_unit_wave(const MegaArgs& a, const Lds& s, const CntLayout& cl, 
       }
     }
   };
-  Raw8<T> ka[RR], va[RR], kb[RR], vb[RR];
-  load_pass(0, ka, va);                                   // before the wait: earlier launches' keys
+  // The first NPF passes of prefix keys and values are requested before the wait (they were
+  // written by earlier launches, so their latency overlaps the QKV phase); pass p + NPF reuses
+  // the registers of pass p, requested as soon as pass p is consumed.
+  constexpr int NPF = NPASS / 2;
+  Raw8<T> kr[NPF][RR], vr[NPF][RR];
+#pragma unroll
+  for (int p = 0; p < NPF; ++p) load_pass(p, kr[p], vr[p]);
   // queries of this head are complete once the head's q/k/v tiles have all signalled
   if (lane == 0) {
     int n = 0;
@@ -979,7 +997,10 @@ LS_DEV void att_unit_wave(const MegaArgs& a, const Lds& s, const CntLayout& cl, 
     const int i = s.grow[g0 + r];
     const int qoff = (i * a.d + h * hd + 8 * e) * 4;
     const u32x4_t qa = ldc128(Rq, dim_ok ? qoff : 0x7fffff00), qb = ldc128(Rq, dim_ok ? qoff + 16 : 0x7fffff00);
-    if (r > 0) load_pass(0, ka, va);                      // a later row re-reads the keys (cached)
+    if (r > 0) {                                          // a later row re-reads the keys (cached)
+#pragma unroll
+      for (int p = 0; p < NPF; ++p) load_pass(p, kr[p], vr[p]);
+    }
     float q8[8];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -987,13 +1008,13 @@ LS_DEV void att_unit_wave(const MegaArgs& a, const Lds& s, const CntLayout& cl, 
       q8[4 + t] = __uint_as_float(qb[t]) * scale;
     }
     float run_m = -INFINITY, lsum = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    auto consume = [&](int p, const Raw8<T>* kr, const Raw8<T>* vr) {
+    auto consume = [&](int p, const Raw8<T>* kp, const Raw8<T>* vp) {
       float sc[RR];
       float pm = -INFINITY;
 #pragma unroll
       for (int rr = 0; rr < RR; ++rr) {
         float kf[8];
-        kr[rr].unpack(kf);
+        kp[rr].unpack(kf);
         float part = 0.f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) part += q8[t] * kf[t];
@@ -1016,23 +1037,17 @@ LS_DEV void att_unit_wave(const MegaArgs& a, const Lds& s, const CntLayout& cl, 
         const float pw = sl[p * RR + rr] >= 0 ? __expf(sc[rr] - nm) : 0.f;
         lsum += pw;
         float vf[8];
-        vr[rr].unpack(vf);
+        vp[rr].unpack(vf);
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc[t] += pw * vf[t];
       }
     };
 #pragma unroll
-    for (int p = 0; p < NPASS; p += 2) {
-      if (p + 1 < NPASS) load_pass(p + 1, kb, vb);
+    for (int p = 0; p < NPASS; ++p) {
+      consume(p, kr[p % NPF], vr[p % NPF]);
       __builtin_amdgcn_sched_barrier(0);
-      consume(p, ka, va);
+      if (p + NPF < NPASS) load_pass(p + NPF, kr[p % NPF], vr[p % NPF]);
       __builtin_amdgcn_sched_barrier(0);
-      if (p + 1 < NPASS) {
-        if (p + 2 < NPASS) load_pass(p + 2, ka, va);
-        __builtin_amdgcn_sched_barrier(0);
-        consume(p + 1, kb, vb);
-        __builtin_amdgcn_sched_barrier(0);
-      }
     }
     // per-lane sums cover the lane's keys; combine the four key groups
     lsum += __shfl_xor(lsum, 16, 64);
@@ -1081,12 +1096,8 @@ LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
     const int a0 = s.raoff[i], na = s.raoff[i + 1] - a0;
     const int nt = na + 1;                           // the row's own keys: ancestors, then itself
     const float* base = a.patt + ((size_t)i * a.nh + h) * a.att_chunks * (hd + 2);
-    float q0 = 0.f, q1 = 0.f;
-    if (dok) {
-      const unsigned long long qw = ldc64(a.q + (size_t)i * a.d + h * hd + 2 * lane);
-      q0 = __uint_as_float((unsigned)qw) * scale;
-      q1 = __uint_as_float((unsigned)(qw >> 32)) * scale;
-    }
+    // the query joins the first batch's loads (it is converted where the scores are formed)
+    const unsigned long long qw = dok ? ldc64(a.q + (size_t)i * a.d + h * hd + 2 * lane) : 0ull;
     float run_m = -INFINITY, den = 0.f, num0 = 0.f, num1 = 0.f;
     const int nbat = max((nu + 15) / 16, (nt + 7) / 8);
     for (int bt = 0; bt < nbat; ++bt) {
@@ -1128,6 +1139,7 @@ LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
       }
       if (bad) ls_flag(a.err, 1);
       // ---- the batch's scores and its maximum
+      const float q0 = __uint_as_float((unsigned)qw) * scale, q1 = __uint_as_float((unsigned)(qw >> 32)) * scale;
       float sc[8];
       float bm = warp_max(mxc);
 #pragma unroll
@@ -1278,11 +1290,20 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
     }
     if (!PROD) {
       if (threadIdx.x == 0 && i == 0) tstamp(a, l, ph, 4);
-      // The four consumer partials meet in LDS (s.nred rotating buffers); consumer (tile mod 4)
-      // sums them in consumer order, runs the epilogue, drains its stores and bumps the tile's
-      // counter while the other consumers go on with the next tile.
+      // The four consumer partials meet in LDS (s.nred rotating buffers) and the epilogue wave
+      // takes the tile from there: consumers never wait for the epilogue's stores to drain.
       const int lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
-      float* buf = s.red + (size_t)(i % s.nred) * NCONS * a.M * 16;
+      const int q = co->seq++;
+      float* buf = s.red + (size_t)(q % s.nred) * NCONS * a.M * 16;
+      if (q >= s.nred && lane == 0) {      // the epilogue wave is done with this buffer's last tile
+        int n = 0;
+        while (lds_peek(s.ints + 2 * s.NS + 2) < q - s.nred + 1) {
+          __builtin_amdgcn_s_sleep(0);
+          if (++n > SPIN_LIMIT) { ls_flag(a.err, LS_TIMEOUT); break; }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" : : : "memory");
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int m = mt * 16 + r;
@@ -1291,30 +1312,56 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
           for (int jj = 0; jj < 4; ++jj) buf[((size_t)co->c * a.M + m) * 16 + 4 * gq + jj] = acc[mt][jj];
         }
       }
-      dstamp(a, co->dbg, 9);
-      cb->sync();
-      dstamp(a, co->dbg, 10);
-      if (i % NCONS == co->c) {
-        for (int idx = lane; idx < a.M * 16; idx += 64) {
-          float y = 0.f;
-#pragma unroll
-          for (int cc = 0; cc < NCONS; ++cc) y += buf[(size_t)cc * a.M * 16 + idx];
-          buf[idx] = y;                   // consumer 0's slot now holds the tile sum
-        }
-        __builtin_amdgcn_wave_barrier();
-        wait_lgkm0();                      // the sums are visible to every lane
-        epilogue<T>(a, cl, s, ph, l, t, buf, lane);
-        dstamp(a, co->dbg, 11);
-        if (ph != PH_HEAD) {
-          drain();
-          dstamp(a, co->dbg, 12);
-          if (lane == 0) tile_signal(a, cl, ph, l, t, s.XC);
-          dstamp(a, co->dbg, 13);
-        }
-      }
-      if (s.nred == 1) cb->sync();        // single buffer: read before the next tile's partials
+      if (lane == 0) lds_bump(s.ints + 2 * s.NS + 1);   // after this wave's partial writes complete
     }
     if (PROD && threadIdx.x == 64 * NCONS && i == sh.count - 1) tstamp(a, l, ph, 6);
+  }
+}
+
+// The epilogue wave's part of a GEMM phase: for each of the workgroup's tiles (in the
+// consumers' order) wait for the four consumer partials, sum them in consumer order, run the
+// epilogue and release the partial buffer.  Stores are drained, and the tiles' counters
+// bumped, once no further tile of the phase is ready, so a burst of tiles costs one drain.
+template <typename T>
+LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int ph, int l, int& deal, int& seq) {
+  const int G = gridDim.x, b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const PhaseGeo g = phase_geo<T>(a, ph);
+  const Share sh = share_of(g.n_tiles, deal, G, b);
+  deal = (deal + g.n_tiles) % G;
+  int pend = 0;                            // first of this phase's tiles not yet signalled
+  for (int i = 0; i < sh.count; ++i) {
+    const int t = sh.first + i * G;
+    const int q = seq++;
+    float* buf = s.red + (size_t)(q % s.nred) * NCONS * a.M * 16;
+    if (lane == 0) {
+      int n = 0;
+      while (lds_peek(s.ints + 2 * s.NS + 1) < NCONS * (q + 1)) {
+        __builtin_amdgcn_s_sleep(0);
+        if (++n > SPIN_LIMIT) { ls_flag(a.err, LS_TIMEOUT); break; }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" : : : "memory");
+    for (int idx = lane; idx < a.M * 16; idx += 64) {
+      float y = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < NCONS; ++cc) y += buf[(size_t)cc * a.M * 16 + idx];
+      buf[idx] = y;                        // consumer 0's slot now holds the tile sum
+    }
+    __builtin_amdgcn_wave_barrier();
+    wait_lgkm0();                          // the sums are visible to every lane
+    epilogue<T>(a, cl, s, ph, l, t, buf, lane);
+    wait_lgkm0();                          // the epilogue's reads of the buffer are complete
+    if (lane == 0) lds_bump(s.ints + 2 * s.NS + 2);
+    if (ph == PH_HEAD) continue;
+    const bool next_ready = i + 1 < sh.count && lds_peek(s.ints + 2 * s.NS + 1) >= NCONS * (q + 2);
+    if (!next_ready) {
+      drain();
+      if (lane == 0)
+        for (int k = pend; k <= i; ++k) tile_signal(a, cl, ph, l, sh.first + k * G, s.XC);
+      pend = i + 1;
+    }
   }
 }
 
@@ -1348,6 +1395,16 @@ LS_DEV void mega_body(const MegaArgs& a) {
   __syncthreads();
   int deal = 0;
   const int n_steps = 5 * a.n_layers + (a.do_head ? 1 : 0);
+  if (wv == EPI_WAVE) {
+    // ------------------------------ epilogue wave ------------------------------
+    int seq = 0;
+#pragma unroll 1
+    for (int st = 0; st < n_steps; ++st) {
+      const Step sp = step_of(a, st);
+      if (sp.ph != PH_ATT) epi_walk<T>(a, s, cl, sp.ph, sp.l, deal, seq);
+    }
+    return;
+  }
   if (wv >= NCONS) {
     // ------------------------------ producer waves ------------------------------
     Producer<T> pr(a, s, wv - NCONS);
