@@ -696,10 +696,27 @@ struct Consumer {
   }
 };
 
-// Epilogue of one finished tile (its sum over the four consumers is in Ts[m*16 + n]).
+// Residual inputs of a tile's epilogue (O: the layer input, DOWN: the post-attention rows):
+// res[u] for row m0 + 4u + lane/16, column 16t + lane%16, through one descriptor; absent rows
+// read as zero (offset beyond the descriptor's range).  Every load is issued before any is used.
+LS_DEV void residual_load(const MegaArgs& a, const Lds& s, int ph, int l, int t, int m0, int lane, float* res) {
+  const __amdgpu_buffer_rsrc_t Rr = rsrc_of(ph == PH_O ? layer_in(a, l) : ys_of(a, l), 0x7fffffff);
+  const int n = 16 * t + (lane & 15);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int m = m0 + 4 * u + (lane >> 4);
+    const int hr = m < a.M ? s.hx[m] : -1;
+    const int row = ph == PH_O && l == 0 ? hr : m;
+    const int off = hr >= 0 ? (row * a.d + n) * 4 : 0x7fffffff;
+    res[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(Rr, off, 0, 0));
+  }
+}
+
+// Epilogue of one finished tile (its sum over the four consumers is in Ts[m*16 + n]).  With
+// have_pre, pre holds the residual inputs of rows 0..15 (O and DOWN), loaded ahead.
 template <typename T>
 LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, const Lds& s, int ph, int l, int t, const float* Ts,
-                     int lane) {
+                     int lane, bool have_pre, const float (&pre)[4]) {
   (void)cl;
   if (ph == PH_QKV) {
     const QkvTile qt = qkv_tile(a, t);
@@ -732,22 +749,16 @@ LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, const Lds& s, int p
     const int nt = a.d / 16;
     float* ssq = a.ssq + ((size_t)l * 2 + (ph == PH_DOWN)) * nt * a.M;
     const int nl = lane & 15, n = 16 * t + nl;
-    const float* xin = layer_in(a, l);
     float* yl = ys_of(a, l);
     const bool last = l == a.n_layers - 1;
     float* xout = (!last || a.do_head) ? a.Xs + (size_t)(l + 1) * a.M * a.d : nullptr;
     for (int m0 = 0; m0 < a.M; m0 += 16) {
-      // residual inputs through one descriptor; rows that are absent read as zero (offset
-      // beyond the descriptor's range)
-      const __amdgpu_buffer_rsrc_t Rr = rsrc_of(ph == PH_O ? xin : yl, 0x7fffffff);
       float res[4];
+      if (have_pre && m0 == 0) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int m = m0 + 4 * u + (lane >> 4);
-        const int hr = m < a.M ? s.hx[m] : -1;
-        const int row = ph == PH_O && l == 0 ? hr : m;
-        const int off = hr >= 0 ? (row * a.d + n) * 4 : 0x7fffffff;
-        res[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(Rr, off, 0, 0));
+        for (int u = 0; u < 4; ++u) res[u] = pre[u];
+      } else {
+        residual_load(a, s, ph, l, t, m0, lane, res);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -1322,13 +1333,23 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
 // consumers' order) wait for the four consumer partials, sum them in consumer order, run the
 // epilogue and release the partial buffer.  Stores are drained, and the tiles' counters
 // bumped, once no further tile of the phase is ready, so a burst of tiles costs one drain.
+//
+// Residual inputs of the first O / DOWN tile are loaded when the walk starts if the workgroup
+// had tiles in the phase before (QKV / GU): their partials having arrived means the consumers
+// passed that phase's dependency wait, which implies the residual rows are complete (the
+// previous layer for O, the O phase for DOWN).  The loads then overlap the consumers' work.
 template <typename T>
-LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int ph, int l, int& deal, int& seq) {
+LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int ph, int l, int& deal, int& seq,
+                     bool& had_tiles) {
   const int G = gridDim.x, b = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const PhaseGeo g = phase_geo<T>(a, ph);
   const Share sh = share_of(g.n_tiles, deal, G, b);
   deal = (deal + g.n_tiles) % G;
+  const bool pref = (ph == PH_O || ph == PH_DOWN) && had_tiles && sh.count > 0 && a.M <= 16;
+  float pre[4] = {0.f, 0.f, 0.f, 0.f};
+  if (pref) residual_load(a, s, ph, l, sh.first, 0, lane, pre);
+  had_tiles = sh.count > 0;
   int pend = 0;                            // first of this phase's tiles not yet signalled
   for (int i = 0; i < sh.count; ++i) {
     const int t = sh.first + i * G;
@@ -1351,7 +1372,7 @@ LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int p
     }
     __builtin_amdgcn_wave_barrier();
     wait_lgkm0();                          // the sums are visible to every lane
-    epilogue<T>(a, cl, s, ph, l, t, buf, lane);
+    epilogue<T>(a, cl, s, ph, l, t, buf, lane, pref && i == 0, pre);
     wait_lgkm0();                          // the epilogue's reads of the buffer are complete
     if (lane == 0) lds_bump(s.ints + 2 * s.NS + 2);
     if (ph == PH_HEAD) continue;
@@ -1398,10 +1419,11 @@ LS_DEV void mega_body(const MegaArgs& a) {
   if (wv == EPI_WAVE) {
     // ------------------------------ epilogue wave ------------------------------
     int seq = 0;
+    bool had_tiles = false;
 #pragma unroll 1
     for (int st = 0; st < n_steps; ++st) {
       const Step sp = step_of(a, st);
-      if (sp.ph != PH_ATT) epi_walk<T>(a, s, cl, sp.ph, sp.l, deal, seq);
+      if (sp.ph != PH_ATT) epi_walk<T>(a, s, cl, sp.ph, sp.l, deal, seq, had_tiles);
     }
     return;
   }
