@@ -44,6 +44,37 @@ LS_DEV float warp_max(float v) {
   return v;
 }
 
+// Reductions with every lane of the wave active, on DPP lane moves instead of LDS-crossbar
+// shuffles.  Within each 16-lane row: swap neighbours, swap pairs, mirror halves of 8, mirror
+// halves of 16 (every lane of the row ends with the row's result); across the four rows the
+// row results are read out to scalars, so the wave-wide result is wave-uniform.
+template <int CTRL>
+LS_DEV float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+LS_DEV float lane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+LS_DEV float row_sum16(float v) {
+  v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);   // row_half_mirror
+  v += dpp_f<0x140>(v);   // row_mirror
+  return v;
+}
+LS_DEV float row_max16(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+// v already uniform within each row: combine the four rows.
+LS_DEV float rows_sum(float v) { return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48)); }
+LS_DEV float rows_max(float v) { return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48))); }
+LS_DEV float wave_sum(float v) { return rows_sum(row_sum16(v)); }
+LS_DEV float wave_max(float v) { return rows_max(row_max16(v)); }
+
 // Block-wide reductions through LDS; every thread gets the result.  `red` must hold
 // blockDim.x / 64 floats; callers separate successive uses with __syncthreads().
 LS_DEV float block_sum(float v, float* red) {

@@ -512,7 +512,7 @@ struct Consumer {
         const u32x4_t v = ld128(R, (p0 + 4 * lane) * 4);
         acc += (__uint_as_float(v.x) + __uint_as_float(v.y)) + (__uint_as_float(v.z) + __uint_as_float(v.w));
       }
-      acc = warp_sum(acc);
+      acc = wave_sum(acc);
       if (lane == 0) s.rinv[m] = 1.0f / sqrtf(acc / (float)a.d + a.eps);
     }
     cb.sync();
@@ -537,7 +537,7 @@ struct Consumer {
           acc += (f0 * f0 + f1 * f1) + (f2 * f2 + f3 * f3);
         }
       }
-      acc = warp_sum(acc);
+      acc = wave_sum(acc);
       if (lane == 0) s.rinv[m] = 1.0f / sqrtf(acc / (float)a.d + a.eps);
     }
     cb.sync();
@@ -572,7 +572,7 @@ struct Consumer {
           const float f2 = __uint_as_float(v[u].z), f3 = __uint_as_float(v[u].w);
           ss += (f0 * f0 + f1 * f1) + (f2 * f2 + f3 * f3);
         }
-        ss = warp_sum(ss);
+        ss = wave_sum(ss);
         dstamp(a, dbg && m == 0, 2);
         const float ri = 1.0f / sqrtf(ss / (float)a.d + a.eps);
 #pragma unroll
@@ -773,9 +773,7 @@ LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, const Lds& s, int p
             if (last && hr >= 0) stc(a.H + (size_t)hr * a.d + n, nv);
           }
         }
-        float sq = nv * nv;
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+        const float sq = row_sum16(nv * nv);
         if (nl == 0 && m < a.M) stc(ssq + (size_t)m * nt + t, sq);
       }
     }
@@ -1029,13 +1027,11 @@ LS_DEV void att_unit_wave(const MegaArgs& a, const Lds& s, const CntLayout& cl, 
         float part = 0.f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) part += q8[t] * kf[t];
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+        part = row_sum16(part);             // the key's score in every lane of its row
         sc[rr] = sl[p * RR + rr] >= 0 ? part : -INFINITY;
         pm = fmaxf(pm, sc[rr]);
       }
-      pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
-      pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+      pm = rows_max(pm);
       const float nm = fmaxf(run_m, pm);
       if (nm == -INFINITY) return;                        // no key so far
       const float rs = run_m == -INFINITY ? 0.f : __expf(run_m - nm);
@@ -1152,10 +1148,10 @@ LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
       // ---- the batch's scores and its maximum
       const float q0 = __uint_as_float((unsigned)qw) * scale, q1 = __uint_as_float((unsigned)(qw >> 32)) * scale;
       float sc[8];
-      float bm = warp_max(mxc);
+      float bm = wave_max(mxc);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        sc[u] = warp_sum(q0 * k2[u].x + q1 * k2[u].y);
+        sc[u] = wave_sum(q0 * k2[u].x + q1 * k2[u].y);
         if (j0 + u < nt) bm = fmaxf(bm, sc[u]);
       }
       const float nm = fmaxf(run_m, bm);
@@ -1165,10 +1161,10 @@ LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
       run_m = nm;
       // prefix chunks: weight w_c = exp(mx_c - m) held by lane c - c0
       const float wl = mxc == -INFINITY ? 0.f : __expf(mxc - nm);
-      den += warp_sum(wl * smc);
+      den += wave_sum(wl * smc);
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const float w = __shfl(wl, u, 64);
+        const float w = lane_f(wl, u);
         num0 += w * ac[u].x;
         num1 += w * ac[u].y;
       }
