@@ -174,6 +174,37 @@ LS_DEV void wait_all_ge(const int* base, int stride, int n, int target, ConsBar&
   cb.sync();
 }
 
+// Completion counts of the O, GU and DOWN tiles are spread over NSPREAD counters (tile t bumps
+// counter t mod NSPREAD, each on a line of its own): a phase's tiles finish within a few
+// microseconds of each other, and atomics on one address would queue behind each other and
+// behind the polls of every workgroup.
+constexpr int NSPREAD = 16;
+
+// Tiles t in [lo, hi) with t mod NSPREAD == k.
+__host__ __device__ inline int spread_count(int lo, int hi, int k) {
+  auto fdiv = [](int x) { return x >= 0 ? x / NSPREAD : -((-x + NSPREAD - 1) / NSPREAD); };
+  return hi > lo ? fdiv(hi - 1 - k) - fdiv(lo - 1 - k) : 0;
+}
+
+// Consumer-side wait until the tiles [lo, hi) have all been counted on the spread counters at
+// base (counter k at base + k * PADC): lanes k < NSPREAD of the first consumer wave poll one
+// counter each.
+LS_DEV void wait_spread(const int* base, int lo, int hi, ConsBar& cb) {
+  if (threadIdx.x < 64) {
+    const int k = threadIdx.x;
+    const int target = k < NSPREAD ? spread_count(lo, hi, k) : 0;
+    int n_polls = 0;
+    bool done = k >= NSPREAD || target == 0;
+    while (true) {
+      if (!done) done = ld_acq(base + (size_t)k * PADC) >= target;
+      if (__all(done)) break;
+      __builtin_amdgcn_s_sleep(POLL_SLEEP);
+      if (++n_polls > SPIN_LIMIT) { if (k == 0) ls_flag(cb.err, LS_TIMEOUT); break; }
+    }
+  }
+  cb.sync();
+}
+
 // ---- counter layout -----------------------------------------------------------------------------
 struct CntLayout {
   int per_layer, nchF;
@@ -187,9 +218,9 @@ __host__ __device__ inline CntLayout cnt_layout(int M, int F, int nh, int XC, in
   int o = 0;
   c.o_qkvh = o; o += nh * PADC;
   c.o_att = o; o += nh * PADC;
-  c.o_o = o; o += PADC;
-  c.o_gu = o; o += c.nchF * PADC;
-  c.o_down = o; o += PADC;
+  c.o_o = o; o += NSPREAD * PADC;
+  c.o_gu = o; o += c.nchF * NSPREAD * PADC;
+  c.o_down = o; o += NSPREAD * PADC;
   c.o_fa = o; o += M * nh;
   o = (o + PADC - 1) / PADC * PADC;
   c.per_layer = o;
@@ -798,9 +829,9 @@ LS_DEV void tile_signal(const MegaArgs& a, const CntLayout& cl, int ph, int l, i
   if (ph == PH_QKV) {
     atomicAdd(C + cl.o_qkvh + qkv_tile(a, t).h * PADC, 1);
   } else if (ph == PH_O || ph == PH_DOWN) {
-    atomicAdd(C + (ph == PH_O ? cl.o_o : cl.o_down), 1);
+    atomicAdd(C + (ph == PH_O ? cl.o_o : cl.o_down) + (t % NSPREAD) * PADC, 1);
   } else if (ph == PH_GU) {
-    atomicAdd(C + cl.o_gu + ((8 * t) / XC) * PADC, 1);
+    atomicAdd(C + cl.o_gu + (((8 * t) / XC) * NSPREAD + t % NSPREAD) * PADC, 1);
   }
 }
 
@@ -1240,7 +1271,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
     if (ph == PH_QKV || ph == PH_HEAD) {
       const int lp = ph == PH_QKV ? l - 1 : a.n_layers - 1;    // layer whose output feeds this phase
       if (lp >= 0) {
-        wait_ge(a.cnt + (size_t)lp * cl.per_layer + cl.o_down, nt, *cb);
+        wait_spread(a.cnt + (size_t)lp * cl.per_layer + cl.o_down, 0, nt, *cb);
         ssq = a.ssq + ((size_t)lp * 2 + 1) * nt * a.M;
       } else if (a.init_mode) {
         wait_ge(a.cnt + cl.o_init, a.M, *cb);
@@ -1250,7 +1281,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
         else co->rinv_from_rows(a.H);            // first layer of the call: the caller's rows
       }
     } else if (ph == PH_GU) {
-      wait_ge(C + cl.o_o, nt, *cb);
+      wait_spread(C + cl.o_o, 0, nt, *cb);
       if (!fuse) co->rinv_from_ssq(a.ssq + ((size_t)l * 2) * nt * a.M);
     }
     if (threadIdx.x == 0) tstamp(a, l, ph, 2);
@@ -1274,7 +1305,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
           for (int hb = h0; hb <= h1; hb += 64)
             wait_all_ge(C + cl.o_att + hb * PADC, PADC, min(64, h1 + 1 - hb), s.goff[64], *cb);
         } else if (ph == PH_DOWN) {
-          wait_ge(C + cl.o_gu + ch * PADC, xn / 8, *cb);
+          wait_spread(C + cl.o_gu + ch * NSPREAD * PADC, x0 / 8, (x0 + xn) / 8, *cb);
         } else {
           cb->sync();                     // earlier readers of the stage are done
         }
