@@ -178,7 +178,7 @@ LS_DEV void wait_all_ge(const int* base, int stride, int n, int target, ConsBar&
 // counter t mod NSPREAD, each on a line of its own): a phase's tiles finish within a few
 // microseconds of each other, and atomics on one address would queue behind each other and
 // behind the polls of every workgroup.
-constexpr int NSPREAD = 16;
+constexpr int NSPREAD = 64;
 
 // Tiles t in [lo, hi) with t mod NSPREAD == k.
 __host__ __device__ inline int spread_count(int lo, int hi, int k) {
@@ -187,8 +187,7 @@ __host__ __device__ inline int spread_count(int lo, int hi, int k) {
 }
 
 // Consumer-side wait until the tiles [lo, hi) have all been counted on the spread counters at
-// base (counter k at base + k * PADC): lanes k < NSPREAD of the first consumer wave poll one
-// counter each.
+// base (counter k at base + k * PADC): lane k of the first consumer wave polls counter k.
 LS_DEV void wait_spread(const int* base, int lo, int hi, ConsBar& cb) {
   if (threadIdx.x < 64) {
     const int k = threadIdx.x;
@@ -212,11 +211,13 @@ struct CntLayout {
   int o_init, total;
 };
 
-__host__ __device__ inline CntLayout cnt_layout(int M, int F, int nh, int XC, int n_layers) {
+// QKV tiles each set a flag of their own (o_qkvh + t * PADC, t head-major), so the attention
+// units of a head wait on its 3 * hd / 16 flags, one per lane, without a shared counter.
+__host__ __device__ inline CntLayout cnt_layout(int M, int d, int F, int nh, int XC, int n_layers) {
   CntLayout c;
   c.nchF = (F + XC - 1) / XC;
   int o = 0;
-  c.o_qkvh = o; o += nh * PADC;
+  c.o_qkvh = o; o += 3 * (d / 16) * PADC;
   c.o_att = o; o += nh * PADC;
   c.o_o = o; o += NSPREAD * PADC;
   c.o_gu = o; o += c.nchF * NSPREAD * PADC;
@@ -267,7 +268,7 @@ size_t mega_counter_ints(int M, int d, int F, int nh, int n_layers) {
   size_t worst = 0;
   for (int m = 1; m <= M; ++m)
     for (int esz = 2; esz <= 4; esz += 2)
-      worst = std::max(worst, (size_t)cnt_layout(m, F, nh, x_chunk_for(m, esz, d), n_layers).total);
+      worst = std::max(worst, (size_t)cnt_layout(m, d, F, nh, x_chunk_for(m, esz, d), n_layers).total);
   return worst;
 }
 
@@ -827,7 +828,7 @@ LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, const Lds& s, int p
 LS_DEV void tile_signal(const MegaArgs& a, const CntLayout& cl, int ph, int l, int t, int XC) {
   int* C = a.cnt + (size_t)l * cl.per_layer;
   if (ph == PH_QKV) {
-    atomicAdd(C + cl.o_qkvh + qkv_tile(a, t).h * PADC, 1);
+    atomicAdd(C + cl.o_qkvh + t * PADC, 1);
   } else if (ph == PH_O || ph == PH_DOWN) {
     atomicAdd(C + (ph == PH_O ? cl.o_o : cl.o_down) + (t % NSPREAD) * PADC, 1);
   } else if (ph == PH_GU) {
@@ -1021,11 +1022,15 @@ LS_DEV void att_unit_wave(const MegaArgs& a, const Lds& s, const CntLayout& cl, 
 #pragma unroll
   for (int p = 0; p < NPF; ++p) load_pass(p, kr[p], vr[p]);
   // queries of this head are complete once the head's q/k/v tiles have all signalled
-  if (lane == 0) {
+  {
+    const int nf = 3 * (hd / 16);                         // the head's QKV tiles: flags h * nf .. + nf
+    bool done = lane >= nf;
     int n = 0;
-    while (ld_acq(C + cl.o_qkvh + h * PADC) < 3 * (hd / 16)) {
+    while (true) {
+      if (!done) done = ld_acq(C + cl.o_qkvh + (h * nf + lane) * PADC) >= 1;
+      if (__all(done)) break;
       __builtin_amdgcn_s_sleep(POLL_SLEEP);
-      if (++n > SPIN_LIMIT) { ls_flag(a.err, LS_TIMEOUT); break; }
+      if (++n > SPIN_LIMIT) { if (lane == 0) ls_flag(a.err, LS_TIMEOUT); break; }
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -1427,7 +1432,7 @@ template <typename T, int MT>
 LS_DEV void mega_body(const MegaArgs& a) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   const Lds s = lds_carve<T>(smem_raw, a.M, a.d);
-  const CntLayout cl = cnt_layout(a.M, a.F, a.nh, x_chunk_for(a.M, (int)sizeof(T), a.d), a.n_layers);
+  const CntLayout cl = cnt_layout(a.M, a.d, a.F, a.nh, x_chunk_for(a.M, (int)sizeof(T), a.d), a.n_layers);
   const int G = gridDim.x, b = blockIdx.x;
   const int wv = wave_id();
   // ring counters and the consumer barrier start at zero
@@ -1540,7 +1545,7 @@ int mega_occupancy(bool bf16, int M, int d) {
 }
 
 hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool loop_block) {
-  const CntLayout cl = cnt_layout(a.M, a.F, a.nh, x_chunk_for(a.M, bf16 ? 2 : 4, a.d), a.n_layers);
+  const CntLayout cl = cnt_layout(a.M, a.d, a.F, a.nh, x_chunk_for(a.M, bf16 ? 2 : 4, a.d), a.n_layers);
   const long long n_prep = std::max<long long>(cl.total, (long long)a.M * (a.hd / 2));
   hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<long long>(1024, (n_prep + 255) / 256)), dim3(256), 0, s, a.cnt,
                      (long long)cl.total, a.rope, a.pos, a.inv_freq, a.M, a.hd / 2);
