@@ -282,8 +282,9 @@ struct Lds {
   int* grow;         // M: rows ordered by KV depth group (attention shares a group's keys)
   int* goff;         // group g's rows: grow[goff[g] .. goff[g+1]); goff[64] = group count
   int *rslot, *rdep, *raoff;   // the rows' validated slot, depth (0 without depths), ancestor offsets
-  int* ints;         // [0..NS) full, [NS..2NS) empty, [2NS] consumer barrier, [2NS+1] partials
-                     // posted (4 per tile), [2NS+2] partial buffers released by the epilogue wave
+  int* ints;         // [0..NS) full, [NS..2NS) empty, [2NS] consumer barrier, [2NS+1+b] partials
+                     // posted to partial buffer b (4 per tile, b < nred <= 2), [2NS+3] tiles whose
+                     // partial buffer the epilogue wave has released
   int xstride;       // elements
   int NS, XC, nred;
 };
@@ -1340,7 +1341,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
       float* buf = s.red + (size_t)(q % s.nred) * NCONS * a.M * 16;
       if (q >= s.nred && lane == 0) {      // the epilogue wave is done with this buffer's last tile
         int n = 0;
-        while (lds_peek(s.ints + 2 * s.NS + 2) < q - s.nred + 1) {
+        while (lds_peek(s.ints + 2 * s.NS + 3) < q - s.nred + 1) {
           __builtin_amdgcn_s_sleep(0);
           if (++n > SPIN_LIMIT) { ls_flag(a.err, LS_TIMEOUT); break; }
         }
@@ -1355,7 +1356,9 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
           for (int jj = 0; jj < 4; ++jj) buf[((size_t)co->c * a.M + m) * 16 + 4 * gq + jj] = acc[mt][jj];
         }
       }
-      if (lane == 0) lds_bump(s.ints + 2 * s.NS + 1);   // after this wave's partial writes complete
+      // Counted per buffer: a consumer may run a tile ahead of the others, but never onto a
+      // buffer the epilogue wave has not released, so buffer b's count covers one tile at a time.
+      if (lane == 0) lds_bump(s.ints + 2 * s.NS + 1 + q % s.nred);   // after this wave's partial writes complete
     }
     if (PROD && threadIdx.x == 64 * NCONS && i == sh.count - 1) tstamp(a, l, ph, 6);
   }
@@ -1389,7 +1392,7 @@ LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int p
     float* buf = s.red + (size_t)(q % s.nred) * NCONS * a.M * 16;
     if (lane == 0) {
       int n = 0;
-      while (lds_peek(s.ints + 2 * s.NS + 1) < NCONS * (q + 1)) {
+      while (lds_peek(s.ints + 2 * s.NS + 1 + q % s.nred) < NCONS * (q / s.nred + 1)) {
         __builtin_amdgcn_s_sleep(0);
         if (++n > SPIN_LIMIT) { ls_flag(a.err, LS_TIMEOUT); break; }
       }
@@ -1406,9 +1409,10 @@ LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int p
     wait_lgkm0();                          // the sums are visible to every lane
     epilogue<T>(a, cl, s, ph, l, t, buf, lane, pref && i == 0, pre);
     wait_lgkm0();                          // the epilogue's reads of the buffer are complete
-    if (lane == 0) lds_bump(s.ints + 2 * s.NS + 2);
+    if (lane == 0) lds_bump(s.ints + 2 * s.NS + 3);
     if (ph == PH_HEAD) continue;
-    const bool next_ready = i + 1 < sh.count && lds_peek(s.ints + 2 * s.NS + 1) >= NCONS * (q + 2);
+    const bool next_ready =
+        i + 1 < sh.count && lds_peek(s.ints + 2 * s.NS + 1 + (q + 1) % s.nred) >= NCONS * ((q + 1) / s.nred + 1);
     if (!next_ready) {
       drain();
       if (lane == 0)
