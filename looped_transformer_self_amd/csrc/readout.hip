@@ -1,8 +1,8 @@
 // Readout distribution of C: temperature, softmax, top-p truncation, normalisation (LoopSpec
 // page, section 2.1: every intermediate readout applies the same processing as the target).
 //
-// One 512-thread workgroup per row; the row lives in registers (thread t holds ids
-// t, t + 512, t + 1024, ...: coalesced loads and stores, one read of the logits and one write
+// One 1024-thread workgroup per row; the row lives in registers (thread t holds ids
+// t, t + 1024, t + 2048, ...: coalesced loads and stores, one read of the logits and one write
 // of the distribution).  Top-p keeps the tokens ordered by probability (then id) up to and
 // including the one at which the kept mass reaches top_p.  The crossing token's key (the
 // float32 bit pattern of its probability, monotone for non-negative floats) is found by a
@@ -14,8 +14,8 @@
 
 namespace ls {
 
-constexpr int DIST_THREADS = 512;
-constexpr int DIST_PT = 128;              // ids per thread: V <= 65536
+constexpr int DIST_THREADS = 1024;
+constexpr int DIST_PT = 64;               // ids per thread: V <= 65536
 constexpr int DIST_BINS = 2048;
 
 LS_DEV unsigned block_sum_u32(unsigned v, unsigned* red) {
@@ -52,7 +52,29 @@ LS_DEV unsigned block_max_u32(unsigned v, unsigned* red) {
   return t;
 }
 
+// Row access through a buffer descriptor: id j*DIST_THREADS + tid is at vector offset tid*4 and
+// scalar offset j*DIST_THREADS*4, so the unrolled loops need no per-element address registers;
+// stores past the row end fall outside the descriptor's range and are dropped.
+LS_DEV __amdgpu_buffer_rsrc_t row_rsrc(const float* base, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, n * 4, 0x00020000);
+}
+LS_DEV float row_ld(__amdgpu_buffer_rsrc_t r, int j) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)threadIdx.x * 4, j * DIST_THREADS * 4, 0));
+}
+LS_DEV void row_st(__amdgpu_buffer_rsrc_t r, int j, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)threadIdx.x * 4, j * DIST_THREADS * 4, 0);
+}
+
 LS_DEV unsigned mass31(float p) { return (unsigned)(p * 2147483648.0f); }   // exact floor(p * 2^31), p in [0, 1]
+// The same value recomputed where it is needed: the radix rounds would otherwise keep all
+// DIST_PT masses live next to the probabilities (the compiler hoists them out of the rounds
+// loop), which spills.  Volatile assembly is not hoisted; v_cvt_u32_f32 truncates like the
+// conversion above.
+LS_DEV unsigned mass31_here(float p) {
+  unsigned r;
+  asm volatile("v_mul_f32 %0, 0x4f000000, %1\n\tv_cvt_u32_f32 %0, %0" : "=v"(r) : "v"(p));
+  return r;
+}
 
 __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int V, int greedy, float T, float top_p,
                                                       float* probs, const int32_t* out_rows, int n_prob_rows,
@@ -69,8 +91,14 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
 
   // ids past V hold -inf logits: probability 0, mass 0, never kept
   float x[DIST_PT];
+  {
+    const __amdgpu_buffer_rsrc_t Rz = row_rsrc(z, V);
 #pragma unroll
-  for (int j = 0; j < DIST_PT; ++j) x[j] = tid + DIST_THREADS * j < V ? z[tid + DIST_THREADS * j] : -INFINITY;
+    for (int j = 0; j < DIST_PT; ++j) {
+      const float v = row_ld(Rz, j);
+      x[j] = tid + DIST_THREADS * j < V ? v : -INFINITY;
+    }
+  }
   // argmax, lowest id on ties (a thread's ids increase with j)
   float best = -INFINITY;
   int bi = 0x7fffffff;
@@ -95,11 +123,12 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
     return;
   }
   float* p = probs + (size_t)orow * V;
+  const __amdgpu_buffer_rsrc_t Rp = row_rsrc(p, V);
   if (greedy) {
 #pragma unroll
     for (int j = 0; j < DIST_PT; ++j) {
       const int v = tid + DIST_THREADS * j;
-      if (v < V) p[v] = v == bi ? 1.0f : 0.0f;
+      row_st(Rp, j, v == bi ? 1.0f : 0.0f);
     }
     return;
   }
@@ -119,7 +148,7 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
 #pragma unroll
     for (int j = 0; j < DIST_PT; ++j) {
       const int v = tid + DIST_THREADS * j;
-      if (v < V) p[v] = x[j];
+      row_st(Rp, j, x[j]);
     }
     return;
   }
@@ -151,7 +180,7 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
 #pragma unroll
     for (int j = 0; j < DIST_PT; ++j) {
       const unsigned off = __float_as_uint(x[j]) - lo;       // keys below lo wrap to large offsets
-      const unsigned ms = mass31(x[j]);
+      const unsigned ms = mass31_here(x[j]);
       if (ms && (width >= 32 || off < (1u << width))) atomicAdd(&hist[off >> shift], ms);   // zero masses add nothing
     }
     __syncthreads();
@@ -207,7 +236,7 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
 #pragma unroll
     for (int j = 0; j < DIST_PT; ++j) {
       const int v = tid + DIST_THREADS * j;
-      if (v < V) p[v] = __float_as_uint(x[j]) >= kstar ? x[j] * scale : 0.0f;
+      row_st(Rp, j, __float_as_uint(x[j]) >= kstar ? x[j] * scale : 0.0f);
     }
     return;
   }
