@@ -17,38 +17,61 @@ def _ptr(t):
     return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
 
 
+_hip = None
+
+
+def _hip_runtime():
+    """The HIP runtime library (already loaded by torch), for raw asynchronous copies."""
+    global _hip
+    if _hip is None:
+        _hip = C.CDLL("libamdhip64.so")
+        _hip.hipMemcpyAsync.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_void_p]
+        _hip.hipMemcpyAsync.restype = C.c_int
+    return _hip
+
+
 class Uploader:
     """Packs host int32/uint32 arrays into one pinned buffer and ships them with a single
-    host-to-device copy per call.  A ring of buffers guarded by events keeps a pending copy
-    from being overwritten."""
+    host-to-device copy per call (hipMemcpyAsync on the engine's stream).  A ring of buffers
+    guarded by reusable events keeps a pending copy from being overwritten."""
 
-    def __init__(self, dev, words=1 << 20, ring=4):
+    H2D = 1   # hipMemcpyHostToDevice
+
+    def __init__(self, dev, stream_ptr, words=1 << 20, ring=4):
         self.dev = dev
+        self.stream = stream_ptr
         self.host = [torch.empty(words, dtype=torch.int32, pin_memory=True) for _ in range(ring)]
+        self.hnp = [h.numpy() for h in self.host]
+        self.hptr = [h.data_ptr() for h in self.host]
         self.devb = [torch.empty(words, dtype=torch.int32, device=dev) for _ in range(ring)]
-        self.events = [None] * ring
+        self.dptr = [d.data_ptr() for d in self.devb]
+        self.events = [torch.cuda.Event() for _ in range(ring)]
+        self.recorded = [False] * ring
         self.i = 0
+        self.hip = _hip_runtime()
 
     def pack(self, arrays):
         k = self.i
         self.i = (self.i + 1) % len(self.host)
-        if self.events[k] is not None:
+        if self.recorded[k]:
             self.events[k].synchronize()
         offs, total = [], 0
         for a in arrays:
             offs.append(total)
             total += (len(a) + 63) // 64 * 64          # 256-byte alignment per array
-        if total > self.host[k].numel():
+        if total > len(self.hnp[k]):
             raise ValueError("upload larger than the staging buffer")
-        hb = self.host[k].numpy()
+        hb = self.hnp[k]
         for a, o in zip(arrays, offs):
             if len(a):
-                hb[o:o + len(a)] = np.asarray(a).view(np.int32) if np.asarray(a).dtype != np.int32 else a
-        self.devb[k][:total].copy_(self.host[k][:total], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record()
-        self.events[k] = ev
-        base = self.devb[k].data_ptr()
+                a = np.asarray(a)
+                hb[o:o + len(a)] = a.view(np.int32) if a.dtype != np.int32 else a
+        err = self.hip.hipMemcpyAsync(self.dptr[k], self.hptr[k], 4 * total, self.H2D, self.stream)
+        if err:
+            raise RuntimeError(f"hipMemcpyAsync failed ({err})")
+        self.events[k].record()
+        self.recorded[k] = True
+        base = self.dptr[k]
         return [C.c_void_p(base + 4 * o) for o in offs], self.devb[k]
 
 
@@ -66,6 +89,7 @@ class Engine:
                  device="cuda"):
         self.cfg = cfg
         self.dev = torch.device(device)
+        self._stream = C.c_void_p(torch.cuda.current_stream(self.dev).cuda_stream)
         self.S = int(slot_capacity)
         self.max_rows = max_rows
         self.max_keys = int(max_keys or slot_capacity)
@@ -122,7 +146,7 @@ class Engine:
         self.ws_ptr = C.c_void_p(self.ws.data_ptr() + off)
         L.check(L.lib.ls_bind_workspace(h, self.ws_ptr, max_rows, self.max_keys, max_jobs, self.stream_ptr()),
                 "ls_bind_workspace")
-        self.up = Uploader(self.dev)
+        self.up = Uploader(self.dev, self._stream)
         self.vout = torch.zeros(max_jobs * 4, dtype=torch.int32, device=self.dev)
         self.vout_host = torch.zeros(max_jobs * 4, dtype=torch.int32, pin_memory=True)
         self.prof = None          # list of (start event, end event, row metadata) when profiling
@@ -136,9 +160,10 @@ class Engine:
         except Exception:
             pass
 
-    @staticmethod
-    def stream_ptr():
-        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    def stream_ptr(self):
+        """The stream every call of this engine is issued on: the current stream when the
+        engine was created."""
+        return self._stream
 
     # ---- descriptors -----------------------------------------------------------------
     def rows(self, slots, pos, depth, n_fin, anc_lists, fin_ptr, extra=()):
