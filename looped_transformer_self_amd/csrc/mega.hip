@@ -75,6 +75,13 @@ LS_DEV u32x4_t ld128(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
 
+// Layer inputs Xs[l] (l >= 1) and post-attention rows Ys[l] start every launch filled with
+// SENT32 (a NaN bit pattern that arithmetic does not produce: generated NaNs are the
+// positive canonical one, and no input element converts to it).  Their readers poll the data
+// itself with agent-coherent loads instead of a completion counter: a row is complete when no
+// element still holds SENT32.  The epilogues still count their tiles for the other readers.
+constexpr unsigned SENT32 = 0xFFFFFFFFu;
+
 // Per-layer activation buffers of one launch (rows m < M):
 //   layer input   l == 0: H[hidx[m]] (the caller's hidden rows), l > 0: Xs[l][m]
 //   after attention residual: Ys[l][m];  attention output o[l][m];  SwiGLU output act[l][m]
@@ -580,7 +587,8 @@ struct Consumer {
   // wave per row, every load of a row pass in flight at once.  With fuse (the chunk is the
   // whole row, d <= 64*4*NVF) the RMSNorm factor comes from the same loads.
   static constexpr int NVF = 8;
-  LS_DEV void stage_norm(const float* src, bool via_hidx, const float* gain, int x0, int xn, bool fuse) {
+  LS_DEV void stage_norm(const float* src, bool via_hidx, const float* gain, int x0, int xn, bool fuse,
+                         bool poll) {
     T* X = (T*)s.X;
     const __amdgpu_buffer_rsrc_t Rg = rsrc_of(gain + x0, xn * 4);
     for (int m = c; m < a.M; m += NCONS) {
@@ -594,9 +602,24 @@ struct Consumer {
         u32x4_t v[NVF], gv[NVF];
         dstamp(a, dbg && m == 0, 0);
 #pragma unroll
-        for (int u = 0; u < NVF; ++u) v[u] = ld128(R, (4 * (lane + 64 * u)) * 4);
-#pragma unroll
         for (int u = 0; u < NVF; ++u) gv[u] = ld128(Rg, (4 * (lane + 64 * u)) * 4);
+        if (poll) {
+          // the row is complete once no element holds the fill pattern
+          int n = 0;
+          while (true) {
+#pragma unroll
+            for (int u = 0; u < NVF; ++u) v[u] = ldc128(R, (4 * (lane + 64 * u)) * 4);
+            bool ok = true;
+#pragma unroll
+            for (int u = 0; u < NVF; ++u) ok = ok && v[u].x != SENT32 && v[u].y != SENT32 && v[u].z != SENT32 && v[u].w != SENT32;
+            if (__all(ok)) break;
+            __builtin_amdgcn_s_sleep(POLL_SLEEP);
+            if (++n > SPIN_LIMIT) { if (lane == 0) ls_flag(a.err, LS_TIMEOUT); break; }
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < NVF; ++u) v[u] = ld128(R, (4 * (lane + 64 * u)) * 4);
+        }
         dstamp(a, dbg && m == 0, 1);
         float ss = 0.f;
 #pragma unroll
@@ -741,7 +764,7 @@ LS_DEV void residual_load(const MegaArgs& a, const Lds& s, int ph, int l, int t,
     const int hr = m < a.M ? s.hx[m] : -1;
     const int row = ph == PH_O && l == 0 ? hr : m;
     const int off = hr >= 0 ? (row * a.d + n) * 4 : 0x7fffffff;
-    res[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(Rr, off, 0, 0));
+    res[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(Rr, off, 0, CPOL_SC1));
   }
 }
 
@@ -1268,6 +1291,8 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
   const float* nsrc = ph == PH_GU ? ys_of(a, l) : layer_in(a, lin);
   const bool nvia = ph != PH_GU && lin == 0;                   // rows addressed through hidx
   const float* gain = ph == PH_QKV ? lw.g1 : (ph == PH_GU ? lw.g2 : a.g_final);
+  // fused normalised phases whose input was written in this launch read it by polling
+  const bool poll = fuse && (ph == PH_GU || lin > 0);
   if (!PROD) {
     co->dbg = l == 0 && ph == PH_QKV;
     dstamp(a, co->dbg, 4);
@@ -1277,7 +1302,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
     if (ph == PH_QKV || ph == PH_HEAD) {
       const int lp = ph == PH_QKV ? l - 1 : a.n_layers - 1;    // layer whose output feeds this phase
       if (lp >= 0) {
-        wait_spread(a.cnt + (size_t)lp * cl.per_layer + cl.o_down, 0, nt, *cb);
+        if (!poll) wait_spread(a.cnt + (size_t)lp * cl.per_layer + cl.o_down, 0, nt, *cb);
         ssq = a.ssq + ((size_t)lp * 2 + 1) * nt * a.M;
       } else if (a.init_mode) {
         wait_ge(a.cnt + cl.o_init, a.M, *cb);
@@ -1287,7 +1312,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
         else co->rinv_from_rows(a.H);            // first layer of the call: the caller's rows
       }
     } else if (ph == PH_GU) {
-      wait_spread(C + cl.o_o, 0, nt, *cb);
+      if (!poll) wait_spread(C + cl.o_o, 0, nt, *cb);
       if (!fuse) co->rinv_from_ssq(a.ssq + ((size_t)l * 2) * nt * a.M);
     }
     if (threadIdx.x == 0) tstamp(a, l, ph, 2);
@@ -1317,7 +1342,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
         }
         dstamp(a, co->dbg, 5);
         if (ph == PH_O || ph == PH_DOWN) co->stage_raw(ph == PH_O ? o_of<T>(a, l) : act_of<T>(a, l), g.K, x0, xn);
-        else co->stage_norm(nsrc, nvia, gain, x0, xn, fuse);
+        else co->stage_norm(nsrc, nvia, gain, x0, xn, fuse, poll);
         if (threadIdx.x == 0 && i == 0 && ch == 0) tstamp(a, l, ph, 3);
       }
       const int k_first = x0 / g.sk;
@@ -1510,9 +1535,12 @@ __global__ __launch_bounds__(MEGA_THREADS) void k_mega(MegaArgs a) { mega_body<T
 template <typename T, int MT>
 __global__ __launch_bounds__(MEGA_THREADS) void k_mega_aux(MegaArgs a) { mega_body<T, MT>(a); }
 
-__global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, const double* inv_freq, int M, int half) {
+__global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, const double* inv_freq, int M, int half,
+                       unsigned* xs_fill, long long n_xs, unsigned* ys_fill, long long n_ys) {
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x, str = (long long)gridDim.x * blockDim.x;
   for (long long i = tid; i < n; i += str) cnt[i] = 0;
+  for (long long i = tid; i < n_xs; i += str) xs_fill[i] = SENT32;
+  for (long long i = tid; i < n_ys; i += str) ys_fill[i] = SENT32;
   for (long long i = tid; i < (long long)M * half; i += str) {
     const int m = (int)(i / half), f = (int)(i % half);
     double sn, cs;
@@ -1551,8 +1579,11 @@ int mega_occupancy(bool bf16, int M, int d) {
 hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool loop_block) {
   const CntLayout cl = cnt_layout(a.M, a.d, a.F, a.nh, x_chunk_for(a.M, bf16 ? 2 : 4, a.d), a.n_layers);
   const long long n_prep = std::max<long long>(cl.total, (long long)a.M * (a.hd / 2));
+  const long long rows = (long long)a.M * a.d;   // one layer slice of Xs / Ys
   hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<long long>(1024, (n_prep + 255) / 256)), dim3(256), 0, s, a.cnt,
-                     (long long)cl.total, a.rope, a.pos, a.inv_freq, a.M, a.hd / 2);
+                     (long long)cl.total, a.rope, a.pos, a.inv_freq, a.M, a.hd / 2,
+                     reinterpret_cast<unsigned*>(a.Xs + rows), (long long)a.n_layers * rows,
+                     reinterpret_cast<unsigned*>(a.Ys), (long long)a.n_layers * rows);
   const size_t smem = mega_smem_bytes(bf16, a.M, a.d);
   void* args[] = {(void*)&a};
   return hipLaunchCooperativeKernel(pick(bf16, a.M, loop_block), dim3(G), dim3(MEGA_THREADS), args, (unsigned)smem, s);
