@@ -81,6 +81,8 @@ LS_DEV u32x4_t ld128(__amdgpu_buffer_rsrc_t r, int byte_off) {
 // itself with agent-coherent loads instead of a completion counter: a row is complete when no
 // element still holds SENT32.  The epilogues still count their tiles for the other readers.
 constexpr unsigned SENT32 = 0xFFFFFFFFu;
+// Rows up to this many columns are staged, normalised and (for Xs / Ys) polled in one pass.
+constexpr int FUSE_MAX_K = 2048;
 
 // Per-layer activation buffers of one launch (rows m < M):
 //   layer input   l == 0: H[hidx[m]] (the caller's hidden rows), l > 0: Xs[l][m]
@@ -587,6 +589,7 @@ struct Consumer {
   // wave per row, every load of a row pass in flight at once.  With fuse (the chunk is the
   // whole row, d <= 64*4*NVF) the RMSNorm factor comes from the same loads.
   static constexpr int NVF = 8;
+  static_assert(64 * 4 * NVF == FUSE_MAX_K, "fused staging covers FUSE_MAX_K columns");
   LS_DEV void stage_norm(const float* src, bool via_hidx, const float* gain, int x0, int xn, bool fuse,
                          bool poll) {
     T* X = (T*)s.X;
@@ -1286,7 +1289,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
 
   // normalised phases (QKV, GU, HEAD) read a whole row when one activation chunk covers it and
   // then take the RMSNorm factor from the same loads; otherwise from the per-tile sums of squares
-  const bool fuse = nchunk == 1 && g.K <= 64 * 4 * Consumer<T, MT>::NVF;
+  const bool fuse = nchunk == 1 && g.K <= FUSE_MAX_K;
   const int lin = ph == PH_HEAD ? a.n_layers : l;              // layer whose input a normalised phase reads
   const float* nsrc = ph == PH_GU ? ys_of(a, l) : layer_in(a, lin);
   const bool nvia = ph != PH_GU && lin == 0;                   // rows addressed through hidx
@@ -1407,6 +1410,10 @@ LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int p
   const Share sh = share_of(g.n_tiles, deal, G, b);
   deal = (deal + g.n_tiles) % G;
   const bool pref = (ph == PH_O || ph == PH_DOWN) && had_tiles && sh.count > 0 && a.M <= 16;
+  // O / DOWN counts are waited for only when the next normalised phase cannot poll its input
+  // (its row does not fit one fused staging pass); otherwise their drain and bump are skipped.
+  const bool next_polls = a.d <= s.XC && a.d <= FUSE_MAX_K;
+  const bool signals = ph != PH_HEAD && !((ph == PH_O || ph == PH_DOWN) && next_polls);
   float pre[4] = {0.f, 0.f, 0.f, 0.f};
   if (pref) residual_load(a, s, ph, l, sh.first, 0, lane, pre);
   had_tiles = sh.count > 0;
@@ -1435,7 +1442,7 @@ LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int p
     epilogue<T>(a, cl, s, ph, l, t, buf, lane, pref && i == 0, pre);
     wait_lgkm0();                          // the epilogue's reads of the buffer are complete
     if (lane == 0) lds_bump(s.ints + 2 * s.NS + 3);
-    if (ph == PH_HEAD) continue;
+    if (!signals) continue;
     const bool next_ready =
         i + 1 < sh.count && lds_peek(s.ints + 2 * s.NS + 1 + (q + 1) % s.nred) >= NCONS * ((q + 1) / s.nred + 1);
     if (!next_ready) {
