@@ -109,10 +109,10 @@ class Decoder:
     def _fin_append(self, slots):
         a = len(self.fin)
         self.fin.extend(slots)
-        src = torch.tensor(np.asarray(slots, np.int32))
         if self.fin_dev.is_cuda:
-            src = src.pin_memory()
-        self.fin_dev[a:a + len(slots)].copy_(src, non_blocking=True)
+            self.e.up.copy_to(self.fin_dev.data_ptr() + 4 * a, slots)
+        else:                                   # host-only engines (scheduler tests)
+            self.fin_dev[a:a + len(slots)] = torch.tensor(np.asarray(slots, np.int32))
 
     def _path(self, n):
         p = []

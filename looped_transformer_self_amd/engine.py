@@ -27,6 +27,14 @@ def _hip_runtime():
         _hip = C.CDLL("libamdhip64.so")
         _hip.hipMemcpyAsync.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_void_p]
         _hip.hipMemcpyAsync.restype = C.c_int
+        _hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        _hip.hipEventCreateWithFlags.restype = C.c_int
+        _hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        _hip.hipEventRecord.restype = C.c_int
+        _hip.hipEventSynchronize.argtypes = [C.c_void_p]
+        _hip.hipEventSynchronize.restype = C.c_int
+        _hip.hipEventDestroy.argtypes = [C.c_void_p]
+        _hip.hipEventDestroy.restype = C.c_int
     return _hip
 
 
@@ -45,16 +53,47 @@ class Uploader:
         self.hptr = [h.data_ptr() for h in self.host]
         self.devb = [torch.empty(words, dtype=torch.int32, device=dev) for _ in range(ring)]
         self.dptr = [d.data_ptr() for d in self.devb]
-        self.events = [torch.cuda.Event() for _ in range(ring)]
+        self.hip = _hip_runtime()
+        self.events = []
+        for _ in range(ring):
+            ev = C.c_void_p()
+            if self.hip.hipEventCreateWithFlags(C.byref(ev), 2):          # hipEventDisableTiming
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.events.append(ev)
         self.recorded = [False] * ring
         self.i = 0
-        self.hip = _hip_runtime()
 
-    def pack(self, arrays):
+    def __del__(self):
+        try:
+            for ev in self.events:
+                self.hip.hipEventDestroy(ev)
+        except Exception:
+            pass
+
+    def _slot(self):
         k = self.i
         self.i = (self.i + 1) % len(self.host)
-        if self.recorded[k]:
-            self.events[k].synchronize()
+        if self.recorded[k] and self.hip.hipEventSynchronize(self.events[k]):
+            raise RuntimeError("hipEventSynchronize failed")
+        return k
+
+    def _ship(self, k, dst, words, src_off=0):
+        err = self.hip.hipMemcpyAsync(dst, self.hptr[k] + 4 * src_off, 4 * words, self.H2D, self.stream)
+        if err:
+            raise RuntimeError(f"hipMemcpyAsync failed ({err})")
+        if self.hip.hipEventRecord(self.events[k], self.stream):
+            raise RuntimeError("hipEventRecord failed")
+        self.recorded[k] = True
+
+    def copy_to(self, dst_ptr, array):
+        """Asynchronous copy of a small int32 array to device address dst_ptr (stream order)."""
+        a = np.asarray(array, np.int32)
+        k = self._slot()
+        self.hnp[k][:len(a)] = a
+        self._ship(k, dst_ptr, len(a))
+
+    def pack(self, arrays):
+        k = self._slot()
         offs, total = [], 0
         for a in arrays:
             offs.append(total)
@@ -66,11 +105,7 @@ class Uploader:
             if len(a):
                 a = np.asarray(a)
                 hb[o:o + len(a)] = a.view(np.int32) if a.dtype != np.int32 else a
-        err = self.hip.hipMemcpyAsync(self.dptr[k], self.hptr[k], 4 * total, self.H2D, self.stream)
-        if err:
-            raise RuntimeError(f"hipMemcpyAsync failed ({err})")
-        self.events[k].record()
-        self.recorded[k] = True
+        self._ship(k, self.dptr[k], total)
         base = self.dptr[k]
         return [C.c_void_p(base + 4 * o) for o in offs], self.devb[k]
 
