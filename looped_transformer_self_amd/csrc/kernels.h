@@ -13,6 +13,19 @@ struct LayerW {
 };
 
 // Arguments of the persistent layer kernel (mega.hip).
+// Row-descriptor check of one call, run by the prep kernel of the call's first launch: rows
+// whose slot, depth, ancestor range or position is out of contract get slot -1 in the checked
+// copy (every kernel skips such rows) and raise the error word.  dep_lo..dep_hi is the legal
+// depth range (dep may be NULL); n == 0 means nothing to check.
+struct ValidateArgs {
+  int n = 0;
+  const int32_t *slot = nullptr, *dep = nullptr, *pos = nullptr, *anc_off = nullptr;
+  int dep_lo = 0, dep_hi = 0, n_fin = 0, max_anc = 0;
+  long long S = 0;
+  int32_t *slot_ok = nullptr, *dep_ok = nullptr, *row_ok = nullptr;
+  int* err = nullptr;
+};
+
 struct MegaArgs {
   int M, d, F, hd, nh, V;
   float theta, eps;
@@ -51,11 +64,8 @@ size_t mega_smem_bytes(bool bf16, int M, int d);
 int mega_occupancy(bool bf16, int M, int d);
 int att_unit_keys(bool bf16);   // prefix keys per attention unit
 // loop_block: launch under the k_mega symbol (shared block B) rather than k_mega_aux
-hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool loop_block);
+hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool loop_block, const ValidateArgs& v);
 
-void launch_validate(int n, const int32_t* slot, const int32_t* dep, int dep_lo, int dep_hi, const int32_t* pos,
-                     const int32_t* anc_off, int n_fin, int max_anc, long long S, int32_t* slot_ok, int32_t* dep_ok,
-                     int32_t* row_ok, int* err, hipStream_t s);
 void launch_fill_i32(int32_t* p, int n, int v, hipStream_t s);
 void launch_dist(const float* logits, int M, int V, int greedy, float T, float top_p, float* probs,
                  const int32_t* out_rows, int n_prob_rows, int32_t* argmax, int* err, hipStream_t s);

@@ -238,11 +238,21 @@ ls_status ls_bind_workspace(ls_model* m, void* ws, int max_rows, int max_keys, i
 
 namespace {
 
-// One launch of the persistent layer kernel over rows [i0, i0 + mc) of `r`.
+// The row check of a call over `r` (depth range dep_lo..dep_hi; dep NULL: no depths).
+ValidateArgs validate_args(ls_model* m, const ls_rows* r, const int32_t* dep, int dep_lo, int dep_hi) {
+  ValidateArgs v;
+  v.n = r->n; v.slot = r->slot; v.dep = dep; v.pos = r->pos; v.anc_off = r->anc_off;
+  v.dep_lo = dep_lo; v.dep_hi = dep_hi; v.n_fin = r->n_fin; v.max_anc = r->max_anc; v.S = m->d.slot_capacity;
+  v.slot_ok = m->slot_ok; v.dep_ok = m->dep_ok; v.row_ok = m->row_ok; v.err = m->err;
+  return v;
+}
+
+// One launch of the persistent layer kernel over rows [i0, i0 + mc) of `r`; its prep kernel
+// runs the row check `v` first (the call's first launch; later launches pass an empty one).
 ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, const int32_t* hidx, const LayerW* tab,
                    int n_layers, void* kv, const int32_t* dep, int dep_off, int blk_mul, int init_mode,
                    const int32_t* tokens, const int32_t* gather, const float* Hg, float* logits, hipStream_t s,
-                   bool loop_block = false) {
+                   const ValidateArgs& v, bool loop_block = false) {
   const ls_model_desc& d = m->d;
   MegaArgs a{};
   a.M = mc; a.d = d.d; a.F = d.F; a.hd = d.head_dim; a.nh = d.n_heads; a.V = d.V;
@@ -274,7 +284,7 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
   const int G = occ * m->n_cu;
   a.trace = m->trace;
   m->last_grid = G;
-  hipError_t e = launch_mega(m->bf16(), a, G, s, loop_block);
+  hipError_t e = launch_mega(m->bf16(), a, G, s, loop_block, v);
   if (e != hipSuccess) return fail(LS_ERR_HIP, "persistent kernel launch: %s", hipGetErrorString(e));
   return LS_OK;
 }
@@ -290,10 +300,8 @@ ls_status ls_prelude(ls_model* m, const ls_rows* r, const int32_t* tokens, float
   if (m->d.L_pre && !kv->pre) return fail(LS_ERR_INVALID, "ls_prelude: prelude layers need kv->pre");
   if (r->n == 0) return LS_OK;
   const ls_model_desc& d = m->d;
-  launch_validate(r->n, r->slot, nullptr, 0, 0, r->pos, r->anc_off, r->n_fin, r->max_anc, d.slot_capacity, m->slot_ok,
-                  m->dep_ok, m->row_ok, m->err, s);
   st = run_mega(m, r, 0, r->n, H, m->slot_ok, m->tab_pre, d.L_pre, kv->pre, nullptr, 0, 0, 1, tokens, nullptr, nullptr,
-                nullptr, s);
+                nullptr, s, validate_args(m, r, nullptr, 0, 0));
   if (st) return st;
   return check_hip("ls_prelude");
 }
@@ -305,10 +313,8 @@ ls_status ls_loop_step(ls_model* m, const ls_rows* r, float* H, const ls_kv* kv,
   if (r->n && !r->depth) return fail(LS_ERR_INVALID, "ls_loop_step: null depth");
   if (r->n == 0) return LS_OK;
   const ls_model_desc& d = m->d;
-  launch_validate(r->n, r->slot, r->depth, 1, d.R, r->pos, r->anc_off, r->n_fin, r->max_anc, d.slot_capacity,
-                  m->slot_ok, m->dep_ok, m->row_ok, m->err, s);
   st = run_mega(m, r, 0, r->n, H, m->slot_ok, m->tab_core, d.L, kv->core, m->dep_ok, -1, d.L, 0, nullptr, nullptr,
-                nullptr, nullptr, s, true);
+                nullptr, nullptr, s, validate_args(m, r, r->depth, 1, d.R), true);
   if (st) return st;
   return check_hip("ls_loop_step");
 }
@@ -326,17 +332,16 @@ ls_status ls_readout(ls_model* m, const ls_rows* r, const float* H, const ls_sam
   if (!out_rows && n_prob_rows < r->n) return fail(LS_ERR_INVALID, "ls_readout: n_prob_rows < rows");
   if (r->n == 0) return LS_OK;
   const ls_model_desc& d = m->d;
-  launch_validate(r->n, r->slot, r->depth, 0, d.n_readout - 1, r->pos, r->anc_off, r->n_fin, r->max_anc,
-                  d.slot_capacity, m->slot_ok, m->dep_ok, m->row_ok, m->err, s);
   float* lg = logits ? logits : m->logits;
+  const ValidateArgs v = validate_args(m, r, r->depth, 0, d.n_readout - 1), none{};
   for (int i0 = 0; i0 < r->n; i0 += 16) {
     const int mc = std::min(16, r->n - i0);
     if (d.L_coda)
       st = run_mega(m, r, i0, mc, m->hc, m->row_ok, m->tab_coda, d.L_coda, kv->coda, m->dep_ok, 0, d.L_coda, 2,
-                    nullptr, m->slot_ok, H, lg + (size_t)i0 * d.V, s);
+                    nullptr, m->slot_ok, H, lg + (size_t)i0 * d.V, s, i0 == 0 ? v : none);
     else
       st = run_mega(m, r, i0, mc, (float*)H, m->slot_ok, nullptr, 0, nullptr, nullptr, 0, 0, 0, nullptr, nullptr,
-                    nullptr, lg + (size_t)i0 * d.V, s);
+                    nullptr, lg + (size_t)i0 * d.V, s, i0 == 0 ? v : none);
     if (st) return st;
   }
   launch_dist(lg, r->n, d.V, smp->greedy, smp->temperature, smp->top_p, probs, out_rows, n_prob_rows, argmax, m->err, s);

@@ -1542,9 +1542,22 @@ __global__ __launch_bounds__(MEGA_THREADS) void k_mega(MegaArgs a) { mega_body<T
 template <typename T, int MT>
 __global__ __launch_bounds__(MEGA_THREADS) void k_mega_aux(MegaArgs a) { mega_body<T, MT>(a); }
 
+// Set-up of one launch: counters to zero, this launch's polled buffers to SENT32, rotary
+// cos/sin of the rows' positions, and (first launch of a call) the row-descriptor check.
 __global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, const double* inv_freq, int M, int half,
-                       unsigned* xs_fill, long long n_xs, unsigned* ys_fill, long long n_ys) {
+                       unsigned* xs_fill, long long n_xs, unsigned* ys_fill, long long n_ys, ValidateArgs v) {
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x, str = (long long)gridDim.x * blockDim.x;
+  for (long long i = tid; i < v.n; i += str) {
+    const int sl = v.slot[i];
+    const int dp = v.dep ? v.dep[i] : v.dep_lo;
+    const int a0 = v.anc_off[i], a1 = v.anc_off[i + 1];
+    bool ok = sl >= 0 && sl < v.S && dp >= v.dep_lo && dp <= v.dep_hi && a0 >= 0 && a1 >= a0 && a1 - a0 <= v.max_anc;
+    if (ok && v.pos) ok = v.pos[i] == v.n_fin + (a1 - a0);
+    if (!ok) ls_flag(v.err, 1);
+    v.slot_ok[i] = ok ? sl : -1;
+    v.dep_ok[i] = ok ? dp : v.dep_lo;
+    v.row_ok[i] = ok ? (int32_t)i : -1;
+  }
   for (long long i = tid; i < n; i += str) cnt[i] = 0;
   for (long long i = tid; i < n_xs; i += str) xs_fill[i] = SENT32;
   for (long long i = tid; i < n_ys; i += str) ys_fill[i] = SENT32;
@@ -1583,14 +1596,14 @@ int mega_occupancy(bool bf16, int M, int d) {
   return n;
 }
 
-hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool loop_block) {
+hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool loop_block, const ValidateArgs& v) {
   const CntLayout cl = cnt_layout(a.M, a.d, a.F, a.nh, x_chunk_for(a.M, bf16 ? 2 : 4, a.d), a.n_layers);
-  const long long n_prep = std::max<long long>(cl.total, (long long)a.M * (a.hd / 2));
+  const long long n_prep = std::max<long long>(std::max<long long>(cl.total, (long long)a.M * (a.hd / 2)), v.n);
   const long long rows = (long long)a.M * a.d;   // one layer slice of Xs / Ys
   hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<long long>(1024, (n_prep + 255) / 256)), dim3(256), 0, s, a.cnt,
                      (long long)cl.total, a.rope, a.pos, a.inv_freq, a.M, a.hd / 2,
                      reinterpret_cast<unsigned*>(a.Xs + rows), (long long)a.n_layers * rows,
-                     reinterpret_cast<unsigned*>(a.Ys), (long long)a.n_layers * rows);
+                     reinterpret_cast<unsigned*>(a.Ys), (long long)a.n_layers * rows, v);
   const size_t smem = mega_smem_bytes(bf16, a.M, a.d);
   void* args[] = {(void*)&a};
   return hipLaunchCooperativeKernel(pick(bf16, a.M, loop_block), dim3(G), dim3(MEGA_THREADS), args, (unsigned)smem, s);

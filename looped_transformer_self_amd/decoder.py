@@ -70,6 +70,7 @@ class Decoder:
         self.free_slots = list(range(engine.S - 1, -1, -1))
         self.free_prob = list(range(engine.prob_rows - 1, -1, -1))
         self.fin = []
+        self.fin_np = np.zeros(engine.S, np.int32)     # host mirror of fin, shipped with each step's rows
         self.fin_dev = torch.zeros(engine.S, dtype=torch.int32, device=engine.dev)
         self.fin_ptr = ctypes.c_void_p(self.fin_dev.data_ptr())
         self.tokens = []
@@ -106,9 +107,14 @@ class Decoder:
             stack.extend(x.kids)
             x.kids = []
 
-    def _fin_append(self, slots):
+    def _fin_append(self, slots, device=True):
+        """Commit slots to the finished prefix.  Decode steps ship the host mirror with their
+        rows, so only prefill (device=True) writes the device table."""
         a = len(self.fin)
         self.fin.extend(slots)
+        self.fin_np[a:a + len(slots)] = slots
+        if not device:
+            return
         if self.fin_dev.is_cuda:
             self.e.up.copy_to(self.fin_dev.data_ptr() + 4 * a, slots)
         else:                                   # host-only engines (scheduler tests)
@@ -204,33 +210,36 @@ class Decoder:
         spec = self.mode == "spec"
         n_fin = len(self.fin)
         self.steps += 1
-        # 1. prelude of branches spawned last step
-        if self.pending:
-            pn = [x for x in self.pending if x.alive]
-            self.pending = []
-            if pn:
-                rp = e.rows([x.slot for x in pn], [x.pos for x in pn], [0] * len(pn), n_fin,
-                            [self._path(x) for x in pn], self.fin_ptr,
-                            extra=[np.asarray([x.token for x in pn], np.int32)])
-                e.prelude(rp, rp.extra[0])
-        # 2. one loop iteration for every active branch
+        # the step's three row sets (prelude of branches spawned last step, one loop iteration
+        # for every active branch, readouts at the depths in D) go to the device in one copy
+        pn = [x for x in self.pending if x.alive]
+        self.pending = []
         act = [x for x in self._nodes() if x.depth < R]
         paths = [self._path(x) for x in act]
-        rl = e.rows([x.slot for x in act], [x.pos for x in act], [x.depth + 1 for x in act], n_fin, paths,
-                    self.fin_ptr)
-        e.loop_step(rl)
+        rd = [(x, p) for x, p in zip(act, paths) if x.depth + 1 in self.didx]
+        out_rows = [self._prob() for _ in rd]
+        specs = []
+        if pn:
+            specs.append(([x.slot for x in pn], [x.pos for x in pn], [0] * len(pn), n_fin, [self._path(x) for x in pn],
+                          [np.asarray([x.token for x in pn], np.int32)]))
+        specs.append(([x.slot for x in act], [x.pos for x in act], [x.depth + 1 for x in act], n_fin, paths, []))
+        if rd:
+            specs.append(([x.slot for x, _ in rd], [x.pos for x, _ in rd], [self.didx[x.depth + 1] for x, _ in rd], n_fin,
+                          [p for _, p in rd], [np.asarray(out_rows, np.int32)]))
+        rs = e.rows_set(specs, self.fin_np[:n_fin])
+        # 1. prelude
+        if pn:
+            rp = rs.pop(0)
+            e.prelude(rp, rp.extra[0])
+        # 2. loop iteration
+        e.loop_step(rs[0])
         self.rows_hist.append(len(act))
         for x in act:
             x.depth += 1
-        # 3. readouts at the depths in D
-        rd = [(x, p) for x, p in zip(act, paths) if x.depth in self.didx]
+        # 3. readouts
         if not rd:
             return
-        out_rows = []
-        for x, _ in rd:
-            out_rows.append(self._prob())
-        rr = e.rows([x.slot for x, _ in rd], [x.pos for x, _ in rd], [self.didx[x.depth] for x, _ in rd], n_fin,
-                    [p for _, p in rd], self.fin_ptr, extra=[np.asarray(out_rows, np.int32)])
+        rr = rs[1]
         e.readout(rr, dec.greedy, dec.T, dec.top_p, rr.extra[0])
         # 4. verification / draw jobs
         jobs, us, cands, tags = [], [], [], []
@@ -361,7 +370,7 @@ class Decoder:
         root.kids = []
         root.alive = False
         self._release_probs(root)
-        self._fin_append([root.slot])
+        self._fin_append([root.slot], device=False)
         if nxt is None or not nxt.alive:
             nxt = Node(self._slot(), pos, token)
             self.pending.append(nxt)
@@ -380,6 +389,7 @@ class Decoder:
         self.free_slots = list(snap["free_slots"])
         self.free_prob = list(snap["free_prob"])
         self.fin = list(snap["fin"])
+        self.fin_np[:len(self.fin)] = self.fin
         self.tokens = list(snap["tokens"])
         self.records = list(snap["records"])
         self.root = Node(*snap["root"])

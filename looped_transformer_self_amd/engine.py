@@ -92,6 +92,19 @@ class Uploader:
         self.hnp[k][:len(a)] = a
         self._ship(k, dst_ptr, len(a))
 
+    def ship_words(self, head, words):
+        """One copy of an int32 array followed by a list of ints; returns the device base
+        address and the buffer that holds it."""
+        k = self._slot()
+        nh, total = len(head), len(head) + len(words)
+        if total > len(self.hnp[k]):
+            raise ValueError("upload larger than the staging buffer")
+        hb = self.hnp[k]
+        hb[:nh] = head
+        hb[nh:total] = words
+        self._ship(k, self.dptr[k], total)
+        return self.dptr[k], self.devb[k]
+
     def pack(self, arrays):
         k = self._slot()
         offs, total = [], 0
@@ -182,7 +195,8 @@ class Engine:
         L.check(L.lib.ls_bind_workspace(h, self.ws_ptr, max_rows, self.max_keys, max_jobs, self.stream_ptr()),
                 "ls_bind_workspace")
         self.up = Uploader(self.dev, self._stream)
-        self.vout = torch.zeros(max_jobs * 4, dtype=torch.int32, device=self.dev)
+        # verification results: pinned host memory that the verify kernel writes directly, so
+        # reading them needs no device-to-host copy after the stream synchronisation
         self.vout_host = torch.zeros(max_jobs * 4, dtype=torch.int32, pin_memory=True)
         self.prof = None          # list of (start event, end event, row metadata) when profiling
         self.n_loop_calls = 0     # ls_loop_step launches with at least one row, since creation
@@ -222,6 +236,50 @@ class Engine:
         r.extra = ptrs[5:]
         r.host = (int(n_fin), list(slots), list(depth), anc_lists)
         return r
+
+    def rows_set(self, specs, fin):
+        """Several ls_rows over ONE upload: specs are (slots, pos, depth, n_fin, anc_lists,
+        extra) tuples as for rows(); `fin` (int32 array) is the finished-prefix slot table,
+        shipped in the same copy and shared by every descriptor.  The descriptors' arrays are
+        laid end to end after it (int32 elements need no wider alignment)."""
+        words, layout = [], []
+        nf = len(fin)
+        for slots, pos, depth, n_fin, anc_lists, extra in specs:
+            n = len(slots)
+            offs = [nf + len(words)]
+            words += slots
+            offs.append(nf + len(words)); words += pos
+            offs.append(nf + len(words)); words += depth
+            offs.append(nf + len(words))
+            acc = 0
+            words.append(0)
+            for a in anc_lists:
+                acc += len(a)
+                words.append(acc)
+            offs.append(nf + len(words))
+            for a in anc_lists:
+                words += a
+            if acc == 0:
+                words.append(0)
+            for x in extra:
+                offs.append(nf + len(words))
+                words += [int(v) for v in x]
+            layout.append(offs)
+        base, keep = self.up.ship_words(fin, words)
+        out = []
+        for (slots, pos, depth, n_fin, anc_lists, extra), offs in zip(specs, layout):
+            p = [C.c_void_p(base + 4 * o) for o in offs]
+            s = L.ls_rows()
+            s.n, s.n_fin = len(slots), int(n_fin)
+            s.max_anc = max((len(a) for a in anc_lists), default=0)
+            s.slot, s.pos, s.depth = p[0], p[1], p[2]
+            s.fin_slots = C.c_void_p(base)
+            s.anc_off, s.anc_slots = p[3], p[4]
+            r = Rows(s, keep)
+            r.extra = p[5:]
+            r.host = (int(n_fin), list(slots), list(depth), anc_lists)
+            out.append(r)
+        return out
 
     # ---- calls ---------------------------------------------------------------------------
     def prelude(self, rows, tokens_ptr):
@@ -275,8 +333,7 @@ class Engine:
         cptr = ptrs[2] if len(ptrs) > 2 else C.c_void_p(0)
         ncand = len(cands) if cands is not None else 0
         L.check(L.lib.ls_verify(self.h, ptrs[0], n, _ptr(self.probs), self.prob_rows, cptr, ncand, ptrs[1],
-                                _ptr(self.vout), self.stream_ptr()), "ls_verify")
-        self.vout_host[:4 * n].copy_(self.vout[:4 * n], non_blocking=True)
+                                _ptr(self.vout_host), self.stream_ptr()), "ls_verify")
         torch.cuda.current_stream().synchronize()
         return self.vout_host[:4 * n].numpy().reshape(n, 4).copy()
 

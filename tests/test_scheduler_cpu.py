@@ -42,6 +42,10 @@ class FakeEngine:
         r = types.SimpleNamespace(n=len(slots), slots=list(slots), pos=list(pos), depth=list(depth), extra=list(extra))
         return r
 
+    def rows_set(self, specs, fin):
+        assert len(fin) == specs[0][3]
+        return [self.rows(sl, p, dp, nf, anc, None, extra) for sl, p, dp, nf, anc, extra in specs]
+
     def prelude(self, rows, tok):
         pass
 
