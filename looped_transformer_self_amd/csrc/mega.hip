@@ -80,6 +80,8 @@ LS_DEV u32x4_t ld128(__amdgpu_buffer_rsrc_t r, int byte_off) {
 // positive canonical one, and no input element converts to it).  Their readers poll the data
 // itself with agent-coherent loads instead of a completion counter: a row is complete when no
 // element still holds SENT32.  The epilogues still count their tiles for the other readers.
+// The attention outputs o[l] are polled the same way by the O phase (all-ones words: 0xFFFF
+// halves in bf16, also a NaN pattern no merge stores), so the merge signals nothing.
 constexpr unsigned SENT32 = 0xFFFFFFFFu;
 // Rows up to this many columns are staged, normalised and (for Xs / Ys) polled in one pass.
 constexpr int FUSE_MAX_K = 2048;
@@ -102,6 +104,10 @@ template <> struct Coh<float> {
   LS_DEV static void store(float* p, float v) { stc(p, v); }
   LS_DEV static float raw(const float* p) { return ldc(p); }
 };
+// A 32-bit word of the polled attention output that still holds (part of) the fill pattern.
+template <typename T> LS_DEV bool holds_fill(unsigned w);
+template <> LS_DEV bool holds_fill<uint16_t>(unsigned w) { return (w & 0xffffu) == 0xffffu || (w >> 16) == 0xffffu; }
+template <> LS_DEV bool holds_fill<float>(unsigned w) { return w == 0xffffffffu; }
 
 // Every wait below is bounded: after SPIN_LIMIT polls (about a second) the wait gives up and
 // records LS_TIMEOUT in the error word, so a broken dependency ends the kernel with an error
@@ -216,7 +222,7 @@ LS_DEV void wait_spread(const int* base, int lo, int hi, ConsBar& cb) {
 // ---- counter layout -----------------------------------------------------------------------------
 struct CntLayout {
   int per_layer, nchF;
-  int o_qkvh, o_att, o_o, o_gu, o_down, o_fa;
+  int o_qkvh, o_o, o_gu, o_down, o_fa;
   int o_init, total;
 };
 
@@ -227,7 +233,6 @@ __host__ __device__ inline CntLayout cnt_layout(int M, int d, int F, int nh, int
   c.nchF = (F + XC - 1) / XC;
   int o = 0;
   c.o_qkvh = o; o += 3 * (d / 16) * PADC;
-  c.o_att = o; o += nh * PADC;
   c.o_o = o; o += NSPREAD * PADC;
   c.o_gu = o; o += c.nchF * NSPREAD * PADC;
   c.o_down = o; o += NSPREAD * PADC;
@@ -674,23 +679,37 @@ struct Consumer {
   }
 
   // Stage columns [x0, x0 + xn) of rows already in GEMM-input precision (attention output or
-  // SwiGLU activations, row stride K) into LDS, 16 bytes per lane.
-  LS_DEV void stage_raw(const T* src, int K, int x0, int xn) {
+  // SwiGLU activations, row stride K) into LDS, 16 bytes per lane.  The chunk is cut into
+  // pieces of 2 x 64 x 16 bytes dealt over the consumer waves; with `poll` (attention output) a
+  // piece is re-read until none of its elements holds the fill pattern.
+  LS_DEV void stage_raw(const T* src, int K, int x0, int xn, bool poll) {
     constexpr int E = 16 / (int)sizeof(T);
-    constexpr int NV = 8;
-    for (int m = c; m < a.M; m += NCONS) {
+    constexpr int PIECE = 2 * 64 * E;                    // elements per piece
+    const int npc = (xn + PIECE - 1) / PIECE;
+    for (int it = c; it < a.M * npc; it += NCONS) {
+      const int m = it / npc, p0 = (it - m * npc) * PIECE;
       const __amdgpu_buffer_rsrc_t R = rsrc_of(src + (size_t)m * K + x0, xn * (int)sizeof(T));
       char* xr = (char*)((T*)s.X + (size_t)m * s.xstride);
-      for (int p0 = 0; p0 < xn; p0 += 64 * E * NV) {
-        u32x4_t v[NV];
+      const int o0 = (p0 + E * lane) * (int)sizeof(T), o1 = (p0 + E * (lane + 64)) * (int)sizeof(T);
+      u32x4_t v0, v1;
+      if (poll) {
+        int n = 0;
+        while (true) {
+          v0 = ldc128(R, o0);
+          v1 = ldc128(R, o1);
+          bool ok = true;
 #pragma unroll
-        for (int u = 0; u < NV; ++u) v[u] = ld128(R, (p0 + E * (lane + 64 * u)) * (int)sizeof(T));
-#pragma unroll
-        for (int u = 0; u < NV; ++u) {
-          const int k = p0 + E * (lane + 64 * u);
-          if (k < xn) *reinterpret_cast<u32x4_t*>(xr + (size_t)k * sizeof(T)) = v[u];
+          for (int j = 0; j < 4; ++j) ok = ok && !holds_fill<T>(v0[j]) && !holds_fill<T>(v1[j]);
+          if (__all(ok)) break;
+          __builtin_amdgcn_s_sleep(POLL_SLEEP);
+          if (++n > SPIN_LIMIT) { if (lane == 0) ls_flag(a.err, LS_TIMEOUT); break; }
         }
+      } else {
+        v0 = ld128(R, o0);
+        v1 = ld128(R, o1);
       }
+      if (p0 + E * lane < xn) *reinterpret_cast<u32x4_t*>(xr + o0) = v0;
+      if (p0 + E * (lane + 64) < xn) *reinterpret_cast<u32x4_t*>(xr + o1) = v1;
     }
     cb.sync();
   }
@@ -1146,7 +1165,6 @@ LS_DEV void att_unit_wave(const MegaArgs& a, const Lds& s, const CntLayout& cl, 
 // batch is issued before any is used, so a batch costs one memory round trip.
 template <typename T>
 LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, int l, int g, int h, int nu) {
-  int* C = a.cnt + (size_t)l * cl.per_layer;
   const int lane = threadIdx.x & 63;
   const int hd = a.hd;
   const bool dok = 2 * lane < hd;
@@ -1241,8 +1259,6 @@ LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
     }
     if (dok) store2_coh<T>(orow + 2 * lane, den > 0.f ? num0 / den : 0.f, den > 0.f ? num1 / den : 0.f);
   }
-  drain();
-  if (lane == 0) atomicAdd(C + cl.o_att + h * PADC, 1);
 }
 
 // ---- init unit: embedding row or gathered hidden row into the working rows ---------------------------
@@ -1334,17 +1350,13 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
       const int xn = min(s.XC, g.K - x0);
       if (!PROD && (restage || i == 0)) {
         const int* C = a.cnt + (size_t)l * cl.per_layer;
-        if (ph == PH_O) {
-          const int h0 = x0 / a.hd, h1 = (x0 + xn - 1) / a.hd;
-          for (int hb = h0; hb <= h1; hb += 64)
-            wait_all_ge(C + cl.o_att + hb * PADC, PADC, min(64, h1 + 1 - hb), s.goff[64], *cb);
-        } else if (ph == PH_DOWN) {
+        if (ph == PH_DOWN) {
           wait_spread(C + cl.o_gu + ch * NSPREAD * PADC, x0 / 8, (x0 + xn) / 8, *cb);
         } else {
           cb->sync();                     // earlier readers of the stage are done
         }
         dstamp(a, co->dbg, 5);
-        if (ph == PH_O || ph == PH_DOWN) co->stage_raw(ph == PH_O ? o_of<T>(a, l) : act_of<T>(a, l), g.K, x0, xn);
+        if (ph == PH_O || ph == PH_DOWN) co->stage_raw(ph == PH_O ? o_of<T>(a, l) : act_of<T>(a, l), g.K, x0, xn, ph == PH_O);
         else co->stage_norm(nsrc, nvia, gain, x0, xn, fuse, poll);
         if (threadIdx.x == 0 && i == 0 && ch == 0) tstamp(a, l, ph, 3);
       }
@@ -1545,7 +1557,8 @@ __global__ __launch_bounds__(MEGA_THREADS) void k_mega_aux(MegaArgs a) { mega_bo
 // Set-up of one launch: counters to zero, this launch's polled buffers to SENT32, rotary
 // cos/sin of the rows' positions, and (first launch of a call) the row-descriptor check.
 __global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, const double* inv_freq, int M, int half,
-                       unsigned* xs_fill, long long n_xs, unsigned* ys_fill, long long n_ys, ValidateArgs v) {
+                       unsigned* xs_fill, long long n_xs, unsigned* ys_fill, long long n_ys, unsigned* o_fill,
+                       long long n_o, ValidateArgs v) {
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x, str = (long long)gridDim.x * blockDim.x;
   for (long long i = tid; i < v.n; i += str) {
     const int sl = v.slot[i];
@@ -1561,6 +1574,7 @@ __global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, c
   for (long long i = tid; i < n; i += str) cnt[i] = 0;
   for (long long i = tid; i < n_xs; i += str) xs_fill[i] = SENT32;
   for (long long i = tid; i < n_ys; i += str) ys_fill[i] = SENT32;
+  for (long long i = tid; i < n_o; i += str) o_fill[i] = 0xffffffffu;
   for (long long i = tid; i < (long long)M * half; i += str) {
     const int m = (int)(i / half), f = (int)(i % half);
     double sn, cs;
@@ -1603,7 +1617,8 @@ hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool 
   hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<long long>(1024, (n_prep + 255) / 256)), dim3(256), 0, s, a.cnt,
                      (long long)cl.total, a.rope, a.pos, a.inv_freq, a.M, a.hd / 2,
                      reinterpret_cast<unsigned*>(a.Xs + rows), (long long)a.n_layers * rows,
-                     reinterpret_cast<unsigned*>(a.Ys), (long long)a.n_layers * rows, v);
+                     reinterpret_cast<unsigned*>(a.Ys), (long long)a.n_layers * rows,
+                     reinterpret_cast<unsigned*>(a.o), (long long)a.n_layers * rows * (bf16 ? 2 : 4) / 4, v);
   const size_t smem = mega_smem_bytes(bf16, a.M, a.d);
   void* args[] = {(void*)&a};
   return hipLaunchCooperativeKernel(pick(bf16, a.M, loop_block), dim3(G), dim3(MEGA_THREADS), args, (unsigned)smem, s);
