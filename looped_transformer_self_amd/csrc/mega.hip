@@ -271,8 +271,11 @@ __host__ __device__ inline LdsPlan lds_plan(int M, int esz, int d) {
   const int ns_opts[5] = {16, 14, 12, 10, 8};
   for (int i = 0; i < 5; ++i)
     if (lds_bytes_for(M, esz, ns_opts[i], xfull, 2) <= LDS_BUDGET) return LdsPlan{ns_opts[i], xfull, 2};
+  // many rows: narrower activation chunks first, then a shallower ring (down to 4 slabs, one
+  // per consumer), so every row count up to the workspace maximum fits
   LdsPlan p{8, xfull, M <= 64 ? 2 : 1};
   while (p.XC > sk && lds_bytes_for(M, esz, p.NS, p.XC, p.nred) > LDS_BUDGET) p.XC = (p.XC / 2 + sk - 1) / sk * sk;
+  while (p.NS > NCONS && lds_bytes_for(M, esz, p.NS, p.XC, p.nred) > LDS_BUDGET) p.NS -= 2;
   return p;
 }
 __host__ __device__ inline int x_chunk_for(int M, int esz, int d) { return lds_plan(M, esz, d).XC; }

@@ -130,3 +130,48 @@ def test_readout_full_size(full_model):
         assert err <= tol(cfg), (r, err)
         assert am[r] == int(np.argmax(lg[r]))
         assert abs(float(pg[r].astype(np.float64).sum()) - 1.0) < 1e-4
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("M", [40, 128])
+def test_loop_step_full_size_many_rows(full_model, M):
+    """Ouro-1.4B shape with many rows per call: the row-tile variants for 4 and 8 tiles, the
+    activation row staged in several chunks (RMSNorm factors from the per-tile sums of
+    squares) and, at 128 rows, the shallower weight ring.  Three rows are checked."""
+    key, cfg, w, _, _, _ = full_model
+    if key != "C2":
+        pytest.skip("one full-size shape is enough for the row-count variants")
+    from looped_transformer_self_amd.engine import Engine
+    n_fin = 256
+    S = n_fin + 4 * M + 16
+    e = Engine(cfg, w, slot_capacity=S, max_rows=M, max_keys=S, max_jobs=16, prob_rows=16)
+    depths = [1 + (i * 3) % cfg.R for i in range(M)]
+    fin, slots, anc, pos = _rows(cfg, n_fin, S, depths, seed=51 + M)
+    check = [0, M // 2, M - 1]
+    keyset = sorted(set(fin) | {x for i in check for x in anc[i]})
+    blocks = sorted({(depths[i] - 1) * cfg.L + l for i in check for l in range(cfg.L)})
+    print(f"[fullsize] {key}: loop_step, {M} rows, {n_fin} prefix keys, rows {check} checked", flush=True)
+    ref_blocks = _fill_blocks(e, cfg, e.kv_core, blocks, keyset, S, seed=300)
+    H0 = np.zeros((S, cfg.d), np.float32)
+    H0[slots] = inputs.hidden_rows(len(slots), cfg.d, seed=52)
+    e.H.copy_(torch.from_numpy(H0))
+    fin_t = torch.tensor(fin, dtype=torch.int32, device="cuda")
+    rows = e.rows(slots, pos, depths, n_fin, anc, C.c_void_p(fin_t.data_ptr()))
+    e.loop_step(rows)
+    assert e.sync_status() == 0
+    Hg = e.H.cpu().numpy()
+    kvg = e.kv_core.view(-1, S, 2, cfg.d)
+    m = Model(cfg, {**w, "emb": w["emb"][:1], "pre": [], "coda": []})
+    for i in check:
+        k = depths[i]
+        blks = [ref_blocks[(k - 1) * cfg.L + l] for l in range(cfg.L)]
+        h_ref, kvs = oracle_row_block(m, m.core, H0[slots[i]][None].astype(np.float64), pos[i], fin + anc[i], blks, cfg)
+        err = rel_l2(Hg[slots[i]], h_ref[0])
+        print(f"[fullsize] {key}: {M} rows, row {i} depth {k} rel-L2 {err:.2e}", flush=True)
+        assert err <= tol(cfg), (i, err)
+        for l in (0, cfg.L - 1):
+            got = as_f64(kvg[(k - 1) * cfg.L + l, slots[i]].cpu().numpy().view(np.uint16), cfg)
+            assert rel_l2(got[0], kvs[l][0]) <= tol(cfg) and rel_l2(got[1], kvs[l][1]) <= tol(cfg), (i, l)
+    del e
+    gc.collect()
+    torch.cuda.empty_cache()

@@ -44,12 +44,14 @@ def _fin_table(fin, S):
 
 
 @pytest.mark.parametrize("cfg", SMALL_CFGS, ids=lambda c: c.name)
-@pytest.mark.parametrize("M,n_fin", [(5, 300), (20, 37), (1, 0)])
+@pytest.mark.parametrize("M,n_fin", [(5, 300), (20, 37), (1, 0), (40, 50), (128, 20)])
 def test_loop_step_parity(cfg, M, n_fin):
+    """Row counts across the kernel's row-tile variants (1, 2, 4 and 8 tiles of 16 rows), up
+    to the workspace maximum of 128 rows per call."""
     print(f"[loop_step] {cfg.name} M={M} n_fin={n_fin}", flush=True)
-    S = 384
+    S = max(384, n_fin + 4 * M + 8)
     w = weights.make_weights(cfg, seed=0)
-    e = _engine(cfg, w, S)
+    e = _engine(cfg, w, S, max_rows=max(32, M))
     m = Model(cfg, w)
     kv = _fill_cache(e, cfg, "core", cfg.R * cfg.L, S, seed=11)
     H0 = inputs.hidden_rows(S, cfg.d, seed=12)
