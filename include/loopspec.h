@@ -161,8 +161,8 @@ typedef struct {
 const char *ls_last_error(void);
 
 /* Create a model handle over caller-owned weights (pointers are retained, not copied).
- * Fails with LS_ERR_UNSUPPORTED if head_dim is not a multiple of 16 or exceeds 128, or d,
- * F are not multiples of 32 (bf16) / 16 (fp32). */
+ * Fails with LS_ERR_UNSUPPORTED if head_dim is not a multiple of 16 or exceeds 128, d or F
+ * is not a multiple of 32 (bf16) / 16 (fp32), or V exceeds 65536. */
 ls_status ls_model_create(const ls_model_desc *desc, const ls_weight_ptrs *w, ls_model **out);
 void ls_model_destroy(ls_model *m);
 

@@ -141,6 +141,7 @@ ls_status ls_model_create(const ls_model_desc* desc, const ls_weight_ptrs* w, ls
   if (d.n_heads * d.head_dim != d.d) return fail(LS_ERR_INVALID, "ls_model_create: n_heads * head_dim != d");
   if (d.dtype != LS_F32 && d.dtype != LS_BF16) return fail(LS_ERR_INVALID, "ls_model_create: bad dtype");
   if (d.head_dim % 16 || d.head_dim > 128) return fail(LS_ERR_UNSUPPORTED, "head_dim must be a multiple of 16, <= 128");
+  if (d.V > 65536) return fail(LS_ERR_UNSUPPORTED, "V must be <= 65536 (the readout keeps a row in one workgroup's registers)");
   const int kmul = d.dtype == LS_BF16 ? 32 : 16;
   if (d.d % kmul || d.F % kmul) return fail(LS_ERR_UNSUPPORTED, "d and F must be multiples of %d", kmul);
   if (d.n_readout < 1 || d.n_readout > LS_MAX_READOUT_DEPTHS) return fail(LS_ERR_INVALID, "bad n_readout");

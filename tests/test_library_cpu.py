@@ -63,3 +63,36 @@ def test_host_philox_matches_oracle(seed, pos):
                            C.c_int(len(purposes)), out.ctypes.data_as(C.c_void_p))
     want = [philox.uniform(seed, pos, int(p)) for p in purposes]
     assert out.tolist() == want
+
+
+def _desc(**kw):
+    from looped_transformer_self_amd import _lib as binding
+    d = binding.ls_model_desc()
+    d.V, d.d, d.n_heads, d.head_dim, d.F = 49152, 2048, 16, 128, 5632
+    d.L, d.L_pre, d.L_coda, d.R = 24, 0, 0, 4
+    d.n_readout = 3
+    for i, r in enumerate((2, 3, 4)):
+        d.readout_depths[i] = r
+    d.dtype, d.rope_theta, d.norm_eps = binding.LS_BF16, 10000.0, 1e-6
+    d.slot_capacity = 1024
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("fields,status", [
+    ({"V": 65537}, 2), ({"head_dim": 136, "d": 16 * 136}, 2), ({"head_dim": 120, "d": 16 * 120}, 2),
+    ({"F": 5640}, 2), ({"n_heads": 15}, 1), ({"R": 0}, 1), ({"slot_capacity": 0}, 1)])
+def test_model_create_rejects_unsupported_shapes(fields, status):
+    """Shape checks happen on the host before any device work: out-of-contract descriptors
+    come back as LS_ERR_INVALID (1) or LS_ERR_UNSUPPORTED (2) with a message."""
+    from looped_transformer_self_amd import _lib as binding
+    lib = _lib()
+    lib.ls_model_create.restype = C.c_int
+    lib.ls_last_error.restype = C.c_char_p
+    d = _desc(**fields)
+    w = binding.ls_weight_ptrs()
+    out = C.c_void_p()
+    st = lib.ls_model_create(C.byref(d), C.byref(w), C.byref(out))
+    assert st == status, (st, lib.ls_last_error())
+    assert lib.ls_last_error()
