@@ -241,43 +241,43 @@ class Engine:
         """Several ls_rows over ONE upload: specs are (slots, pos, depth, n_fin, anc_lists,
         extra) tuples as for rows(); `fin` (int32 array) is the finished-prefix slot table,
         shipped in the same copy and shared by every descriptor.  The descriptors' arrays are
-        laid end to end after it (int32 elements need no wider alignment)."""
+        laid end to end after it (int32 elements need no wider alignment).  This runs between
+        a step's verification result and its next launch, so it is kept to plain list work."""
         words, layout = [], []
         nf = len(fin)
         for slots, pos, depth, n_fin, anc_lists, extra in specs:
-            n = len(slots)
-            offs = [nf + len(words)]
+            o_slot = nf + len(words)
             words += slots
-            offs.append(nf + len(words)); words += pos
-            offs.append(nf + len(words)); words += depth
-            offs.append(nf + len(words))
-            acc = 0
+            words += pos
+            words += depth
+            o_off = nf + len(words)
+            acc = mx = 0
             words.append(0)
             for a in anc_lists:
-                acc += len(a)
+                na = len(a)
+                acc += na
+                if na > mx:
+                    mx = na
                 words.append(acc)
-            offs.append(nf + len(words))
+            o_anc = nf + len(words)
             for a in anc_lists:
                 words += a
             if acc == 0:
                 words.append(0)
+            o_extra = []
             for x in extra:
-                offs.append(nf + len(words))
-                words += [int(v) for v in x]
-            layout.append(offs)
+                o_extra.append(nf + len(words))
+                words += x.tolist() if isinstance(x, np.ndarray) else list(x)
+            layout.append((o_slot, o_off, o_anc, mx, o_extra))
         base, keep = self.up.ship_words(fin, words)
         out = []
-        for (slots, pos, depth, n_fin, anc_lists, extra), offs in zip(specs, layout):
-            p = [C.c_void_p(base + 4 * o) for o in offs]
-            s = L.ls_rows()
-            s.n, s.n_fin = len(slots), int(n_fin)
-            s.max_anc = max((len(a) for a in anc_lists), default=0)
-            s.slot, s.pos, s.depth = p[0], p[1], p[2]
-            s.fin_slots = C.c_void_p(base)
-            s.anc_off, s.anc_slots = p[3], p[4]
+        for (slots, pos, depth, n_fin, anc_lists, extra), (o_slot, o_off, o_anc, mx, o_extra) in zip(specs, layout):
+            n = len(slots)
+            s = L.ls_rows(n, n_fin, mx, base + 4 * o_slot, base + 4 * (o_slot + n), base + 4 * (o_slot + 2 * n), base,
+                          base + 4 * o_off, base + 4 * o_anc)
             r = Rows(s, keep)
-            r.extra = p[5:]
-            r.host = (int(n_fin), list(slots), list(depth), anc_lists)
+            r.extra = [C.c_void_p(base + 4 * o) for o in o_extra]
+            r.host = (n_fin, slots, depth, anc_lists)
             out.append(r)
         return out
 
