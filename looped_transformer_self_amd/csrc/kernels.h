@@ -39,7 +39,8 @@ struct MegaArgs {
   float* Ys;                    // per-layer attention-residual outputs at Ys + l*M*d
   const int32_t *slot, *pos, *dep, *fin, *anc_off, *anc, *tokens;
   int n_fin;
-  int att_chunks;               // attention units per (group, head): ceil(n_fin / att_unit_keys), >= 1
+  int att_chunks;               // attention units per (group, head): ceil(n_fin / (att_unit_keys * att_sub)), >= 1
+  int att_sub;                  // sub-units of att_unit_keys keys per attention unit, >= 1
   void* kv;                     // cache tensor; block(i, l) = (dep[i] + dep_off) * blk_mul + layer0 + l
   int dep_off, blk_mul, layer0;
   long long S;

@@ -239,6 +239,10 @@ ls_status ls_bind_workspace(ls_model* m, void* ws, int max_rows, int max_keys, i
 
 namespace {
 
+#ifndef LS_ATT_SUB_MAX
+#define LS_ATT_SUB_MAX 16
+#endif
+
 // The row check of a call over `r` (depth range dep_lo..dep_hi; dep NULL: no depths).
 ValidateArgs validate_args(ls_model* m, const ls_rows* r, const int32_t* dep, int dep_lo, int dep_hi) {
   ValidateArgs v;
@@ -265,8 +269,6 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
   a.fin = r->fin_slots; a.anc_off = r->anc_off + i0; a.anc = r->anc_slots;
   a.tokens = tokens ? tokens + i0 : nullptr;
   a.n_fin = r->n_fin;
-  const int uk = att_unit_keys(m->bf16());
-  a.att_chunks = std::max(1, (r->n_fin + uk - 1) / uk);   // attention units of the finished prefix
   a.kv = kv; a.dep_off = dep_off; a.blk_mul = blk_mul; a.layer0 = 0; a.S = d.slot_capacity;
   a.q = m->q; a.o = m->o; a.act = m->act;
   a.logits = logits; a.ldo = d.V;
@@ -283,6 +285,12 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
     occ = std::min(occ, 4);
   }
   const int G = occ * m->n_cu;
+  // attention units of the finished prefix: 64-key sub-units, several per unit once a single
+  // depth group would give every consumer wave (4 per workgroup) more than one unit
+  const int uk = att_unit_keys(m->bf16());
+  const long long per_wave = (long long)d.n_heads * r->n_fin / ((long long)uk * 4 * G);
+  a.att_sub = (int)std::max(1LL, std::min<long long>(per_wave, LS_ATT_SUB_MAX));
+  a.att_chunks = std::max(1, (r->n_fin + uk * a.att_sub - 1) / (uk * a.att_sub));
   a.trace = m->trace;
   m->last_grid = G;
   hipError_t e = launch_mega(m->bf16(), a, G, s, loop_block, v);

@@ -1163,6 +1163,171 @@ LS_DEV void att_unit_wave(const MegaArgs& a, const Lds& s, const CntLayout& cl, 
   if (arrived == nu - 1) att_merge<T>(a, s, cl, l, g, h, nu);
 }
 
+// Long prefixes (att_sub > 1): one wave processes unit (g, h, c): prefix keys [span*c,
+// span*c + span), span = KEYS *
+// att_sub, for every row of group g, with no workgroup synchronisation.  The unit walks its
+// att_sub sub-units of KEYS keys in order; lane = (key kk of each group of four, dims
+// 8e..8e+7); key j of a sub-unit's pass p = 4*RR*p + kk + 4*rr.  Online log-sum-exp over all
+// passes; partial (max, sum, acc[hd]) per row to the partial buffer; the wave that completes
+// the last unit of (g, h) merges.  Long prefixes use several sub-units per unit (fewer
+// partials to merge, and the key loads run on from one sub-unit into the next).
+template <typename T>
+LS_DEV void att_unit_wave_long(const MegaArgs& a, const Lds& s, const CntLayout& cl, int l, int g, int h, int c, int nu) {
+  constexpr int RR = AttUnit<T>::RR, NPASS = AttUnit<T>::NPASS, KEYS = AttUnit<T>::KEYS;
+  int* C = a.cnt + (size_t)l * cl.per_layer;
+  const int lane = threadIdx.x & 63;
+  const int kk = lane >> 4, e = lane & 15;
+  const int hd = a.hd;
+  const bool dim_ok = 8 * e < hd;
+  const int g0 = s.goff[g], ng = s.goff[g + 1] - g0;
+  const int rep = s.grow[g0];
+  const int blk = (a.dep ? s.rdep[rep] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
+  const T* cache = (const T*)a.kv + (size_t)blk * a.S * 2 * a.d + h * hd + 8 * e;
+  const int k0 = c * KEYS * a.att_sub;
+  const int nsub = max(1, min(a.att_sub, (a.n_fin - k0 + KEYS - 1) / KEYS));   // sub-units holding keys
+
+  // slots of this lane's keys in the sub-unit starting at key kb (prefix keys were written by
+  // earlier launches: plain loads); out-of-range slots raise the error word and are skipped
+  auto fill_sl = [&](int kb, int* sl) {
+    const int kn = max(0, min(KEYS, a.n_fin - kb));
+#pragma unroll
+    for (int q = 0; q < NPASS * RR; ++q) {
+      const int j = (q / RR) * 4 * RR + kk + 4 * (q % RR);
+      sl[q] = j < kn ? a.fin[kb + min(j, kn - 1)] : -1;
+    }
+    bool bad = false;
+#pragma unroll
+    for (int q = 0; q < NPASS * RR; ++q) {
+      const int j = (q / RR) * 4 * RR + kk + 4 * (q % RR);
+      if (j < kn && (sl[q] < 0 || sl[q] >= a.S)) { bad = true; sl[q] = -1; }
+    }
+    if (bad) ls_flag(a.err, 1);
+  };
+  auto load_pass = [&](const int* sl, int p, Raw8<T>* kr, Raw8<T>* vr) {
+#pragma unroll
+    for (int rr = 0; rr < RR; ++rr) {
+      const int x = sl[p * RR + rr];
+      kr[rr].zero();
+      vr[rr].zero();
+      if (x >= 0 && dim_ok) {
+        kr[rr].load(cache + (size_t)x * 2 * a.d);
+        vr[rr].load(cache + (size_t)x * 2 * a.d + a.d);
+      }
+    }
+  };
+  // The first NPF passes of prefix keys and values are requested before the wait (they were
+  // written by earlier launches, so their latency overlaps the QKV phase); pass p + NPF reuses
+  // the registers of pass p, requested as soon as pass p is consumed (from the next sub-unit
+  // once the current one has no further pass).
+  constexpr int NPF = NPASS / 2;
+  int sl[NPASS * RR], sn[NPASS * RR];
+  fill_sl(k0, sl);
+  Raw8<T> kr[NPF][RR], vr[NPF][RR];
+#pragma unroll
+  for (int p = 0; p < NPF; ++p) load_pass(sl, p, kr[p], vr[p]);
+  // queries of this head are complete once the head's q/k/v tiles have all signalled
+  {
+    const int nf = 3 * (hd / 16);                         // the head's QKV tiles: flags h * nf .. + nf
+    bool done = lane >= nf;
+    int n = 0;
+    while (true) {
+      if (!done) done = ld_acq(C + cl.o_qkvh + (h * nf + lane) * PADC) >= 1;
+      if (__all(done)) break;
+      __builtin_amdgcn_s_sleep(POLL_SLEEP);
+      if (++n > SPIN_LIMIT) { if (lane == 0) ls_flag(a.err, LS_TIMEOUT); break; }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" : : : "memory");
+
+  const float scale = 1.0f / sqrtf((float)hd);
+  const __amdgpu_buffer_rsrc_t Rq = rsrc_of(a.q, a.M * a.d * 4);
+  for (int r = 0; r < ng; ++r) {
+    const int i = s.grow[g0 + r];
+    const int qoff = (i * a.d + h * hd + 8 * e) * 4;
+    const u32x4_t qa = ldc128(Rq, dim_ok ? qoff : 0x7fffff00), qb = ldc128(Rq, dim_ok ? qoff + 16 : 0x7fffff00);
+    if (r > 0) {                                          // a later row re-reads the keys (cached)
+      if (nsub > 1) fill_sl(k0, sl);
+#pragma unroll
+      for (int p = 0; p < NPF; ++p) load_pass(sl, p, kr[p], vr[p]);
+    }
+    float q8[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      q8[t] = __uint_as_float(qa[t]) * scale;
+      q8[4 + t] = __uint_as_float(qb[t]) * scale;
+    }
+    float run_m = -INFINITY, lsum = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    auto consume = [&](int p, const Raw8<T>* kp, const Raw8<T>* vp) {
+      float sc[RR];
+      float pm = -INFINITY;
+#pragma unroll
+      for (int rr = 0; rr < RR; ++rr) {
+        float kf[8];
+        kp[rr].unpack(kf);
+        float part = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) part += q8[t] * kf[t];
+        part = row_sum16(part);             // the key's score in every lane of its row
+        sc[rr] = sl[p * RR + rr] >= 0 ? part : -INFINITY;
+        pm = fmaxf(pm, sc[rr]);
+      }
+      pm = rows_max(pm);
+      const float nm = fmaxf(run_m, pm);
+      if (nm == -INFINITY) return;                        // no key so far
+      const float rs = run_m == -INFINITY ? 0.f : __expf(run_m - nm);
+      lsum *= rs;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] *= rs;
+      run_m = nm;
+#pragma unroll
+      for (int rr = 0; rr < RR; ++rr) {
+        const float pw = sl[p * RR + rr] >= 0 ? __expf(sc[rr] - nm) : 0.f;
+        lsum += pw;
+        float vf[8];
+        vp[rr].unpack(vf);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] += pw * vf[t];
+      }
+    };
+    for (int j = 0; j < nsub; ++j) {
+      const bool more = j + 1 < nsub;
+      if (more) fill_sl(k0 + (j + 1) * KEYS, sn);        // next sub-unit's slots, in flight meanwhile
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        consume(p, kr[p % NPF], vr[p % NPF]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (p + NPF < NPASS) load_pass(sl, p + NPF, kr[p % NPF], vr[p % NPF]);
+        else if (more) load_pass(sn, p + NPF - NPASS, kr[p % NPF], vr[p % NPF]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (more) {
+#pragma unroll
+        for (int q = 0; q < NPASS * RR; ++q) sl[q] = sn[q];
+      }
+    }
+    // per-lane sums cover the lane's keys; combine the four key groups
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      acc[t] += __shfl_xor(acc[t], 16, 64);
+      acc[t] += __shfl_xor(acc[t], 32, 64);
+    }
+    float* out = a.patt + (((size_t)i * a.nh + h) * a.att_chunks + c) * (hd + 2);
+    if (lane == 0) { stc(out, run_m); stc(out + 1, lsum); }
+    if (kk == 0 && dim_ok) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) stc(out + 2 + 8 * e + t, acc[t]);
+    }
+  }
+  drain();
+  int arrived = 0;
+  if (lane == 0) arrived = atomicAdd(C + cl.o_fa + g * a.nh + h, 1);
+  arrived = __shfl(arrived, 0, 64);
+  if (arrived == nu - 1) att_merge<T>(a, s, cl, l, g, h, nu);
+}
+
 // Merge of head h for the rows of group g, by one wave, row by row; lane = dims 2*lane, 2*lane + 1.
 // Online log-sum-exp over batches of (16 prefix-chunk partials, 8 own keys); every load of a
 // batch is issued before any is used, so a batch costs one memory round trip.
@@ -1479,7 +1644,7 @@ LS_DEV Step step_of(const MegaArgs& a, int st) {
   return Step{k == 0 ? PH_QKV : (k == 1 ? PH_ATT : (k == 2 ? PH_O : (k == 3 ? PH_GU : PH_DOWN))), st / 5};
 }
 
-template <typename T, int MT>
+template <typename T, int MT, bool LONG>
 LS_DEV void mega_body(const MegaArgs& a) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   const Lds s = lds_carve<T>(smem_raw, a.M, a.d);
@@ -1541,7 +1706,8 @@ LS_DEV void mega_body(const MegaArgs& a) {
       for (int k = co.c; k < sa.count; k += NCONS) {
         const int u = sa.first + k * G;
         const int cch = u % nu, gh = u / nu;
-        att_unit_wave<T>(a, s, cl, sp.l, gh / a.nh, gh % a.nh, cch, nu);
+        if constexpr (LONG) att_unit_wave_long<T>(a, s, cl, sp.l, gh / a.nh, gh % a.nh, cch, nu);
+        else att_unit_wave<T>(a, s, cl, sp.l, gh / a.nh, gh % a.nh, cch, nu);
       }
     } else {
       walk_gemm<T, MT, false>(a, s, cl, sp.ph, sp.l, deal, nullptr, &co, &cb);
@@ -1552,10 +1718,12 @@ LS_DEV void mega_body(const MegaArgs& a) {
 
 // Two entry symbols over the same body, so that profiles tell the loop block's launches
 // (ls_loop_step) apart from the prelude, coda and LM-head launches.
-template <typename T, int MT>
-__global__ __launch_bounds__(MEGA_THREADS) void k_mega(MegaArgs a) { mega_body<T, MT>(a); }
-template <typename T, int MT>
-__global__ __launch_bounds__(MEGA_THREADS) void k_mega_aux(MegaArgs a) { mega_body<T, MT>(a); }
+// LONG: attention units of several sub-units (long prefixes), compiled separately so that the
+// short-prefix kernels keep their code size.
+template <typename T, int MT, bool LONG>
+__global__ __launch_bounds__(MEGA_THREADS) void k_mega(MegaArgs a) { mega_body<T, MT, LONG>(a); }
+template <typename T, int MT, bool LONG>
+__global__ __launch_bounds__(MEGA_THREADS) void k_mega_aux(MegaArgs a) { mega_body<T, MT, LONG>(a); }
 
 // Set-up of one launch: counters to zero, this launch's polled buffers to SENT32, rotary
 // cos/sin of the rows' positions, and (first launch of a call) the row-descriptor check.
@@ -1587,23 +1755,24 @@ __global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, c
   }
 }
 
-template <typename T>
-static const void* pick_t(int mt, bool loop) {
+template <typename T, bool LONG>
+static const void* pick_tl(int mt, bool loop) {
   if (loop) {
-    if (mt <= 1) return reinterpret_cast<const void*>(&k_mega<T, 1>);
-    if (mt <= 2) return reinterpret_cast<const void*>(&k_mega<T, 2>);
-    if (mt <= 4) return reinterpret_cast<const void*>(&k_mega<T, 4>);
-    return reinterpret_cast<const void*>(&k_mega<T, 8>);
+    if (mt <= 1) return reinterpret_cast<const void*>(&k_mega<T, 1, LONG>);
+    if (mt <= 2) return reinterpret_cast<const void*>(&k_mega<T, 2, LONG>);
+    if (mt <= 4) return reinterpret_cast<const void*>(&k_mega<T, 4, LONG>);
+    return reinterpret_cast<const void*>(&k_mega<T, 8, LONG>);
   }
-  if (mt <= 1) return reinterpret_cast<const void*>(&k_mega_aux<T, 1>);
-  if (mt <= 2) return reinterpret_cast<const void*>(&k_mega_aux<T, 2>);
-  if (mt <= 4) return reinterpret_cast<const void*>(&k_mega_aux<T, 4>);
-  return reinterpret_cast<const void*>(&k_mega_aux<T, 8>);
+  if (mt <= 1) return reinterpret_cast<const void*>(&k_mega_aux<T, 1, LONG>);
+  if (mt <= 2) return reinterpret_cast<const void*>(&k_mega_aux<T, 2, LONG>);
+  if (mt <= 4) return reinterpret_cast<const void*>(&k_mega_aux<T, 4, LONG>);
+  return reinterpret_cast<const void*>(&k_mega_aux<T, 8, LONG>);
 }
 
-static const void* pick(bool bf16, int M, bool loop = true) {
+static const void* pick(bool bf16, int M, bool loop = true, bool lng = false) {
   const int mt = (M + 15) / 16;
-  return bf16 ? pick_t<uint16_t>(mt, loop) : pick_t<float>(mt, loop);
+  if (lng) return bf16 ? pick_tl<uint16_t, true>(mt, loop) : pick_tl<float, true>(mt, loop);
+  return bf16 ? pick_tl<uint16_t, false>(mt, loop) : pick_tl<float, false>(mt, loop);
 }
 
 int mega_occupancy(bool bf16, int M, int d) {
@@ -1624,7 +1793,8 @@ hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool 
                      reinterpret_cast<unsigned*>(a.o), (long long)a.n_layers * rows * (bf16 ? 2 : 4) / 4, v);
   const size_t smem = mega_smem_bytes(bf16, a.M, a.d);
   void* args[] = {(void*)&a};
-  return hipLaunchCooperativeKernel(pick(bf16, a.M, loop_block), dim3(G), dim3(MEGA_THREADS), args, (unsigned)smem, s);
+  return hipLaunchCooperativeKernel(pick(bf16, a.M, loop_block, a.att_sub > 1), dim3(G), dim3(MEGA_THREADS), args,
+                                    (unsigned)smem, s);
 }
 
 }  // namespace ls

@@ -175,3 +175,45 @@ def test_loop_step_full_size_many_rows(full_model, M):
     del e
     gc.collect()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_loop_step_full_size_long_prefix(full_model):
+    """Huginn-3.5B shape with a 4800-key finished prefix: 55 heads x 75 key chunks give every
+    consumer wave several chunks, so each attention unit walks several 64-key sub-units
+    (the last unit a ragged number of them) before its partial is merged."""
+    key, cfg, w, _, _, _ = full_model
+    if key != "C4":
+        pytest.skip("the long-prefix unit layout needs many heads and keys (Huginn shape)")
+    from looped_transformer_self_amd.engine import Engine
+    n_fin = 4800
+    S = n_fin + 64
+    e = Engine(cfg, w, slot_capacity=S, max_rows=16, max_keys=S, max_jobs=16, prob_rows=16)
+    depths = [cfg.R, 2, 1]
+    fin, slots, anc, pos = _rows(cfg, n_fin, S, depths, seed=61)
+    keyset = sorted(set(fin) | {x for a in anc for x in a})
+    blocks = sorted({(k - 1) * cfg.L + l for k in depths for l in range(cfg.L)})
+    print(f"[fullsize] {key}: loop_step, {len(depths)} rows, {n_fin} prefix keys", flush=True)
+    ref_blocks = _fill_blocks(e, cfg, e.kv_core, blocks, keyset, S, seed=400)
+    H0 = np.zeros((S, cfg.d), np.float32)
+    H0[slots] = inputs.hidden_rows(len(slots), cfg.d, seed=62)
+    e.H.copy_(torch.from_numpy(H0))
+    fin_t = torch.tensor(fin, dtype=torch.int32, device="cuda")
+    rows = e.rows(slots, pos, depths, n_fin, anc, C.c_void_p(fin_t.data_ptr()))
+    e.loop_step(rows)
+    assert e.sync_status() == 0
+    Hg = e.H.cpu().numpy()
+    kvg = e.kv_core.view(-1, S, 2, cfg.d)
+    m = Model(cfg, {**w, "emb": w["emb"][:1], "pre": [], "coda": []})
+    for i, k in enumerate(depths):
+        blks = [ref_blocks[(k - 1) * cfg.L + l] for l in range(cfg.L)]
+        h_ref, kvs = oracle_row_block(m, m.core, H0[slots[i]][None].astype(np.float64), pos[i], fin + anc[i], blks, cfg)
+        err = rel_l2(Hg[slots[i]], h_ref[0])
+        print(f"[fullsize] {key}: long prefix, row {i} depth {k} rel-L2 {err:.2e}", flush=True)
+        assert err <= tol(cfg), (i, err)
+        for l in (0, cfg.L - 1):
+            got = as_f64(kvg[(k - 1) * cfg.L + l, slots[i]].cpu().numpy().view(np.uint16), cfg)
+            assert rel_l2(got[0], kvs[l][0]) <= tol(cfg) and rel_l2(got[1], kvs[l][1]) <= tol(cfg), (i, l)
+    del e
+    gc.collect()
+    torch.cuda.empty_cache()
