@@ -124,6 +124,25 @@ def _counter_per_dispatch(d, counter, prefix):
     return [float(v) for _, v in rows]
 
 
+def _profile_commands(a):
+    """The command sequence that produces the databases this summary reads (directory names
+    taken from the arguments)."""
+    b = "python3 -u bench.py --steps 1 --warmup 0 --no-cpu-baseline"
+    cmds = [f"rocprofv3 --kernel-trace --stats -d {a.trace_dir} -o c2 -- {b} > {a.bench_log} 2>&1",
+            f"rocprofv3 --pmc FETCH_SIZE -d {a.fetch_dir} -o c2 -- {b}",
+            f"rocprofv3 --pmc WRITE_SIZE -d {a.write_dir} -o c2 -- {b}"]
+    if a.mfma_dir:
+        cmds.append(f"rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 -d {a.mfma_dir} -o c2 -- {b}")
+    cmds += [f"rocprofv3 --pmc FETCH_SIZE -d {a.copy_fetch_dir} -o copy -- python3 -u bench.py --copy-calibration",
+             f"rocprofv3 --pmc WRITE_SIZE -d {a.copy_write_dir} -o copy -- python3 -u bench.py --copy-calibration"]
+    summ = (f"python3 bench.py --pmc-summary --workload {a.workload} --bench-log {a.bench_log} "
+            f"--trace-dir {a.trace_dir} --fetch-dir {a.fetch_dir} --write-dir {a.write_dir} "
+            f"--copy-fetch-dir {a.copy_fetch_dir} --copy-write-dir {a.copy_write_dir}")
+    if a.mfma_dir:
+        summ += f" --mfma-dir {a.mfma_dir}"
+    return cmds + [summ + (f" --out {a.out}" if a.out else "")]
+
+
 def pmc_summary(a):
     """Digest of the rocprofv3 runs of one benchmark command: the loop-block kernel's
     per-launch duration (kernel trace) and HBM bytes (FETCH_SIZE / WRITE_SIZE runs, scaled
@@ -159,7 +178,8 @@ def pmc_summary(a):
            "trace_us_per_launch": round(mean(dur[sl]), 2), "event_us_per_launch": ev_us}
     out = [f"# k_mega (ls_loop_step) on workload {a.workload}: duration and HBM traffic per launch", "",
            "Commands (repo root, MI355X, one GPU), in this order:", ""]
-    out += [f"    {c}" for c in a.commands]
+    cmds = a.commands or _profile_commands(a)
+    out += [f"    {c}" for c in cmds]
     out += ["", f"Timed region: launches {nb}..{nb + nt - 1} of the loop-block kernel (the {nb} before it are "
             "the untimed prefill/warmup); the decode is deterministic, so every run makes the same launches.", "",
             "| quantity | value |", "|---|---|",
@@ -177,6 +197,23 @@ def pmc_summary(a):
             f"| bench line | {bench_line['value']} {bench_line['unit']}, frac {bench_line['roofline']['frac']} |",
             "", "All kernels of the kernel-trace run (rocprofv3 top_kernels; prefill and decode):", "",
             "| kernel | calls | total us | avg us | % |", "|---|---|---|---|---|"]
+    if a.mfma_dir:
+        # matrix-core use of the same launches: MfmaUtil (busy cycles of the MFMA units, % of
+        # all SIMDs' cycles) and MfmaFlopsBF16 (512 flops per bf16 MFMA op counted), both
+        # rocprofv3 derived counters; issued flops include the zero rows of tiles with M < 16
+        mu = _counter_per_dispatch(a.mfma_dir, "MfmaUtil", LOOP_KERNEL)
+        mf = _counter_per_dispatch(a.mfma_dir, "MfmaFlopsBF16", LOOP_KERNEL)
+        for name, v in (("MfmaUtil run", mu), ("MfmaFlopsBF16 run", mf)):
+            if len(v) != nb + nt:
+                raise SystemExit(f"{name}: {len(v)} loop-block launches, the bench log says {nb} + {nt}")
+        util, flops = mean(mu[sl]), mean(mf[sl])
+        tflops = flops / (mean(dur[sl]) * 1e-6) / 1e12
+        rec.update({"mfma_util_percent": round(util, 3), "mfma_flops_per_launch": round(flops),
+                    "mfma_tflops": round(tflops, 2)})
+        at = next(i for i, x in enumerate(out) if x.startswith("| bench line |"))
+        out[at:at] = [f"| MFMA busy (MfmaUtil), timed launches | {util:.2f} % |",
+                      f"| MFMA flops issued per launch (MfmaFlopsBF16) | {flops / 1e12:.3f} T |",
+                      f"| MFMA rate issued / bf16 dense peak | {tflops:.1f} of 2500 TFLOP/s ({tflops / 2500:.4f}) |"]
     for name, calls, tot, avg, pct in db.execute(
             "select name, total_calls, total_duration, average, percentage from top_kernels"):
         out.append(f"| `{name[:90]}` | {calls} | {tot:.0f} | {avg:.1f} | {pct:.2f} |")
@@ -220,6 +257,7 @@ def main():
     ap.add_argument("--write-dir")
     ap.add_argument("--copy-fetch-dir")
     ap.add_argument("--copy-write-dir")
+    ap.add_argument("--mfma-dir", help="rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 run of the same command")
     ap.add_argument("--out")
     ap.add_argument("--commands", nargs="*", default=[])
     args = ap.parse_args()
@@ -307,6 +345,10 @@ def main():
                      "launches": n_calls},
         "decode_stats": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in st.items()},
     }
+    if traffic and "mfma_util_percent" in traffic:
+        # matrix-core use of the same kernel from the committed counter summary
+        out["roofline"]["mfma_util_percent"] = traffic["mfma_util_percent"]
+        out["roofline"]["mfma_tflops_issued"] = traffic["mfma_tflops"]
     if not args.no_cpu_baseline:
         print("[bench] CPU reference baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, dec, w)
