@@ -2,29 +2,31 @@
 // the shared block B applied once to every branch row; ls_prelude: embedding + prelude
 // layers; ls_readout: coda layers + final norm + LM head).
 //
-// One cooperative launch of resident 384-thread workgroups (one or more per CU).  Each
-// workgroup owns a static share of every projection's 16-output-feature tiles (dealt
-// round-robin across the phases of the call, so every workgroup streams about the same
-// bytes) and of the attention units.  Its six waves are specialised:
+// One cooperative launch of resident 448-thread workgroups (one per CU for the model shapes
+// here).  Each workgroup owns a static share of every projection's 16-output-feature tiles
+// (dealt round-robin across the phases of the call, so every workgroup streams about the same
+// bytes) and of the attention units.  Its seven waves are specialised:
 //   * 2 producer waves walk the workgroup's weight-slab sequence (slab = 16 rows x 512 bytes)
 //     across all phases and layers and copy whole slabs straight into an LDS ring with
 //     global_load_lds_dwordx4.  Weights never depend on activations, so producers never wait
 //     on other workgroups: HBM keeps streaming while consumers wait on dependencies.
-//   * 4 consumer waves wait on the dependency counters of exactly the producers they need,
-//     stage the activation columns (RMSNorm applied on the fly) in LDS, run 16x16 MFMAs
-//     from the ring (A = weights) and the staged activations (B), reduce the four consumer
-//     partials of each tile in fixed order, apply the fused epilogue (rotary embedding + KV
-//     write, residual add + per-tile sum of squares, SwiGLU, or a plain store) and bump the
-//     counters their consumers poll.  Between the QKV and O projections they run attention:
-//     one wave per (depth group, head, 64-key unit of the shared prefix), with the rows of
-//     one depth group sharing the prefix keys; the last unit of a (group, head) to finish
-//     merges the partials with the log-sum-exp rule.
+//   * 4 consumer waves wait for their inputs (polling the data itself where it is filled
+//     with a NaN pattern beforehand, else the producing tiles' counters), stage the
+//     activation columns (RMSNorm applied on the fly) in LDS, run 16x16 MFMAs from the ring
+//     (A = weights) and the staged activations (B), and post their partial tile sums to LDS.
+//     Between the QKV and O projections they run attention: one wave per (depth group, head,
+//     unit of the shared prefix's keys), with the rows of one depth group sharing the prefix
+//     keys; the last unit of a (group, head) to finish merges the partials with the
+//     log-sum-exp rule.
+//   * 1 epilogue wave sums each tile's four partials in fixed order and applies the fused
+//     epilogue (rotary embedding + q and KV stores, residual add + per-tile sum of squares,
+//     SwiGLU, or the logits store), then signals the tile where its readers use counters.
 // Every tile is reduced over its full K inside one workgroup, so there are no cross-workgroup
 // partial sums on the weight path.  Progress is guaranteed because work only waits on earlier
-// phases and all workgroups are co-resident.
+// phases and all workgroups are co-resident; every wait is bounded.
 //
 // Cross-XCD visibility without L2 maintenance: values handed between workgroups are stored and
-// loaded with agent-scope coherent accesses; a producer of such values drains its stores
+// loaded with agent-scope coherent accesses; a producer of counted values drains its stores
 // before bumping a counter, and consumers load them only after observing the counter.
 #include <algorithm>
 
