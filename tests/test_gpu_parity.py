@@ -253,3 +253,28 @@ def test_descriptor_errors_are_reported_not_faulted():
     # host-side capacity checks
     with pytest.raises(L.LoopSpecError):
         e.loop_step(e.rows(list(range(40)), [0] * 40, [1] * 40, 0, [[]] * 40, C.c_void_p(fin_t.data_ptr())))
+
+
+@pytest.mark.parametrize("bad", ["fin_slot", "ancestor_slot", "position"])
+def test_bad_key_slots_are_reported_not_faulted(bad):
+    """A prefix slot or an ancestor slot outside the cache, or a position that does not match
+    the key count, is skipped by the kernels and reported through the error word; the call
+    never reads outside the cache."""
+    cfg = configs.TINY
+    S = 64
+    w = weights.make_weights(cfg, seed=0)
+    e = _engine(cfg, w, S)
+    from looped_transformer_self_amd import _lib as L
+    fin = [0, 1, 2, 3]
+    anc = [[], [10]]
+    pos = [4, 5]
+    if bad == "fin_slot":
+        fin[2] = S + 7
+    elif bad == "ancestor_slot":
+        anc[1] = [-5]
+    else:
+        pos[1] = 9
+    fin_t = _fin_table(fin, S)
+    rows = e.rows([20, 21], pos, [1, 2], len(fin), anc, C.c_void_p(fin_t.data_ptr()))
+    e.loop_step(rows)
+    assert e.sync_status() == L.LS_ERR_INVALID
