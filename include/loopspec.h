@@ -198,12 +198,14 @@ ls_status ls_readout(ls_model *m, const ls_rows *rows, const float *H, const ls_
                      const ls_kv *kv, hipStream_t stream);
 
 /* Lossless verification jobs (section 2.2-2.3), one integer pass over V per job; results
- * are bit-identical for identical inputs.  jobs: device [n_jobs]; probs: fp32
+ * are bit-identical for identical inputs.  jobs: [n_jobs]; probs: fp32
  * [n_prob_rows][V], each row a probability vector (entries in [0, 1], sum <= ~1; a row whose
- * fixed-point mass reaches 2^41 is rejected); cands: device int32 [n_cands] (VERIFY_COPY
- * reads cands[cand_off .. cand_off + n_cand), n_cand <= 16); uniforms: device uint32
- * [n_jobs][24]; out: [n_jobs], device memory or pinned host memory (hipHostMalloc), which the
- * kernel writes directly: complete once the stream is synchronised.  A job with an
+ * fixed-point mass reaches 2^41 is rejected); cands: int32 [n_cands] (VERIFY_COPY reads
+ * cands[cand_off .. cand_off + n_cand), n_cand <= 16); uniforms: uint32 [n_jobs][24]; out:
+ * [n_jobs].  jobs, cands, uniforms and out may be device memory or pinned host memory
+ * (hipHostMalloc): the kernel reads each job, its uniforms and candidates once and writes
+ * its result directly; out is complete once the stream is synchronised; the caller keeps
+ * host inputs unchanged until then.  A job with an
  * out-of-range row, token or candidate yields token -1, outcome 0 and LS_ERR_INVALID in the
  * error word. */
 ls_status ls_verify(ls_model *m, const ls_verify_job *jobs, int n_jobs, const float *probs, int n_prob_rows,

@@ -194,8 +194,17 @@ __global__ __launch_bounds__(VT) void k_verify(const ls_verify_job* jobs, const 
                                               const int32_t* cands, int n_cands, const uint32_t* uniforms,
                                               ls_verify_out* out, int* err) {
   __shared__ Scratch sc;
-  const ls_verify_job jb = jobs[blockIdx.x];
-  const uint32_t* u = uniforms + (size_t)blockIdx.x * LS_UNIFORMS_PER_JOB;
+  // the job and its uniforms are read once, into LDS (they may live in pinned host memory,
+  // where every access crosses the bus)
+  __shared__ int32_t s_job[sizeof(ls_verify_job) / 4];
+  __shared__ uint32_t s_u[LS_UNIFORMS_PER_JOB];
+  if (threadIdx.x < sizeof(ls_verify_job) / 4)
+    s_job[threadIdx.x] = reinterpret_cast<const int32_t*>(jobs + blockIdx.x)[threadIdx.x];
+  else if (threadIdx.x >= 64 && threadIdx.x < 64 + LS_UNIFORMS_PER_JOB)
+    s_u[threadIdx.x - 64] = uniforms[(size_t)blockIdx.x * LS_UNIFORMS_PER_JOB + threadIdx.x - 64];
+  __syncthreads();
+  const ls_verify_job jb = *reinterpret_cast<const ls_verify_job*>(s_job);
+  const uint32_t* u = s_u;
   ls_verify_out o = {-1, 0, 0, -1};
   const Range rg(V);
 

@@ -198,6 +198,12 @@ class Engine:
         # verification results: pinned host memory that the verify kernel writes directly, so
         # reading them needs no device-to-host copy after the stream synchronisation
         self.vout_host = torch.zeros(max_jobs * 4, dtype=torch.int32, pin_memory=True)
+        # verification inputs (jobs, uniforms, copy candidates) in pinned host memory that the
+        # kernel reads once per job: no host-to-device copy ahead of it.  verify() returns only
+        # after the stream has synchronised, so the next call may overwrite them.
+        self._vin_jobs = max_jobs
+        self.vin_host = torch.zeros(max_jobs * (10 + 24 + 16), dtype=torch.int32, pin_memory=True)
+        self.vin_np = self.vin_host.numpy()
         self.prof = None          # list of (start event, end event, row metadata) when profiling
         self.n_loop_calls = 0     # ls_loop_step launches with at least one row, since creation
 
@@ -326,14 +332,19 @@ class Engine:
         """jobs: int32 array [n][10]; uniforms: uint32 [n][24]; cands: int32 array or None.
         Returns an int32 numpy array [n][4] (token, outcome, gate, aux) after a stream sync."""
         n = len(jobs)
-        arrays = [np.ascontiguousarray(jobs, np.int32).ravel(), np.ascontiguousarray(uniforms, np.uint32).ravel()]
-        if cands is not None and len(cands):
-            arrays.append(np.asarray(cands, np.int32))
-        ptrs, keep = self.up.pack(arrays)
-        cptr = ptrs[2] if len(ptrs) > 2 else C.c_void_p(0)
         ncand = len(cands) if cands is not None else 0
-        L.check(L.lib.ls_verify(self.h, ptrs[0], n, _ptr(self.probs), self.prob_rows, cptr, ncand, ptrs[1],
-                                _ptr(self.vout_host), self.stream_ptr()), "ls_verify")
+        if n > self._vin_jobs or ncand > 16 * self._vin_jobs:
+            raise ValueError("more verification jobs or candidates than the engine was built for")
+        mj = self._vin_jobs
+        vin, base = self.vin_np, self.vin_host.data_ptr()
+        vin[:10 * n] = np.asarray(jobs, np.int32).ravel()
+        vin[10 * mj:10 * mj + 24 * n] = np.asarray(uniforms, np.uint32).ravel().view(np.int32)
+        if ncand:
+            vin[34 * mj:34 * mj + ncand] = np.asarray(cands, np.int32)
+        L.check(L.lib.ls_verify(self.h, C.c_void_p(base), n, _ptr(self.probs), self.prob_rows,
+                                C.c_void_p(base + 4 * 34 * mj) if ncand else C.c_void_p(0), ncand,
+                                C.c_void_p(base + 4 * 10 * mj), _ptr(self.vout_host), self.stream_ptr()),
+                "ls_verify")
         torch.cuda.current_stream().synchronize()
         return self.vout_host[:4 * n].numpy().reshape(n, 4).copy()
 
