@@ -114,18 +114,20 @@ def _check_dist(pg, lg_ref, greedy, T, top_p, cfg):
 
 @pytest.mark.parametrize("cfg", SMALL_CFGS, ids=lambda c: c.name)
 @pytest.mark.parametrize("mode", ["greedy", "sample"])
-def test_readout_parity(cfg, mode):
-    print(f"[readout] {cfg.name} {mode}", flush=True)
-    S = 300
+@pytest.mark.parametrize("M", [7, 37])
+def test_readout_parity(cfg, mode, M):
+    """7 rows in one launch; 37 rows in launches of 16, 16 and 5 rows (the row check runs with
+    the first)."""
+    print(f"[readout] {cfg.name} {mode} M={M}", flush=True)
+    S = max(300, 260 + 4 * M + 8)
     greedy, T, top_p = (True, 1.0, 1.0) if mode == "greedy" else (False, 0.8, 0.9)
     w = weights.make_weights(cfg, seed=0)
-    e = _engine(cfg, w, S)
+    e = _engine(cfg, w, S, max_rows=max(32, M))
     m = Model(cfg, w)
     nD = len(cfg.readout_depths)
     coda = _fill_cache(e, cfg, "coda", nD * cfg.L_coda, S, seed=21) if cfg.L_coda else None
     H0 = inputs.hidden_rows(S, cfg.d, seed=22)
     e.H.copy_(torch.from_numpy(H0))
-    M = 7
     rng = np.random.Generator(np.random.PCG64(23))
     fin, slots, anc, pos, depth = branch_rows(M, 260, lambda i: i % nD, rng, S)
     fin_t = _fin_table(fin, S)
