@@ -253,6 +253,9 @@ struct LdsPlan {
   int NS, XC, nred;
 };
 constexpr int LDS_BUDGET = 160 * 1024 - 512;
+#ifndef LS_GU_AVOID
+#define LS_GU_AVOID 1
+#endif
 __host__ __device__ inline size_t x_region_bytes(int M, int esz, int XC) { return (size_t)M * (XC + 16 / esz) * esz; }
 // Per-launch row tables in LDS: rows by group [M], depth histogram [64], group offsets and
 // count [65], and copies of the rows' slot [M], depth [M] and ancestor offsets [M + 1].
@@ -412,6 +415,38 @@ LS_DEV Share share_of(int n, int deal, int G, int b) {
   s.first = ((b - deal) % G + G) % G;
   s.count = s.first < n ? (n - 1 - s.first) / G + 1 : 0;
   return s;
+}
+
+// A phase's tiles for workgroup b, in order.  Round-robin (tile first + i*G), except that the
+// gate/up phase deals its tiles beyond the last full round only to workgroups that will own
+// no down-projection tile (the down phase is dealt next, from deal + n): otherwise a quarter of
+// the workgroups would stream three gate/up tiles and then a 2.8x larger down tile while
+// others sit idle.
+struct PhaseShare {
+  int first, count;   // round-robin part: tiles first + i*G, i < rounds
+  int rounds;
+  int rem0, nN, kN;   // extra tiles rem0 + kN + m*nN (m >= 0) of a workgroup outside the down set
+  LS_DEV int tile(int i, int G) const { return i < rounds ? first + i * G : rem0 + kN + (i - rounds) * nN; }
+};
+LS_DEV PhaseShare phase_share(const MegaArgs& a, int ph, int n, int deal, int G, int b) {
+  PhaseShare p;
+  const Share s = share_of(n, deal, G, b);
+  p.first = s.first;
+  p.count = s.count;
+  p.rounds = s.count;
+  p.rem0 = 0; p.nN = 1; p.kN = 0;
+  const int nd = a.d / 16;                                  // down-projection tiles
+  if (LS_GU_AVOID && ph == PH_GU && nd < G && n % G != 0) {
+    const int full = n / G;                                 // complete rounds for everyone
+    const int jd = ((s.first - n) % G + G) % G;             // this workgroup's index in the down deal
+    p.rounds = full;
+    p.rem0 = full * G;
+    p.nN = G - nd;
+    p.kN = jd - nd;
+    const int rem = n - full * G;
+    p.count = full + (jd >= nd && p.kN < rem ? (rem - 1 - p.kN) / p.nN + 1 : 0);
+  }
+  return p;
 }
 
 // Wait for this wave's LDS (and scalar memory) operations only.
@@ -1467,7 +1502,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
                       Producer<T>* pr, Consumer<T, MT>* co, ConsBar* cb) {
   const int G = gridDim.x, b = blockIdx.x;
   const PhaseGeo g = phase_geo<T>(a, ph);
-  const Share sh = share_of(g.n_tiles, deal, G, b);
+  const PhaseShare sh = phase_share(a, ph, g.n_tiles, deal, G, b);
   deal = (deal + g.n_tiles) % G;
   if (sh.count == 0) return;
   const LayerW lw = ph == PH_HEAD ? LayerW{} : a.layers[l];
@@ -1511,7 +1546,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
   // for all of the workgroup's tiles; with several, every tile re-stages its chunks.
   const bool restage = nchunk > 1;
   for (int i = 0; i < sh.count; ++i) {
-    const int t = sh.first + i * G;
+    const int t = sh.tile(i, G);
     f32x4_t acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1589,7 +1624,7 @@ LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int p
   const int G = gridDim.x, b = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const PhaseGeo g = phase_geo<T>(a, ph);
-  const Share sh = share_of(g.n_tiles, deal, G, b);
+  const PhaseShare sh = phase_share(a, ph, g.n_tiles, deal, G, b);
   deal = (deal + g.n_tiles) % G;
   const bool pref = (ph == PH_O || ph == PH_DOWN) && had_tiles && sh.count > 0 && a.M <= 16;
   // O / DOWN counts are waited for only when the next normalised phase cannot poll its input
@@ -1597,11 +1632,11 @@ LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int p
   const bool next_polls = a.d <= s.XC && a.d <= FUSE_MAX_K;
   const bool signals = ph != PH_HEAD && !((ph == PH_O || ph == PH_DOWN) && next_polls);
   float pre[4] = {0.f, 0.f, 0.f, 0.f};
-  if (pref) residual_load(a, s, ph, l, sh.first, 0, lane, pre);
+  if (pref) residual_load(a, s, ph, l, sh.tile(0, G), 0, lane, pre);
   had_tiles = sh.count > 0;
   int pend = 0;                            // first of this phase's tiles not yet signalled
   for (int i = 0; i < sh.count; ++i) {
-    const int t = sh.first + i * G;
+    const int t = sh.tile(i, G);
     const int q = seq++;
     float* buf = s.red + (size_t)(q % s.nred) * NCONS * a.M * 16;
     if (lane == 0) {
@@ -1630,7 +1665,7 @@ LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int p
     if (!next_ready) {
       drain();
       if (lane == 0)
-        for (int k = pend; k <= i; ++k) tile_signal(a, cl, ph, l, sh.first + k * G, s.XC);
+        for (int k = pend; k <= i; ++k) tile_signal(a, cl, ph, l, sh.tile(k, G), s.XC);
       pend = i + 1;
     }
   }
