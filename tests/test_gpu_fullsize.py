@@ -181,7 +181,8 @@ def test_loop_step_full_size_many_rows(full_model, M):
 def test_loop_step_full_size_long_prefix(full_model):
     """Huginn-3.5B shape with a 4800-key finished prefix: 55 heads x 75 key chunks give every
     consumer wave several chunks, so each attention unit walks several 64-key sub-units
-    (the last unit a ragged number of them) before its partial is merged."""
+    (the last unit a ragged number of them) before its partial is merged; rows sharing a
+    depth walk the same units one after another (groups of 2, 3 and 1 rows)."""
     key, cfg, w, _, _, _ = full_model
     if key != "C4":
         pytest.skip("the long-prefix unit layout needs many heads and keys (Huginn shape)")
@@ -189,7 +190,7 @@ def test_loop_step_full_size_long_prefix(full_model):
     n_fin = 4800
     S = n_fin + 64
     e = Engine(cfg, w, slot_capacity=S, max_rows=16, max_keys=S, max_jobs=16, prob_rows=16)
-    depths = [cfg.R, 2, 1]
+    depths = [cfg.R, cfg.R, 2, 2, 2, 1]                  # depth groups of 2, 3 and 1 rows
     fin, slots, anc, pos = _rows(cfg, n_fin, S, depths, seed=61)
     keyset = sorted(set(fin) | {x for a in anc for x in a})
     blocks = sorted({(k - 1) * cfg.L + l for k in depths for l in range(cfg.L)})
