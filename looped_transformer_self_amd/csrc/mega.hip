@@ -1792,6 +1792,12 @@ __global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, c
   }
 }
 
+hipError_t launch_validate(const ValidateArgs& v, hipStream_t s) {
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)std::max(1, (v.n + 255) / 256)), dim3(256), 0, s, nullptr, 0LL, nullptr,
+                     nullptr, nullptr, 0, 0, nullptr, 0LL, nullptr, 0LL, nullptr, 0LL, v);
+  return hipGetLastError();
+}
+
 template <typename T, bool LONG>
 static const void* pick_tl(int mt, bool loop) {
   if (loop) {

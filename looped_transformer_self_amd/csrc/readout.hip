@@ -270,6 +270,101 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
   }
 }
 
+// ---- LM head without coda layers: logits[m][n] = RMSNorm(H[hidx[m]]) . E[n] -----------------
+// A plain streaming kernel (no persistent workgroups): one wave per 16 vocabulary rows, 4 waves
+// per workgroup, many workgroups per CU, so the 16-row weight tiles of the whole vocabulary
+// are in flight at once.  Each workgroup first normalises the M <= 16 rows (final RMSNorm,
+// gains g) into LDS, rounded to bf16 like every GEMM input; a wave then runs
+// v_mfma_f32_16x16x32_bf16 with A = 16 embedding rows read straight from memory (lane l:
+// row l%16, 8 columns at 8*(l/16)) and B = the normalised rows from LDS, its loads issued
+// eight k-steps ahead of the multiplies.
+constexpr int HEAD_WAVES = 4;
+
+__global__ __launch_bounds__(64 * HEAD_WAVES) void k_head(const float* H, const int32_t* hidx, int M, int d, int V,
+                                                         const uint16_t* emb, const float* g, float eps,
+                                                         float* logits, int ldo) {
+  extern __shared__ __attribute__((aligned(16))) char hsm[];
+  const int xs = d + 8;                                   // LDS row stride (elements)
+  uint16_t* X = reinterpret_cast<uint16_t*>(hsm);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // normalised rows: wave w takes rows w, w + 4, ...; rejected rows are zero
+  for (int m = w; m < M; m += HEAD_WAVES) {
+    uint16_t* xr = X + (size_t)m * xs;
+    const int hr = hidx[m];
+    if (hr < 0) {
+      for (int k = 8 * lane; k < d; k += 512) *reinterpret_cast<uint4*>(xr + k) = make_uint4(0, 0, 0, 0);
+      continue;
+    }
+    const float* row = H + (size_t)hr * d;
+    float ss = 0.f;
+    for (int k = 4 * lane; k < d; k += 256) {
+      const float4 v = *reinterpret_cast<const float4*>(row + k);
+      ss += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+    }
+    const float ri = 1.0f / sqrtf(wave_sum(ss) / (float)d + eps);
+    for (int k = 4 * lane; k < d; k += 256) {
+      const float4 v = *reinterpret_cast<const float4*>(row + k);
+      const float4 gg = *reinterpret_cast<const float4*>(g + k);
+      const unsigned lo = (unsigned)f2bf(v.x * ri * gg.x) | ((unsigned)f2bf(v.y * ri * gg.y) << 16);
+      const unsigned hi = (unsigned)f2bf(v.z * ri * gg.z) | ((unsigned)f2bf(v.w * ri * gg.w) << 16);
+      *reinterpret_cast<uint2*>(xr + k) = make_uint2(lo, hi);
+    }
+  }
+  __syncthreads();
+  const int tile = blockIdx.x * HEAD_WAVES + w;
+  const int n0 = tile * 16;
+  if (n0 >= V) return;
+  const int r = lane & 15, kq = lane >> 4;
+  const uint16_t* arow = emb + (size_t)min(n0 + r, V - 1) * d + 8 * kq;   // rows past V: any valid row
+  const uint16_t* brow = X + (size_t)min(r, M - 1) * xs + 8 * kq;   // rows m >= M multiply zeros
+  const bool live = r < M;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int B8 = 8;                                   // k-steps of 32 per batch
+  u32x4_t wa[B8], wb[B8];
+#pragma unroll
+  for (int u = 0; u < B8; ++u) wa[u] = *reinterpret_cast<const u32x4_t*>(arow + 32 * u);
+  for (int kb = 0; kb < d; kb += 64 * B8) {
+    const bool more = kb + 32 * B8 < d;
+#pragma unroll
+    for (int u = 0; u < B8; ++u)
+      if (more) wb[u] = *reinterpret_cast<const u32x4_t*>(arow + kb + 32 * (B8 + u));
+#pragma unroll
+    for (int u = 0; u < B8; ++u) {
+      u32x4_t xv = *reinterpret_cast<const u32x4_t*>(brow + kb + 32 * u);
+      if (!live) xv = u32x4_t{0u, 0u, 0u, 0u};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[u]), __builtin_bit_cast(bf16x8_t, xv),
+                                                    acc, 0, 0, 0);
+    }
+    if (!more) break;
+    const bool more2 = kb + 64 * B8 < d;
+#pragma unroll
+    for (int u = 0; u < B8; ++u)
+      if (more2) wa[u] = *reinterpret_cast<const u32x4_t*>(arow + kb + 64 * B8 + 32 * u);
+#pragma unroll
+    for (int u = 0; u < B8; ++u) {
+      u32x4_t xv = *reinterpret_cast<const u32x4_t*>(brow + kb + 32 * (B8 + u));
+      if (!live) xv = u32x4_t{0u, 0u, 0u, 0u};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wb[u]), __builtin_bit_cast(bf16x8_t, xv),
+                                                    acc, 0, 0, 0);
+    }
+  }
+  // lane l holds rows n = 4*(l/16) + j of the tile for activation row m = l%16
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 4 * kq + j;
+    if (r < M && n < V) logits[(size_t)r * ldo + n] = acc[j];
+  }
+}
+
+size_t head_smem_bytes(int M, int d) { return (size_t)M * (d + 8) * 2; }
+
+void launch_head(const float* H, const int32_t* hidx, int M, int d, int V, const void* emb, const float* g, float eps,
+                 float* logits, int ldo, hipStream_t s) {
+  const int tiles = (V + 15) / 16;
+  hipLaunchKernelGGL(k_head, dim3((tiles + HEAD_WAVES - 1) / HEAD_WAVES), dim3(64 * HEAD_WAVES), head_smem_bytes(M, d), s,
+                     H, hidx, M, d, V, static_cast<const uint16_t*>(emb), g, eps, logits, ldo);
+}
+
 void launch_dist(const float* logits, int M, int V, int greedy, float T, float top_p, float* probs,
                  const int32_t* out_rows, int n_prob_rows, int32_t* argmax, int* err, hipStream_t s) {
   hipLaunchKernelGGL(k_dist, dim3(M), dim3(DIST_THREADS), 0, s, logits, V, greedy, T, top_p, probs, out_rows, n_prob_rows,
