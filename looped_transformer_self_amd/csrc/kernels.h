@@ -72,6 +72,9 @@ void launch_fill_i32(int32_t* p, int n, int v, hipStream_t s);
 // multiple of 256.
 void launch_head(const float* H, const int32_t* hidx, int M, int d, int V, const void* emb, const float* g, float eps,
                  float* logits, int ldo, hipStream_t s);
+// P without prelude layers: row check and embedding gather into H[slot] (one kernel).
+hipError_t launch_embed(bool bf16, const ValidateArgs& v, const int32_t* tokens, const void* emb, int V, int d, float* H,
+                        hipStream_t s);
 // The row check alone (the prep kernel of a call without a persistent launch).
 hipError_t launch_validate(const ValidateArgs& v, hipStream_t s);
 void launch_dist(const float* logits, int M, int V, int greedy, float T, float top_p, float* probs,

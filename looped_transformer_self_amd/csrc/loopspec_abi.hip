@@ -312,6 +312,11 @@ ls_status ls_prelude(ls_model* m, const ls_rows* r, const int32_t* tokens, float
   if (m->d.L_pre && !kv->pre) return fail(LS_ERR_INVALID, "ls_prelude: prelude layers need kv->pre");
   if (r->n == 0) return LS_OK;
   const ls_model_desc& d = m->d;
+  if (!d.L_pre) {                                    // embedding rows only: one small kernel
+    hipError_t e = launch_embed(m->bf16(), validate_args(m, r, nullptr, 0, 0), tokens, m->emb, d.V, d.d, H, s);
+    if (e != hipSuccess) return fail(LS_ERR_HIP, "ls_prelude: embedding launch: %s", hipGetErrorString(e));
+    return LS_OK;
+  }
   st = run_mega(m, r, 0, r->n, H, m->slot_ok, m->tab_pre, d.L_pre, kv->pre, nullptr, 0, 0, 1, tokens, nullptr, nullptr,
                 nullptr, s, validate_args(m, r, nullptr, 0, 0));
   if (st) return st;

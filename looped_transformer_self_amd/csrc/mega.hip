@@ -1762,23 +1762,56 @@ __global__ __launch_bounds__(MEGA_THREADS) void k_mega(MegaArgs a) { mega_body<T
 template <typename T, int MT, bool LONG>
 __global__ __launch_bounds__(MEGA_THREADS) void k_mega_aux(MegaArgs a) { mega_body<T, MT, LONG>(a); }
 
+// The row check: a row whose slot, depth, ancestor range or position is out of contract gets
+// slot -1 in the checked copy and raises the error word.  Returns the checked slot.
+LS_DEV int check_row(const ValidateArgs& v, int i) {
+  const int sl = v.slot[i];
+  const int dp = v.dep ? v.dep[i] : v.dep_lo;
+  const int a0 = v.anc_off[i], a1 = v.anc_off[i + 1];
+  bool ok = sl >= 0 && sl < v.S && dp >= v.dep_lo && dp <= v.dep_hi && a0 >= 0 && a1 >= a0 && a1 - a0 <= v.max_anc;
+  if (ok && v.pos) ok = v.pos[i] == v.n_fin + (a1 - a0);
+  if (!ok) ls_flag(v.err, 1);
+  v.slot_ok[i] = ok ? sl : -1;
+  v.dep_ok[i] = ok ? dp : v.dep_lo;
+  v.row_ok[i] = ok ? i : -1;
+  return ok ? sl : -1;
+}
+
+// P of a model without prelude layers (eq. 1: the embedding row): one workgroup per row checks
+// the row and copies its token's embedding into H[slot] in fp32.
+template <typename T>
+__global__ __launch_bounds__(256) void k_embed(ValidateArgs v, const int32_t* tokens, const T* emb, int V, int d,
+                                               float* H) {
+  __shared__ int s_slot;
+  const int i = blockIdx.x;
+  if (threadIdx.x == 0) s_slot = check_row(v, i);
+  __syncthreads();
+  const int hr = s_slot;
+  if (hr < 0) return;
+  const int tok = tokens[i];
+  if (tok < 0 || tok >= V) {
+    if (threadIdx.x == 0) ls_flag(v.err, 1);
+    return;
+  }
+  for (int k = threadIdx.x; k < d; k += blockDim.x) H[(size_t)hr * d + k] = Elem<T>::load(emb + (size_t)tok * d + k);
+}
+
+hipError_t launch_embed(bool bf16, const ValidateArgs& v, const int32_t* tokens, const void* emb, int V, int d, float* H,
+                        hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(k_embed<uint16_t>, dim3(v.n), dim3(256), 0, s, v, tokens, (const uint16_t*)emb, V, d, H);
+  else
+    hipLaunchKernelGGL(k_embed<float>, dim3(v.n), dim3(256), 0, s, v, tokens, (const float*)emb, V, d, H);
+  return hipGetLastError();
+}
+
 // Set-up of one launch: counters to zero, this launch's polled buffers to SENT32, rotary
 // cos/sin of the rows' positions, and (first launch of a call) the row-descriptor check.
 __global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, const double* inv_freq, int M, int half,
                        unsigned* xs_fill, long long n_xs, unsigned* ys_fill, long long n_ys, unsigned* o_fill,
                        long long n_o, ValidateArgs v) {
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x, str = (long long)gridDim.x * blockDim.x;
-  for (long long i = tid; i < v.n; i += str) {
-    const int sl = v.slot[i];
-    const int dp = v.dep ? v.dep[i] : v.dep_lo;
-    const int a0 = v.anc_off[i], a1 = v.anc_off[i + 1];
-    bool ok = sl >= 0 && sl < v.S && dp >= v.dep_lo && dp <= v.dep_hi && a0 >= 0 && a1 >= a0 && a1 - a0 <= v.max_anc;
-    if (ok && v.pos) ok = v.pos[i] == v.n_fin + (a1 - a0);
-    if (!ok) ls_flag(v.err, 1);
-    v.slot_ok[i] = ok ? sl : -1;
-    v.dep_ok[i] = ok ? dp : v.dep_lo;
-    v.row_ok[i] = ok ? (int32_t)i : -1;
-  }
+  for (long long i = tid; i < v.n; i += str) check_row(v, (int)i);
   for (long long i = tid; i < n; i += str) cnt[i] = 0;
   for (long long i = tid; i < n_xs; i += str) xs_fill[i] = SENT32;
   for (long long i = tid; i < n_ys; i += str) ys_fill[i] = SENT32;
