@@ -212,7 +212,7 @@ def test_verify_bit_exact(V):
         assert tuple(int(v) for v in out[k, :3]) == want, (k, op, out[k], want)
 
 
-@pytest.mark.parametrize("cfg", [configs.TINY, configs.MINI_HUGINN], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.MINI_OURO, configs.MINI_HUGINN], ids=lambda c: c.name)
 def test_prelude_parity(cfg):
     print(f"[prelude] {cfg.name}", flush=True)
     S = 200
@@ -255,6 +255,33 @@ def test_descriptor_errors_are_reported_not_faulted():
     # host-side capacity checks
     with pytest.raises(L.LoopSpecError):
         e.loop_step(e.rows(list(range(40)), [0] * 40, [1] * 40, 0, [[]] * 40, C.c_void_p(fin_t.data_ptr())))
+
+
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.MINI_OURO, configs.MINI_HUGINN], ids=lambda c: c.name)
+@pytest.mark.parametrize("bad", ["token", "slot"])
+def test_prelude_bad_rows_are_reported_not_faulted(cfg, bad):
+    """A token outside the vocabulary or a slot outside the cache in a prelude call is reported
+    through the error word, with and without prelude layers; a good row of the same call still
+    gets its embedding row (checked where P is the embedding alone)."""
+    print(f"[prelude-bad] {cfg.name} {bad}", flush=True)
+    S = 64
+    w = weights.make_weights(cfg, seed=0)
+    e = _engine(cfg, w, S)
+    from looped_transformer_self_amd import _lib as L
+    m = Model(cfg, w)
+    fin = [0, 1, 2]
+    slots, toks = [5, 6], np.array([3, 4], np.int32)
+    if bad == "token":
+        toks[1] = cfg.V + 10
+    else:
+        slots[1] = S + 3
+    fin_t = _fin_table(fin, S)
+    rows = e.rows(slots, [3, 3], [0, 0], len(fin), [[], []], C.c_void_p(fin_t.data_ptr()), extra=[toks])
+    e.prelude(rows, rows.extra[0])
+    assert e.sync_status() == L.LS_ERR_INVALID
+    if not cfg.L_pre:
+        Hg = e.H.cpu().numpy()
+        assert rel_l2(Hg[5], m.r32(m.emb[3][None])[0]) <= tol(cfg)
 
 
 @pytest.mark.parametrize("bad", ["fin_slot", "ancestor_slot", "position"])
