@@ -113,14 +113,14 @@ def _check_dist(pg, lg_ref, greedy, T, top_p, cfg):
 
 
 @pytest.mark.parametrize("cfg", SMALL_CFGS, ids=lambda c: c.name)
-@pytest.mark.parametrize("mode", ["greedy", "sample"])
+@pytest.mark.parametrize("mode", ["greedy", "sample", "sample_t1"])
 @pytest.mark.parametrize("M", [7, 37])
 def test_readout_parity(cfg, mode, M):
     """7 rows in one launch; 37 rows in launches of 16, 16 and 5 rows (the row check runs with
     the first)."""
     print(f"[readout] {cfg.name} {mode} M={M}", flush=True)
     S = max(300, 260 + 4 * M + 8)
-    greedy, T, top_p = (True, 1.0, 1.0) if mode == "greedy" else (False, 0.8, 0.9)
+    greedy, T, top_p = {"greedy": (True, 1.0, 1.0), "sample": (False, 0.8, 0.9), "sample_t1": (False, 1.0, 0.9)}[mode]
     w = weights.make_weights(cfg, seed=0)
     e = _engine(cfg, w, S, max_rows=max(32, M))
     m = Model(cfg, w)
