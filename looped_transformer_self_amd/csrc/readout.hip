@@ -15,7 +15,7 @@
 namespace ls {
 
 constexpr int DIST_THREADS = 1024;
-constexpr int DIST_PT = 64;               // ids per thread: V <= 65536
+constexpr int DIST_PT_MAX = 64;           // ids per thread: V <= 65536
 constexpr int DIST_BINS = 2048;
 
 LS_DEV unsigned block_sum_u32(unsigned v, unsigned* red) {
@@ -67,7 +67,7 @@ LS_DEV void row_st(__amdgpu_buffer_rsrc_t r, int j, float v) {
 
 LS_DEV unsigned mass31(float p) { return (unsigned)(p * 2147483648.0f); }   // exact floor(p * 2^31), p in [0, 1]
 // The same value recomputed where it is needed: the radix rounds would otherwise keep all
-// DIST_PT masses live next to the probabilities (the compiler hoists them out of the rounds
+// PT masses live next to the probabilities (the compiler hoists them out of the rounds
 // loop), which spills.  Volatile assembly is not hoisted; v_cvt_u32_f32 truncates like the
 // conversion above.
 LS_DEV unsigned mass31_here(float p) {
@@ -76,6 +76,9 @@ LS_DEV unsigned mass31_here(float p) {
   return r;
 }
 
+// PT ids per thread (PT * DIST_THREADS >= V): the smallest multiple of 16 that covers the row,
+// so a vocabulary below 65536 runs no padding columns.
+template <int PT>
 __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int V, int greedy, float T, float top_p,
                                                       float* probs, const int32_t* out_rows, int n_prob_rows,
                                                       int32_t* argmax, int* err) {
@@ -90,11 +93,11 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
   __shared__ unsigned s_sel[2];
 
   // ids past V hold -inf logits: probability 0, mass 0, never kept
-  float x[DIST_PT];
+  float x[PT];
   {
     const __amdgpu_buffer_rsrc_t Rz = row_rsrc(z, V);
 #pragma unroll
-    for (int j = 0; j < DIST_PT; ++j) {
+    for (int j = 0; j < PT; ++j) {
       const float v = row_ld(Rz, j);
       x[j] = tid + DIST_THREADS * j < V ? v : -INFINITY;
     }
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
   float best = -INFINITY;
   int bi = 0x7fffffff;
 #pragma unroll
-  for (int j = 0; j < DIST_PT; ++j)
+  for (int j = 0; j < PT; ++j)
     if (x[j] > best) { best = x[j]; bi = tid + DIST_THREADS * j; }
   for (int o = 32; o > 0; o >>= 1) {
     const float ob = __shfl_xor(best, o, 64);
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
   const __amdgpu_buffer_rsrc_t Rp = row_rsrc(p, V);
   if (greedy) {
 #pragma unroll
-    for (int j = 0; j < DIST_PT; ++j) {
+    for (int j = 0; j < PT; ++j) {
       const int v = tid + DIST_THREADS * j;
       row_st(Rp, j, v == bi ? 1.0f : 0.0f);
     }
@@ -137,16 +140,16 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
   const float mx = best / T;
   float sacc = 0.f;
 #pragma unroll
-  for (int j = 0; j < DIST_PT; ++j) {
+  for (int j = 0; j < PT; ++j) {
     x[j] = __expf(x[j] / T - mx);
     sacc += x[j];
   }
   const float inv = 1.0f / block_sum(sacc, redf);
 #pragma unroll
-  for (int j = 0; j < DIST_PT; ++j) x[j] *= inv;
+  for (int j = 0; j < PT; ++j) x[j] *= inv;
   if (!(top_p < 1.0f)) {
 #pragma unroll
-    for (int j = 0; j < DIST_PT; ++j) {
+    for (int j = 0; j < PT; ++j) {
       const int v = tid + DIST_THREADS * j;
       row_st(Rp, j, x[j]);
     }
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
   // fixed-point masses and the top-p target
   unsigned zl = 0, kmin = 0xffffffffu, kmax = 0;
 #pragma unroll
-  for (int j = 0; j < DIST_PT; ++j) {
+  for (int j = 0; j < PT; ++j) {
     zl += mass31(x[j]);
     const unsigned k = __float_as_uint(x[j]);
     kmin = min(kmin, k);
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
     for (int b = tid; b < nb; b += DIST_THREADS) hist[b] = 0;
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < DIST_PT; ++j) {
+    for (int j = 0; j < PT; ++j) {
       const unsigned off = __float_as_uint(x[j]) - lo;       // keys below lo wrap to large offsets
       const unsigned ms = mass31_here(x[j]);
       if (ms && (width >= 32 || off < (1u << width))) atomicAdd(&hist[off >> shift], ms);   // zero masses add nothing
@@ -227,14 +230,14 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
   if (n_keep == 0) n_keep = 1;
   unsigned nt_local = 0;
 #pragma unroll
-  for (int j = 0; j < DIST_PT; ++j) nt_local += __float_as_uint(x[j]) == kstar;
+  for (int j = 0; j < PT; ++j) nt_local += __float_as_uint(x[j]) == kstar;
   const unsigned n_ties = block_sum_u32(nt_local, redu);
   const unsigned kept_ties = min(n_keep, n_ties);
   const double Zk = (double)above + (double)kept_ties * (double)Pk;
   const float scale = (float)(2147483648.0 / Zk);
   if (n_keep >= n_ties) {
 #pragma unroll
-    for (int j = 0; j < DIST_PT; ++j) {
+    for (int j = 0; j < PT; ++j) {
       const int v = tid + DIST_THREADS * j;
       row_st(Rp, j, __float_as_uint(x[j]) >= kstar ? x[j] * scale : 0.0f);
     }
@@ -243,11 +246,11 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
   // rare: more ties at kstar than are kept.  The row goes to the output first, then the ties
   // are ranked by id (column j, then thread) reading it back.
 #pragma unroll
-  for (int j = 0; j < DIST_PT; ++j)
+  for (int j = 0; j < PT; ++j)
     if (tid + DIST_THREADS * j < V) p[tid + DIST_THREADS * j] = x[j];
   __syncthreads();
   unsigned before = 0;                          // ties with smaller ids in earlier columns
-  for (int j = 0; j < DIST_PT; ++j) {
+  for (int j = 0; j < PT; ++j) {
     const int v = tid + DIST_THREADS * j;
     const float pv = v < V ? p[v] : 0.f;
     const bool tie = v < V && __float_as_uint(pv) == kstar;
@@ -367,7 +370,9 @@ void launch_head(const float* H, const int32_t* hidx, int M, int d, int V, const
 
 void launch_dist(const float* logits, int M, int V, int greedy, float T, float top_p, float* probs,
                  const int32_t* out_rows, int n_prob_rows, int32_t* argmax, int* err, hipStream_t s) {
-  hipLaunchKernelGGL(k_dist, dim3(M), dim3(DIST_THREADS), 0, s, logits, V, greedy, T, top_p, probs, out_rows, n_prob_rows,
+  const int cols = (V + DIST_THREADS - 1) / DIST_THREADS;
+  auto k = cols <= 16 ? k_dist<16> : cols <= 32 ? k_dist<32> : cols <= 48 ? k_dist<48> : k_dist<DIST_PT_MAX>;
+  hipLaunchKernelGGL(k, dim3(M), dim3(DIST_THREADS), 0, s, logits, V, greedy, T, top_p, probs, out_rows, n_prob_rows,
                      argmax, err);
 }
 
