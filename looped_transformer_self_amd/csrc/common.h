@@ -105,3 +105,25 @@ LS_DEV void ls_flag(int* err, int code) { atomicCAS(err, 0, code); }
 LS_DEV int key_slot(int j, int n_fin, const int32_t* fin, const int32_t* anc, int a0, int na, int self) {
   return j < n_fin ? fin[j] : (j < n_fin + na ? anc[a0 + (j - n_fin)] : self);
 }
+
+// The row check (VA is the launchers' ValidateArgs): a row whose slot, depth, ancestor range or
+// position is out of contract has checked slot -1.  row_slot only reads; check_row also writes
+// the checked copies and raises the error word.
+template <typename VA>
+LS_DEV int row_slot(const VA& v, int i) {
+  const int sl = v.slot[i];
+  const int dp = v.dep ? v.dep[i] : v.dep_lo;
+  const int a0 = v.anc_off[i], a1 = v.anc_off[i + 1];
+  bool ok = sl >= 0 && sl < v.S && dp >= v.dep_lo && dp <= v.dep_hi && a0 >= 0 && a1 >= a0 && a1 - a0 <= v.max_anc;
+  if (ok && v.pos) ok = v.pos[i] == v.n_fin + (a1 - a0);
+  return ok ? sl : -1;
+}
+template <typename VA>
+LS_DEV int check_row(const VA& v, int i) {
+  const int sl = row_slot(v, i);
+  if (sl < 0) ls_flag(v.err, 1);
+  v.slot_ok[i] = sl;
+  v.dep_ok[i] = sl >= 0 && v.dep ? v.dep[i] : v.dep_lo;
+  v.row_ok[i] = sl >= 0 ? i : -1;
+  return sl;
+}

@@ -68,15 +68,13 @@ int att_unit_keys(bool bf16);   // prefix keys per attention unit
 hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool loop_block, const ValidateArgs& v);
 
 void launch_fill_i32(int32_t* p, int n, int v, hipStream_t s);
-// LM head without coda layers (bf16 models): logits of 1 <= M <= 16 rows H[hidx[m]], d a
-// multiple of 256.
-void launch_head(const float* H, const int32_t* hidx, int M, int d, int V, const void* emb, const float* g, float eps,
-                 float* logits, int ldo, hipStream_t s);
+// LM head without coda layers (bf16 models): logits of rows i0 .. i0+M-1 (1 <= M <= 16) of the
+// call, H at their checked slots, d a multiple of 256; the kernel runs the row check itself.
+void launch_head(const float* H, const ValidateArgs& v, int i0, int M, int d, int V, const void* emb, const float* g,
+                 float eps, float* logits, int ldo, hipStream_t s);
 // P without prelude layers: row check and embedding gather into H[slot] (one kernel).
 hipError_t launch_embed(bool bf16, const ValidateArgs& v, const int32_t* tokens, const void* emb, int V, int d, float* H,
                         hipStream_t s);
-// The row check alone (the prep kernel of a call without a persistent launch).
-hipError_t launch_validate(const ValidateArgs& v, hipStream_t s);
 void launch_dist(const float* logits, int M, int V, int greedy, float T, float top_p, float* probs,
                  const int32_t* out_rows, int n_prob_rows, int32_t* argmax, int* err, hipStream_t s);
 void launch_verify(const void* jobs, int n_jobs, const float* probs, int V, int n_rows, const int32_t* cands, int n_cands,

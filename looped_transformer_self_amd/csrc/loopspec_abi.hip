@@ -352,12 +352,10 @@ ls_status ls_readout(ls_model* m, const ls_rows* r, const float* H, const ls_sam
   float* lg = logits ? logits : m->logits;
   const ValidateArgs v = validate_args(m, r, r->depth, 0, d.n_readout - 1), none{};
   if (!d.L_coda && m->bf16() && d.d % 256 == 0 && LS_HEAD_KERNEL) {
-    // no coda layers: the row check, then the streaming head kernel per 16 rows
-    hipError_t e = launch_validate(v, s);
-    if (e != hipSuccess) return fail(LS_ERR_HIP, "ls_readout: row check launch: %s", hipGetErrorString(e));
+    // no coda layers: the streaming head kernel per 16 rows, which checks its rows itself
     for (int i0 = 0; i0 < r->n; i0 += 16) {
       const int mc = std::min(16, r->n - i0);
-      launch_head(H, m->slot_ok + i0, mc, d.d, d.V, m->emb, m->g_final, d.norm_eps, lg + (size_t)i0 * d.V, d.V, s);
+      launch_head(H, v, i0, mc, d.d, d.V, m->emb, m->g_final, d.norm_eps, lg + (size_t)i0 * d.V, d.V, s);
     }
     launch_dist(lg, r->n, d.V, smp->greedy, smp->temperature, smp->top_p, probs, out_rows, n_prob_rows, argmax, m->err, s);
     return check_hip("ls_readout");

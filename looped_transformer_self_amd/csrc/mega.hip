@@ -1762,21 +1762,6 @@ __global__ __launch_bounds__(MEGA_THREADS) void k_mega(MegaArgs a) { mega_body<T
 template <typename T, int MT, bool LONG>
 __global__ __launch_bounds__(MEGA_THREADS) void k_mega_aux(MegaArgs a) { mega_body<T, MT, LONG>(a); }
 
-// The row check: a row whose slot, depth, ancestor range or position is out of contract gets
-// slot -1 in the checked copy and raises the error word.  Returns the checked slot.
-LS_DEV int check_row(const ValidateArgs& v, int i) {
-  const int sl = v.slot[i];
-  const int dp = v.dep ? v.dep[i] : v.dep_lo;
-  const int a0 = v.anc_off[i], a1 = v.anc_off[i + 1];
-  bool ok = sl >= 0 && sl < v.S && dp >= v.dep_lo && dp <= v.dep_hi && a0 >= 0 && a1 >= a0 && a1 - a0 <= v.max_anc;
-  if (ok && v.pos) ok = v.pos[i] == v.n_fin + (a1 - a0);
-  if (!ok) ls_flag(v.err, 1);
-  v.slot_ok[i] = ok ? sl : -1;
-  v.dep_ok[i] = ok ? dp : v.dep_lo;
-  v.row_ok[i] = ok ? i : -1;
-  return ok ? sl : -1;
-}
-
 // P of a model without prelude layers (eq. 1: the embedding row): one workgroup per row checks
 // the row and copies its token's embedding into H[slot] in fp32.
 template <typename T>
@@ -1823,12 +1808,6 @@ __global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, c
     rope[2 * i] = (float)cs;
     rope[2 * i + 1] = (float)sn;
   }
-}
-
-hipError_t launch_validate(const ValidateArgs& v, hipStream_t s) {
-  hipLaunchKernelGGL(k_prep, dim3((unsigned)std::max(1, (v.n + 255) / 256)), dim3(256), 0, s, nullptr, 0LL, nullptr,
-                     nullptr, nullptr, 0, 0, nullptr, 0LL, nullptr, 0LL, nullptr, 0LL, v);
-  return hipGetLastError();
 }
 
 template <typename T, bool LONG>

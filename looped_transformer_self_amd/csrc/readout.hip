@@ -273,7 +273,7 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
   }
 }
 
-// ---- LM head without coda layers: logits[m][n] = RMSNorm(H[hidx[m]]) . E[n] -----------------
+// ---- LM head without coda layers: logits[m][n] = RMSNorm(H[slot of row m]) . E[n] ------------
 // A plain streaming kernel (no persistent workgroups): one wave per 16 vocabulary rows, 4 waves
 // per workgroup, many workgroups per CU, so the 16-row weight tiles of the whole vocabulary
 // are in flight at once.  Each workgroup first normalises the M <= 16 rows (final RMSNorm,
@@ -283,17 +283,19 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
 // eight k-steps ahead of the multiplies.
 constexpr int HEAD_WAVES = 4;
 
-__global__ __launch_bounds__(64 * HEAD_WAVES) void k_head(const float* H, const int32_t* hidx, int M, int d, int V,
+__global__ __launch_bounds__(64 * HEAD_WAVES) void k_head(const float* H, ValidateArgs rc, int i0, int M, int d, int V,
                                                          const uint16_t* emb, const float* g, float eps,
                                                          float* logits, int ldo) {
   extern __shared__ __attribute__((aligned(16))) char hsm[];
   const int xs = d + 8;                                   // LDS row stride (elements)
   uint16_t* X = reinterpret_cast<uint16_t*>(hsm);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // normalised rows: wave w takes rows w, w + 4, ...; rejected rows are zero
+  // normalised rows: wave w takes rows w, w + 4, ...; each workgroup checks the rows itself
+  // (workgroup 0 records the check), rejected rows are zero
   for (int m = w; m < M; m += HEAD_WAVES) {
     uint16_t* xr = X + (size_t)m * xs;
-    const int hr = hidx[m];
+    const int hr = row_slot(rc, i0 + m);
+    if (blockIdx.x == 0 && lane == 0) check_row(rc, i0 + m);
     if (hr < 0) {
       for (int k = 8 * lane; k < d; k += 512) *reinterpret_cast<uint4*>(xr + k) = make_uint4(0, 0, 0, 0);
       continue;
@@ -361,11 +363,11 @@ __global__ __launch_bounds__(64 * HEAD_WAVES) void k_head(const float* H, const 
 
 size_t head_smem_bytes(int M, int d) { return (size_t)M * (d + 8) * 2; }
 
-void launch_head(const float* H, const int32_t* hidx, int M, int d, int V, const void* emb, const float* g, float eps,
-                 float* logits, int ldo, hipStream_t s) {
+void launch_head(const float* H, const ValidateArgs& v, int i0, int M, int d, int V, const void* emb, const float* g,
+                 float eps, float* logits, int ldo, hipStream_t s) {
   const int tiles = (V + 15) / 16;
   hipLaunchKernelGGL(k_head, dim3((tiles + HEAD_WAVES - 1) / HEAD_WAVES), dim3(64 * HEAD_WAVES), head_smem_bytes(M, d), s,
-                     H, hidx, M, d, V, static_cast<const uint16_t*>(emb), g, eps, logits, ldo);
+                     H, v, i0, M, d, V, static_cast<const uint16_t*>(emb), g, eps, logits, ldo);
 }
 
 void launch_dist(const float* logits, int M, int V, int greedy, float T, float top_p, float* probs,

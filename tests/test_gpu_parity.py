@@ -284,6 +284,28 @@ def test_prelude_bad_rows_are_reported_not_faulted(cfg, bad):
         assert rel_l2(Hg[5], m.r32(m.emb[3][None])[0]) <= tol(cfg)
 
 
+@pytest.mark.parametrize("cfg", [configs.MINI_OURO, configs.MINI_HUGINN], ids=lambda c: c.name)
+def test_readout_bad_rows_are_reported_not_faulted(cfg):
+    """A readout row with a slot outside the cache or a readout depth outside the model's list is
+    reported through the error word (the row check runs inside the LM-head kernel for models
+    without coda layers); the good row of the call still gets its logits."""
+    print(f"[readout-bad] {cfg.name}", flush=True)
+    S = 64
+    w = weights.make_weights(cfg, seed=0)
+    e = _engine(cfg, w, S)
+    from looped_transformer_self_amd import _lib as L
+    e.H.copy_(torch.from_numpy(inputs.hidden_rows(S, cfg.d, seed=5)))
+    fin_t = _fin_table([0, 1, 2], S)
+    nD = len(cfg.readout_depths)
+    for slots, depth in (([5, S + 2], [0, 0]), ([5, 6], [0, nD])):
+        rows = e.rows(slots, [3, 3], depth, 3, [[], []], C.c_void_p(fin_t.data_ptr()),
+                      extra=[np.arange(2, dtype=np.int32)])
+        lg = torch.zeros(2, cfg.V, device="cuda")
+        e.readout(rows, True, 1.0, 1.0, rows.extra[0], logits=lg)
+        assert e.sync_status() == L.LS_ERR_INVALID
+        assert np.all(np.isfinite(lg.cpu().numpy()[0])) and np.abs(lg.cpu().numpy()[0]).max() > 0
+
+
 @pytest.mark.parametrize("bad", ["fin_slot", "ancestor_slot", "position"])
 def test_bad_key_slots_are_reported_not_faulted(bad):
     """A prefix slot or an ancestor slot outside the cache, or a position that does not match
