@@ -1762,8 +1762,9 @@ __global__ __launch_bounds__(MEGA_THREADS) void k_mega(MegaArgs a) { mega_body<T
 template <typename T, int MT, bool LONG>
 __global__ __launch_bounds__(MEGA_THREADS) void k_mega_aux(MegaArgs a) { mega_body<T, MT, LONG>(a); }
 
-// P of a model without prelude layers (eq. 1: the embedding row): one workgroup per row checks
-// the row and copies its token's embedding into H[slot] in fp32.
+// P of a model without prelude layers (LoopSpec page, section 2.1, eq. 1; here P is the
+// embedding row alone): one workgroup per row checks the row and copies its token's embedding
+// into H[slot] in fp32.
 template <typename T>
 __global__ __launch_bounds__(256) void k_embed(ValidateArgs v, const int32_t* tokens, const T* emb, int V, int d,
                                                float* H) {
