@@ -130,14 +130,26 @@ typedef struct {
 /* Verification jobs (section 2.2-2.3).  Probabilities are rows of `probs` ([*][V] fp32,
  * as written by ls_readout); each is read in fixed point A(v) = floor(p(v) * 2^40).
  * Uniform words: uniforms[job][k], k = 0 first draw, 1 second draw, 2 first accept,
- * 3 second accept, 4 residual resample, 5 plain draw, 8+j copy candidate j. */
+ * 3 second accept, 4 residual resample, 5 plain draw, 8+j copy candidate j.
+ * The second proposal q2 is q2_row (-) q1_row (eq. 5), or, with LS_JOB_NON_RESIDUAL in
+ * flags, q2_row with x1 masked out (the non-residual ablation of Table 3, section 3.4);
+ * DRAW2 and VERIFY of one branch must use the same form.
+ * SCREEN is the shallow screening of copied candidates (CopyLoop page, "shallow screening"):
+ * candidate c survives when A(c) >= thr, thr = (uint32)x1 | (uint64)(uint32)x2 << 32 (the
+ * fixed-point threshold floor(tau * 2^40)); the survivors, ordered by A descending then id,
+ * are written back to the front of the job's range cands[cand_off .. + n_cand), the rest
+ * after them in input order; out.aux = number of survivors; with none, the job draws one
+ * proposal token ~ p_row with u[0] (outcome DRAWN), else outcome SCREENED (token -1). */
 typedef enum {
   LS_JOB_SAMPLE = 0,       /* token ~ p_row                                  (uses u[5]) */
   LS_JOB_DRAW1 = 1,        /* x1 ~ q1 = q1_row                               (u[0])      */
-  LS_JOB_DRAW2 = 2,        /* gate (eq. 6) and x2 ~ q2 = q2_row (-) q1_row   (u[1])      */
+  LS_JOB_DRAW2 = 2,        /* gate (eq. 6) and x2 ~ q2                       (u[1])      */
   LS_JOB_VERIFY = 3,       /* cascade of x1 (and x2 if gate) against p_row   (u[2,3,4])  */
-  LS_JOB_VERIFY_COPY = 4   /* point-mass cascade over cands[cand_off..+n_cand] (u[8+j], u[4]) */
+  LS_JOB_VERIFY_COPY = 4,  /* point-mass cascade over cands[cand_off..+n_cand] (u[8+j], u[4]) */
+  LS_JOB_SCREEN = 5        /* keep cands with A(c) >= thr, in order; else draw (u[0])      */
 } ls_job_op;
+
+#define LS_JOB_NON_RESIDUAL 1   /* flags bit: q2 = q2_row with x1 masked (DRAW2, VERIFY) */
 
 typedef struct {
   int32_t op;
@@ -145,16 +157,17 @@ typedef struct {
   int32_t x1, x2;
   int32_t gate;            /* VERIFY: second candidate present; DRAW2: 1 = gated, 0 = ungated */
   int32_t cand_off, n_cand;
-  int32_t pad;
+  int32_t flags;           /* LS_JOB_NON_RESIDUAL or 0 */
 } ls_verify_job;
 
-typedef enum { LS_OUT_ACC1 = 1, LS_OUT_ACC2 = 2, LS_OUT_RESAMPLED = 3, LS_OUT_DRAWN = 4, LS_OUT_ACC_COPY = 5 } ls_outcome;
+typedef enum { LS_OUT_ACC1 = 1, LS_OUT_ACC2 = 2, LS_OUT_RESAMPLED = 3, LS_OUT_DRAWN = 4, LS_OUT_ACC_COPY = 5,
+               LS_OUT_SCREENED = 6 } ls_outcome;
 
 typedef struct {
   int32_t token;
   int32_t outcome;         /* ls_outcome */
   int32_t gate;            /* DRAW2: gate open */
-  int32_t aux;             /* VERIFY_COPY: index of the accepted candidate or -1 */
+  int32_t aux;             /* VERIFY_COPY: index of the accepted candidate or -1; SCREEN: survivors */
 } ls_verify_out;
 
 /* Last error message of the calling thread (static storage, never NULL). */
@@ -200,16 +213,17 @@ ls_status ls_readout(ls_model *m, const ls_rows *rows, const float *H, const ls_
 /* Lossless verification jobs (section 2.2-2.3), one integer pass over V per job; results
  * are bit-identical for identical inputs.  jobs: [n_jobs]; probs: fp32
  * [n_prob_rows][V], each row a probability vector (entries in [0, 1], sum <= ~1; a row whose
- * fixed-point mass reaches 2^41 is rejected); cands: int32 [n_cands] (VERIFY_COPY reads
- * cands[cand_off .. cand_off + n_cand), n_cand <= 16); uniforms: uint32 [n_jobs][24]; out:
- * [n_jobs].  jobs, cands, uniforms and out may be device memory or pinned host memory
- * (hipHostMalloc): the kernel reads each job, its uniforms and candidates once and writes
- * its result directly; out is complete once the stream is synchronised; the caller keeps
- * host inputs unchanged until then.  A job with an
+ * fixed-point mass reaches 2^41 is rejected); cands: int32 [n_cands] (VERIFY_COPY and SCREEN
+ * use cands[cand_off .. cand_off + n_cand), n_cand <= 16; SCREEN rewrites its range, every
+ * other job only reads; the ranges of jobs of one call must not overlap); uniforms: uint32
+ * [n_jobs][24]; out: [n_jobs].  jobs, cands, uniforms and out may be device memory or pinned
+ * host memory (hipHostMalloc): the kernel reads each job, its uniforms and candidates once
+ * and writes its results directly; out and the rewritten candidates are complete once the
+ * stream is synchronised; the caller keeps host inputs unchanged until then.  A job with an
  * out-of-range row, token or candidate yields token -1, outcome 0 and LS_ERR_INVALID in the
  * error word. */
 ls_status ls_verify(ls_model *m, const ls_verify_job *jobs, int n_jobs, const float *probs, int n_prob_rows,
-                    const int32_t *cands, int n_cands, const uint32_t *uniforms, ls_verify_out *out,
+                    int32_t *cands, int n_cands, const uint32_t *uniforms, ls_verify_out *out,
                     hipStream_t stream);
 
 /* Synchronise `stream` and report the first device-side error recorded in the workspace

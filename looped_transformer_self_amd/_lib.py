@@ -16,8 +16,9 @@ LS_F32, LS_BF16 = 0, 1
 LS_MAX_READOUT_DEPTHS = 8
 LS_MAX_ROWS = 128
 LS_UNIFORMS_PER_JOB = 24
-LS_JOB_SAMPLE, LS_JOB_DRAW1, LS_JOB_DRAW2, LS_JOB_VERIFY, LS_JOB_VERIFY_COPY = range(5)
-LS_OUT_ACC1, LS_OUT_ACC2, LS_OUT_RESAMPLED, LS_OUT_DRAWN, LS_OUT_ACC_COPY = 1, 2, 3, 4, 5
+LS_JOB_SAMPLE, LS_JOB_DRAW1, LS_JOB_DRAW2, LS_JOB_VERIFY, LS_JOB_VERIFY_COPY, LS_JOB_SCREEN = range(6)
+LS_JOB_NON_RESIDUAL = 1
+LS_OUT_ACC1, LS_OUT_ACC2, LS_OUT_RESAMPLED, LS_OUT_DRAWN, LS_OUT_ACC_COPY, LS_OUT_SCREENED = 1, 2, 3, 4, 5, 6
 
 EXPORTS = ("ls_last_error", "ls_model_create", "ls_model_destroy", "ls_workspace_bytes", "ls_bind_workspace",
            "ls_prelude", "ls_loop_step", "ls_readout", "ls_verify", "ls_sync_status", "ls_philox_uniforms",
@@ -57,7 +58,7 @@ class ls_sampling(C.Structure):
 
 class ls_verify_job(C.Structure):
     _fields_ = [(k, C.c_int32) for k in ("op", "p_row", "q1_row", "q2_row", "x1", "x2", "gate", "cand_off",
-                                          "n_cand", "pad")]
+                                          "n_cand", "flags")]
 
 
 class ls_verify_out(C.Structure):

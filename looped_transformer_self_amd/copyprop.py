@@ -6,8 +6,9 @@ The rule (which tokens, in which order) must be a function of the prefix alone, 
 the pipelined decoder verifies the same candidates a serial decoder would; the rule itself
 only affects speed.  Here: the longest n in {3, 2, 1} for which the last n tokens occurred
 earlier; the tokens that followed those occurrences, most recent occurrence first, without
-repeats, at most `max_cands`.  Screening keeps c when floor(p_s(c) * 2^40) >= floor(tau *
-2^40) and orders survivors by that value (descending), then by token id.
+repeats, at most `max_cands`.  Screening (on the device, ls_verify's SCREEN job) keeps c when
+floor(p_s(c) * 2^40) >= floor(tau * 2^40) and orders survivors by that value (descending),
+then by token id.
 """
 
 import numpy as np
@@ -37,9 +38,7 @@ def candidates(prefix, max_cands=16):
     return []
 
 
-def screen(cands, probs_row, tau):
-    thr = int(tau * float(1 << 40))
-    fx = {c: int(np.floor(np.float64(probs_row[c]) * float(1 << 40))) for c in cands}
-    keep = [c for c in cands if fx[c] >= thr]
-    keep.sort(key=lambda c: (-fx[c], c))
-    return keep
+def threshold(tau):
+    """Fixed-point screening threshold floor(tau * 2^40): candidate c survives when
+    floor(p_s(c) * 2^40) reaches it (the device screening job compares in that fixed point)."""
+    return int(tau * float(1 << 40))

@@ -77,7 +77,7 @@ hipError_t launch_embed(bool bf16, const ValidateArgs& v, const int32_t* tokens,
                         hipStream_t s);
 void launch_dist(const float* logits, int M, int V, int greedy, float T, float top_p, float* probs,
                  const int32_t* out_rows, int n_prob_rows, int32_t* argmax, int* err, hipStream_t s);
-void launch_verify(const void* jobs, int n_jobs, const float* probs, int V, int n_rows, const int32_t* cands, int n_cands,
+void launch_verify(const void* jobs, int n_jobs, const float* probs, int V, int n_rows, int32_t* cands, int n_cands,
                    const uint32_t* uniforms, void* out, int* err, hipStream_t s);
 
 }  // namespace ls

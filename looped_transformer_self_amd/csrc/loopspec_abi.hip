@@ -375,7 +375,7 @@ ls_status ls_readout(ls_model* m, const ls_rows* r, const float* H, const ls_sam
 }
 
 ls_status ls_verify(ls_model* m, const ls_verify_job* jobs, int n_jobs, const float* probs, int n_prob_rows,
-                    const int32_t* cands, int n_cands, const uint32_t* uniforms, ls_verify_out* out, hipStream_t s) {
+                    int32_t* cands, int n_cands, const uint32_t* uniforms, ls_verify_out* out, hipStream_t s) {
   if (!m || !m->ws) return fail(LS_ERR_INVALID, "ls_verify: null model or no workspace");
   if (n_jobs < 0 || n_prob_rows < 0) return fail(LS_ERR_INVALID, "ls_verify: negative count");
   if (n_jobs == 0) return LS_OK;

@@ -1,6 +1,8 @@
 // Lossless verification (LoopSpec page, section 2.2-2.3): residual operator (eq. 2), single
-// candidate rejection (eq. 3-4), gate and residual second proposal (eq. 5-6), cascade, and the
-// point-mass cascade used for copied candidates.  Probabilities enter as the fixed-point
+// candidate rejection (eq. 3-4), gate and residual second proposal (eq. 5-6; or p_d2 with the
+// first candidate masked, the non-residual form of the ablation in Table 3, section 3.4),
+// cascade, the shallow screening of copied candidates (CopyLoop page) and the point-mass
+// cascade that verifies them.  Probabilities enter as the fixed-point
 // integers A(v) = floor(p(v) * 2^40); every decision is exact integer arithmetic (u64/u128),
 // so identical inputs give identical outputs whatever the thread schedule.  One 1024-thread
 // workgroup per job; thread t owns a contiguous id range; one pass over the vocabulary per
@@ -191,7 +193,7 @@ LS_DEV int sample128(F A, const Range& r, uint32_t U, Scratch& sc) {
 }
 
 __global__ __launch_bounds__(VT) void k_verify(const ls_verify_job* jobs, const float* probs, int V, int n_rows,
-                                              const int32_t* cands, int n_cands, const uint32_t* uniforms,
+                                              int32_t* cands, int n_cands, const uint32_t* uniforms,
                                               ls_verify_out* out, int* err) {
   __shared__ Scratch sc;
   // the job and its uniforms are read once, into LDS (they may live in pinned host memory,
@@ -218,7 +220,15 @@ __global__ __launch_bounds__(VT) void k_verify(const ls_verify_job* jobs, const 
   auto P = [&](int v) { return fixp(pR[v]); };
   auto Q1 = [&](int v) { return fixp(q1[v]); };
   auto Q2 = [&](int v) { return fixp(q2[v]); };
-  auto r2 = [&](int v) { const u64 a = fixp(q2[v]), b = fixp(q1[v]); return a > b ? a - b : (u64)0; };
+  // second proposal: residual q2 (-) q1 (eq. 5), or q2 with x1 masked (non-residual ablation)
+  const bool nonres = (jb.flags & LS_JOB_NON_RESIDUAL) != 0;
+  const int x1m = jb.x1;
+  auto r2 = [&](int v) {
+    const u64 a = fixp(q2[v]);
+    if (nonres) return v == x1m ? (u64)0 : a;
+    const u64 b = fixp(q1[v]);
+    return a > b ? a - b : (u64)0;
+  };
 
   if (jb.op == LS_JOB_SAMPLE) {
     if (!row_ok(jb.p_row) || total64(P, rg, sc) >= LIM) bad = true;
@@ -305,6 +315,51 @@ __global__ __launch_bounds__(VT) void k_verify(const ls_verify_job* jobs, const 
         }
       }
     }
+  } else if (jb.op == LS_JOB_SCREEN) {
+    // shallow screening of copied candidates: keep c when P(c) >= thr (thr = x1 | x2 << 32),
+    // survivors ordered by P descending then id, written back to the front of the job's
+    // candidate range; with no survivor, one proposal x ~ p_row (first-draw uniform)
+    __shared__ int cs[16];
+    __shared__ int s_ns;
+    if (!row_ok(jb.p_row) || jb.n_cand < 0 || jb.n_cand > 16 || jb.cand_off < 0 ||
+        jb.cand_off + jb.n_cand > n_cands)
+      bad = true;
+    else {
+      for (int j = threadIdx.x; j < jb.n_cand; j += VT) cs[j] = cands[jb.cand_off + j];
+      __syncthreads();
+      for (int j = 0; j < jb.n_cand; ++j) bad |= !tok_ok(cs[j]);
+      if (!bad && total64(P, rg, sc) >= LIM) bad = true;
+      if (!bad) {
+        if (threadIdx.x == 0) {
+          const u64 thr = (u64)(uint32_t)jb.x1 | ((u64)(uint32_t)jb.x2 << 32);
+          int keep[16];
+          u64 mass[16];
+          int ns = 0;
+          for (int j = 0; j < jb.n_cand; ++j) {
+            const u64 m = P(cs[j]);
+            if (m < thr) continue;
+            int k = ns++;
+            while (k > 0 && (mass[k - 1] < m || (mass[k - 1] == m && keep[k - 1] > cs[j]))) {
+              keep[k] = keep[k - 1]; mass[k] = mass[k - 1]; --k;
+            }
+            keep[k] = cs[j]; mass[k] = m;
+          }
+          int w = 0;
+          for (int k = 0; k < ns; ++k) cands[jb.cand_off + w++] = keep[k];
+          for (int j = 0; j < jb.n_cand; ++j)
+            if (P(cs[j]) < thr) cands[jb.cand_off + w++] = cs[j];
+          s_ns = ns;
+        }
+        __syncthreads();
+        o.aux = s_ns;
+        if (s_ns > 0) {
+          o.outcome = LS_OUT_SCREENED;
+        } else {
+          o.token = sample64(P, rg, u[0], sc);
+          o.outcome = LS_OUT_DRAWN;
+        }
+      }
+    }
   } else {
     bad = true;
   }
@@ -314,7 +369,7 @@ __global__ __launch_bounds__(VT) void k_verify(const ls_verify_job* jobs, const 
   }
 }
 
-void launch_verify(const void* jobs, int n_jobs, const float* probs, int V, int n_rows, const int32_t* cands, int n_cands,
+void launch_verify(const void* jobs, int n_jobs, const float* probs, int V, int n_rows, int32_t* cands, int n_cands,
                    const uint32_t* uniforms, void* out, int* err, hipStream_t s) {
   hipLaunchKernelGGL(k_verify, dim3(n_jobs), dim3(VT), 0, s, (const ls_verify_job*)jobs, probs, V, n_rows, cands, n_cands,
                      uniforms, (ls_verify_out*)out, err);

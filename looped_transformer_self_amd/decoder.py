@@ -10,10 +10,14 @@ the cascade, commits a token, keeps the accepted child's subtree (re-rooting) an
 rest, or restarts from the committed token.  Children reuse the parent's KV by slot index;
 pruning only returns slots to the free list.
 
+The second proposal is the residual p_d2 (-) p_d1 (eq. 5) or, as an ablation (Table 3),
+p_d2 with x1 masked out; the gate can be switched off (ungated forking).
+
 Copy-suffix proposals (CopyLoop page) replace the draws: at the screening depth a branch
-reads p_s, keeps the copied candidates with p_s(c) >= tau, spawns one child per survivor, and
-the root verifies them with the point-mass cascade; with no survivor a single proposal is
-drawn from p_s.
+takes the candidates copied from its context (host), the device keeps those with
+p_s(c) >= tau in screening order, the branch spawns one child per survivor, and the root
+verifies them with the point-mass cascade; with no survivor the same device job draws a
+single proposal from p_s.
 
 When the branch cap (or the slot pool) would be exceeded, a proposal is still drawn and
 verified but gets no precomputed child; if it is accepted a fresh branch starts at depth 0,
@@ -37,7 +41,7 @@ PURPOSES = list(range(6)) + list(range(8, 24))   # uniform words per job (index 
 
 class Node:
     __slots__ = ("slot", "pos", "token", "depth", "parent", "kids", "kind", "x1", "x2", "gate", "q1_row",
-                 "q2_row", "child1", "child2", "cands", "copy_kids", "qs_row", "alive")
+                 "q2_row", "child1", "child2", "cands", "copy_kids", "qs_row", "alive", "trace")
 
     def __init__(self, slot, pos, token, parent=None, kind="root"):
         self.slot, self.pos, self.token = slot, pos, token
@@ -51,6 +55,7 @@ class Node:
         self.cands = []          # screened copy candidates (ordered)
         self.copy_kids = {}      # token -> child
         self.alive = True
+        self.trace = {}          # depth -> (logits, probs) host copies (decoders built with trace=True)
 
 
 class CapacityError(RuntimeError):
@@ -58,10 +63,13 @@ class CapacityError(RuntimeError):
 
 
 class Decoder:
-    def __init__(self, engine, dec, mode="spec"):
+    def __init__(self, engine, dec, mode="spec", trace=False):
         """mode: "spec" (pipelined speculative decoding) or "ar" (plain full-depth decoding
-        on the same kernels, proposals off)."""
+        on the same kernels, proposals off: only the readout at R runs).  trace: keep a host
+        copy of every readout's logits and distribution on its branch and hand the committed
+        branch's copies out with its record (for tests; it synchronises after every readout)."""
         self.e = engine
+        self.trace = trace
         self.cfg = engine.cfg
         self.dec = dec
         self.mode = mode
@@ -146,6 +154,22 @@ class Decoder:
         u[8:24] = words[6:22]
         return u
 
+    def _trace_args(self, n):
+        """Extra readout arguments of a traced decoder: a logits buffer for n rows."""
+        if not self.trace:
+            return {}
+        if getattr(self, "_tr_logits", None) is None or self._tr_logits.shape[0] < n:
+            self._tr_logits = torch.zeros(max(n, self.e.max_rows), self.cfg.V, dtype=torch.float32, device=self.e.dev)
+        return {"logits": self._tr_logits}
+
+    def _trace_rows(self, rows, prob_rows):
+        """Host copies (logits, probabilities) of readout rows after the readout completed."""
+        if self.e.dev.type == "cuda":
+            torch.cuda.synchronize(self.e.dev)
+        lg = self._tr_logits.cpu().numpy()
+        pr = self.e.probs.cpu().numpy()
+        return [(lg[i].copy(), pr[j].copy()) for i, j in zip(rows, prob_rows)]
+
     # ---- prefill ----------------------------------------------------------------------
     def prefill(self, prompt, chunk=None, progress=None):
         """Run the prompt through P, all R loops and the readouts, then commit the first new
@@ -168,14 +192,19 @@ class Decoder:
             for k in range(1, cfg.R + 1):
                 rk = e.rows(slots, pos, [k] * n, c0, anc, self.fin_ptr)
                 e.loop_step(rk)
-                if k in self.didx and (cfg.L_coda or (final and k == cfg.R)):
+                # coda caches are filled at every readout depth a later decode step may read
+                need = (cfg.L_coda and (self.mode == "spec" or k == cfg.R)) or (final and k == cfg.R)
+                if k in self.didx and need:
                     out_rows = [-1] * n
                     if final and k == cfg.R:
                         last_row = self._prob()
                         out_rows[-1] = last_row
                     rr = e.rows(slots, pos, [self.didx[k]] * n, c0, anc, self.fin_ptr,
                                 extra=[np.asarray(out_rows, np.int32)])
-                    e.readout(rr, self.dec.greedy, self.dec.T, self.dec.top_p, rr.extra[0])
+                    e.readout(rr, self.dec.greedy, self.dec.T, self.dec.top_p, rr.extra[0],
+                              **self._trace_args(n))
+                    if self.trace and final and k == cfg.R:
+                        self.prefill_trace = {k: self._trace_rows([n - 1], [last_row])[0]}
             self._fin_append(slots)
             if progress is not None:
                 progress(c0 + n, T0)
@@ -191,6 +220,8 @@ class Decoder:
             raise L.LoopSpecError(st, "prefill")
         self.tokens.append(x0)
         self.records.append({"pos": T0, "token": x0, "outcome": L.LS_OUT_DRAWN, "x1": -1, "gate": False, "x2": -1})
+        if self.trace:
+            self.records[-1]["trace"] = self.prefill_trace
         self.root = Node(self._slot(), T0, x0)
         self.pending = [self.root]
         return x0
@@ -216,7 +247,7 @@ class Decoder:
         self.pending = []
         act = [x for x in self._nodes() if x.depth < R]
         paths = [self._path(x) for x in act]
-        rd = [(x, p) for x, p in zip(act, paths) if x.depth + 1 in self.didx]
+        rd = [(x, p) for x, p in zip(act, paths) if x.depth + 1 in self.didx and (spec or x.depth + 1 == R)]
         out_rows = [self._prob() for _ in rd]
         specs = []
         if pn:
@@ -240,10 +271,15 @@ class Decoder:
         if not rd:
             return
         rr = rs[1]
-        e.readout(rr, dec.greedy, dec.T, dec.top_p, rr.extra[0])
-        # 4. verification / draw jobs
+        e.readout(rr, dec.greedy, dec.T, dec.top_p, rr.extra[0], **self._trace_args(len(rd)))
+        if self.trace:
+            for (x, _), tr in zip(rd, self._trace_rows(range(len(rd)), out_rows)):
+                x.trace[x.depth] = tr
+        # 4. verification / draw / screening jobs
         jobs, us, cands, tags = [], [], [], []
         tmp_rows = []
+        flags = 0 if getattr(dec, "residual", True) else L.LS_JOB_NON_RESIDUAL
+        screen_off = {}
         for (x, _), prow in zip(rd, out_rows):
             keep_row = False
             if x.depth == R:
@@ -257,11 +293,22 @@ class Decoder:
                     j[0], j[1], j[2] = L.LS_JOB_VERIFY, prow, x.q1_row
                     j[3] = x.q2_row if x.gate else -1
                     j[4], j[5], j[6] = x.x1, x.x2 if x.gate else -1, int(x.gate)
+                    j[9] = flags
                 jobs.append(j); tags.append(("verify", x)); us.append(self._urow(self._uniforms(x.pos + 1)))
             elif spec and dec.copy and x.depth == dec.screen_depth:
+                # copy candidates from the committed prefix and the branch path (host); the
+                # device keeps those reaching tau in screening order, or draws one proposal
                 x.qs_row = prow
                 keep_row = True
-                tags.append(("screen", x))
+                prefix = self.tokens + [y.token for y in self._ancestors_and_self(x)]
+                cc = copyprop.candidates(prefix, dec.copy_max_cands)
+                thr = copyprop.threshold(dec.tau)
+                j = np.zeros(10, np.int32)
+                j[0], j[1], j[7], j[8] = L.LS_JOB_SCREEN, prow, len(cands), len(cc)
+                j[4:6] = np.array([thr & 0xFFFFFFFF, thr >> 32], np.uint32).view(np.int32)
+                screen_off[x] = len(cands)
+                cands.extend(cc)
+                jobs.append(j); tags.append(("screen", x)); us.append(self._urow(self._uniforms(x.pos + 1)))
             elif spec and not dec.copy and x.depth == dec.d1:
                 x.q1_row = prow
                 keep_row = True
@@ -273,20 +320,16 @@ class Decoder:
                 keep_row = True
                 j = np.zeros(10, np.int32)
                 j[0], j[2], j[3], j[4], j[6] = L.LS_JOB_DRAW2, x.q1_row, prow, x.x1, int(dec.gate)
+                j[9] = flags
                 jobs.append(j); tags.append(("draw2", x)); us.append(self._urow(self._uniforms(x.pos + 1)))
             if not keep_row:
                 tmp_rows.append(prow)
-        # copy-mode screening needs the screened distribution on the host side only for the
-        # threshold test, done below from the device probabilities of the candidates
-        screen = [x for t, x in tags if t == "screen"]
-        if screen:
-            self._screen(screen, jobs, tags, us)
         res = e.verify(np.asarray(jobs, np.int32).reshape(-1, 10), np.asarray(us, np.uint32).reshape(-1, 24),
                        np.asarray(cands, np.int32) if cands else None) if jobs else np.zeros((0, 4), np.int32)
         for r in tmp_rows:
             self.free_prob.append(r)
         # 5. host updates: verification first (it decides which subtree survives)
-        results = list(zip([t for t in tags if t[0] != "screen"], res))
+        results = list(zip(tags, res))
         for (tag, x), o in results:
             if tag == "verify":
                 self._commit(x, int(o[0]), int(o[1]), int(o[3]))
@@ -303,13 +346,19 @@ class Decoder:
                 if x.gate:
                     x.x2 = int(o[0])
                     spawn.append((-x.depth, 1, x, x.x2, "p2"))
-            elif tag == "drawc":
-                x.x1 = int(o[0])
-                spawn.append((-x.depth, 0, x, x.x1, "p1"))
-        for x in screen:
-            if x.alive:
-                for c in x.cands:
-                    spawn.append((-x.depth, 0, x, c, "copy"))
+            elif tag == "screen":
+                n_s = int(o[3])
+                if n_s > 0:
+                    # survivors, in screening order, at the front of the job's candidate range
+                    c0 = screen_off[x]
+                    x.cands = [int(c) for c in e.last_cands[c0:c0 + n_s]]
+                    for c in x.cands:
+                        spawn.append((-x.depth, 0, x, c, "copy"))
+                else:
+                    # no survivor: the job drew one proposal from p_s
+                    x.q1_row, x.qs_row = x.qs_row, -1
+                    x.x1 = int(o[0])
+                    spawn.append((-x.depth, 0, x, x.x1, "p1"))
         spawn.sort(key=lambda t: (t[0], t[1]))
         for _, _, x, tok, kind in spawn:
             c = self._spawn(x, tok, kind, n_active)
@@ -321,25 +370,6 @@ class Decoder:
                 x.child2 = c
             elif c is not None:
                 x.copy_kids[tok] = c
-
-    def _screen(self, nodes, jobs, tags, us):
-        """Copy proposals: candidates from the committed prefix plus the branch path, kept
-        when their screened probability reaches tau; nodes without survivors draw one
-        proposal from p_s instead."""
-        rows = [x.qs_row for x in nodes]
-        P = self.e.probs[torch.tensor(rows, device=self.e.dev)].cpu().numpy()
-        for x, p in zip(nodes, P):
-            prefix = self.tokens + [y.token for y in self._ancestors_and_self(x)]
-            cands = copyprop.candidates(prefix, self.dec.copy_max_cands)
-            x.cands = copyprop.screen(cands, p, self.dec.tau)
-            if not x.cands:
-                j = np.zeros(10, np.int32)
-                j[0], j[2] = L.LS_JOB_DRAW1, x.qs_row
-                x.q1_row = x.qs_row
-                x.qs_row = -1
-                jobs.append(j)
-                tags.append(("drawc", x))
-                us.append(self._urow(self._uniforms(x.pos + 1)))
 
     def _ancestors_and_self(self, x):
         out = []
@@ -356,7 +386,9 @@ class Decoder:
         pos = root.pos + 1
         self.tokens.append(token)
         self.records.append({"pos": pos, "token": token, "outcome": outcome, "x1": root.x1, "gate": root.gate,
-                             "x2": root.x2 if root.gate else -1, "aux": aux})
+                             "x2": root.x2 if root.gate else -1, "aux": aux, "cands": list(root.cands)})
+        if self.trace:
+            self.records[-1]["trace"] = root.trace
         nxt = None
         if outcome == L.LS_OUT_ACC1:
             nxt = root.child1
@@ -422,7 +454,9 @@ class Decoder:
         return {"steps": self.steps, "committed": N + 1, "accept1": n1, "accept2": n2,
                 "fallback": cnt(L.LS_OUT_RESAMPLED), "gate_open": sum(1 for r in recs if r["gate"]),
                 "gamma": gamma, "rows_mean": float(np.mean(self.rows_hist)) if self.rows_hist else 0.0,
-                "rows_max": int(max(self.rows_hist)) if self.rows_hist else 0}
+                "rows_max": int(max(self.rows_hist)) if self.rows_hist else 0,
+                "rows_hist": {int(k): int(v) for k, v in zip(*np.unique(self.rows_hist, return_counts=True))}
+                if self.rows_hist else {}}
 
 
 def generate(engine, prompt, n_new, dec, mode="spec"):

@@ -63,12 +63,13 @@ class Uploader:
         self.recorded = [False] * ring
         self.i = 0
 
-    def __del__(self):
-        try:
-            for ev in self.events:
-                self.hip.hipEventDestroy(ev)
-        except Exception:
-            pass
+    def close(self):
+        """Destroy the events; call before the process exits (interpreter teardown may run
+        after the HIP runtime has shut down, when a destructor's HIP call is unsafe)."""
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
+        self.recorded = []
 
     def _slot(self):
         k = self.i
@@ -207,13 +208,26 @@ class Engine:
         self.prof = None          # list of (start event, end event, row metadata) when profiling
         self.n_loop_calls = 0     # ls_loop_step launches with at least one row, since creation
 
-    def __del__(self):
-        try:
-            if getattr(self, "h", None):
-                L.lib.ls_model_destroy(self.h)
-                self.h = None
-        except Exception:
-            pass
+    def close(self):
+        """Release the model handle, the events and the device buffers, in that order, after
+        the engine's stream has drained.  Programs call this before they exit: left to
+        interpreter teardown, these releases can run after the HIP runtime (or a profiler
+        attached to it) has already shut down."""
+        if getattr(self, "h", None) is None:
+            return
+        torch.cuda.current_stream(self.dev).synchronize()
+        L.lib.ls_model_destroy(self.h)
+        self.h = None
+        self.up.close()
+        for name in ("kv_core", "kv_pre", "kv_coda", "H", "probs", "ws", "w", "layers", "vout_host", "vin_host"):
+            setattr(self, name, None)
+        self.vin_np = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
 
     def stream_ptr(self):
         """The stream every call of this engine is issued on: the current stream when the
@@ -330,7 +344,9 @@ class Engine:
 
     def verify(self, jobs, uniforms, cands=None):
         """jobs: int32 array [n][10]; uniforms: uint32 [n][24]; cands: int32 array or None.
-        Returns an int32 numpy array [n][4] (token, outcome, gate, aux) after a stream sync."""
+        Returns an int32 numpy array [n][4] (token, outcome, gate, aux) after a stream sync;
+        `last_cands` then holds the candidate array as the kernel left it (screening jobs
+        reorder their range)."""
         n = len(jobs)
         ncand = len(cands) if cands is not None else 0
         if n > self._vin_jobs or ncand > 16 * self._vin_jobs:
@@ -346,6 +362,8 @@ class Engine:
                                 C.c_void_p(base + 4 * 10 * mj), _ptr(self.vout_host), self.stream_ptr()),
                 "ls_verify")
         torch.cuda.current_stream().synchronize()
+        # candidate ranges as the screening jobs left them (survivors first)
+        self.last_cands = vin[34 * mj:34 * mj + ncand].copy()
         return self.vout_host[:4 * n].numpy().reshape(n, 4).copy()
 
     def sync_status(self):

@@ -47,19 +47,31 @@ def ar_decode(model, prompt, n_new, dec, return_logits=False):
     return (toks, logits) if return_logits else toks
 
 
+def distributions(cfg, dec, lg_by_depth):
+    """Fixed-point readout distributions {depth: P} from logits {depth: logits}."""
+    return {r: sampler.fixed(_dist(lg, dec)) for r, lg in lg_by_depth.items()}
+
+
 def decide(cfg, dec, pos, lg_by_depth, prefix=None):
     """The decision at one position from its readouts {depth: logits}.
 
     Returns a record dict: token, outcome, x1, gate, x2 (and cands for copy mode).
     """
+    return decide_fixed(cfg, dec, pos, distributions(cfg, dec, lg_by_depth), prefix)
+
+
+def decide_fixed(cfg, dec, pos, P_by_depth, prefix=None):
+    """The decision at one position from its fixed-point readout distributions
+    {depth: P} (P(v) = floor(p(v) * 2^40)), with the position-keyed uniforms."""
     R, d1, d2 = cfg.R, dec.d1, dec.d2
     seed = dec.seed_s
+    residual = getattr(dec, "residual", True)
     U = lambda purpose: philox.uniform(seed, pos, purpose)
-    P_R = sampler.fixed(_dist(lg_by_depth[R], dec))
+    P_R = P_by_depth[R]
     rec = {"pos": pos, "x1": -1, "gate": False, "x2": -1, "cands": []}
     if dec.copy:
         s = dec.screen_depth
-        P_s = sampler.fixed(_dist(lg_by_depth[s], dec))
+        P_s = P_by_depth[s]
         cands = copyprop.screen(copyprop.candidates(prefix, dec.copy_max_cands), P_s, dec.tau)
         rec["cands"] = cands
         if cands:
@@ -69,18 +81,32 @@ def decide(cfg, dec, pos, lg_by_depth, prefix=None):
             return rec
         P_1 = P_s
     else:
-        P_1 = sampler.fixed(_dist(lg_by_depth[d1], dec))
+        P_1 = P_by_depth[d1]
     x1 = sampler.draw1(P_1, U(philox.P_DRAW1))
     rec["x1"] = x1
     gate, x2, P_2 = False, -1, None
     if d2 is not None and not dec.copy:
-        P_2 = sampler.fixed(_dist(lg_by_depth[d2], dec))
-        gate, x2 = sampler.draw2(P_1, P_2, x1, U(philox.P_DRAW2), gated=dec.gate)
+        P_2 = P_by_depth[d2]
+        gate, x2 = sampler.draw2(P_1, P_2, x1, U(philox.P_DRAW2), gated=dec.gate, residual=residual)
     rec["gate"], rec["x2"] = gate, x2
     tok, out = sampler.verify(P_R, P_1, x1, U(philox.P_ACC1), U(philox.P_RESAMPLE),
-                              gate_open=gate, P_d2=P_2, x2=x2, U3=U(philox.P_ACC2))
+                              gate_open=gate, P_d2=P_2, x2=x2, U3=U(philox.P_ACC2), residual=residual)
     rec.update(token=tok, outcome=out)
     return rec
+
+
+def forced_logits(model, prompt, forced, depths=None):
+    """Logits along a teacher-forced stream, in one whole-sequence pass: returns a list whose
+    entry i holds {r: logits} of the position that decides new token i (the last prompt
+    position for i = 0, the position of forced[i - 1] after that).  Equal to the cached
+    token-by-token decode of spec_decode_serial(forced=...) (pinned: cached decoding equals
+    recomputation) at a fraction of its cost for large models."""
+    cfg = model.cfg
+    depths = cfg.readout_depths if depths is None else tuple(depths)
+    toks = list(prompt) + list(forced[:-1])
+    lg = model.new_seq().extend(toks, depths=depths, last_only=False)
+    T0 = len(prompt)
+    return [{r: lg[r][T0 - 1 + i] for r in depths} for i in range(len(forced))]
 
 
 def spec_decode_serial(model, prompt, n_new, dec, forced=None, return_logits=False):
@@ -127,7 +153,7 @@ def gamma(recs, cfg, dec):
     return N * cfg.R / (n1 * d1 + n2 * d2 + (N - n1 - n2) * cfg.R)
 
 
-def exact_commit_distribution(P_R, P_1, P_2=None, gated=True):
+def exact_commit_distribution(P_R, P_1, P_2=None, gated=True, residual=True):
     """Exact law of the committed token under the fixed-point sampler, by counting the
     uniform words that lead to each outcome (2^32 equally likely values per word).
 
@@ -169,7 +195,7 @@ def exact_commit_distribution(P_R, P_1, P_2=None, gated=True):
         rej = q1[x1] * (1 - a1)
         if rej == 0:
             continue
-        r2 = sampler.resid(P_2, P_1) if P_2 is not None else None
+        r2 = sampler.proposal2(P_1, P_2, x1, residual) if P_2 is not None else None
         open_ = P_2 is not None and sum(r2) > 0 and (not gated or P_2[x1] < P_1[x1])
         if not open_:
             for v, pv in enumerate(law_sample(r1)):

@@ -7,6 +7,10 @@ LoopSpec page, section 2.2 and 2.3:
   x ~ p (-) q.
 * eq. 5-6, second proposal q2 = p_d2 (-) p_d1, drawn only when the gate is open:
   p_d2(x~1) < p_d1(x~1).
+* Table 3 (section 3.4) ablates the residual form: the non-residual second proposal is
+  p_d2 with the first candidate removed and renormalised; everything after it (the
+  cascade below, with this q2) is unchanged, and it stays lossless because after x~1 is
+  rejected the target is rho1 whatever distribution x~2 came from.
 * cascade: rho1 = p_R (-) q1; the second candidate is accepted with
   min(1, rho1(x~2)/q2(x~2)); after two rejections x ~ rho1 (-) q2; with the gate closed
   the first rejection draws from rho1.  The second candidate is never re-verified against
@@ -63,9 +67,19 @@ def draw1(P_d1, U0):
     return sample(P_d1, U0)
 
 
-def draw2(P_d1, P_d2, x1, U1, gated=True):
-    """Gate (eq. 6) and residual second proposal (eq. 5).  Returns (gate_open, x2 or -1)."""
-    r2 = resid(P_d2, P_d1)
+def proposal2(P_d1, P_d2, x1, residual=True):
+    """Unnormalised second proposal: the residual p_d2 (-) p_d1 of eq. 5, or (residual=False,
+    Table 3's non-residual ablation) p_d2 with the first candidate x1 masked to zero."""
+    if residual:
+        return resid(P_d2, P_d1)
+    r = list(P_d2)
+    r[x1] = 0
+    return r
+
+
+def draw2(P_d1, P_d2, x1, U1, gated=True, residual=True):
+    """Gate (eq. 6) and second proposal (eq. 5).  Returns (gate_open, x2 or -1)."""
+    r2 = proposal2(P_d1, P_d2, x1, residual)
     if sum(r2) == 0:
         return False, -1
     if gated and not (P_d2[x1] < P_d1[x1]):
@@ -73,7 +87,7 @@ def draw2(P_d1, P_d2, x1, U1, gated=True):
     return True, sample(r2, U1)
 
 
-def verify(P_R, P_d1, x1, U2, U4, gate_open=False, P_d2=None, x2=-1, U3=0):
+def verify(P_R, P_d1, x1, U2, U4, gate_open=False, P_d2=None, x2=-1, U3=0, residual=True):
     """Cascade verification at full depth.  Returns (token, outcome)."""
     if accept(P_R, P_d1, x1, U2):
         return x1, ACC1
@@ -82,7 +96,7 @@ def verify(P_R, P_d1, x1, U2, U4, gate_open=False, P_d2=None, x2=-1, U3=0):
         r1 = list(P_R)
     if not gate_open:
         return sample(r1, U4), RESAMPLED
-    r2 = resid(P_d2, P_d1)
+    r2 = proposal2(P_d1, P_d2, x1, residual)
     Z1, Z2 = sum(r1), sum(r2)
     # accept x~2 with probability min(1, rho1(x2) / q2(x2)), rho1 = r1/Z1, q2 = r2/Z2
     if U3 * Z1 * r2[x2] < ((r1[x2] * Z2) << 32):

@@ -47,6 +47,7 @@ class DecodeCfg:
     d1: int = 2
     d2: Optional[int] = None          # second (residual) proposal depth; None = single proposal
     gate: bool = True
+    residual: bool = True             # False: Table 3's non-residual second proposal (p_d2, x1 masked)
     max_branches: int = 8
     prompt_len: int = 32
     new_tokens: int = 64

@@ -1,8 +1,11 @@
 """Seeded synthetic weights for a looped decoder (random init, no trained checkpoint).
 
-Order of generation (NumPy PCG64(seed), standard normal scaled by init_std, float32):
-embedding; then, for each prelude layer, each layer of the shared block and each coda
-layer: Wq, Wk, Wv, Wo, Wgate, Wup, Wdown.  RMSNorm gains are ones.  The LM head is tied
+Every matrix has a PCG64 stream of its own, seeded by (seed, tensor index) through NumPy's
+SeedSequence, and is filled with standard normals scaled by init_std (float32).  Tensor
+indices follow a fixed order: 0 the embedding; then, for each prelude layer, each layer of
+the shared block and each coda layer, Wq, Wk, Wv, Wo, Wgate, Wup, Wdown.  Independent
+streams let the matrices be drawn in parallel threads (NumPy releases the GIL while it
+fills an array) without changing any value.  RMSNorm gains are ones.  The LM head is tied
 to the embedding.  For bf16 models every matrix is rounded to bfloat16
 (round-to-nearest-even) and returned as uint16 bit patterns; both the GPU path and the
 CPU reference consume exactly these arrays.
@@ -10,9 +13,13 @@ CPU reference consume exactly these arrays.
 Matrices follow the y = x @ W.T convention: W has shape [out_features, in_features].
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 LAYER_KEYS = ("Wq", "Wk", "Wv", "Wo", "Wg", "Wu", "Wd")
+_ROWS_PER_PIECE = 1024          # rows drawn and rounded per piece of a large matrix
 
 
 def _round_bf16_bits(x32: np.ndarray) -> np.ndarray:
@@ -27,36 +34,49 @@ def _layer_shapes(cfg):
     return {"Wq": (d, d), "Wk": (d, d), "Wv": (d, d), "Wo": (d, d), "Wg": (F, d), "Wu": (F, d), "Wd": (d, F)}
 
 
-def make_weights(cfg, seed: int = 0, zero=()):
+def _draw(seed, index, shape, std, bf16):
+    """Tensor `index`: standard normals from its own stream, scaled, optionally rounded.
+    Drawn in row pieces so that the float32 temporary of a large matrix stays small."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(index)])))
+    out = np.empty(shape, np.uint16 if bf16 else np.float32)
+    for r0 in range(0, shape[0], _ROWS_PER_PIECE):
+        r1 = min(shape[0], r0 + _ROWS_PER_PIECE)
+        x = rng.standard_normal(size=(r1 - r0,) + tuple(shape[1:]), dtype=np.float32)
+        x *= std
+        out[r0:r1] = _round_bf16_bits(x) if bf16 else x
+    return out
+
+
+def make_weights(cfg, seed: int = 0, zero=(), threads=None):
     """Return {"emb": [V,d], "pre": [layer dicts], "core": [...], "coda": [...], gains...}.
 
     `zero` names layer matrices (e.g. ("Wo", "Wd")) to replace by zeros after drawing,
     which turns every layer into the identity map on the residual stream (a special case
     used by tests).
     """
-    rng = np.random.Generator(np.random.PCG64(seed))
     std = np.float32(cfg.init_std)
     bf16 = cfg.dtype == "bf16"
-
-    def draw(shape):
-        x = rng.standard_normal(size=shape, dtype=np.float32)
-        x *= std
-        return _round_bf16_bits(x) if bf16 else x
-
-    out = {"emb": draw((cfg.V, cfg.d))}
     shapes = _layer_shapes(cfg)
+    jobs = [("emb", None, None, (cfg.V, cfg.d))]
     for part, n in (("pre", cfg.L_pre), ("core", cfg.L), ("coda", cfg.L_coda)):
-        layers = []
-        for _ in range(n):
-            lw = {}
+        for li in range(n):
             for k in LAYER_KEYS:
-                lw[k] = draw(shapes[k])
-                if k in zero:
-                    lw[k][...] = 0
+                jobs.append((part, li, k, shapes[k]))
+    threads = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(threads) as ex:
+        arrs = list(ex.map(lambda ij: _draw(seed, ij[0], ij[1][3], std, bf16), enumerate(jobs)))
+    out = {"emb": arrs[0]}
+    for part, n in (("pre", cfg.L_pre), ("core", cfg.L), ("coda", cfg.L_coda)):
+        out[part] = [dict() for _ in range(n)]
+    for (part, li, k, _), a in zip(jobs[1:], arrs[1:]):
+        lw = out[part][li]
+        if k in zero:
+            a[...] = 0
+        lw[k] = a
+    for part in ("pre", "core", "coda"):
+        for lw in out[part]:
             lw["g1"] = np.ones(cfg.d, np.float32)
             lw["g2"] = np.ones(cfg.d, np.float32)
-            layers.append(lw)
-        out[part] = layers
     out["g_final"] = np.ones(cfg.d, np.float32)
     return out
 

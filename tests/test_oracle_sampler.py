@@ -80,6 +80,19 @@ def test_residual_mass_equals_tv():
         assert abs(got - tv) <= drift + 64 * 2.0 ** -40
 
 
+def test_non_residual_proposal_masks_the_first_candidate():
+    """Table 3's non-residual second proposal: p_d2 renormalised without x~1, so x~2 != x~1;
+    with the gate off it is drawn whenever p_d2 has mass outside x~1."""
+    for seed in range(40):
+        P1, P2 = _fixed_rows(2, 16, 300 + seed, peaked=2.0)
+        x1 = sampler.draw1(P1, philox.uniform(seed, 3, 0))
+        gate, x2 = sampler.draw2(P1, P2, x1, philox.uniform(seed, 3, 1), gated=False, residual=False)
+        assert gate and x2 != x1 and P2[x2] > 0
+    one_hot = [0] * 4
+    one_hot[2] = 1 << 40
+    assert sampler.draw2(one_hot, one_hot, 2, 12345, gated=False, residual=False) == (False, -1)
+
+
 def test_gate_open_zeroes_residual_at_first_candidate():
     for seed in range(40):
         P1, P2 = _fixed_rows(2, 16, 100 + seed, peaked=2.0)
@@ -104,17 +117,22 @@ def _equal_total_rows(n, V, seed):
     return rows
 
 
-@pytest.mark.parametrize("mode", ["single", "gated", "ungated"])
+MODES = {"single": (False, True, True), "gated": (True, True, True), "ungated": (True, False, True),
+         "nonres-ungated": (True, False, False), "nonres-gated": (True, True, False)}
+
+
+@pytest.mark.parametrize("mode", list(MODES))
 def test_exact_commit_law_is_p_R(mode):
     """Exact law of the committed token (by counting uniform words) equals P_R/sum(P_R)
-    (the method is lossless: section 2.2 and 2.3).  With equal fixed-point totals the
-    only error left is the 2^-32 granularity of the uniform words."""
+    (the method is lossless: section 2.2 and 2.3; Table 3's non-residual second proposal
+    too).  With equal fixed-point totals the only error left is the 2^-32 granularity of
+    the uniform words."""
+    second, gated, residual = MODES[mode]
     rng = np.random.Generator(np.random.PCG64(7))
     for trial in range(12):
         V = int(rng.integers(2, 7))
         P_R, P_1, P_2 = _equal_total_rows(3, V, 1000 + trial)
-        law = decode.exact_commit_distribution(P_R, P_1, None if mode == "single" else P_2,
-                                               gated=(mode == "gated"))
+        law = decode.exact_commit_distribution(P_R, P_1, P_2 if second else None, gated=gated, residual=residual)
         Z = sum(P_R)
         for v in range(V):
             assert abs(float(law[v]) - P_R[v] / Z) < 8 * V * 2.0 ** -32, (trial, v)
@@ -189,7 +207,7 @@ def _chi2_sf(x, k):
     return float(chi2.sf(x, k))
 
 
-@pytest.mark.parametrize("mode", ["single", "gated", "ungated"])
+@pytest.mark.parametrize("mode", list(MODES))
 def test_cascade_chi_square_synthetic(mode):
     """10^5 seeded Philox draws through draw1/draw2/verify on fixed distributions chosen
     so every branch (first accept, second accept, double reject) is frequent."""
@@ -205,9 +223,10 @@ def test_cascade_chi_square_synthetic(mode):
         U = [philox.uniform(s, 17, k) for k in range(5)]
         x1 = sampler.draw1(P_1, U[0])
         gate, x2 = (False, -1)
-        if mode != "single":
-            gate, x2 = sampler.draw2(P_1, P_2, x1, U[1], gated=(mode == "gated"))
-        tok, out = sampler.verify(P_R, P_1, x1, U[2], U[4], gate, P_2, x2, U[3])
+        second, gated, residual = MODES[mode]
+        if second:
+            gate, x2 = sampler.draw2(P_1, P_2, x1, U[1], gated=gated, residual=residual)
+        tok, out = sampler.verify(P_R, P_1, x1, U[2], U[4], gate, P_2, x2, U[3], residual=residual)
         counts[tok] += 1
         outcomes[out] += 1
     exp = p_R.astype(np.float64) / p_R.sum() * N
