@@ -1,18 +1,24 @@
-"""Benchmark: committed tokens/s at batch 1 of pipelined self-speculative decoding on the
-Ouro-1.4B-shaped looped decoder (bf16, vocab 49152, d 2048, 16 heads, shared 24-layer block
-applied R = 4 times, SwiGLU 5632; prompt 512 random tokens, 256 new tokens, T = 1.0, top-p
-0.9, first proposal at depth 2, residual second proposal at depth 3, <= 8 active branches),
-random-init weights and synthetic prompt.
+"""Benchmark: committed tokens/s at batch 1 of pipelined self-speculative decoding.
 
-One step = one complete decode of the 256 new tokens from the prefilled state (prefill is
-excluded from timing, as on the LoopSpec page, section 3.1): every pipeline step of it runs
-the prelude of new branches, ls_loop_step over all active rows, ls_readout at the readout
-depths and ls_verify, plus the host scheduler.  `value` counts the tokens committed inside
-the timed decode (the first new token comes from the prefill readout).
+Default workload: the Huginn/Raven-3.5B-shaped looped decoder (bf16, vocabulary 65536,
+d 5280, 55 heads of 96, prelude 2 layers, shared core block of 4 layers applied R = 32 times,
+coda 2 layers recomputed per readout, SwiGLU 17920), random-init weights, a 2048-token
+synthetic prompt, 512 new tokens, greedy, proposals at depths 8 and 16, <= 16 active
+branches: the largest configuration of the workload list that fits one GPU.  --workload
+selects the others (C1-C5).
 
-Also reported: the roofline of ls_loop_step (algorithmic HBM bytes per call / its
-event-timed duration, against 8 TB/s), and the CPU reference (plain NumPy full-depth
-autoregressive decoding) timed on a bounded sample on the host cores.
+One step = one slice of 32 committed tokens of the workload's decode (prefill is excluded
+from timing, as on the LoopSpec page, section 3.1).  Steps continue the same decode; when it
+has committed all new tokens the next step restarts it from the prefilled state.  The timed
+region starts a fresh decode, so K steps cover the first 32*K tokens (wrapping every
+n_new - 1 decode-committed tokens).  Every pipeline step runs the prelude of new branches,
+ls_loop_step over all active rows, ls_readout at the readout depths and ls_verify, plus the
+host scheduler.  `value` counts the tokens committed inside the timed region.
+
+Also reported: the same kernels in plain full-depth mode (proposals off) over the first
+slices, and the speed-up over it; the roofline of ls_loop_step (algorithmic HBM bytes per
+call / its event-timed duration, against 8 TB/s); and the CPU reference (plain NumPy
+full-depth autoregressive decoding) timed on a bounded sample on the host cores.
 """
 
 import argparse
@@ -29,7 +35,10 @@ HBM_PEAK_GBS = 8000.0
 
 def cpu_baseline(cfg, dec, w, prompt_len=16, n_tok=3):
     """Plain full-depth AR decoding by the CPU reference on a bounded sample: a 16-token
-    prompt (the workload's first 16 prompt tokens) and 3 decoded tokens; decode-only rate."""
+    prompt (the workload's first 16 prompt tokens) and 3 decoded tokens; decode-only rate.
+    The workload's own context is cut because the float64 prefill of a 2048-token prompt
+    through the Huginn shape alone is ~220 TFLOP; at batch 1 a decoded token's cost is its
+    weight products (attention over 2048 keys adds ~5 % to them)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -52,7 +61,8 @@ def cpu_baseline(cfg, dec, w, prompt_len=16, n_tok=3):
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"float64 NumPy full-depth AR decode of {n_tok} tokens after a {prompt_len}-token prefix "
-                      f"of the workload prompt (prefill untimed), same weights",
+                      f"of the workload prompt (prefill untimed; the workload's {dec.prompt_len}-token context "
+                      f"is cut to bound the float64 prefill), same weights",
             "cpu": _cpu_model()}
 
 
@@ -127,12 +137,13 @@ def _counter_per_dispatch(d, counter, prefix):
 def _profile_commands(a):
     """The command sequence that produces the databases this summary reads (directory names
     taken from the arguments)."""
-    b = "python3 -u bench.py --steps 1 --warmup 0 --no-cpu-baseline"
-    cmds = [f"rocprofv3 --kernel-trace --stats -d {a.trace_dir} -o c2 -- {b} > {a.bench_log} 2>&1",
-            f"rocprofv3 --pmc FETCH_SIZE -d {a.fetch_dir} -o c2 -- {b}",
-            f"rocprofv3 --pmc WRITE_SIZE -d {a.write_dir} -o c2 -- {b}"]
+    w = a.workload.lower()
+    b = f"python3 -u bench.py --workload {a.workload} --steps 2 --warmup 0 --no-cpu-baseline --no-ar"
+    cmds = [f"rocprofv3 --kernel-trace --stats -d {a.trace_dir} -o {w} -- {b} > {a.bench_log} 2>&1",
+            f"rocprofv3 --pmc FETCH_SIZE -d {a.fetch_dir} -o {w} -- {b}",
+            f"rocprofv3 --pmc WRITE_SIZE -d {a.write_dir} -o {w} -- {b}"]
     if a.mfma_dir:
-        cmds.append(f"rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 -d {a.mfma_dir} -o c2 -- {b}")
+        cmds.append(f"rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 -d {a.mfma_dir} -o {w} -- {b}")
     cmds += [f"rocprofv3 --pmc FETCH_SIZE -d {a.copy_fetch_dir} -o copy -- python3 -u bench.py --copy-calibration",
              f"rocprofv3 --pmc WRITE_SIZE -d {a.copy_write_dir} -o copy -- python3 -u bench.py --copy-calibration"]
     summ = (f"python3 bench.py --pmc-summary --workload {a.workload} --bench-log {a.bench_log} "
@@ -239,14 +250,66 @@ class _Progress:
             print(f"[bench] {self.what} {done}/{total}", file=sys.stderr, flush=True)
 
 
+SLICE = 32                      # committed tokens per benchmark step
+AR_SLICES = 2                   # slices decoded again in plain full-depth mode
+
+
+class SliceRunner:
+    """Steps of the benchmark: consecutive slices of SLICE committed tokens of one decode,
+    restarted from the prefilled snapshot after its last token."""
+
+    def __init__(self, d, snap, n_new):
+        self.d, self.snap, self.n_new = d, snap, n_new
+        self.done = n_new               # forces a restart at the first step
+        self.finished = []              # stats of completed decodes
+
+    def restart(self):
+        if self.done > 1:
+            self.finished.append(self.d.stats())
+        self.d.restore(self.snap)
+        self.done = 1                   # the first new token comes from the prefill
+
+    def step(self, progress=None):
+        if self.done >= self.n_new:
+            self.restart()
+        before = self.done
+        self.d.decode(min(self.n_new, self.done + SLICE))
+        self.done = len(self.d.tokens) - self.d.prompt_len
+        return self.done - before
+
+
+def _merge_stats(stats, gamma_depths=None):
+    out = {}
+    for st in stats:
+        for k, v in st.items():
+            if k == "rows_hist":
+                h = out.setdefault(k, {})
+                for r, c in v.items():
+                    h[r] = h.get(r, 0) + c
+            elif isinstance(v, (int, float)) and k not in ("gamma", "rows_mean", "rows_max"):
+                out[k] = out.get(k, 0) + v
+    n_rows = sum(r * c for r, c in out.get("rows_hist", {}).items())
+    if gamma_depths:
+        # eq. 9 over all decodes: N R / (N1 d1 + N2 d2 + (N - N1 - N2) R)
+        d1, d2, R = gamma_depths
+        n1, n2 = out.get("accept1", 0), out.get("accept2", 0)
+        N = n1 + n2 + out.get("fallback", 0)
+        out["gamma"] = N * R / max(1, n1 * d1 + n2 * d2 + (N - n1 - n2) * R)
+    n_steps = sum(out.get("rows_hist", {}).values())
+    out["rows_mean"] = n_rows / n_steps if n_steps else 0.0
+    out["rows_max"] = max(out.get("rows_hist", {0: 0}))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="C2")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C4")
     ap.add_argument("--mode", default="spec", choices=["spec", "ar"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ar", action="store_true", help="skip the plain full-depth comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run one plain device copy of 1 GiB (byte-counter calibration)")
     ap.add_argument("--pmc-summary", action="store_true",
@@ -272,7 +335,6 @@ def main():
         copy_calibration()
         return
 
-    import numpy as np
     import torch
 
     from looped_transformer_self_amd.decoder import Decoder
@@ -293,23 +355,27 @@ def main():
     d.prefill(prompt, progress=_Progress("prefill"))
     snap = d.snapshot()
     torch.cuda.synchronize()
+    run = SliceRunner(d, snap, n_new)
     for i in range(args.warmup):
-        d.restore(snap)
-        d.decode(n_new, progress=_Progress(f"warmup {i}"))
-        print(f"[bench] warmup {i} done", file=sys.stderr, flush=True)
+        run.step()
+        print(f"[bench] warmup step {i} done", file=sys.stderr, flush=True)
+    run.restart()                             # the timed region starts a fresh decode
+    run.finished = []
     torch.cuda.synchronize()
     e.prof = []
     n_before = e.n_loop_calls
-    stats = []
+    committed, step_s = 0, []
+    prog = _Progress("step", every=30.0)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        d.restore(snap)
-        toks = d.decode(n_new, progress=_Progress(f"step {i}", every=60.0))
-        stats.append(d.stats())
+        ts = time.perf_counter()
+        committed += run.step()
+        step_s.append(time.perf_counter() - ts)
+        prog(i + 1, args.steps)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    committed = args.steps * (n_new - 1)
     value = committed / dt
+    run.finished.append(d.stats())
     # ls_loop_step roofline over the timed region
     t_ms = sum(b.elapsed_time(en) for b, en, _ in e.prof)
     by = sum(e.loop_step_bytes(h) for _, _, h in e.prof)
@@ -320,7 +386,6 @@ def main():
     print(f"[bench] algorithmic bytes per ls_loop_step launch: {by / n_calls:.1f}", file=sys.stderr)
     print(f"[bench] event-timed us per ls_loop_step launch: {t_ms / n_calls * 1e3:.2f}", file=sys.stderr, flush=True)
     traffic = _measured_traffic(wl.key)
-    st = stats[-1]
     out = {
         "metric": "committed tokens/s at batch 1",
         "value": round(value, 3),
@@ -333,9 +398,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
-        "data": "synthetic (seeded random-init weights, uniform random prompt)",
+        "data": "synthetic (seeded random-init weights, synthetic prompt)",
         "config": {"workload": f"{wl.key}: {wl.description}", "prompt_len": dec.prompt_len, "new_tokens": n_new,
-                   "mode": args.mode, "batch": 1},
+                   "mode": args.mode, "batch": 1, "step": f"{SLICE} committed tokens of the decode",
+                   "timed_tokens": committed},
         "roofline": {"kernel": "ls_loop_step (one call: all layers of the shared block, all active rows)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -343,16 +409,35 @@ def main():
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_call": round(by / n_calls), "us_per_call": round(t_ms / n_calls * 1e3, 2),
                      "launches": n_calls},
-        "decode_stats": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in st.items()},
+        "decode_stats": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in _merge_stats(
+            run.finished, (dec.screen_depth if dec.copy else dec.d1, dec.d2 or cfg.R, cfg.R)).items()},
     }
     if traffic and "mfma_util_percent" in traffic:
         # matrix-core use of the same kernel from the committed counter summary
         out["roofline"]["mfma_util_percent"] = traffic["mfma_util_percent"]
         out["roofline"]["mfma_tflops_issued"] = traffic["mfma_tflops"]
+    if args.mode == "spec" and not args.no_ar:
+        # the same kernels with proposals off, over the first AR_SLICES slices of a fresh decode,
+        # against the spec steps that decoded the same slices
+        n_ar = min(AR_SLICES, args.steps, (n_new - 2) // SLICE + 1)
+        da = Decoder(e, dec, "ar")
+        ra = SliceRunner(da, snap, n_new)
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        c_ar = sum(ra.step() for _ in range(n_ar))
+        torch.cuda.synchronize()
+        t_ar = time.perf_counter() - ta
+        spec_s = sum(step_s[:n_ar])
+        out["ar_mode"] = {"value": round(c_ar / t_ar, 3), "unit": "tokens/s", "tokens": c_ar,
+                          "spec_value_same_tokens": round(c_ar / spec_s, 3),
+                          "speedup": round(t_ar / spec_s, 4),
+                          "note": "same kernels, proposals off (full-depth decoding), same first tokens"}
+        print(f"[bench] plain full-depth mode: {c_ar / t_ar:.2f} tokens/s", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("[bench] CPU reference baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, dec, w)
     print(json.dumps(out), flush=True)
+    e.close()
 
 
 if __name__ == "__main__":

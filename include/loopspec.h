@@ -230,6 +230,14 @@ ls_status ls_verify(ls_model *m, const ls_verify_job *jobs, int n_jobs, const fl
  * (LS_ERR_INVALID for a rejected descriptor) or LS_ERR_HIP for a runtime error. */
 ls_status ls_sync_status(ls_model *m, hipStream_t stream);
 
+/* Bound on every dependency wait inside one layer-kernel launch (default 2 s): workgroups
+ * wait for each other's results, and a wait still unmet that long after the launch started
+ * gives up, records a timeout in the error word (ls_sync_status then returns LS_ERR_HIP) and
+ * lets the launch run to its end without waiting; every later wait of the launch gives up at
+ * its first poll.  Results of a launch that timed out are undefined.  seconds in [0, 3600];
+ * 0 makes every wait that would block give up at once (a test of the give-up path). */
+ls_status ls_set_wait_limit(ls_model *m, double seconds);
+
 /* Diagnostics: while dev_buf is non-NULL, each later layer-kernel launch writes wall-clock
  * stamps (phase begin/end, dependency met, first chunk staged, first tile batch multiplied,
  * first/last weight slab issued; first 4 layers) per workgroup into dev_buf (device int64

@@ -22,7 +22,7 @@ LS_OUT_ACC1, LS_OUT_ACC2, LS_OUT_RESAMPLED, LS_OUT_DRAWN, LS_OUT_ACC_COPY, LS_OU
 
 EXPORTS = ("ls_last_error", "ls_model_create", "ls_model_destroy", "ls_workspace_bytes", "ls_bind_workspace",
            "ls_prelude", "ls_loop_step", "ls_readout", "ls_verify", "ls_sync_status", "ls_philox_uniforms",
-           "ls_debug_trace")
+           "ls_debug_trace", "ls_set_wait_limit")
 
 
 class ls_model_desc(C.Structure):
@@ -84,6 +84,7 @@ def _load():
         "ls_verify": (C.c_int, [P, P, C.c_int, P, C.c_int, P, C.c_int, P, P, P]),
         "ls_sync_status": (C.c_int, [P, P]),
         "ls_debug_trace": (C.c_int, [P, P, C.POINTER(C.c_int)]),
+        "ls_set_wait_limit": (C.c_int, [P, C.c_double]),
         "ls_philox_uniforms": (None, [C.c_uint64, C.c_int64, C.POINTER(C.c_int32), C.c_int,
                                       C.POINTER(C.c_uint32)]),
     }

@@ -98,6 +98,12 @@ LS_DEV float block_max(float v, float* red) {
   return t;
 }
 
+// NaN in its canonical (positive, quiet) encoding, other values unchanged.  Buffers whose
+// readers poll for the disappearance of an all-ones fill pattern store through this, so a NaN
+// carried in from a caller's input (which may keep its payload through arithmetic) can never
+// look like the fill.
+LS_DEV float canon_nan(float v) { return v == v ? v : __uint_as_float(0x7fc00000u); }
+
 // Device error word (first error wins).
 LS_DEV void ls_flag(int* err, int code) { atomicCAS(err, 0, code); }
 

@@ -58,11 +58,13 @@ struct MegaArgs {
   const float* Hg;
   int do_head;
   long long* trace;             // optional: per-workgroup phase timestamps (wall clock)
+  long long wait_ticks;         // bound on every dependency wait, wall-clock ticks from launch start
 };
 
 size_t mega_counter_ints(int M, int d, int F, int nh, int n_layers);
 size_t mega_smem_bytes(bool bf16, int M, int d);
-int mega_occupancy(bool bf16, int M, int d);
+// resident workgroups per CU of the variant launch_mega picks for (M, loop_block, long_att)
+int mega_occupancy(bool bf16, int M, int d, bool loop_block, bool long_att);
 int att_unit_keys(bool bf16);   // prefix keys per attention unit
 // loop_block: launch under the k_mega symbol (shared block B) rather than k_mega_aux
 hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool loop_block, const ValidateArgs& v);

@@ -51,7 +51,11 @@ struct ls_model {
   LayerW *tab_pre = nullptr, *tab_core = nullptr, *tab_coda = nullptr;
   std::vector<LayerW> host_tab;
   int n_cu = 0;
-  int occ[LS_MAX_ROWS + 1] = {0};   // resident workgroups per CU, by rows per launch
+  // resident workgroups per CU of the persistent kernel, by [loop-block symbol][long-prefix
+  // attention][rows per launch] (each variant is a separately compiled kernel)
+  int occ[2][2][LS_MAX_ROWS + 1] = {};
+  long long clock_khz = 100000;     // wall-clock rate of the device
+  double wait_seconds = 2.0;        // bound on every dependency wait inside a launch
   long long* trace = nullptr;   // optional phase timestamps of the next ls_loop_step
   int last_grid = 0;
   bool bf16() const { return d.dtype == LS_BF16; }
@@ -230,7 +234,11 @@ ls_status ls_bind_workspace(ls_model* m, void* ws, int max_rows, int max_keys, i
   int dev = 0;
   hipGetDevice(&dev);
   hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-  for (int& o : m->occ) o = 0;
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0) m->clock_khz = khz;
+  for (auto& x : m->occ)
+    for (auto& y : x)
+      for (int& o : y) o = 0;
   launch_fill_i32(m->err, 1, 0, stream);
   return check_hip("ls_bind_workspace");
 }
@@ -281,19 +289,34 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
   a.cnt = m->cnt; a.err = m->err;
   a.init_mode = init_mode; a.gather = gather ? gather + i0 : nullptr; a.Hg = Hg;
   a.do_head = logits != nullptr;
-  int& occ = m->occ[mc];
-  if (!occ) {
-    occ = mega_occupancy(m->bf16(), mc, d.d);
-    if (occ <= 0) return fail(LS_ERR_HIP, "persistent kernel: no resident workgroup fits (M=%d)", mc);
-    occ = std::min(occ, 4);
-  }
-  const int G = occ * m->n_cu;
+  // resident workgroups per CU of the kernel variant that is launched (cached per variant)
+  auto occupancy = [&](bool lng) {
+    int& occ = m->occ[loop_block ? 1 : 0][lng ? 1 : 0][mc];
+    if (!occ) occ = std::min(mega_occupancy(m->bf16(), mc, d.d, loop_block, lng), 4);
+    return occ;
+  };
+  int occ = occupancy(false);
+  if (occ <= 0) return fail(LS_ERR_HIP, "persistent kernel: no resident workgroup fits (M=%d)", mc);
+  int G = occ * m->n_cu;
   // attention units of the finished prefix: 64-key sub-units, several per unit once a single
-  // depth group would give every consumer wave (4 per workgroup) more than one unit
+  // depth group would give every consumer wave (4 per workgroup) more than one unit; those
+  // units are a kernel of their own, whose occupancy may be lower
   const int uk = att_unit_keys(m->bf16());
-  const long long per_wave = (long long)d.n_heads * r->n_fin / ((long long)uk * 4 * G);
-  a.att_sub = (int)std::max(1LL, std::min<long long>(per_wave, LS_ATT_SUB_MAX));
+  auto sub_units = [&](int G_) {
+    const long long per_wave = (long long)d.n_heads * r->n_fin / ((long long)uk * 4 * G_);
+    return (int)std::max(1LL, std::min<long long>(per_wave, LS_ATT_SUB_MAX));
+  };
+  a.att_sub = sub_units(G);
+  if (a.att_sub > 1) {
+    const int occ_l = occupancy(true);
+    if (occ_l <= 0) return fail(LS_ERR_HIP, "persistent kernel: no resident workgroup fits (M=%d)", mc);
+    if (occ_l < occ) {
+      G = occ_l * m->n_cu;
+      a.att_sub = sub_units(G);
+    }
+  }
   a.att_chunks = std::max(1, (r->n_fin + uk * a.att_sub - 1) / (uk * a.att_sub));
+  a.wait_ticks = (long long)(m->wait_seconds * 1e3 * (double)m->clock_khz);
   a.trace = m->trace;
   m->last_grid = G;
   hipError_t e = launch_mega(m->bf16(), a, G, s, loop_block, v);
@@ -395,6 +418,13 @@ ls_status ls_sync_status(ls_model* m, hipStream_t s) {
   if (e != hipSuccess) return fail(LS_ERR_HIP, "error word: %s", hipGetErrorString(e));
   if (h == 5) return fail(LS_ERR_HIP, "a device-side dependency wait timed out (error word 5)");
   if (h) return fail((ls_status)h, "a kernel rejected a descriptor (device error word %d)", h);
+  return LS_OK;
+}
+
+ls_status ls_set_wait_limit(ls_model* m, double seconds) {
+  if (!m) return fail(LS_ERR_INVALID, "ls_set_wait_limit: null model");
+  if (!(seconds >= 0.0) || seconds > 3600.0) return fail(LS_ERR_INVALID, "ls_set_wait_limit: seconds must be in [0, 3600]");
+  m->wait_seconds = seconds;
   return LS_OK;
 }
 

@@ -111,10 +111,20 @@ template <typename T> LS_DEV bool holds_fill(unsigned w);
 template <> LS_DEV bool holds_fill<uint16_t>(unsigned w) { return (w & 0xffffu) == 0xffffu || (w >> 16) == 0xffffu; }
 template <> LS_DEV bool holds_fill<float>(unsigned w) { return w == 0xffffffffu; }
 
-// Every wait below is bounded: after SPIN_LIMIT polls (about a second) the wait gives up and
-// records LS_TIMEOUT in the error word, so a broken dependency ends the kernel with an error
-// instead of hanging the device.
-constexpr int SPIN_LIMIT = 1 << 25;
+// Every wait below is bounded by one deadline per launch on the constant-rate wall clock: each
+// workgroup sets it when it starts (MegaArgs::wait_ticks later; every workgroup of a cooperative
+// launch starts together), and a wait checks it on its first poll and every WAIT_CHECK polls
+// after that.  A wait still unmet at the deadline records LS_TIMEOUT in the error word and gives
+// up; since the deadline is shared, every later wait of the launch gives up after one poll too,
+// so a broken dependency ends the whole launch shortly after the deadline (the remaining work
+// runs on unchecked data) instead of each wait spending a budget of its own.  Only the clock is
+// read in the loops: an error-word load there would delay the wake-up of waits in tight LDS
+// spin loops.
+__shared__ long long ls_wait_deadline;
+constexpr int WAIT_CHECK = 256;
+LS_DEV void set_deadline(long long ticks) {
+  if (threadIdx.x == 0) ls_wait_deadline = (long long)wall_clock64() + ticks;
+}
 // Global counters are polled by up to every workgroup at once; each poll is a memory access
 // to the same line, so polls are spaced (s_sleep units of 64 cycles) to leave that line's
 // bandwidth to the atomics that move the counter.
@@ -123,6 +133,14 @@ constexpr int SPIN_LIMIT = 1 << 25;
 #endif
 constexpr int POLL_SLEEP = LS_POLL_SLEEP;
 constexpr int LS_TIMEOUT = 5;
+
+// Poll count n of a wait: true (after recording LS_TIMEOUT) once the launch's deadline passed.
+LS_DEV bool give_up(int& n, int* err) {
+  if ((++n & (WAIT_CHECK - 1)) != 1) return false;
+  if ((long long)wall_clock64() < ls_wait_deadline) return false;
+  ls_flag(err, LS_TIMEOUT);
+  return true;
+}
 
 // ---- LDS synchronisation among the consumer waves only -----------------------------------------
 
@@ -154,7 +172,7 @@ struct ConsBar {
       int n = 0;
       while (lds_peek(ctr) < gen) {
         __builtin_amdgcn_s_sleep(0);
-        if (++n > SPIN_LIMIT) { ls_flag(err, LS_TIMEOUT); break; }
+        if (give_up(n, err)) break;
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -168,7 +186,7 @@ LS_DEV void wait_ge(const int* c, int target, ConsBar& cb) {
     int n = 0;
     while (ld_acq(c) < target) {
       __builtin_amdgcn_s_sleep(POLL_SLEEP);
-      if (++n > SPIN_LIMIT) { ls_flag(cb.err, LS_TIMEOUT); break; }
+      if (give_up(n, cb.err)) break;
     }
   }
   cb.sync();
@@ -185,7 +203,7 @@ LS_DEV void wait_all_ge(const int* base, int stride, int n, int target, ConsBar&
       if (!done) done = ld_acq(base + (size_t)i * stride) >= target;
       if (__all(done)) break;
       __builtin_amdgcn_s_sleep(POLL_SLEEP);
-      if (++n_polls > SPIN_LIMIT) { if (i == 0) ls_flag(cb.err, LS_TIMEOUT); break; }
+      if (give_up(n_polls, cb.err)) break;
     }
   }
   cb.sync();
@@ -215,7 +233,7 @@ LS_DEV void wait_spread(const int* base, int lo, int hi, ConsBar& cb) {
       if (!done) done = ld_acq(base + (size_t)k * PADC) >= target;
       if (__all(done)) break;
       __builtin_amdgcn_s_sleep(POLL_SLEEP);
-      if (++n_polls > SPIN_LIMIT) { if (k == 0) ls_flag(cb.err, LS_TIMEOUT); break; }
+      if (give_up(n_polls, cb.err)) break;
     }
   }
   cb.sync();
@@ -532,10 +550,7 @@ struct Producer {
           publish_one();
         } else {
           __builtin_amdgcn_s_sleep(0);
-          if (++n > SPIN_LIMIT) {
-            if (lane == 0) ls_flag(a.err, LS_TIMEOUT);
-            break;
-          }
+          if (give_up(n, a.err)) break;
         }
       }
     }
@@ -662,7 +677,7 @@ struct Consumer {
             for (int u = 0; u < NVF; ++u) ok = ok && v[u].x != SENT32 && v[u].y != SENT32 && v[u].z != SENT32 && v[u].w != SENT32;
             if (__all(ok)) break;
             __builtin_amdgcn_s_sleep(POLL_SLEEP);
-            if (++n > SPIN_LIMIT) { if (lane == 0) ls_flag(a.err, LS_TIMEOUT); break; }
+            if (give_up(n, a.err)) break;
           }
         } else {
 #pragma unroll
@@ -742,7 +757,7 @@ struct Consumer {
           for (int j = 0; j < 4; ++j) ok = ok && !holds_fill<T>(v0[j]) && !holds_fill<T>(v1[j]);
           if (__all(ok)) break;
           __builtin_amdgcn_s_sleep(POLL_SLEEP);
-          if (++n > SPIN_LIMIT) { if (lane == 0) ls_flag(a.err, LS_TIMEOUT); break; }
+          if (give_up(n, a.err)) break;
         }
       } else {
         v0 = ld128(R, o0);
@@ -763,7 +778,7 @@ struct Consumer {
       int n = 0;
       while (lds_peek(s.ints + slot) < use + 1) {
         __builtin_amdgcn_s_sleep(0);
-        if (++n > SPIN_LIMIT) { ls_flag(a.err, LS_TIMEOUT); break; }
+        if (give_up(n, a.err)) break;
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -882,7 +897,7 @@ LS_DEV void epilogue(const MegaArgs& a, const CntLayout& cl, const Lds& s, int p
       for (int u = 0; u < 4; ++u) {
         const int m = m0 + 4 * u + (lane >> 4);
         const int hr = m < a.M ? s.hx[m] : -1;
-        const float nv = hr >= 0 ? res[u] + Ts[m * 16 + nl] : 0.f;
+        const float nv = hr >= 0 ? canon_nan(res[u] + Ts[m * 16 + nl]) : 0.f;
         if (m < a.M) {
           if (ph == PH_O) {
             stc(yl + (size_t)m * a.d + n, nv);
@@ -1116,7 +1131,7 @@ LS_DEV void att_unit_wave(const MegaArgs& a, const Lds& s, const CntLayout& cl, 
       if (!done) done = ld_acq(C + cl.o_qkvh + (h * nf + lane) * PADC) >= 1;
       if (__all(done)) break;
       __builtin_amdgcn_s_sleep(POLL_SLEEP);
-      if (++n > SPIN_LIMIT) { if (lane == 0) ls_flag(a.err, LS_TIMEOUT); break; }
+      if (give_up(n, a.err)) break;
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -1271,7 +1286,7 @@ LS_DEV void att_unit_wave_long(const MegaArgs& a, const Lds& s, const CntLayout&
       if (!done) done = ld_acq(C + cl.o_qkvh + (h * nf + lane) * PADC) >= 1;
       if (__all(done)) break;
       __builtin_amdgcn_s_sleep(POLL_SLEEP);
-      if (++n > SPIN_LIMIT) { if (lane == 0) ls_flag(a.err, LS_TIMEOUT); break; }
+      if (give_up(n, a.err)) break;
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -1462,7 +1477,7 @@ LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
         num1 += w * v2[u].y;
       }
     }
-    if (dok) store2_coh<T>(orow + 2 * lane, den > 0.f ? num0 / den : 0.f, den > 0.f ? num1 / den : 0.f);
+    if (dok) store2_coh<T>(orow + 2 * lane, den > 0.f ? canon_nan(num0 / den) : 0.f, den > 0.f ? canon_nan(num1 / den) : 0.f);
   }
 }
 
@@ -1588,7 +1603,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
         int n = 0;
         while (lds_peek(s.ints + 2 * s.NS + 3) < q - s.nred + 1) {
           __builtin_amdgcn_s_sleep(0);
-          if (++n > SPIN_LIMIT) { ls_flag(a.err, LS_TIMEOUT); break; }
+          if (give_up(n, a.err)) break;
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -1643,7 +1658,7 @@ LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int p
       int n = 0;
       while (lds_peek(s.ints + 2 * s.NS + 1 + q % s.nred) < NCONS * (q / s.nred + 1)) {
         __builtin_amdgcn_s_sleep(0);
-        if (++n > SPIN_LIMIT) { ls_flag(a.err, LS_TIMEOUT); break; }
+        if (give_up(n, a.err)) break;
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -1690,6 +1705,7 @@ LS_DEV void mega_body(const MegaArgs& a) {
   const int wv = wave_id();
   // ring counters and the consumer barrier start at zero
   for (int i = threadIdx.x; i < 2 * s.NS + 8; i += MEGA_THREADS) s.ints[i] = 0;
+  set_deadline(a.wait_ticks);
   for (int i = threadIdx.x; i < a.M; i += MEGA_THREADS) {
     s.hx[i] = a.hidx ? a.hidx[i] : i;
     s.rslot[i] = a.slot[i];
@@ -1831,10 +1847,12 @@ static const void* pick(bool bf16, int M, bool loop = true, bool lng = false) {
   return bf16 ? pick_tl<uint16_t, false>(mt, loop) : pick_tl<float, false>(mt, loop);
 }
 
-int mega_occupancy(bool bf16, int M, int d) {
+int mega_occupancy(bool bf16, int M, int d, bool loop_block, bool long_att) {
   const size_t smem = mega_smem_bytes(bf16, M, d);
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick(bf16, M), MEGA_THREADS, smem) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick(bf16, M, loop_block, long_att), MEGA_THREADS, smem) !=
+      hipSuccess)
+    return 0;
   return n;
 }
 

@@ -8,7 +8,8 @@
 // float32 bit pattern of its probability, monotone for non-negative floats) is found by a
 // radix select over the occupied key range, accumulating mass in 32-bit fixed point
 // (floor(p * 2^31)), so the selection is exact for those masses and independent of summation
-// order.  Ties at the crossing key are kept in id order.
+// order.  Ties at the crossing key are kept in id order.  The kept tokens are renormalised by
+// their kept mass (the 31-bit masses plus the fractions they dropped).
 #include "common.h"
 #include "kernels.h"
 
@@ -228,13 +229,23 @@ __global__ __launch_bounds__(DIST_THREADS) void k_dist(const float* logits, int 
   // tokens at kstar kept: enough of them (in id order) to reach TP; at least one
   unsigned n_keep = Pk > 0 ? (TP - above + Pk - 1) / Pk : 0xffffffffu;
   if (n_keep == 0) n_keep = 1;
+  // ties at kstar, and the kept mass for the renormalisation.  The radix select left the exact
+  // 31-bit mass of the tokens above kstar in `above`; what floor(p * 2^31) dropped from each of
+  // them is the fraction of p * 2^31 (exact in float32), summed here, so the kept mass is known
+  // to float32 rounding of that small correction rather than off by up to V * 2^-31 relative
   unsigned nt_local = 0;
+  float fl = 0.f;
 #pragma unroll
-  for (int j = 0; j < PT; ++j) nt_local += __float_as_uint(x[j]) == kstar;
+  for (int j = 0; j < PT; ++j) {
+    const unsigned k = __float_as_uint(x[j]);
+    nt_local += k == kstar;
+    fl += k > kstar ? __builtin_amdgcn_fractf(x[j] * 2147483648.0f) : 0.f;
+  }
   const unsigned n_ties = block_sum_u32(nt_local, redu);
   const unsigned kept_ties = min(n_keep, n_ties);
-  const double Zk = (double)above + (double)kept_ties * (double)Pk;
-  const float scale = (float)(2147483648.0 / Zk);
+  const double kept = ((double)above + (double)block_sum(fl, redf)) * 0x1p-31 +
+                      (double)kept_ties * (double)__uint_as_float(kstar);
+  const float scale = (float)(1.0 / kept);
   if (n_keep >= n_ties) {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {

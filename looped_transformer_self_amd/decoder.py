@@ -413,11 +413,15 @@ class Decoder:
     def snapshot(self):
         """Host state right after prefill.  Decoding never writes the prompt's slots, so
         restoring this state replays the same decode on the same device caches."""
-        return {"free_slots": list(self.free_slots), "free_prob": list(self.free_prob), "fin": list(self.fin),
+        return {"prompt_len": self.prompt_len, "free_slots": list(self.free_slots), "free_prob": list(self.free_prob),
+                "fin": list(self.fin),
                 "tokens": list(self.tokens), "records": list(self.records), "root": (self.root.slot, self.root.pos,
                                                                                       self.root.token)}
 
     def restore(self, snap):
+        """Return to a snapshot, also from another decoder of the same engine (e.g. plain
+        decoding from a speculative decoder's prefill)."""
+        self.prompt_len = snap["prompt_len"]
         self.free_slots = list(snap["free_slots"])
         self.free_prob = list(snap["free_prob"])
         self.fin = list(snap["fin"])

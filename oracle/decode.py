@@ -60,13 +60,14 @@ def decide(cfg, dec, pos, lg_by_depth, prefix=None):
     return decide_fixed(cfg, dec, pos, distributions(cfg, dec, lg_by_depth), prefix)
 
 
-def decide_fixed(cfg, dec, pos, P_by_depth, prefix=None):
+def decide_fixed(cfg, dec, pos, P_by_depth, prefix=None, uniform=None):
     """The decision at one position from its fixed-point readout distributions
-    {depth: P} (P(v) = floor(p(v) * 2^40)), with the position-keyed uniforms."""
+    {depth: P} (P(v) = floor(p(v) * 2^40)), with the position-keyed uniforms (or, for tests of
+    how far a decision is from a boundary, uniform(purpose) in their place)."""
     R, d1, d2 = cfg.R, dec.d1, dec.d2
     seed = dec.seed_s
     residual = getattr(dec, "residual", True)
-    U = lambda purpose: philox.uniform(seed, pos, purpose)
+    U = uniform or (lambda purpose: philox.uniform(seed, pos, purpose))
     P_R = P_by_depth[R]
     rec = {"pos": pos, "x1": -1, "gate": False, "x2": -1, "cands": []}
     if dec.copy:

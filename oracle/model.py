@@ -44,16 +44,28 @@ class KV:
 
 
 class Model:
-    def __init__(self, cfg, weights):
+    def __init__(self, cfg, weights, products="f64"):
+        """products: "f64" (the reference) computes every matrix product in float64.  "f32"
+        computes them with float32 operands and accumulation instead (the stored values are
+        float32-exact, so only the summation precision changes): a second implementation of
+        the same model, used to measure how far rounding-level differences carry through
+        many loop iterations."""
         self.cfg = cfg
         self.dt = cfg.dtype
         # float32 tensors of the model (residual stream, queries, products); left
         # unrounded in the "f64" pinning mode
         self.r32 = (lambda x: x) if cfg.dtype == "f64" else round_f32
-        self.emb = weight_f64(weights["emb"])                     # [V, d], also the tied head
+        wdt = np.float64 if products == "f64" else np.float32
+        if products == "f64":
+            self.mm = lambda a, W: a @ W.T
+        elif products == "f32":
+            self.mm = lambda a, W: (np.asarray(a, np.float32) @ W.T).astype(np.float64)
+        else:
+            raise ValueError(products)
+        self.emb = weight_f64(weights["emb"]).astype(wdt, copy=False)     # [V, d], also the tied head
 
         def conv(layers):
-            return [{k: (weight_f64(v) if k.startswith("W") else np.asarray(v, np.float64))
+            return [{k: (weight_f64(v).astype(wdt, copy=False) if k.startswith("W") else np.asarray(v, np.float64))
                      for k, v in lw.items()} for lw in layers]
 
         self.pre = conv(weights["pre"])
@@ -113,21 +125,21 @@ class Model:
         n = h.shape[0]
         pos = np.arange(first_pos, first_pos + n)
         a = store(self.rmsnorm(h, lw["g1"]), dt)
-        q = R32(a @ lw["Wq"].T)
-        k = R32(a @ lw["Wk"].T)
-        v = R32(a @ lw["Wv"].T)
+        q = R32(self.mm(a, lw["Wq"]))
+        k = R32(self.mm(a, lw["Wk"]))
+        v = R32(self.mm(a, lw["Wv"]))
         q = R32(self.rope(q, pos))
         k = store(self.rope(k, pos), dt)
         v = store(v, dt)
         assert kv.n == first_pos, "positions must be appended in order"
         kv.append(k, v)
         o = store(self.attention(q, kv, first_pos), dt)
-        h = R32(h + R32(o @ lw["Wo"].T))
+        h = R32(h + R32(self.mm(o, lw["Wo"])))
         b = store(self.rmsnorm(h, lw["g2"]), dt)
-        g = R32(b @ lw["Wg"].T)
-        u = R32(b @ lw["Wu"].T)
+        g = R32(self.mm(b, lw["Wg"]))
+        u = R32(self.mm(b, lw["Wu"]))
         act = store(g / (1.0 + np.exp(-g)) * u, dt)                            # silu(g) * u
-        h = R32(h + R32(act @ lw["Wd"].T))
+        h = R32(h + R32(self.mm(act, lw["Wd"])))
         return h
 
     # ---- sequences ---------------------------------------------------------------------
@@ -172,7 +184,7 @@ class Seq:
         for l, lw in enumerate(m.coda):
             h = m.layer(lw, h, first, self.cache("coda", r, l))
         a = store(m.rmsnorm(h, m.g_final), m.dt)
-        return m.r32(a @ m.emb.T)
+        return m.r32(m.mm(a, m.emb))
 
     def extend(self, tokens, depths=None, last_only=True, keep_hidden=False):
         """Append tokens; run P, loops 1..R, and readouts at `depths` (default: all of D).

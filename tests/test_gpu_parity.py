@@ -17,9 +17,16 @@ from oracle import readout as oreadout
 from oracle import sampler as osampler
 from oracle.model import Model
 from synth import configs, inputs, weights
+from oracle import copyprop as ocopyprop
+from tests.decode_checks import check_distribution
 from tests.gpu_helpers import as_f64, branch_rows, kv_values, oracle_row_block, rel_l2, to_dev, tol
 
 pytestmark = pytest.mark.gpu
+
+
+def _L():
+    from looped_transformer_self_amd import _lib
+    return _lib
 
 SMALL_CFGS = [configs.TINY, configs.MINI_OURO, configs.MINI_HUGINN]
 
@@ -90,28 +97,6 @@ def _readout_ref(m, cfg, w, h, pos, keys, coda_blocks, j):
     return round_f32(store(a, cfg.dtype) @ m.emb.T)[0]
 
 
-def _check_dist(pg, lg_ref, greedy, T, top_p, cfg):
-    pr = oreadout.distribution(lg_ref, greedy, T, top_p).astype(np.float64)
-    pg = pg.astype(np.float64)
-    assert abs(pg.sum() - 1) < 1e-5
-    if greedy:
-        top2 = np.sort(lg_ref)[-2:]
-        if top2[1] - top2[0] > 4 * tol(cfg) * np.abs(lg_ref).max():
-            assert np.array_equal(pg, pr)
-        return
-    both = (pg > 0) & (pr > 0)
-    rel = np.abs(pg[both] - pr[both]) / pr[both]
-    assert rel.max() <= (1e-4 if cfg.dtype == "f32" else 0.25), rel.max()
-    diff = np.nonzero((pg > 0) != (pr > 0))[0]
-    if len(diff):
-        p = oreadout.softmax_t(lg_ref, T)
-        order = np.lexsort((np.arange(len(p)), -p))
-        before = np.concatenate([[0.0], np.cumsum(p[order])[:-1]])
-        rank_before = np.empty(len(p)); rank_before[order] = before
-        slack = 1e-5 if cfg.dtype == "f32" else 2e-2
-        assert np.all(np.abs(rank_before[diff] - top_p) <= slack), (len(diff), rank_before[diff])
-
-
 @pytest.mark.parametrize("cfg", SMALL_CFGS, ids=lambda c: c.name)
 @pytest.mark.parametrize("mode", ["greedy", "sample", "sample_t1"])
 @pytest.mark.parametrize("M", [7, 37])
@@ -143,16 +128,23 @@ def test_readout_parity(cfg, mode, M):
         ref = _readout_ref(m, cfg, w, H0[slots[i]], pos[i], fin + anc[i], blocks, depth[i])
         assert rel_l2(lg[i], ref) <= tol(cfg), (i, rel_l2(lg[i], ref))
         assert am[i] == int(np.argmax(lg[i]))
-        _check_dist(pg[out_rows[i]], ref, greedy, T, top_p, cfg)
+        # the distribution: the reference processing of the GPU's own logits
+        check_distribution(pg[out_rows[i]], lg[i], greedy, T, top_p)
 
 
 def _py(P):
     return [int(x) for x in P]
 
 
+def ocopyprop_threshold(tau):
+    """The reference's screening threshold floor(tau * 2^40) (CopyLoop reading)."""
+    return int(tau * (1 << ocopyprop.SHIFT))
+
+
 @pytest.mark.parametrize("V", [37, 1000, 49152])
 def test_verify_bit_exact(V):
     print(f"[verify] V={V}", flush=True)
+    L = _L()
     cfg = replace(configs.TINY, V=V)
     w = weights.make_weights(replace(cfg, V=16), seed=0)
     w["emb"] = np.zeros((V, cfg.d), np.float32)
@@ -168,47 +160,70 @@ def test_verify_bit_exact(V):
     e.probs.copy_(torch.from_numpy(P))
     fx = [osampler.fixed(p) for p in P]
     rng = np.random.Generator(np.random.PCG64(34))
-    n_jobs = 200 if V < 10000 else 40
+    n_jobs = 240 if V < 10000 else 48
     jobs = np.zeros((n_jobs, 10), np.int32)
     us = inputs.uniforms_u32((n_jobs, 24), 35)
     cands_all = []
+    thr_of = {}
     for k in range(n_jobs):
-        op = k % 5
+        op = k % 6
         p, q1, q2 = (int(x) for x in rng.integers(0, n_rows, 3))
         if k % 17 == 0:
             q1 = p
         x1 = osampler.sample(fx[q1], int(us[k, 0]))
         j = jobs[k]
         j[0], j[1], j[2], j[3], j[4] = op, p, q1, q2, x1
+        res = (k // 6) % 3 != 2                      # every third DRAW2 / VERIFY job: non-residual
+        if op in (2, 3) and not res:
+            j[9] = L.LS_JOB_NON_RESIDUAL
         if op == 2:
             j[6] = k % 2
         if op == 3:
-            g, x2 = osampler.draw2(fx[q1], fx[q2], x1, int(us[k, 1]))
+            g, x2 = osampler.draw2(fx[q1], fx[q2], x1, int(us[k, 1]), gated=bool(k % 2), residual=res)
             j[6], j[5] = int(g), x2
-        if op == 4:
+        if op in (4, 5):
             nc = int(rng.integers(0, 17))
             c = rng.choice(V, size=min(nc, V), replace=False).tolist()
             j[7], j[8] = len(cands_all), len(c)
             cands_all.extend(c)
+        if op == 5:
+            # thresholds around the candidates' masses: none, some and all survive
+            tau = [0.0, 1.0 / V, 2.0 / V, 0.5][(k // 6) % 4]
+            thr = ocopyprop_threshold(tau)
+            thr_of[k] = thr
+            j[4:6] = np.array([thr & 0xFFFFFFFF, thr >> 32], np.uint32).view(np.int32)
     out = e.verify(jobs, us, np.asarray(cands_all, np.int32) if cands_all else None)
     assert e.sync_status() == 0
+    got_cands = e.last_cands
     for k in range(n_jobs):
-        op, p, q1, q2, x1, x2, g, co, nc = (int(v) for v in jobs[k][:9])
+        op, p, q1, q2, x1, x2, g, co, nc, fl = (int(v) for v in jobs[k][:10])
         u = [int(v) for v in us[k]]
+        res = not (fl & L.LS_JOB_NON_RESIDUAL)
         if op == 0:
             want = (osampler.sample(fx[p], u[5]), osampler.DRAWN, 0)
         elif op == 1:
             want = (osampler.sample(fx[q1], u[0]), osampler.DRAWN, 0)
         elif op == 2:
-            gate, t = osampler.draw2(fx[q1], fx[q2], x1, u[1], gated=bool(g))
+            gate, t = osampler.draw2(fx[q1], fx[q2], x1, u[1], gated=bool(g), residual=res)
             want = (t, osampler.DRAWN, int(gate))
         elif op == 3:
-            t, o = osampler.verify(fx[p], fx[q1], x1, u[2], u[4], bool(g), fx[q2], x2, u[3])
+            t, o = osampler.verify(fx[p], fx[q1], x1, u[2], u[4], bool(g), fx[q2], x2, u[3], residual=res)
             want = (t, o, 0)
-        else:
+        elif op == 4:
             t, o, jj = osampler.verify_copy(fx[p], cands_all[co:co + nc], u[8:8 + nc], u[4])
             want = (t, o, 0)
             assert out[k, 3] == jj
+        else:
+            cc = cands_all[co:co + nc]
+            keep = [c for c in cc if fx[p][c] >= thr_of[k]]
+            keep.sort(key=lambda c: (-fx[p][c], c))
+            assert out[k, 3] == len(keep)
+            assert got_cands[co:co + len(keep)].tolist() == keep
+            assert sorted(got_cands[co:co + nc].tolist()) == sorted(cc)
+            if keep:
+                want = (-1, L.LS_OUT_SCREENED, 0)
+            else:
+                want = (osampler.sample(fx[p], u[0]), osampler.DRAWN, 0)
         assert tuple(int(v) for v in out[k, :3]) == want, (k, op, out[k], want)
 
 
@@ -329,3 +344,86 @@ def test_bad_key_slots_are_reported_not_faulted(bad):
     rows = e.rows([20, 21], pos, [1, 2], len(fin), anc, C.c_void_p(fin_t.data_ptr()))
     e.loop_step(rows)
     assert e.sync_status() == L.LS_ERR_INVALID
+
+
+READ_MODES = {"greedy": (True, 1.0, 1.0), "t1-p0.9": (False, 1.0, 0.9), "t0.7-p0.95": (False, 0.7, 0.95),
+              "t1-p1": (False, 1.0, 1.0)}
+
+
+@pytest.mark.parametrize("V", [1000, 20000, 49152, 65536])
+@pytest.mark.parametrize("mode", list(READ_MODES))
+def test_readout_distribution_at_benchmark_vocabularies(V, mode):
+    """LoopSpec page, section 2.1 (temperature, top-p, normalisation) at the vocabularies of
+    the benchmark shapes: 49152 (Ouro) and 65536 (Huginn) plus 1000 and 20000, so every
+    register-resident row layout of the distribution kernel runs (16, 32, 48 and 64 ids per
+    thread).  A narrow model (d 256, bf16, the streaming LM-head kernel) keeps the reference
+    cheap; the distribution is compared with the reference processing of the GPU's own
+    logits, element by element."""
+    print(f"[readout-V] V={V} {mode}", flush=True)
+    greedy, T, top_p = READ_MODES[mode]
+    cfg = replace(configs.MINI_OURO, V=V)
+    w = weights.make_weights(cfg, seed=0)
+    S = 64
+    e = _engine(cfg, w, S, max_rows=16, prob_rows=16)
+    m = Model(cfg, {**w, "core": [], "pre": [], "coda": []})
+    M = 5
+    H0 = inputs.hidden_rows(S, cfg.d, seed=70, scale=3.0)
+    e.H.copy_(torch.from_numpy(H0))
+    slots = [3, 9, 17, 30, 41]
+    fin_t = _fin_table([0, 1], S)
+    rows = e.rows(slots, [2] * M, [0, 1, 2, 2, 1], 2, [[]] * M, C.c_void_p(fin_t.data_ptr()),
+                  extra=[np.arange(M, dtype=np.int32)])
+    lg = torch.zeros(M, V, device="cuda")
+    am = torch.zeros(M, dtype=torch.int32, device="cuda")
+    e.readout(rows, greedy, T, top_p, rows.extra[0], argmax=am, logits=lg)
+    assert e.sync_status() == 0
+    lg, am, pg = lg.cpu().numpy(), am.cpu().numpy(), e.probs.cpu().numpy()
+    e.close()
+    from oracle.numerics import round_f32, store
+    nb = 0
+    for i in range(M):
+        ref = round_f32(store(m.rmsnorm(H0[slots[i]][None].astype(np.float64), m.g_final), cfg.dtype) @ m.emb.T)[0]
+        assert rel_l2(lg[i], ref) <= tol(cfg), (i, rel_l2(lg[i], ref))
+        assert am[i] == int(np.argmax(lg[i]))
+        nb += check_distribution(pg[i], lg[i], greedy, T, top_p)
+    print(f"  top-p boundary tokens differing: {nb}", flush=True)
+
+
+def test_wait_limit_gives_up_and_reports():
+    """Every dependency wait inside a launch is bounded.  With the bound forced to zero from
+    the host, every wait that would block gives up at its first poll: the launch still runs
+    to its end (no wait is left spinning), it is reported as a timeout, and after the bound
+    is restored and the workspace re-bound the same call is correct again."""
+    import time
+    L = _L()
+    cfg = configs.MINI_OURO
+    S = 128
+    w = weights.make_weights(cfg, seed=0)
+    e = _engine(cfg, w, S)
+    m = Model(cfg, w)
+    kv = _fill_cache(e, cfg, "core", cfg.R * cfg.L, S, seed=81)
+    H0 = inputs.hidden_rows(S, cfg.d, seed=82)
+    rng = np.random.Generator(np.random.PCG64(83))
+    fin, slots, anc, pos, depth = branch_rows(3, 40, lambda i: 1 + i, rng, S)
+    fin_t = _fin_table(fin, S)
+    L.check(L.lib.ls_set_wait_limit(e.h, 0.0), "ls_set_wait_limit")
+    e.H.copy_(torch.from_numpy(H0))
+    t0 = time.perf_counter()
+    e.loop_step(e.rows(slots, pos, depth, len(fin), anc, C.c_void_p(fin_t.data_ptr())))
+    st = e.sync_status()
+    dt = time.perf_counter() - t0
+    assert st == L.LS_ERR_HIP and b"timed out" in L.lib.ls_last_error(), (st, L.lib.ls_last_error())
+    assert dt < 1.0, dt
+    L.check(L.lib.ls_set_wait_limit(e.h, 2.0), "ls_set_wait_limit")
+    L.check(L.lib.ls_bind_workspace(e.h, e.ws_ptr, e.max_rows, e.max_keys, e.max_jobs, e.stream_ptr()),
+            "ls_bind_workspace")
+    e.H.copy_(torch.from_numpy(H0))
+    e.loop_step(e.rows(slots, pos, depth, len(fin), anc, C.c_void_p(fin_t.data_ptr())))
+    assert e.sync_status() == L.LS_OK
+    Hg = e.H.cpu().numpy()
+    for i in range(3):
+        k = depth[i]
+        blocks = [as_f64(kv[(k - 1) * cfg.L + l], cfg) for l in range(cfg.L)]
+        h_ref, _ = oracle_row_block(m, m.core, H0[slots[i]][None].astype(np.float64), pos[i], fin + anc[i], blocks, cfg)
+        assert rel_l2(Hg[slots[i]], h_ref[0]) <= tol(cfg)
+    e.close()

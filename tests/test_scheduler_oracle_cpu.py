@@ -71,6 +71,8 @@ class OracleEngine:
         assert len(set(rows.slots)) == len(rows.slots)
         self.loop_rows.append(rows.n)
 
+    noise = 0.0          # relative noise planted on the logits (tests of the decode checker)
+
     def readout(self, rows, greedy, T, top_p, out_rows, logits=None):
         for i in range(rows.n):
             o = int(out_rows[i])
@@ -80,6 +82,11 @@ class OracleEngine:
             if seq not in self.memo:
                 self.memo[seq] = self.model.new_seq().extend(list(seq))
             lg = self.memo[seq][self.cfg.readout_depths[rows.depth[i]]]
+            if self.noise:
+                rng = np.random.Generator(np.random.PCG64(hash(seq) & 0xFFFFFFFF))
+                lg = (lg * (1 + self.noise * rng.standard_normal(len(lg)))).astype(np.float32)
+            if logits is not None:
+                logits[i] = torch.from_numpy(np.asarray(lg, np.float32))
             self.probs[o] = torch.from_numpy(oreadout.distribution(lg, greedy, T, top_p))
 
     def verify(self, jobs, uniforms, cands=None):
@@ -207,3 +214,34 @@ def test_branch_cap_keeps_the_serial_decisions():
         d, e, toks, ref_toks, ref_recs = _run(wl, replace(dec, max_branches=cap), 16)
         _compare(d, toks, ref_toks, ref_recs, 16)
         assert max(d.rows_hist) <= cap + 1
+
+
+@pytest.mark.parametrize("noise", [0.0, 3e-3])
+def test_decode_checker(noise):
+    """The per-position checker the GPU decode tests use (tests/decode_checks.py), run on the
+    CPU stand-in: with exact readouts every decision agrees with the reference; with noise
+    planted on the readout logits the checker still passes (every decision equals the
+    sampler's on the engine's own distributions, and every disagreement with the reference's
+    own decision is flagged as within the measured error of a boundary), and a planted wrong
+    decision is caught."""
+    from tests.decode_checks import check_stream
+    cfg, dec = CASES["sample-gated"]
+    cfg = replace(cfg, dtype="bf16")           # the bf16 logit tolerance admits the planted noise
+    w = weights.make_weights(cfg, seed=dec.seed_w)
+    prompt = [int(t) for t in inputs.prompt(cfg.V, dec.prompt_len, seed=dec.seed_p)]
+    e = OracleEngine(cfg, w)
+    e.noise = noise
+    d = D.Decoder(e, dec, "spec", trace=True)
+    d.prefill(prompt)
+    n_new = 16
+    toks = d.decode(n_new)
+    recs = d.records[:n_new]
+    rep = check_stream(cfg, dec, e.model, prompt, toks, recs)
+    if noise == 0.0:
+        assert rep["oracle_agree"] == n_new and rep["max_rel_l2"] < 1e-12, rep
+    else:
+        assert rep["max_rel_l2"] > 1e-4
+    bad = [dict(r) for r in recs]
+    bad[5]["x1"] = (bad[5]["x1"] + 1) % cfg.V
+    with pytest.raises(AssertionError):
+        check_stream(cfg, dec, e.model, prompt, toks, bad)
