@@ -230,6 +230,24 @@ ls_status ls_verify(ls_model *m, const ls_verify_job *jobs, int n_jobs, const fl
  * (LS_ERR_INVALID for a rejected descriptor) or LS_ERR_HIP for a runtime error. */
 ls_status ls_sync_status(ls_model *m, hipStream_t stream);
 
+/* ls_loop_step without a caller workspace, for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * kernels and results as ls_loop_step, with every buffer the kernels need beyond the caller's
+ * inputs and outputs in the library's static scratch (LS_STATIC_SCRATCH_BYTES of device
+ * memory per GPU, held until the process ends).  No workspace needs to be bound; the call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).  The model's layer
+ * and rotary tables are copied into the scratch when a model other than the last one to use
+ * it on this GPU calls.  Calls that would need more scratch than LS_STATIC_SCRATCH_BYTES (many
+ * rows with long prefixes) fail with LS_ERR_CAPACITY before anything is enqueued.  Every call on
+ * a GPU shares that GPU's scratch: calls that overlap on one GPU (other streams, other threads,
+ * other models) race and must be serialised by the caller.  err_out: optional device int32
+ * that the caller zeroes; descriptor errors and wait timeouts of this call are recorded there
+ * (first error wins, codes as in the workspace error word: 1 rejected descriptor, 5 timeout);
+ * with NULL they are recorded in the scratch and not reported. */
+#define LS_STATIC_SCRATCH_BYTES (64u << 20)
+ls_status ls_loop_step_static(ls_model *m, const ls_rows *rows, float *H, const ls_kv *kv, int *err_out,
+                              hipStream_t stream);
+
 /* Bound on every dependency wait inside one layer-kernel launch (default 2 s): workgroups
  * wait for each other's results, and a wait still unmet that long after the launch started
  * gives up, records a timeout in the error word (ls_sync_status then returns LS_ERR_HIP) and

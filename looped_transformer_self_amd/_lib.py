@@ -15,6 +15,7 @@ LS_OK, LS_ERR_INVALID, LS_ERR_UNSUPPORTED, LS_ERR_CAPACITY, LS_ERR_HIP = range(5
 LS_F32, LS_BF16 = 0, 1
 LS_MAX_READOUT_DEPTHS = 8
 LS_MAX_ROWS = 128
+LS_STATIC_SCRATCH_BYTES = 64 << 20
 LS_UNIFORMS_PER_JOB = 24
 LS_JOB_SAMPLE, LS_JOB_DRAW1, LS_JOB_DRAW2, LS_JOB_VERIFY, LS_JOB_VERIFY_COPY, LS_JOB_SCREEN = range(6)
 LS_JOB_NON_RESIDUAL = 1
@@ -22,7 +23,7 @@ LS_OUT_ACC1, LS_OUT_ACC2, LS_OUT_RESAMPLED, LS_OUT_DRAWN, LS_OUT_ACC_COPY, LS_OU
 
 EXPORTS = ("ls_last_error", "ls_model_create", "ls_model_destroy", "ls_workspace_bytes", "ls_bind_workspace",
            "ls_prelude", "ls_loop_step", "ls_readout", "ls_verify", "ls_sync_status", "ls_philox_uniforms",
-           "ls_debug_trace", "ls_set_wait_limit")
+           "ls_debug_trace", "ls_set_wait_limit", "ls_loop_step_static")
 
 
 class ls_model_desc(C.Structure):
@@ -85,6 +86,7 @@ def _load():
         "ls_sync_status": (C.c_int, [P, P]),
         "ls_debug_trace": (C.c_int, [P, P, C.POINTER(C.c_int)]),
         "ls_set_wait_limit": (C.c_int, [P, C.c_double]),
+        "ls_loop_step_static": (C.c_int, [P, C.POINTER(ls_rows), P, C.POINTER(ls_kv), P, P]),
         "ls_philox_uniforms": (None, [C.c_uint64, C.c_int64, C.POINTER(C.c_int32), C.c_int,
                                       C.POINTER(C.c_uint32)]),
     }

@@ -1,7 +1,9 @@
 // C ABI of libloopspec: argument validation, workspace carving and kernel orchestration for
 // ls_prelude / ls_loop_step / ls_readout / ls_verify (see include/loopspec.h).
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -15,6 +17,7 @@ using namespace ls;
 namespace {
 
 thread_local char g_err[512] = "";
+std::atomic<unsigned long long> g_model_ids{0};   // ids of created models
 
 ls_status fail(ls_status st, const char* fmt, ...) {
   va_list ap;
@@ -28,13 +31,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-struct ls_model {
-  ls_model_desc d;
-  const void* emb = nullptr;
-  const float* g_final = nullptr;
-  std::vector<ls_layer_ptrs> pre, core, coda;
-  // bound workspace
-  char* ws = nullptr;
+// Device buffers of one workspace (a caller's, bound by ls_bind_workspace, or the library's
+// static scratch for ls_loop_step_static): plain pointers into it.
+struct Workspace {
+  char* base = nullptr;
   int max_rows = 0, max_keys = 0, max_jobs = 0;
   int* err = nullptr;
   int32_t *slot_ok = nullptr, *dep_ok = nullptr, *row_ok = nullptr;
@@ -45,11 +45,20 @@ struct ls_model {
   void *o = nullptr, *act = nullptr;
   double* invf = nullptr;
   float* rope = nullptr;
-  std::vector<double> host_invf;
   float *patt = nullptr, *ssq = nullptr;
   int* cnt = nullptr;
   LayerW *tab_pre = nullptr, *tab_core = nullptr, *tab_coda = nullptr;
-  std::vector<LayerW> host_tab;
+};
+
+struct ls_model {
+  ls_model_desc d;
+  unsigned long long id = 0;        // unique per created model
+  const void* emb = nullptr;
+  const float* g_final = nullptr;
+  std::vector<ls_layer_ptrs> pre, core, coda;
+  std::vector<LayerW> host_tab;     // device layer table contents (prelude, core, coda)
+  std::vector<double> host_invf;    // rotary frequencies theta^(-2i/hd)
+  Workspace w;                      // the bound workspace
   int n_cu = 0;
   // resident workgroups per CU of the persistent kernel, by [loop-block symbol][long-prefix
   // attention][rows per launch] (each variant is a separately compiled kernel)
@@ -110,23 +119,85 @@ Carve carve(const ls_model* m, int max_rows, int max_keys, int max_jobs) {
   return c;
 }
 
+// Pointers of a workspace laid out by `c` from `b`.
+Workspace carve_into(const Carve& c, char* b) {
+  Workspace w;
+  w.base = b;
+  w.max_rows = c.max_rows; w.max_keys = c.max_keys; w.max_jobs = c.max_jobs;
+  w.err = (int*)(b + c.off_err);
+  w.slot_ok = (int32_t*)(b + c.off_slot);
+  w.dep_ok = (int32_t*)(b + c.off_dep);
+  w.row_ok = (int32_t*)(b + c.off_row);
+  w.q = (float*)(b + c.off_q);
+  w.hc = (float*)(b + c.off_hc);
+  w.logits = (float*)(b + c.off_logits);
+  w.Xs = (float*)(b + c.off_Xs);
+  w.Ys = (float*)(b + c.off_Ys);
+  w.o = b + c.off_o;
+  w.act = b + c.off_act;
+  w.invf = (double*)(b + c.off_invf);
+  w.rope = (float*)(b + c.off_rope);
+  w.patt = (float*)(b + c.off_patt);
+  w.ssq = (float*)(b + c.off_ssq);
+  w.cnt = (int*)(b + c.off_cnt);
+  return w;
+}
+
 ls_status check_hip(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(LS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return LS_OK;
 }
 
+// The model's layer table (into w.tab_*) and rotary frequencies (w.invf) go to the device
+// (stream-ordered copies from the host vectors built at model creation).
+ls_status upload_tables(ls_model* m, Workspace& w, hipStream_t stream, const char* who);
+
+// Where the layer table and the rotary frequencies live in workspace w.
+void set_tables(const ls_model* m, Workspace& w, LayerW* tab, double* invf) {
+  w.tab_pre = tab;
+  w.tab_core = tab + m->pre.size();
+  w.tab_coda = tab + m->pre.size() + m->core.size();
+  w.invf = invf;
+}
+
+// Device attributes the launches need (multiprocessor count, wall-clock rate), once per bind.
+ls_status device_setup(ls_model* m) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || m->n_cu <= 0)
+    return fail(LS_ERR_HIP, "no usable current device");
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0) m->clock_khz = khz;
+  for (auto& x : m->occ)
+    for (auto& y : x)
+      for (int& o : y) o = 0;
+  return LS_OK;
+}
+
 ls_status check_rows(const ls_model* m, const ls_rows* r, const char* who) {
   if (!m || !r) return fail(LS_ERR_INVALID, "%s: null model or rows", who);
-  if (!m->ws) return fail(LS_ERR_INVALID, "%s: no workspace bound", who);
+  if (!m->w.base) return fail(LS_ERR_INVALID, "%s: no workspace bound", who);
   if (r->n < 0 || r->n_fin < 0 || r->max_anc < 0) return fail(LS_ERR_INVALID, "%s: negative sizes", who);
-  if (r->n > m->max_rows) return fail(LS_ERR_CAPACITY, "%s: %d rows > workspace max_rows %d", who, r->n, m->max_rows);
-  if ((long long)r->n_fin + r->max_anc + 1 > m->max_keys)
+  if (r->n > m->w.max_rows) return fail(LS_ERR_CAPACITY, "%s: %d rows > workspace max_rows %d", who, r->n, m->w.max_rows);
+  if ((long long)r->n_fin + r->max_anc + 1 > m->w.max_keys)
     return fail(LS_ERR_CAPACITY, "%s: n_fin + max_anc + 1 = %lld > workspace max_keys %d", who,
-                (long long)r->n_fin + r->max_anc + 1, m->max_keys);
+                (long long)r->n_fin + r->max_anc + 1, m->w.max_keys);
   if (r->n > 0 && (!r->slot || !r->pos || !r->anc_off)) return fail(LS_ERR_INVALID, "%s: null row array", who);
   if (r->n_fin > 0 && !r->fin_slots) return fail(LS_ERR_INVALID, "%s: null fin_slots", who);
   if (r->max_anc > 0 && !r->anc_slots) return fail(LS_ERR_INVALID, "%s: null anc_slots", who);
+  return LS_OK;
+}
+
+ls_status upload_tables(ls_model* m, Workspace& w, hipStream_t stream, const char* who) {
+  hipError_t e = hipMemcpyAsync(w.invf, m->host_invf.data(), m->host_invf.size() * sizeof(double),
+                                hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return fail(LS_ERR_HIP, "%s: rotary table upload: %s", who, hipGetErrorString(e));
+  if (!m->host_tab.empty()) {
+    e = hipMemcpyAsync(w.tab_pre, m->host_tab.data(), m->host_tab.size() * sizeof(LayerW), hipMemcpyHostToDevice,
+                       stream);
+    if (e != hipSuccess) return fail(LS_ERR_HIP, "%s: layer table upload: %s", who, hipGetErrorString(e));
+  }
   return LS_OK;
 }
 
@@ -166,11 +237,19 @@ ls_status ls_model_create(const ls_model_desc* desc, const ls_weight_ptrs* w, ls
     return fail(LS_ERR_INVALID, "ls_model_create: null layer weight");
   ls_model* m = new ls_model();
   m->d = d;
+  m->id = ++g_model_ids;
   m->emb = w->emb;
   m->g_final = w->g_final;
   m->core.assign(w->core, w->core + d.L);
   if (d.L_pre) m->pre.assign(w->pre, w->pre + d.L_pre);
   if (d.L_coda) m->coda.assign(w->coda, w->coda + d.L_coda);
+  auto add = [&](const std::vector<ls_layer_ptrs>& v) {
+    for (const auto& p : v) m->host_tab.push_back(LayerW{p.Wq, p.Wk, p.Wv, p.Wo, p.Wg, p.Wu, p.Wd, p.g1, p.g2});
+  };
+  add(m->pre); add(m->core); add(m->coda);
+  m->host_invf.resize(d.head_dim / 2);
+  for (int i = 0; i < d.head_dim / 2; ++i)
+    m->host_invf[i] = std::pow((double)d.rope_theta, -2.0 * (double)i / (double)d.head_dim);
   *out = m;
   return LS_OK;
 }
@@ -189,57 +268,15 @@ ls_status ls_bind_workspace(ls_model* m, void* ws, int max_rows, int max_keys, i
   if ((uintptr_t)ws % 256) return fail(LS_ERR_INVALID, "ls_bind_workspace: workspace not 256-byte aligned");
   const Carve c = carve(m, max_rows, max_keys, max_jobs);
   char* b = (char*)ws;
-  m->ws = b;
-  m->max_rows = max_rows; m->max_keys = max_keys; m->max_jobs = max_jobs;
-  m->err = (int*)(b + c.off_err);
-  m->slot_ok = (int32_t*)(b + c.off_slot);
-  m->dep_ok = (int32_t*)(b + c.off_dep);
-  m->row_ok = (int32_t*)(b + c.off_row);
-  m->q = (float*)(b + c.off_q);
-  m->hc = (float*)(b + c.off_hc);
-  m->logits = (float*)(b + c.off_logits);
-  m->Xs = (float*)(b + c.off_Xs);
-  m->Ys = (float*)(b + c.off_Ys);
-  m->o = b + c.off_o;
-  m->act = b + c.off_act;
-  m->invf = (double*)(b + c.off_invf);
-  m->rope = (float*)(b + c.off_rope);
-  m->patt = (float*)(b + c.off_patt);
-  m->ssq = (float*)(b + c.off_ssq);
-  m->cnt = (int*)(b + c.off_cnt);
-  LayerW* tab = (LayerW*)(b + c.off_tab);
-  m->host_tab.clear();
-  auto add = [&](const std::vector<ls_layer_ptrs>& v) {
-    for (const auto& p : v) m->host_tab.push_back(LayerW{p.Wq, p.Wk, p.Wv, p.Wo, p.Wg, p.Wu, p.Wd, p.g1, p.g2});
-  };
-  add(m->pre); add(m->core); add(m->coda);
-  m->tab_pre = tab;
-  m->tab_core = tab + m->pre.size();
-  m->tab_coda = tab + m->pre.size() + m->core.size();
-  m->host_invf.resize(m->d.head_dim / 2);
-  for (int i = 0; i < m->d.head_dim / 2; ++i)
-    m->host_invf[i] = std::pow((double)m->d.rope_theta, -2.0 * (double)i / (double)m->d.head_dim);
-  {
-    hipError_t e = hipMemcpyAsync(m->invf, m->host_invf.data(), m->host_invf.size() * sizeof(double),
-                                  hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return fail(LS_ERR_HIP, "ls_bind_workspace: rotary table upload: %s", hipGetErrorString(e));
-  }
-  if (!m->host_tab.empty()) {
-    hipError_t e = hipMemcpyAsync(tab, m->host_tab.data(), m->host_tab.size() * sizeof(LayerW), hipMemcpyHostToDevice,
-                                  stream);
-    if (e != hipSuccess) return fail(LS_ERR_HIP, "ls_bind_workspace: layer table upload: %s", hipGetErrorString(e));
-    e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return fail(LS_ERR_HIP, "ls_bind_workspace: %s", hipGetErrorString(e));
-  }
-  int dev = 0;
-  hipGetDevice(&dev);
-  hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-  int khz = 0;
-  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0) m->clock_khz = khz;
-  for (auto& x : m->occ)
-    for (auto& y : x)
-      for (int& o : y) o = 0;
-  launch_fill_i32(m->err, 1, 0, stream);
+  m->w = carve_into(c, b);
+  set_tables(m, m->w, (LayerW*)(b + c.off_tab), (double*)(b + c.off_invf));
+  ls_status st = upload_tables(m, m->w, stream, "ls_bind_workspace");
+  if (st) return st;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(LS_ERR_HIP, "ls_bind_workspace: %s", hipGetErrorString(e));
+  st = device_setup(m);
+  if (st) return st;
+  launch_fill_i32(m->w.err, 1, 0, stream);
   return check_hip("ls_bind_workspace");
 }
 
@@ -259,7 +296,7 @@ ValidateArgs validate_args(ls_model* m, const ls_rows* r, const int32_t* dep, in
   ValidateArgs v;
   v.n = r->n; v.slot = r->slot; v.dep = dep; v.pos = r->pos; v.anc_off = r->anc_off;
   v.dep_lo = dep_lo; v.dep_hi = dep_hi; v.n_fin = r->n_fin; v.max_anc = r->max_anc; v.S = m->d.slot_capacity;
-  v.slot_ok = m->slot_ok; v.dep_ok = m->dep_ok; v.row_ok = m->row_ok; v.err = m->err;
+  v.slot_ok = m->w.slot_ok; v.dep_ok = m->w.dep_ok; v.row_ok = m->w.row_ok; v.err = m->w.err;
   return v;
 }
 
@@ -275,18 +312,18 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
   a.theta = d.rope_theta; a.eps = d.norm_eps;
   a.layers = tab; a.n_layers = n_layers;
   a.g_final = m->g_final; a.emb = m->emb;
-  a.H = H; a.hidx = hidx ? hidx + i0 : nullptr; a.Xs = m->Xs; a.Ys = m->Ys;
-  a.slot = m->slot_ok + i0; a.pos = r->pos + i0; a.dep = dep ? dep + i0 : nullptr;
+  a.H = H; a.hidx = hidx ? hidx + i0 : nullptr; a.Xs = m->w.Xs; a.Ys = m->w.Ys;
+  a.slot = m->w.slot_ok + i0; a.pos = r->pos + i0; a.dep = dep ? dep + i0 : nullptr;
   a.fin = r->fin_slots; a.anc_off = r->anc_off + i0; a.anc = r->anc_slots;
   a.tokens = tokens ? tokens + i0 : nullptr;
   a.n_fin = r->n_fin;
   a.kv = kv; a.dep_off = dep_off; a.blk_mul = blk_mul; a.layer0 = 0; a.S = d.slot_capacity;
-  a.q = m->q; a.o = m->o; a.act = m->act;
+  a.q = m->w.q; a.o = m->w.o; a.act = m->w.act;
   a.logits = logits; a.ldo = d.V;
-  a.inv_freq = m->invf;
-  a.rope = m->rope;
-  a.patt = m->patt; a.ssq = m->ssq;
-  a.cnt = m->cnt; a.err = m->err;
+  a.inv_freq = m->w.invf;
+  a.rope = m->w.rope;
+  a.patt = m->w.patt; a.ssq = m->w.ssq;
+  a.cnt = m->w.cnt; a.err = m->w.err;
   a.init_mode = init_mode; a.gather = gather ? gather + i0 : nullptr; a.Hg = Hg;
   a.do_head = logits != nullptr;
   // resident workgroups per CU of the kernel variant that is launched (cached per variant)
@@ -340,7 +377,7 @@ ls_status ls_prelude(ls_model* m, const ls_rows* r, const int32_t* tokens, float
     if (e != hipSuccess) return fail(LS_ERR_HIP, "ls_prelude: embedding launch: %s", hipGetErrorString(e));
     return LS_OK;
   }
-  st = run_mega(m, r, 0, r->n, H, m->slot_ok, m->tab_pre, d.L_pre, kv->pre, nullptr, 0, 0, 1, tokens, nullptr, nullptr,
+  st = run_mega(m, r, 0, r->n, H, m->w.slot_ok, m->w.tab_pre, d.L_pre, kv->pre, nullptr, 0, 0, 1, tokens, nullptr, nullptr,
                 nullptr, s, validate_args(m, r, nullptr, 0, 0));
   if (st) return st;
   return check_hip("ls_prelude");
@@ -353,10 +390,86 @@ ls_status ls_loop_step(ls_model* m, const ls_rows* r, float* H, const ls_kv* kv,
   if (r->n && !r->depth) return fail(LS_ERR_INVALID, "ls_loop_step: null depth");
   if (r->n == 0) return LS_OK;
   const ls_model_desc& d = m->d;
-  st = run_mega(m, r, 0, r->n, H, m->slot_ok, m->tab_core, d.L, kv->core, m->dep_ok, -1, d.L, 0, nullptr, nullptr,
+  st = run_mega(m, r, 0, r->n, H, m->w.slot_ok, m->w.tab_core, d.L, kv->core, m->w.dep_ok, -1, d.L, 0, nullptr, nullptr,
                 nullptr, nullptr, s, validate_args(m, r, r->depth, 1, d.R), true);
   if (st) return st;
   return check_hip("ls_loop_step");
+}
+
+}  // extern "C"
+
+// ---- the loop step without a caller workspace -----------------------------------------------
+// The device memory of ls_loop_step_static is this file-scope array: one copy per GPU, held
+// until the process ends.  It starts with a header (error word, rotary frequencies, layer
+// table) followed by the loop step's buffers laid out as in a workspace.  Host code never uses
+// the array's name as an address: each device's address comes from hipGetSymbolAddress at the
+// first call on that device, with that device current.
+static __device__ __align__(256) char scratch[LS_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t STATIC_INVF = 256, STATIC_TAB = 1280, STATIC_HDR = 72 * 1024;
+constexpr int MAX_DEVICES = 64;
+struct StaticScratch {
+  char* ptr = nullptr;          // device address of `scratch` on this device
+  unsigned long long owner = 0; // model whose tables the header holds
+};
+StaticScratch g_static[MAX_DEVICES];
+std::mutex g_static_mu;
+
+}  // namespace
+
+extern "C" {
+
+ls_status ls_loop_step_static(ls_model* m, const ls_rows* r, float* H, const ls_kv* kv, int* err_out, hipStream_t s) {
+  if (!m || !r || !H || !kv || !kv->core) return fail(LS_ERR_INVALID, "ls_loop_step_static: null argument");
+  if (r->n < 0 || r->n_fin < 0 || r->max_anc < 0) return fail(LS_ERR_INVALID, "ls_loop_step_static: negative sizes");
+  if (r->n > LS_MAX_ROWS) return fail(LS_ERR_CAPACITY, "ls_loop_step_static: %d rows > %d", r->n, LS_MAX_ROWS);
+  if (r->n > 0 && (!r->slot || !r->pos || !r->anc_off || !r->depth))
+    return fail(LS_ERR_INVALID, "ls_loop_step_static: null row array");
+  if (r->n_fin > 0 && !r->fin_slots) return fail(LS_ERR_INVALID, "ls_loop_step_static: null fin_slots");
+  if (r->max_anc > 0 && !r->anc_slots) return fail(LS_ERR_INVALID, "ls_loop_step_static: null anc_slots");
+  if (r->n == 0) return LS_OK;
+  const long long keys = (long long)r->n_fin + r->max_anc + 1;
+  if (keys > (1LL << 30)) return fail(LS_ERR_CAPACITY, "ls_loop_step_static: %lld keys", keys);
+  const Carve c = carve(m, r->n, (int)keys, 0);
+  if (STATIC_HDR + c.total > (size_t)LS_STATIC_SCRATCH_BYTES)
+    return fail(LS_ERR_CAPACITY, "ls_loop_step_static: %d rows with %lld keys need %zu bytes of scratch, the static "
+                "scratch holds %zu", r->n, keys, STATIC_HDR + c.total, (size_t)LS_STATIC_SCRATCH_BYTES);
+  if (STATIC_TAB + m->host_tab.size() * sizeof(LayerW) > STATIC_HDR || m->host_invf.size() * sizeof(double) > STATIC_TAB - STATIC_INVF)
+    return fail(LS_ERR_UNSUPPORTED, "ls_loop_step_static: too many layers for the scratch header");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+    return fail(LS_ERR_HIP, "ls_loop_step_static: no usable current device");
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticScratch& ss = g_static[dev];
+  if (!ss.ptr) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(LS_ERR_HIP, "ls_loop_step_static: scratch address: %s", hipGetErrorString(e));
+    ss.ptr = (char*)p;
+  }
+  if (!m->n_cu) {
+    ls_status st = device_setup(m);
+    if (st) return st;
+  }
+  Workspace w = carve_into(c, ss.ptr + STATIC_HDR);
+  set_tables(m, w, (LayerW*)(ss.ptr + STATIC_TAB), (double*)(ss.ptr + STATIC_INVF));
+  w.err = err_out ? err_out : (int*)ss.ptr;
+  if (ss.owner != m->id) {
+    ls_status st = upload_tables(m, w, s, "ls_loop_step_static");
+    if (st) return st;
+    ss.owner = m->id;
+  }
+  if (!err_out) launch_fill_i32(w.err, 1, 0, s);
+  const Workspace saved = m->w;
+  m->w = w;
+  const ls_model_desc& d = m->d;
+  ls_status st = run_mega(m, r, 0, r->n, H, m->w.slot_ok, m->w.tab_core, d.L, kv->core, m->w.dep_ok, -1, d.L, 0, nullptr,
+                          nullptr, nullptr, nullptr, s, validate_args(m, r, r->depth, 1, d.R), true);
+  m->w = saved;
+  if (st) return st;
+  return check_hip("ls_loop_step_static");
 }
 
 ls_status ls_readout(ls_model* m, const ls_rows* r, const float* H, const ls_sampling* smp, float* probs,
@@ -372,7 +485,7 @@ ls_status ls_readout(ls_model* m, const ls_rows* r, const float* H, const ls_sam
   if (!out_rows && n_prob_rows < r->n) return fail(LS_ERR_INVALID, "ls_readout: n_prob_rows < rows");
   if (r->n == 0) return LS_OK;
   const ls_model_desc& d = m->d;
-  float* lg = logits ? logits : m->logits;
+  float* lg = logits ? logits : m->w.logits;
   const ValidateArgs v = validate_args(m, r, r->depth, 0, d.n_readout - 1), none{};
   if (!d.L_coda && m->bf16() && d.d % 256 == 0 && LS_HEAD_KERNEL) {
     // no coda layers: the streaming head kernel per 16 rows, which checks its rows itself
@@ -380,41 +493,41 @@ ls_status ls_readout(ls_model* m, const ls_rows* r, const float* H, const ls_sam
       const int mc = std::min(16, r->n - i0);
       launch_head(H, v, i0, mc, d.d, d.V, m->emb, m->g_final, d.norm_eps, lg + (size_t)i0 * d.V, d.V, s);
     }
-    launch_dist(lg, r->n, d.V, smp->greedy, smp->temperature, smp->top_p, probs, out_rows, n_prob_rows, argmax, m->err, s);
+    launch_dist(lg, r->n, d.V, smp->greedy, smp->temperature, smp->top_p, probs, out_rows, n_prob_rows, argmax, m->w.err, s);
     return check_hip("ls_readout");
   }
   for (int i0 = 0; i0 < r->n; i0 += 16) {
     const int mc = std::min(16, r->n - i0);
     if (d.L_coda)
-      st = run_mega(m, r, i0, mc, m->hc, m->row_ok, m->tab_coda, d.L_coda, kv->coda, m->dep_ok, 0, d.L_coda, 2,
-                    nullptr, m->slot_ok, H, lg + (size_t)i0 * d.V, s, i0 == 0 ? v : none);
+      st = run_mega(m, r, i0, mc, m->w.hc, m->w.row_ok, m->w.tab_coda, d.L_coda, kv->coda, m->w.dep_ok, 0, d.L_coda, 2,
+                    nullptr, m->w.slot_ok, H, lg + (size_t)i0 * d.V, s, i0 == 0 ? v : none);
     else
-      st = run_mega(m, r, i0, mc, (float*)H, m->slot_ok, nullptr, 0, nullptr, nullptr, 0, 0, 0, nullptr, nullptr,
+      st = run_mega(m, r, i0, mc, (float*)H, m->w.slot_ok, nullptr, 0, nullptr, nullptr, 0, 0, 0, nullptr, nullptr,
                     nullptr, lg + (size_t)i0 * d.V, s, i0 == 0 ? v : none);
     if (st) return st;
   }
-  launch_dist(lg, r->n, d.V, smp->greedy, smp->temperature, smp->top_p, probs, out_rows, n_prob_rows, argmax, m->err, s);
+  launch_dist(lg, r->n, d.V, smp->greedy, smp->temperature, smp->top_p, probs, out_rows, n_prob_rows, argmax, m->w.err, s);
   return check_hip("ls_readout");
 }
 
 ls_status ls_verify(ls_model* m, const ls_verify_job* jobs, int n_jobs, const float* probs, int n_prob_rows,
                     int32_t* cands, int n_cands, const uint32_t* uniforms, ls_verify_out* out, hipStream_t s) {
-  if (!m || !m->ws) return fail(LS_ERR_INVALID, "ls_verify: null model or no workspace");
+  if (!m || !m->w.base) return fail(LS_ERR_INVALID, "ls_verify: null model or no workspace");
   if (n_jobs < 0 || n_prob_rows < 0) return fail(LS_ERR_INVALID, "ls_verify: negative count");
   if (n_jobs == 0) return LS_OK;
-  if (n_jobs > m->max_jobs) return fail(LS_ERR_CAPACITY, "ls_verify: %d jobs > workspace max_jobs %d", n_jobs, m->max_jobs);
+  if (n_jobs > m->w.max_jobs) return fail(LS_ERR_CAPACITY, "ls_verify: %d jobs > workspace max_jobs %d", n_jobs, m->w.max_jobs);
   if (!jobs || !probs || !uniforms || !out) return fail(LS_ERR_INVALID, "ls_verify: null argument");
   if (n_cands < 0 || (n_cands > 0 && !cands)) return fail(LS_ERR_INVALID, "ls_verify: bad candidate array");
-  launch_verify(jobs, n_jobs, probs, m->d.V, n_prob_rows, cands, n_cands, uniforms, out, m->err, s);
+  launch_verify(jobs, n_jobs, probs, m->d.V, n_prob_rows, cands, n_cands, uniforms, out, m->w.err, s);
   return check_hip("ls_verify");
 }
 
 ls_status ls_sync_status(ls_model* m, hipStream_t s) {
-  if (!m || !m->err) return fail(LS_ERR_INVALID, "ls_sync_status: no workspace bound");
+  if (!m || !m->w.err) return fail(LS_ERR_INVALID, "ls_sync_status: no workspace bound");
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(LS_ERR_HIP, "stream: %s", hipGetErrorString(e));
   int h = 0;
-  e = hipMemcpy(&h, m->err, sizeof(int), hipMemcpyDeviceToHost);
+  e = hipMemcpy(&h, m->w.err, sizeof(int), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(LS_ERR_HIP, "error word: %s", hipGetErrorString(e));
   if (h == 5) return fail(LS_ERR_HIP, "a device-side dependency wait timed out (error word 5)");
   if (h) return fail((ls_status)h, "a kernel rejected a descriptor (device error word %d)", h);
