@@ -250,6 +250,75 @@ class _Progress:
             print(f"[bench] {self.what} {done}/{total}", file=sys.stderr, flush=True)
 
 
+def microbench(workload, Ms=(1, 2, 3, 4, 8, 16, 128), reps=10):
+    """ls_loop_step at fixed row counts M on the workload's model shape: rows at loop depths
+    spread over 1..R, each attending to a finished prefix of the workload's full context
+    (prompt + new tokens), inputs resident in HBM (seeded synthetic hidden rows and KV
+    entries).  Per M: event-timed microseconds per call, algorithmic bytes per call, GB/s and
+    the fraction of 8 TB/s.  Also a streaming-read reference: PyTorch's sum over a 4 GiB
+    bf16 tensor (reads only), the rate a plain library kernel sustains on this device."""
+    import ctypes
+
+    import torch
+
+    from looped_transformer_self_amd.engine import Engine
+    from synth import configs, weights
+
+    wl = configs.get(workload)
+    cfg, dec = wl.model, wl.decode
+    n_fin = dec.prompt_len + dec.new_tokens
+    Mmax = max(Ms)
+    S = n_fin + Mmax + 8
+    w = weights.make_weights(cfg, seed=dec.seed_w)
+    e = Engine(cfg, w, slot_capacity=S, max_rows=Mmax, max_keys=S, max_jobs=4, prob_rows=4)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    kv = e.kv_core.view(torch.bfloat16) if cfg.dtype == "bf16" else e.kv_core
+    for i in range(0, kv.numel(), 1 << 28):
+        n = min(1 << 28, kv.numel() - i)
+        kv[i:i + n] = torch.randn(n, generator=g, device="cuda", dtype=torch.float32).to(kv.dtype)
+    e.H.copy_(torch.randn(e.H.shape, generator=g, device="cuda"))
+    fin = torch.arange(S, dtype=torch.int32, device="cuda")
+    fin_ptr = ctypes.c_void_p(fin.data_ptr())
+    res = []
+    for M in Ms:
+        if M > Mmax:
+            continue
+        slots = list(range(n_fin, n_fin + M))
+        depth = [1 + (cfg.R - 1 - (i * cfg.R) // M) % cfg.R for i in range(M)]
+        rows = e.rows(slots, [n_fin] * M, depth, n_fin, [[]] * M, fin_ptr)
+        for _ in range(2):
+            e.loop_step(rows)
+        torch.cuda.synchronize()
+        b, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record()
+        for _ in range(reps):
+            e.loop_step(rows)
+        en.record()
+        torch.cuda.synchronize()
+        assert e.sync_status() == 0
+        us = b.elapsed_time(en) / reps * 1e3
+        by = e.loop_step_bytes(rows.host)
+        res.append({"M": M, "distinct_depths": len(set(depth)), "us": round(us, 1), "bytes": by,
+                    "GB_s": round(by / us / 1e3, 1), "frac": round(by / us / 1e3 / HBM_PEAK_GBS, 4)})
+        print(f"[microbench] {wl.key} M={M}: {us:.1f} us, {by / 1e9:.3f} GB, {by / us / 1e3:.0f} GB/s", file=sys.stderr,
+              flush=True)
+    e.close()
+    x = torch.empty(1 << 31, dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+    for _ in range(2):
+        x.sum(dtype=torch.float32)
+    torch.cuda.synchronize()
+    b, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b.record()
+    for _ in range(reps):
+        x.sum(dtype=torch.float32)
+    en.record()
+    torch.cuda.synchronize()
+    read_gbs = x.numel() * 2 / (b.elapsed_time(en) / reps * 1e-3) / 1e9
+    out = {"workload": f"{wl.key}: {wl.description}", "prefix_keys": n_fin, "loop_step": res,
+           "streaming_read_GB_s": round(read_gbs, 1), "streaming_read_note": "torch sum over a 4 GiB bf16 tensor"}
+    print(json.dumps(out), flush=True)
+
+
 SLICE = 32                      # committed tokens per benchmark step
 AR_SLICES = 2                   # slices decoded again in plain full-depth mode
 
@@ -310,6 +379,8 @@ def main():
     ap.add_argument("--mode", default="spec", choices=["spec", "ar"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ar", action="store_true", help="skip the plain full-depth comparison")
+    ap.add_argument("--microbench", action="store_true",
+                    help="ls_loop_step at fixed row counts on the workload's shape, and a streaming-read reference")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run one plain device copy of 1 GiB (byte-counter calibration)")
     ap.add_argument("--pmc-summary", action="store_true",
@@ -333,6 +404,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.microbench:
+        microbench(args.workload)
         return
 
     import torch

@@ -70,6 +70,11 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with looped_transformer_self_amd.build_lib.build() "
                           "(there is no CPU fallback)")
+    # PyTorch owns the device memory and streams the library works on, and it brings its own
+    # HIP runtime (same soname as the system one).  Loading torch first makes the library bind
+    # to that runtime; loaded the other way round, the process would hold two HIP runtimes and
+    # the library would see none of torch's allocations.
+    import torch  # noqa: F401
     lib = C.CDLL(LIB_PATH)
     P = C.c_void_p
     sig = {

@@ -496,7 +496,18 @@ LS_DEV void wait_vm_le8(int n) { wait_vm_le8_impl<56>(__builtin_amdgcn_readfirst
 // PFL of its slabs in flight.  A GCN/CDNA wave issues at most one instruction per four cycles,
 // so the per-slab instruction count is what bounds a wave's streaming rate: row addresses are
 // computed once per tile, and a slab costs a compare, eight address adds and eight loads.
-constexpr int PFL = 2;
+#ifndef LS_PFL
+#define LS_PFL 2
+#endif
+constexpr int PFL = LS_PFL;
+// Cache policy of the weight loads: non-temporal.  Every weight byte is read once per call, by
+// one workgroup; marked as streaming, the loads sustain ~7.0 TB/s on MI355X where the default
+// policy sustains ~6.1 (a 16-row x 512-byte slab pattern read straight into LDS, 256
+// workgroups of two loading waves, measured on the device).
+#ifndef LS_WEIGHT_CPOL
+#define LS_WEIGHT_CPOL 2
+#endif
+constexpr int WEIGHT_CPOL = LS_WEIGHT_CPOL;
 
 template <typename T>
 struct Producer {
@@ -565,7 +576,7 @@ struct Producer {
     for (int i = 0; i < 8; ++i) {
       const char* src = rp[i] + kb;
       if (vb < 512 && co[i] >= vb) src -= co[i];      // chunk past the row end: any valid chunk will do
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, WEIGHT_CPOL);
     }
     ++mine;
     slot += NPROD;

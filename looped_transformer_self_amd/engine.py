@@ -6,6 +6,7 @@ slot-indexed hidden states H[S][d], a pool of probability rows, and the workspac
 """
 
 import ctypes as C
+import os
 
 import numpy as np
 import torch
@@ -21,10 +22,11 @@ _hip = None
 
 
 def _hip_runtime():
-    """The HIP runtime library (already loaded by torch), for raw asynchronous copies."""
+    """The HIP runtime library that torch and libloopspec already share (found by soname, never
+    loaded a second time), for raw asynchronous copies."""
     global _hip
     if _hip is None:
-        _hip = C.CDLL("libamdhip64.so")
+        _hip = C.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
         _hip.hipMemcpyAsync.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_void_p]
         _hip.hipMemcpyAsync.restype = C.c_int
         _hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
