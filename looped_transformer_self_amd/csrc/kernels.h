@@ -39,8 +39,7 @@ struct MegaArgs {
   float* Ys;                    // per-layer attention-residual outputs at Ys + l*M*d
   const int32_t *slot, *pos, *dep, *fin, *anc_off, *anc, *tokens;
   int n_fin;
-  int att_chunks;               // attention units per (group, head): ceil(n_fin / (att_unit_keys * att_sub)), >= 1
-  int att_sub;                  // sub-units of att_unit_keys keys per attention unit, >= 1
+  int att_pmax;                 // attention partials per (row, head) that patt holds (att_pmax_for)
   void* kv;                     // cache tensor; block(i, l) = (dep[i] + dep_off) * blk_mul + layer0 + l
   int dep_off, blk_mul, layer0;
   long long S;
@@ -63,9 +62,27 @@ struct MegaArgs {
 
 size_t mega_counter_ints(int M, int d, int F, int nh, int n_layers);
 size_t mega_smem_bytes(bool bf16, int M, int d);
-// resident workgroups per CU of the variant launch_mega picks for (M, loop_block, long_att)
-int mega_occupancy(bool bf16, int M, int d, bool loop_block, bool long_att);
-int att_unit_keys(bool bf16);   // prefix keys per attention unit
+// resident workgroups per CU of the variant launch_mega picks for (M, loop_block)
+int mega_occupancy(bool bf16, int M, int d, bool loop_block);
+
+// Attention tiles of the layer kernel: 8 prefix keys x a block of heads, the block at most 8
+// heads and at most 2048 bytes of one key's K piece (so a tile is at most 4 ring slabs).
+__host__ __device__ inline int att_heads_per_block(int nh, int hd, int esz) {
+  int h = 2048 / (hd * esz);
+  h = h < 1 ? 1 : (h > 8 ? 8 : h);
+  return h < nh ? h : nh;
+}
+// Most workgroups a launch of the layer kernel uses (4 per CU on 256 CUs).
+constexpr int MEGA_MAX_GRID = 1024;
+// Partials per (row, head) that a workspace for keys up to max_keys holds: the workgroups that
+// share one segment (one head block of one row group) of the contiguous tile deal, at most
+// ceil(G / n_hb) + 1, and never more than the segment's 8-key tiles.
+inline int att_pmax_for(int max_keys, int nh, int hd, int esz) {
+  const int n_hb = (nh + att_heads_per_block(nh, hd, esz) - 1) / att_heads_per_block(nh, hd, esz);
+  const int kt = max_keys > 8 ? (max_keys + 7) / 8 : 1;
+  const int g = (MEGA_MAX_GRID + n_hb - 1) / n_hb + 1;
+  return kt < g ? kt : g;
+}
 // loop_block: launch under the k_mega symbol (shared block B) rather than k_mega_aux
 hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool loop_block, const ValidateArgs& v);
 

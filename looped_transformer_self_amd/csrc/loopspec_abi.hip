@@ -46,6 +46,7 @@ struct Workspace {
   double* invf = nullptr;
   float* rope = nullptr;
   float *patt = nullptr, *ssq = nullptr;
+  int att_pmax = 0;                 // attention partials per (row, head) in patt
   int* cnt = nullptr;
   LayerW *tab_pre = nullptr, *tab_core = nullptr, *tab_coda = nullptr;
 };
@@ -62,7 +63,7 @@ struct ls_model {
   int n_cu = 0;
   // resident workgroups per CU of the persistent kernel, by [loop-block symbol][long-prefix
   // attention][rows per launch] (each variant is a separately compiled kernel)
-  int occ[2][2][LS_MAX_ROWS + 1] = {};
+  int occ[2][LS_MAX_ROWS + 1] = {};
   long long clock_khz = 100000;     // wall-clock rate of the device
   double wait_seconds = 2.0;        // bound on every dependency wait inside a launch
   long long* trace = nullptr;   // optional phase timestamps of the next ls_loop_step
@@ -75,7 +76,7 @@ struct ls_model {
 namespace {
 
 struct Carve {
-  int max_rows, max_keys, max_jobs;
+  int max_rows, max_keys, max_jobs, att_pmax;
   size_t off_err, off_slot, off_dep, off_row, off_q, off_o, off_act, off_hc, off_logits;
   size_t off_Xs, off_Ys, off_invf, off_rope, off_patt, off_ssq, off_cnt, off_tab, total;
 };
@@ -109,9 +110,8 @@ Carve carve(const ls_model* m, int max_rows, int max_keys, int max_jobs) {
   c.off_act = take(nl * layer_slice(R, d.F) * es);
   c.off_invf = take((size_t)d.head_dim / 2 * 8);
   c.off_rope = take(R * (size_t)d.head_dim * 4);
-  const int uk = att_unit_keys(d.dtype == LS_BF16);
-  const size_t att_chunks = std::max(1, (max_keys + uk - 1) / uk);
-  c.off_patt = take(R * d.n_heads * att_chunks * (d.head_dim + 2) * 4);
+  c.att_pmax = att_pmax_for(max_keys, d.n_heads, d.head_dim, (int)es);
+  c.off_patt = take(R * d.n_heads * (size_t)c.att_pmax * (d.head_dim + 2) * 4);
   c.off_ssq = take(nl * 2 * (d.d / 16) * R * 4);
   c.off_cnt = take(mega_counter_ints(max_rows, d.d, d.F, d.n_heads, (int)nl) * 4);
   c.off_tab = take((size_t)(d.L + d.L_pre + d.L_coda) * sizeof(LayerW));
@@ -138,6 +138,7 @@ Workspace carve_into(const Carve& c, char* b) {
   w.invf = (double*)(b + c.off_invf);
   w.rope = (float*)(b + c.off_rope);
   w.patt = (float*)(b + c.off_patt);
+  w.att_pmax = c.att_pmax;
   w.ssq = (float*)(b + c.off_ssq);
   w.cnt = (int*)(b + c.off_cnt);
   return w;
@@ -170,8 +171,7 @@ ls_status device_setup(ls_model* m) {
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0) m->clock_khz = khz;
   for (auto& x : m->occ)
-    for (auto& y : x)
-      for (int& o : y) o = 0;
+    for (int& o : x) o = 0;
   return LS_OK;
 }
 
@@ -287,9 +287,6 @@ namespace {
 #ifndef LS_HEAD_KERNEL
 #define LS_HEAD_KERNEL 1
 #endif
-#ifndef LS_ATT_SUB_MAX
-#define LS_ATT_SUB_MAX 16
-#endif
 
 // The row check of a call over `r` (depth range dep_lo..dep_hi; dep NULL: no depths).
 ValidateArgs validate_args(ls_model* m, const ls_rows* r, const int32_t* dep, int dep_lo, int dep_hi) {
@@ -327,32 +324,22 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
   a.init_mode = init_mode; a.gather = gather ? gather + i0 : nullptr; a.Hg = Hg;
   a.do_head = logits != nullptr;
   // resident workgroups per CU of the kernel variant that is launched (cached per variant)
-  auto occupancy = [&](bool lng) {
-    int& occ = m->occ[loop_block ? 1 : 0][lng ? 1 : 0][mc];
-    if (!occ) occ = std::min(mega_occupancy(m->bf16(), mc, d.d, loop_block, lng), 4);
-    return occ;
-  };
-  int occ = occupancy(false);
+  int& occ = m->occ[loop_block ? 1 : 0][mc];
+  if (!occ) occ = std::min(mega_occupancy(m->bf16(), mc, d.d, loop_block), 4);
   if (occ <= 0) return fail(LS_ERR_HIP, "persistent kernel: no resident workgroup fits (M=%d)", mc);
-  int G = occ * m->n_cu;
-  // attention units of the finished prefix: 64-key sub-units, several per unit once a single
-  // depth group would give every consumer wave (4 per workgroup) more than one unit; those
-  // units are a kernel of their own, whose occupancy may be lower
-  const int uk = att_unit_keys(m->bf16());
-  auto sub_units = [&](int G_) {
-    const long long per_wave = (long long)d.n_heads * r->n_fin / ((long long)uk * 4 * G_);
-    return (int)std::max(1LL, std::min<long long>(per_wave, LS_ATT_SUB_MAX));
-  };
-  a.att_sub = sub_units(G);
-  if (a.att_sub > 1) {
-    const int occ_l = occupancy(true);
-    if (occ_l <= 0) return fail(LS_ERR_HIP, "persistent kernel: no resident workgroup fits (M=%d)", mc);
-    if (occ_l < occ) {
-      G = occ_l * m->n_cu;
-      a.att_sub = sub_units(G);
-    }
+  const int G = occ * m->n_cu;
+  // attention partials per (row, head): at most the workgroups one segment's tiles span
+  {
+    const int esz = m->bf16() ? 2 : 4;
+    const int hb = att_heads_per_block(d.n_heads, d.head_dim, esz);
+    const int n_hb = (d.n_heads + hb - 1) / hb;
+    const int n_kt = std::max(1, (r->n_fin + 7) / 8);
+    const int need = std::min(n_kt, (G + n_hb - 1) / n_hb + 1);
+    if (G > MEGA_MAX_GRID || need > m->w.att_pmax)
+      return fail(LS_ERR_UNSUPPORTED, "persistent kernel: %d workgroups need %d attention partials, workspace holds %d",
+                  G, need, m->w.att_pmax);
   }
-  a.att_chunks = std::max(1, (r->n_fin + uk * a.att_sub - 1) / (uk * a.att_sub));
+  a.att_pmax = m->w.att_pmax;
   a.wait_ticks = (long long)(m->wait_seconds * 1e3 * (double)m->clock_khz);
   a.trace = m->trace;
   m->last_grid = G;

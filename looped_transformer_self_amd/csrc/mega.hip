@@ -154,9 +154,23 @@ LS_DEV int lds_peek(const int* p) {
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
   return __builtin_amdgcn_readfirstlane(v);      // every lane read the same word
 }
-LS_DEV void lds_bump(int* p) {
+LS_DEV void lds_add(int* p, int v) {
   const unsigned addr = (unsigned)(size_t)(__attribute__((address_space(3))) int*)p;
-  asm volatile("s_waitcnt lgkmcnt(0)\n\tds_add_u32 %0, %1" : : "v"(addr), "v"(1) : "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)\n\tds_add_u32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+LS_DEV void lds_bump(int* p) { lds_add(p, 1); }
+// Per-lane read of an LDS word (every lane its own address).
+LS_DEV int lds_read_lane(const int* p) {
+  const unsigned addr = (unsigned)(size_t)(__attribute__((address_space(3))) const int*)p;
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+// The producers' bump: their LDS operations complete in order and nothing they read from LDS
+// is pending, so no wait is needed (which leaves scalar loads of key slots in flight).
+LS_DEV void lds_bump_nw(int* p) {
+  const unsigned addr = (unsigned)(size_t)(__attribute__((address_space(3))) int*)p;
+  asm volatile("ds_add_u32 %0, %1" : : "v"(addr), "v"(1) : "memory");
 }
 
 // Barrier among the consumer waves (an LDS counter; the producer waves never take part).  It
@@ -276,10 +290,14 @@ constexpr int LDS_BUDGET = 160 * 1024 - 512;
 #endif
 __host__ __device__ inline size_t x_region_bytes(int M, int esz, int XC) { return (size_t)M * (XC + 16 / esz) * esz; }
 // Per-launch row tables in LDS: rows by group [M], depth histogram [64], group offsets and
-// count [65], and copies of the rows' slot [M], depth [M] and ancestor offsets [M + 1].
-__host__ __device__ inline int row_table_ints(int M) { return M + 64 + 65 + M + M + M + 1; }
+// count [65], copies of the rows' slot [M], depth [M] and ancestor offsets [M + 1], and the
+// virtual groups of the attention phase [M + 1].
+__host__ __device__ inline int row_table_ints(int M) { return M + 64 + 65 + M + M + M + 1 + M + 1; }
+// Key-slot windows of the producer waves (ATT_WPW slots each).
+constexpr int ATT_WPW = 256;
+constexpr int ATT_WIN = 2 * ATT_WPW;
 __host__ __device__ inline size_t lds_bytes_for(int M, int esz, int NS, int XC, int nred) {
-  size_t off = (size_t)NS * SLAB;
+  size_t off = (size_t)NS * SLAB + ATT_WIN * 4;
   off = (off + x_region_bytes(M, esz, XC) + 15) & ~(size_t)15;
   off = (off + (size_t)row_table_ints(M) * 4 + 15) & ~(size_t)15;
   off = (off + (size_t)nred * NCONS * M * 16 * 4 + 15) & ~(size_t)15;
@@ -315,6 +333,7 @@ size_t mega_counter_ints(int M, int d, int F, int nh, int n_layers) {
 // ---- LDS layout -----------------------------------------------------------------------------------
 struct Lds {
   char* ring;        // NS slabs
+  int* win;          // key-slot windows of the producer waves, ATT_WPW each
   char* X;           // M x (XC + pad) elements
   float* red;        // nred x NCONS x M x 16: per-tile partials of the consumer waves
   float* rinv;       // M
@@ -322,7 +341,8 @@ struct Lds {
   int* grow;         // M: rows ordered by KV depth group (attention shares a group's keys)
   int* goff;         // group g's rows: grow[goff[g] .. goff[g+1]); goff[64] = group count
   int *rslot, *rdep, *raoff;   // the rows' validated slot, depth (0 without depths), ancestor offsets
-  int* ints;         // [0..NS) full, [NS..2NS) empty, [2NS] consumer barrier, [2NS+1+b] partials
+  int* vgt;          // virtual groups (attention): g + 64 * first row within group g; [M] = count
+  int* ints;         // [0..NS) full, [NS..2NS) empty (NCONS per release), [2NS] consumer barrier, [2NS+1+b] partials
                      // posted to partial buffer b (4 per tile, b < nred <= 2), [2NS+3] tiles whose
                      // partial buffer the epilogue wave has released
   int xstride;       // elements
@@ -341,12 +361,14 @@ LS_DEV Lds lds_carve(char* base, int M, int d) {
   s.xstride = s.XC + 16 / (int)sizeof(T);
   size_t off = 0;
   s.ring = base; off += (size_t)s.NS * SLAB;
+  s.win = (int*)(base + off); off += ATT_WIN * 4;
   s.X = base + off; off = align16(off + x_region_bytes(M, (int)sizeof(T), s.XC));
   s.grow = (int*)(base + off);
   s.goff = s.grow + M + 64;
   s.rslot = s.goff + 65;
   s.rdep = s.rslot + M;
   s.raoff = s.rdep + M;
+  s.vgt = s.raoff + M + 1;
   off = align16(off + (size_t)row_table_ints(M) * 4);
   s.red = (float*)(base + off); off = align16(off + (size_t)s.nred * NCONS * M * 16 * 4);
   s.rinv = (float*)(base + off); off = align16(off + (size_t)M * 4);
@@ -531,7 +553,7 @@ struct Producer {
   // LDS access here would get a conservative wait for every direct-to-LDS load still in flight,
   // i.e. drain the prefetch pipeline at each slab.
   LS_DEV void publish_one() {
-    if (lane == 0) lds_bump(s.ints + pslot);
+    if (lane == 0) lds_bump_nw(s.ints + pslot);
     ++pub;
     pslot += NPROD;
     if (pslot >= s.NS) pslot -= s.NS;
@@ -547,6 +569,20 @@ struct Producer {
     }
   }
 
+  // Row addresses of an attention tile: row 2i (lanes 0-31) is key i's K piece, row 2i + 1
+  // (lanes 32-63) its V piece, `hoff` bytes into the cache entries of slots sl[0..7] of the
+  // cache block at `cache`.
+  LS_DEV void begin_kv_tile(const char* cache, const int (&sl)[8], int hoff) {
+    const size_t ent = (size_t)2 * a.d * sizeof(T);
+    const int vo = (lane >> 5) * a.d * (int)sizeof(T) + hoff;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rho = 2 * i + (lane >> 5);
+      co[i] = ((lane & 31) ^ rho) * 16;
+      rp[i] = cache + (size_t)sl[i] * ent + vo + co[i];
+    }
+  }
+
   // Slab k (512-byte column segment k) of the current tile.
   LS_DEV void issue(int k, const PhaseGeo& g) {
     const int jj = j++;
@@ -555,7 +591,7 @@ struct Producer {
       // Wait for the consumers to release the slot.  Meanwhile publish, oldest first, every
       // issued slab whose loads have landed, so a full ring never holds back ready slabs.
       int n = 0;
-      while (lds_peek(s.ints + s.NS + slot) < use) {
+      while (lds_peek(s.ints + s.NS + slot) < NCONS * use) {
         if (pub < mine) {
           wait_vm_le8(8 * (mine - pub - 1));
           publish_one();
@@ -835,7 +871,7 @@ struct Consumer {
       }
     }
     // ring reads are complete (their values fed the MFMAs) before the slot is released
-    if (lane == 0) lds_bump(s.ints + s.NS + slot);
+    if (lane == 0) lds_add(s.ints + s.NS + slot, NCONS);
     dstamp(a, dbg, 8);
   }
 };
@@ -948,35 +984,39 @@ LS_DEV void tile_signal(const MegaArgs& a, const CntLayout& cl, int ph, int l, i
   }
 }
 
-// ---- attention (consumer waves) -------------------------------------------------------------------
+// ---- attention -------------------------------------------------------------------------------------
 // Causal decode attention of layer l, split over keys and merged with the log-sum-exp rule.
 // Rows are grouped by KV depth (a row at loop iteration k reads the depth-k cache, LoopSpec
-// section 2.1 and 2.4), and rows of one group share the finished prefix's keys:
-//  1. unit (group g, head h, chunk c): the prefix keys [64c, 64c + 64), for every row of the
-//     group at once, so those keys are read once per unit.  Wave w takes keys 16w..16w+15;
-//     lane = (key kk + 4rr, dims 8e..8e+7).  Partial (max, sum, acc[hd]) per row.
-//  2. the workgroup that finishes the group's last unit of head h merges, per row, those
-//     partials with the row's own keys (its speculative ancestors and itself, written by this
-//     launch) and stores o[l][row][h].
-
+// section 2.1 and 2.4); rows of one group share the finished prefix's keys and are taken NRA at
+// a time (a virtual group), so that each key is read once per virtual group.  The prefix keys
+// stream through the producers' ring like weights:
+//  1. tile (vg, hb, kt): keys [8kt, 8kt + 8) x heads [hb*HB, hb*HB + HB) of virtual group vg;
+//     its 16 rows are the keys' K pieces (rows 2i) and V pieces (rows 2i + 1) of HB * hd
+//     elements.  The consumers of a workgroup update a partial softmax state per (row, head)
+//     from the ring; a (vg, hb) pair is a segment, and each workgroup that holds tiles of it
+//     leaves one partial (max, sum, acc[hd]) per (row, head).
+//  2. the last workgroup of a segment to finish merges, per (row, head), those partials with
+//     the row's own keys (its speculative ancestors and itself, written by this launch) and
+//     stores o[l][row][h].
+constexpr int NRA = 1;
+struct AttGeo {
+  int HB, n_hb, n_kt, n_vg;
+  int N;                    // tiles: (vg * n_hb + hb) * n_kt + kt
+};
 template <typename T>
-LS_DEV void load8_plain(const T* p, float* v);
-template <>
-LS_DEV void load8_plain<uint16_t>(const uint16_t* p, float* v) {
-  const uint4 x = *reinterpret_cast<const uint4*>(p);
-  const unsigned w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
+LS_DEV AttGeo att_geo(const MegaArgs& a, int n_vg) {
+  AttGeo g;
+  g.HB = att_heads_per_block(a.nh, a.hd, (int)sizeof(T));
+  g.n_hb = (a.nh + g.HB - 1) / g.HB;
+  g.n_kt = max(1, (a.n_fin + 7) / 8);
+  g.n_vg = n_vg;
+  g.N = n_vg * g.n_hb * g.n_kt;
+  return g;
 }
-template <>
-LS_DEV void load8_plain<float>(const float* p, float* v) {
-  const float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-  v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-}
+// Workgroup b < Ga = min(G, N) takes tiles [b*N/Ga, (b+1)*N/Ga) (a share of at least one tile, so
+// that the workgroups holding a segment's tiles are consecutive); the owner of tile t.
+LS_DEV int att_grid(int N) { return min((int)gridDim.x, N); }
+LS_DEV int att_owner(int t, int N, int Ga) { return (int)(((long long)(t + 1) * Ga - 1) / N); }
 
 // Two adjacent elements of a K/V entry written by this launch (agent-coherent load).
 template <typename T>
@@ -1005,7 +1045,8 @@ LS_DEV void store2_coh<float>(float* p, float x, float y) {
 }
 
 // Group the call's rows by KV depth (at kernel start, all threads).  Depth values index a
-// 64-bin histogram; rows with no depth array form one group.
+// 64-bin histogram; rows with no depth array form one group.  Then the virtual groups of the
+// attention phase: each group's rows, NRA at a time.
 LS_DEV void group_rows(const MegaArgs& a, const Lds& s) {
   int* hist = s.grow + a.M;
   for (int i = threadIdx.x; i < 64; i += blockDim.x) hist[i] = 0;
@@ -1031,465 +1072,460 @@ LS_DEV void group_rows(const MegaArgs& a, const Lds& s) {
     hist[lane] = start;                          // fill cursor of the bin
   }
   __syncthreads();
+  // rows of a group in row order: every workgroup must split a group into the same virtual
+  // groups, whose partial results other workgroups merge
   for (int m = threadIdx.x; m < a.M; m += blockDim.x) {
     const int dv = min(max(s.rdep[m], 0), 63);
-    s.grow[atomicAdd(hist + dv, 1)] = m;         // order inside a group does not affect results
+    int rank = 0;
+    for (int m2 = 0; m2 < m; ++m2) rank += min(max(s.rdep[m2], 0), 63) == dv;
+    s.grow[hist[dv] + rank] = m;
   }
   __syncthreads();
+  // virtual groups: each group's rows NRA at a time
+  if (threadIdx.x == 0) {
+    int nv = 0;
+    for (int g = 0; g < s.goff[64]; ++g)
+      for (int r0 = 0; r0 < s.goff[g + 1] - s.goff[g]; r0 += NRA) s.vgt[nv++] = g + 64 * r0;
+    s.vgt[a.M] = nv;
+  }
 }
 
-// Keys of the finished prefix one attention unit covers: NPASS passes, each giving every lane
-// RR keys (for its 8 head dims); lanes hold one pass in registers while the next is in flight.
-template <typename T>
-struct AttUnit {
-  static constexpr int RR = sizeof(T) == 2 ? 2 : 1;     // keys per lane per pass
-  static constexpr int NPASS = 8;
-  static constexpr int KEYS = 4 * RR * NPASS;             // 64 (bf16) / 32 (fp32)
+// A producer wave's window of key slots in LDS: slots of keys [base, base + ATT_WPW), keys past
+// the prefix and out-of-range slots stored as slot 0 (the prep kernel reports the latter; the
+// consumers mask keys past the prefix), so a tile's eight slots are two 16-byte LDS reads.  A
+// workgroup's attention share is the same in every layer and its tiles' keys are consecutive
+// within a segment, so the window is refilled only when a tile falls outside it.
+struct AttWindow {
+  int base = -(1 << 30);
+  int* tab = nullptr;
+  LS_DEV void fill(const MegaArgs& a, int kb) {
+    base = kb;
+    const int lane = threadIdx.x & 63;
+    const unsigned S32 = (unsigned)a.S;
+    int v[ATT_WPW / 64];
+#pragma unroll
+    for (int j = 0; j < ATT_WPW / 64; ++j) {
+      const int k = kb + 64 * j + lane;
+      const int x = k < a.n_fin ? a.fin[k] : 0;
+      v[j] = (unsigned)x < S32 ? x : 0;
+    }
+    // (the compiler waits for the loads before the writes: a refill drains this wave's loads)
+#pragma unroll
+    for (int j = 0; j < ATT_WPW / 64; ++j) {
+      const unsigned addr = (unsigned)(size_t)(__attribute__((address_space(3))) int*)(tab + 64 * j + lane);
+      asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v[j]) : "memory");
+    }
+  }
+  // Slots of tile kt's eight keys.
+  LS_DEV void slots(const MegaArgs& a, int kt, int (&sl)[8]) {
+    const int k0 = 8 * kt;
+    if (k0 < base || k0 + 8 > base + ATT_WPW) fill(a, k0);
+    const unsigned addr = (unsigned)(size_t)(__attribute__((address_space(3))) int*)(tab + (k0 - base));
+    u32x4_t x0, x1;
+    // early-clobber outputs: the first read's destination must not share a register with the
+    // address the second read still needs
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(x0), "=&v"(x1) : "v"(addr) : "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sl[i] = __builtin_amdgcn_readfirstlane((int)x0[i]);
+      sl[4 + i] = __builtin_amdgcn_readfirstlane((int)x1[i]);
+    }
+  }
 };
-int att_unit_keys(bool bf16) { return bf16 ? AttUnit<uint16_t>::KEYS : AttUnit<float>::KEYS; }
 
-// 8 consecutive elements of a K or V entry as raw storage words.
+// The producer waves' part of the attention phase: the workgroup's tiles in order, each as
+// ceil(HB * hd * esz / 512) slabs of its 16 rows (key i's K piece is row 2i, its V piece row
+// 2i + 1).
 template <typename T>
-struct Raw8 {
-  u32x4_t w[sizeof(T) / 2];
-  LS_DEV void load(const T* p) {
-#pragma unroll
-    for (int i = 0; i < (int)(sizeof(T) / 2); ++i) w[i] = *reinterpret_cast<const u32x4_t*>(p + i * (16 / sizeof(T)));
-  }
-  LS_DEV void zero() {
-#pragma unroll
-    for (int i = 0; i < (int)(sizeof(T) / 2); ++i) w[i] = u32x4_t{0u, 0u, 0u, 0u};
-  }
-  LS_DEV void unpack(float* f) const {
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __uint_as_float(w[0][i] << 16);
-        f[2 * i + 1] = __uint_as_float(w[0][i] & 0xffff0000u);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[i] = __uint_as_float(w[0][i]);
-        f[4 + i] = __uint_as_float(w[1][i]);
-      }
+LS_DEV void walk_att_prod(const MegaArgs& a, const Lds& s, int l, Producer<T>& pr, AttWindow& win) {
+  const AttGeo ag = att_geo<T>(a, lds_peek(s.vgt + a.M));
+  const int G = att_grid(ag.N), b = blockIdx.x;
+  if (b >= G) return;
+  const int T0 = (int)((long long)b * ag.N / G), T1 = (int)((long long)(b + 1) * ag.N / G);
+  constexpr int esz = (int)sizeof(T);
+  int seg = T0 / ag.n_kt, kt = T0 - seg * ag.n_kt;
+  int vg = seg / ag.n_hb, hb = seg - vg * ag.n_hb;
+  int cur[8];
+  int cur_vg = -1;
+  const char* cache = nullptr;
+  for (int t = T0; t < T1; ++t) {
+    win.slots(a, kt, cur);
+    if (vg != cur_vg) {
+      cur_vg = vg;
+      const int g = lds_peek(s.vgt + vg) & 63;
+      const int rep = lds_peek(s.grow + lds_peek(s.goff + g));
+      const int blk = (a.dep ? lds_peek(s.rdep + rep) + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
+      cache = (const char*)a.kv + (size_t)blk * a.S * 2 * a.d * esz;
+    }
+    const int h0 = hb * ag.HB;
+    PhaseGeo g;
+    g.n_tiles = 0;
+    g.K = min(ag.HB, a.nh - h0) * a.hd;
+    g.sk = 512 / esz;
+    if (threadIdx.x == 64 * NCONS && t == T0) tstamp(a, l, PH_ATT, 5);
+    pr.begin_kv_tile(cache, cur, h0 * a.hd * esz);
+    const int ns = (g.K + g.sk - 1) / g.sk;
+    for (int k = 0; k < ns; ++k) pr.issue(k, g);
+    if (++kt == ag.n_kt) {
+      kt = 0;
+      if (++hb == ag.n_hb) { hb = 0; ++vg; }
     }
   }
-};
-
-template <typename T>
-LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, int l, int g, int h, int nu);
-
-// One wave processes unit (g, h, c): prefix keys [KEYS*c, KEYS*c + KEYS) for every row of
-// group g, with no workgroup synchronisation.  Lane = (key kk of each group of four, dims
-// 8e..8e+7); key j of pass p = 4*RR*p + kk + 4*rr.  Online log-sum-exp over the passes;
-// partial (max, sum, acc[hd]) per row to the partial buffer; the wave that completes the last
-// unit of (g, h) merges.
-template <typename T>
-LS_DEV void att_unit_wave(const MegaArgs& a, const Lds& s, const CntLayout& cl, int l, int g, int h, int c, int nu) {
-  constexpr int RR = AttUnit<T>::RR, NPASS = AttUnit<T>::NPASS, KEYS = AttUnit<T>::KEYS;
-  int* C = a.cnt + (size_t)l * cl.per_layer;
-  const int lane = threadIdx.x & 63;
-  const int kk = lane >> 4, e = lane & 15;
-  const int hd = a.hd;
-  const bool dim_ok = 8 * e < hd;
-  const int g0 = s.goff[g], ng = s.goff[g + 1] - g0;
-  const int rep = s.grow[g0];
-  const int blk = (a.dep ? s.rdep[rep] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
-  const T* cache = (const T*)a.kv + (size_t)blk * a.S * 2 * a.d + h * hd + 8 * e;
-  const int k0 = c * KEYS;
-  const int kn = max(0, min(KEYS, a.n_fin - k0));
-
-  // slots of this lane's keys (prefix keys were written by earlier launches: plain loads)
-  int sl[NPASS * RR];
-#pragma unroll
-  for (int q = 0; q < NPASS * RR; ++q) {
-    const int j = (q / RR) * 4 * RR + kk + 4 * (q % RR);
-    sl[q] = j < kn ? a.fin[k0 + min(j, kn - 1)] : -1;
-  }
-  bool bad = false;
-#pragma unroll
-  for (int q = 0; q < NPASS * RR; ++q) {
-    const int j = (q / RR) * 4 * RR + kk + 4 * (q % RR);
-    if (j < kn && (sl[q] < 0 || sl[q] >= a.S)) { bad = true; sl[q] = -1; }
-  }
-  if (bad) ls_flag(a.err, 1);
-  auto load_pass = [&](int p, Raw8<T>* kr, Raw8<T>* vr) {
-#pragma unroll
-    for (int rr = 0; rr < RR; ++rr) {
-      const int x = sl[p * RR + rr];
-      kr[rr].zero();
-      vr[rr].zero();
-      if (x >= 0 && dim_ok) {
-        kr[rr].load(cache + (size_t)x * 2 * a.d);
-        vr[rr].load(cache + (size_t)x * 2 * a.d + a.d);
-      }
-    }
-  };
-  // The first NPF passes of prefix keys and values are requested before the wait (they were
-  // written by earlier launches, so their latency overlaps the QKV phase); pass p + NPF reuses
-  // the registers of pass p, requested as soon as pass p is consumed.
-  constexpr int NPF = NPASS / 2;
-  Raw8<T> kr[NPF][RR], vr[NPF][RR];
-#pragma unroll
-  for (int p = 0; p < NPF; ++p) load_pass(p, kr[p], vr[p]);
-  // queries of this head are complete once the head's q/k/v tiles have all signalled
-  {
-    const int nf = 3 * (hd / 16);                         // the head's QKV tiles: flags h * nf .. + nf
-    bool done = lane >= nf;
-    int n = 0;
-    while (true) {
-      if (!done) done = ld_acq(C + cl.o_qkvh + (h * nf + lane) * PADC) >= 1;
-      if (__all(done)) break;
-      __builtin_amdgcn_s_sleep(POLL_SLEEP);
-      if (give_up(n, a.err)) break;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  asm volatile("" : : : "memory");
-
-  const float scale = 1.0f / sqrtf((float)hd);
-  const __amdgpu_buffer_rsrc_t Rq = rsrc_of(a.q, a.M * a.d * 4);
-  for (int r = 0; r < ng; ++r) {
-    const int i = s.grow[g0 + r];
-    const int qoff = (i * a.d + h * hd + 8 * e) * 4;
-    const u32x4_t qa = ldc128(Rq, dim_ok ? qoff : 0x7fffff00), qb = ldc128(Rq, dim_ok ? qoff + 16 : 0x7fffff00);
-    if (r > 0) {                                          // a later row re-reads the keys (cached)
-#pragma unroll
-      for (int p = 0; p < NPF; ++p) load_pass(p, kr[p], vr[p]);
-    }
-    float q8[8];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      q8[t] = __uint_as_float(qa[t]) * scale;
-      q8[4 + t] = __uint_as_float(qb[t]) * scale;
-    }
-    float run_m = -INFINITY, lsum = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    auto consume = [&](int p, const Raw8<T>* kp, const Raw8<T>* vp) {
-      float sc[RR];
-      float pm = -INFINITY;
-#pragma unroll
-      for (int rr = 0; rr < RR; ++rr) {
-        float kf[8];
-        kp[rr].unpack(kf);
-        float part = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) part += q8[t] * kf[t];
-        part = row_sum16(part);             // the key's score in every lane of its row
-        sc[rr] = sl[p * RR + rr] >= 0 ? part : -INFINITY;
-        pm = fmaxf(pm, sc[rr]);
-      }
-      pm = rows_max(pm);
-      const float nm = fmaxf(run_m, pm);
-      if (nm == -INFINITY) return;                        // no key so far
-      const float rs = run_m == -INFINITY ? 0.f : __expf(run_m - nm);
-      lsum *= rs;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] *= rs;
-      run_m = nm;
-#pragma unroll
-      for (int rr = 0; rr < RR; ++rr) {
-        const float pw = sl[p * RR + rr] >= 0 ? __expf(sc[rr] - nm) : 0.f;
-        lsum += pw;
-        float vf[8];
-        vp[rr].unpack(vf);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] += pw * vf[t];
-      }
-    };
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-      consume(p, kr[p % NPF], vr[p % NPF]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (p + NPF < NPASS) load_pass(p + NPF, kr[p % NPF], vr[p % NPF]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // per-lane sums cover the lane's keys; combine the four key groups
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      acc[t] += __shfl_xor(acc[t], 16, 64);
-      acc[t] += __shfl_xor(acc[t], 32, 64);
-    }
-    float* out = a.patt + (((size_t)i * a.nh + h) * a.att_chunks + c) * (hd + 2);
-    if (lane == 0) { stc(out, run_m); stc(out + 1, lsum); }
-    if (kk == 0 && dim_ok) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) stc(out + 2 + 8 * e + t, acc[t]);
-    }
-  }
-  drain();
-  int arrived = 0;
-  if (lane == 0) arrived = atomicAdd(C + cl.o_fa + g * a.nh + h, 1);
-  arrived = __shfl(arrived, 0, 64);
-  if (arrived == nu - 1) att_merge<T>(a, s, cl, l, g, h, nu);
+  if (threadIdx.x == 64 * NCONS) tstamp(a, l, PH_ATT, 6);
 }
 
-// Long prefixes (att_sub > 1): one wave processes unit (g, h, c): prefix keys [span*c,
-// span*c + span), span = KEYS *
-// att_sub, for every row of group g, with no workgroup synchronisation.  The unit walks its
-// att_sub sub-units of KEYS keys in order; lane = (key kk of each group of four, dims
-// 8e..8e+7); key j of a sub-unit's pass p = 4*RR*p + kk + 4*rr.  Online log-sum-exp over all
-// passes; partial (max, sum, acc[hd]) per row to the partial buffer; the wave that completes
-// the last unit of (g, h) merges.  Long prefixes use several sub-units per unit (fewer
-// partials to merge, and the key loads run on from one sub-unit into the next).
+// Merge of head h for row i (by one wave; lane = dims 2*lane, 2*lane + 1): the np prefix
+// partials of the row's segment and the row's own keys (its speculative ancestors, then
+// itself, written by this launch), online log-sum-exp over batches of (16 partials, 8 own
+// keys); every load of a batch is issued before any is used, so a batch costs one memory
+// round trip.
 template <typename T>
-LS_DEV void att_unit_wave_long(const MegaArgs& a, const Lds& s, const CntLayout& cl, int l, int g, int h, int c, int nu) {
-  constexpr int RR = AttUnit<T>::RR, NPASS = AttUnit<T>::NPASS, KEYS = AttUnit<T>::KEYS;
-  int* C = a.cnt + (size_t)l * cl.per_layer;
-  const int lane = threadIdx.x & 63;
-  const int kk = lane >> 4, e = lane & 15;
-  const int hd = a.hd;
-  const bool dim_ok = 8 * e < hd;
-  const int g0 = s.goff[g], ng = s.goff[g + 1] - g0;
-  const int rep = s.grow[g0];
-  const int blk = (a.dep ? s.rdep[rep] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
-  const T* cache = (const T*)a.kv + (size_t)blk * a.S * 2 * a.d + h * hd + 8 * e;
-  const int k0 = c * KEYS * a.att_sub;
-  const int nsub = max(1, min(a.att_sub, (a.n_fin - k0 + KEYS - 1) / KEYS));   // sub-units holding keys
-
-  // slots of this lane's keys in the sub-unit starting at key kb (prefix keys were written by
-  // earlier launches: plain loads); out-of-range slots raise the error word and are skipped
-  auto fill_sl = [&](int kb, int* sl) {
-    const int kn = max(0, min(KEYS, a.n_fin - kb));
-#pragma unroll
-    for (int q = 0; q < NPASS * RR; ++q) {
-      const int j = (q / RR) * 4 * RR + kk + 4 * (q % RR);
-      sl[q] = j < kn ? a.fin[kb + min(j, kn - 1)] : -1;
-    }
-    bool bad = false;
-#pragma unroll
-    for (int q = 0; q < NPASS * RR; ++q) {
-      const int j = (q / RR) * 4 * RR + kk + 4 * (q % RR);
-      if (j < kn && (sl[q] < 0 || sl[q] >= a.S)) { bad = true; sl[q] = -1; }
-    }
-    if (bad) ls_flag(a.err, 1);
-  };
-  auto load_pass = [&](const int* sl, int p, Raw8<T>* kr, Raw8<T>* vr) {
-#pragma unroll
-    for (int rr = 0; rr < RR; ++rr) {
-      const int x = sl[p * RR + rr];
-      kr[rr].zero();
-      vr[rr].zero();
-      if (x >= 0 && dim_ok) {
-        kr[rr].load(cache + (size_t)x * 2 * a.d);
-        vr[rr].load(cache + (size_t)x * 2 * a.d + a.d);
-      }
-    }
-  };
-  // The first NPF passes of prefix keys and values are requested before the wait (they were
-  // written by earlier launches, so their latency overlaps the QKV phase); pass p + NPF reuses
-  // the registers of pass p, requested as soon as pass p is consumed (from the next sub-unit
-  // once the current one has no further pass).
-  constexpr int NPF = NPASS / 2;
-  int sl[NPASS * RR], sn[NPASS * RR];
-  fill_sl(k0, sl);
-  Raw8<T> kr[NPF][RR], vr[NPF][RR];
-#pragma unroll
-  for (int p = 0; p < NPF; ++p) load_pass(sl, p, kr[p], vr[p]);
-  // queries of this head are complete once the head's q/k/v tiles have all signalled
-  {
-    const int nf = 3 * (hd / 16);                         // the head's QKV tiles: flags h * nf .. + nf
-    bool done = lane >= nf;
-    int n = 0;
-    while (true) {
-      if (!done) done = ld_acq(C + cl.o_qkvh + (h * nf + lane) * PADC) >= 1;
-      if (__all(done)) break;
-      __builtin_amdgcn_s_sleep(POLL_SLEEP);
-      if (give_up(n, a.err)) break;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  asm volatile("" : : : "memory");
-
-  const float scale = 1.0f / sqrtf((float)hd);
-  const __amdgpu_buffer_rsrc_t Rq = rsrc_of(a.q, a.M * a.d * 4);
-  for (int r = 0; r < ng; ++r) {
-    const int i = s.grow[g0 + r];
-    const int qoff = (i * a.d + h * hd + 8 * e) * 4;
-    const u32x4_t qa = ldc128(Rq, dim_ok ? qoff : 0x7fffff00), qb = ldc128(Rq, dim_ok ? qoff + 16 : 0x7fffff00);
-    if (r > 0) {                                          // a later row re-reads the keys (cached)
-      if (nsub > 1) fill_sl(k0, sl);
-#pragma unroll
-      for (int p = 0; p < NPF; ++p) load_pass(sl, p, kr[p], vr[p]);
-    }
-    float q8[8];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      q8[t] = __uint_as_float(qa[t]) * scale;
-      q8[4 + t] = __uint_as_float(qb[t]) * scale;
-    }
-    float run_m = -INFINITY, lsum = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    auto consume = [&](int p, const Raw8<T>* kp, const Raw8<T>* vp) {
-      float sc[RR];
-      float pm = -INFINITY;
-#pragma unroll
-      for (int rr = 0; rr < RR; ++rr) {
-        float kf[8];
-        kp[rr].unpack(kf);
-        float part = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) part += q8[t] * kf[t];
-        part = row_sum16(part);             // the key's score in every lane of its row
-        sc[rr] = sl[p * RR + rr] >= 0 ? part : -INFINITY;
-        pm = fmaxf(pm, sc[rr]);
-      }
-      pm = rows_max(pm);
-      const float nm = fmaxf(run_m, pm);
-      if (nm == -INFINITY) return;                        // no key so far
-      const float rs = run_m == -INFINITY ? 0.f : __expf(run_m - nm);
-      lsum *= rs;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] *= rs;
-      run_m = nm;
-#pragma unroll
-      for (int rr = 0; rr < RR; ++rr) {
-        const float pw = sl[p * RR + rr] >= 0 ? __expf(sc[rr] - nm) : 0.f;
-        lsum += pw;
-        float vf[8];
-        vp[rr].unpack(vf);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] += pw * vf[t];
-      }
-    };
-    for (int j = 0; j < nsub; ++j) {
-      const bool more = j + 1 < nsub;
-      if (more) fill_sl(k0 + (j + 1) * KEYS, sn);        // next sub-unit's slots, in flight meanwhile
-#pragma unroll
-      for (int p = 0; p < NPASS; ++p) {
-        consume(p, kr[p % NPF], vr[p % NPF]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (p + NPF < NPASS) load_pass(sl, p + NPF, kr[p % NPF], vr[p % NPF]);
-        else if (more) load_pass(sn, p + NPF - NPASS, kr[p % NPF], vr[p % NPF]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (more) {
-#pragma unroll
-        for (int q = 0; q < NPASS * RR; ++q) sl[q] = sn[q];
-      }
-    }
-    // per-lane sums cover the lane's keys; combine the four key groups
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      acc[t] += __shfl_xor(acc[t], 16, 64);
-      acc[t] += __shfl_xor(acc[t], 32, 64);
-    }
-    float* out = a.patt + (((size_t)i * a.nh + h) * a.att_chunks + c) * (hd + 2);
-    if (lane == 0) { stc(out, run_m); stc(out + 1, lsum); }
-    if (kk == 0 && dim_ok) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) stc(out + 2 + 8 * e + t, acc[t]);
-    }
-  }
-  drain();
-  int arrived = 0;
-  if (lane == 0) arrived = atomicAdd(C + cl.o_fa + g * a.nh + h, 1);
-  arrived = __shfl(arrived, 0, 64);
-  if (arrived == nu - 1) att_merge<T>(a, s, cl, l, g, h, nu);
-}
-
-// Merge of head h for the rows of group g, by one wave, row by row; lane = dims 2*lane, 2*lane + 1.
-// Online log-sum-exp over batches of (16 prefix-chunk partials, 8 own keys); every load of a
-// batch is issued before any is used, so a batch costs one memory round trip.
-template <typename T>
-LS_DEV void att_merge(const MegaArgs& a, const Lds& s, const CntLayout& cl, int l, int g, int h, int nu) {
+LS_DEV void att_merge_row(const MegaArgs& a, const Lds& s, int l, int blk, int i, int h, int np) {
   const int lane = threadIdx.x & 63;
   const int hd = a.hd;
   const bool dok = 2 * lane < hd;
-  const int g0 = s.goff[g], ng = s.goff[g + 1] - g0;
-  const int rep = s.grow[g0];
-  const int blk = (a.dep ? s.rdep[rep] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
   const T* cache = (const T*)a.kv + (size_t)blk * a.S * 2 * a.d;
   const float scale = 1.0f / sqrtf((float)hd);
-  for (int r = 0; r < ng; ++r) {
-    const int i = s.grow[g0 + r];
-    T* orow = o_of<T>(a, l) + (size_t)i * a.d + h * hd;
-    const int self = s.rslot[i];
-    if (self < 0) {                                  // rejected row: zero output
-      if (dok) store2_coh<T>(orow + 2 * lane, 0.f, 0.f);
-      continue;
-    }
-    const int a0 = s.raoff[i], na = s.raoff[i + 1] - a0;
-    const int nt = na + 1;                           // the row's own keys: ancestors, then itself
-    const float* base = a.patt + ((size_t)i * a.nh + h) * a.att_chunks * (hd + 2);
-    // the query joins the first batch's loads (it is converted where the scores are formed)
-    const unsigned long long qw = dok ? ldc64(a.q + (size_t)i * a.d + h * hd + 2 * lane) : 0ull;
-    float run_m = -INFINITY, den = 0.f, num0 = 0.f, num1 = 0.f;
-    const int nbat = max((nu + 15) / 16, (nt + 7) / 8);
-    for (int bt = 0; bt < nbat; ++bt) {
-      const int c0 = bt * 16, j0 = bt * 8;
-      // ---- issue the batch's loads
-      const int cl_ = c0 + lane;                     // chunk whose statistics this lane holds
-      float mxc = -INFINITY, smc = 0.f;
-      if (lane < 16 && cl_ < nu) {
-        mxc = ldc(base + (size_t)cl_ * (hd + 2));
-        smc = ldc(base + (size_t)cl_ * (hd + 2) + 1);
-      }
-      float2 ac[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int cc = min(c0 + u, nu - 1);
-        ac[u] = make_float2(0.f, 0.f);
-        if (dok && c0 + u < nu) {
-          const unsigned long long w = ldc64(base + (size_t)cc * (hd + 2) + 2 + 2 * lane);
-          ac[u] = make_float2(__uint_as_float((unsigned)w), __uint_as_float((unsigned)(w >> 32)));
-        }
-      }
-      float2 k2[8], v2[8];
-      int xs[8];
-      bool bad = false;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = min(j0 + u, nt - 1);
-        xs[u] = j < na ? a.anc[a0 + j] : self;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (xs[u] < 0 || xs[u] >= a.S) { bad = bad || j0 + u < nt; xs[u] = self; }
-        const T* ent = cache + (size_t)xs[u] * 2 * a.d + h * hd + 2 * lane;
-        k2[u] = v2[u] = make_float2(0.f, 0.f);
-        if (dok && j0 + u < nt) {
-          k2[u] = load2_coh<T>(ent);
-          v2[u] = load2_coh<T>(ent + a.d);
-        }
-      }
-      if (bad) ls_flag(a.err, 1);
-      // ---- the batch's scores and its maximum
-      const float q0 = __uint_as_float((unsigned)qw) * scale, q1 = __uint_as_float((unsigned)(qw >> 32)) * scale;
-      float sc[8];
-      float bm = wave_max(mxc);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        sc[u] = wave_sum(q0 * k2[u].x + q1 * k2[u].y);
-        if (j0 + u < nt) bm = fmaxf(bm, sc[u]);
-      }
-      const float nm = fmaxf(run_m, bm);
-      if (nm == -INFINITY) continue;                 // nothing in this batch or before
-      const float rs = run_m == -INFINITY ? 0.f : __expf(run_m - nm);
-      den *= rs; num0 *= rs; num1 *= rs;
-      run_m = nm;
-      // prefix chunks: weight w_c = exp(mx_c - m) held by lane c - c0
-      const float wl = mxc == -INFINITY ? 0.f : __expf(mxc - nm);
-      den += wave_sum(wl * smc);
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const float w = lane_f(wl, u);
-        num0 += w * ac[u].x;
-        num1 += w * ac[u].y;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float w = j0 + u < nt ? __expf(sc[u] - nm) : 0.f;
-        den += w;
-        num0 += w * v2[u].x;
-        num1 += w * v2[u].y;
-      }
-    }
-    if (dok) store2_coh<T>(orow + 2 * lane, den > 0.f ? canon_nan(num0 / den) : 0.f, den > 0.f ? canon_nan(num1 / den) : 0.f);
+  T* orow = o_of<T>(a, l) + (size_t)i * a.d + h * hd;
+  const int self = s.rslot[i];
+  if (self < 0) {                                  // rejected row: zero output
+    if (dok) store2_coh<T>(orow + 2 * lane, 0.f, 0.f);
+    return;
   }
+  const int a0 = s.raoff[i], na = s.raoff[i + 1] - a0;
+  const int nt = na + 1;                           // the row's own keys: ancestors, then itself
+  const float* base = a.patt + ((size_t)i * a.nh + h) * a.att_pmax * (hd + 2);
+  // the query joins the first batch's loads (it is converted where the scores are formed)
+  const unsigned long long qw = dok ? ldc64(a.q + (size_t)i * a.d + h * hd + 2 * lane) : 0ull;
+  float run_m = -INFINITY, den = 0.f, num0 = 0.f, num1 = 0.f;
+  const int nbat = max((np + 15) / 16, (nt + 7) / 8);
+  for (int bt = 0; bt < nbat; ++bt) {
+    const int c0 = bt * 16, j0 = bt * 8;
+    // ---- issue the batch's loads
+    const int cl_ = c0 + lane;                     // partial whose statistics this lane holds
+    float mxc = -INFINITY, smc = 0.f;
+    if (lane < 16 && cl_ < np) {
+      mxc = ldc(base + (size_t)cl_ * (hd + 2));
+      smc = ldc(base + (size_t)cl_ * (hd + 2) + 1);
+    }
+    float2 ac[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int cc = min(c0 + u, np - 1);
+      ac[u] = make_float2(0.f, 0.f);
+      if (dok && c0 + u < np) {
+        const unsigned long long w = ldc64(base + (size_t)cc * (hd + 2) + 2 + 2 * lane);
+        ac[u] = make_float2(__uint_as_float((unsigned)w), __uint_as_float((unsigned)(w >> 32)));
+      }
+    }
+    float2 k2[8], v2[8];
+    int xs[8];
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + u, nt - 1);
+      xs[u] = j < na ? a.anc[a0 + j] : self;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (xs[u] < 0 || xs[u] >= a.S) { bad = bad || j0 + u < nt; xs[u] = self; }
+      const T* ent = cache + (size_t)xs[u] * 2 * a.d + h * hd + 2 * lane;
+      k2[u] = v2[u] = make_float2(0.f, 0.f);
+      if (dok && j0 + u < nt) {
+        k2[u] = load2_coh<T>(ent);
+        v2[u] = load2_coh<T>(ent + a.d);
+      }
+    }
+    if (bad) ls_flag(a.err, 1);
+    // ---- the batch's scores and its maximum
+    const float q0 = __uint_as_float((unsigned)qw) * scale, q1 = __uint_as_float((unsigned)(qw >> 32)) * scale;
+    float sc[8];
+    float bm = wave_max(mxc);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sc[u] = wave_sum(q0 * k2[u].x + q1 * k2[u].y);
+      if (j0 + u < nt) bm = fmaxf(bm, sc[u]);
+    }
+    const float nm = fmaxf(run_m, bm);
+    if (nm == -INFINITY) continue;                 // nothing in this batch or before
+    const float rs = run_m == -INFINITY ? 0.f : __expf(run_m - nm);
+    den *= rs; num0 *= rs; num1 *= rs;
+    run_m = nm;
+    // prefix partials: weight w_c = exp(mx_c - m) held by lane c - c0
+    const float wl = mxc == -INFINITY ? 0.f : __expf(mxc - nm);
+    den += wave_sum(wl * smc);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float w = lane_f(wl, u);
+      num0 += w * ac[u].x;
+      num1 += w * ac[u].y;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = j0 + u < nt ? __expf(sc[u] - nm) : 0.f;
+      den += w;
+      num0 += w * v2[u].x;
+      num1 += w * v2[u].y;
+    }
+  }
+  if (dok) store2_coh<T>(orow + 2 * lane, den > 0.f ? canon_nan(num0 / den) : 0.f, den > 0.f ? canon_nan(num1 / den) : 0.f);
+}
+
+// 16 bytes of LDS at byte address addr.
+LS_DEV u32x4_t lds_ld128(unsigned addr) {
+  return *(const __attribute__((address_space(3))) u32x4_t*)(size_t)addr;
+}
+
+// 16 ring bytes as E floats.
+template <typename T> struct AttLane;
+template <> struct AttLane<uint16_t> {
+  static constexpr int E = 8;
+  LS_DEV static void unpack(const u32x4_t& w, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[2 * k] = __uint_as_float(w[k] << 16);
+      f[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  }
+};
+template <> struct AttLane<float> {
+  static constexpr int E = 4;
+  LS_DEV static void unpack(const u32x4_t& w, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(w[k]);
+  }
+};
+
+// The consumer waves' part of the attention phase.  All four consumers read every tile of the
+// workgroup's share; consumer c owns heads c and c + 4 of the block, lane = (head jj of the two,
+// key kk, dims quarter sub): lane sub holds the 16-byte chunks sub, sub + 4, ... of the head's K
+// and V pieces.  Per row (up to NRA, the rows of the segment's virtual group) a lane keeps the
+// query chunks and a partial softmax state over the keys it has seen (its own key position kk
+// in every tile; running maximum shared by the head's lanes), so a tile costs the 16-byte LDS
+// reads of one K and one V pass, two DPP steps for the score, three for the tile maximum.  At
+// the end of its part of a segment the workgroup sums the state over the key lanes, leaves one
+// partial per (row, head), and the last workgroup of the segment merges.
+template <typename T, int MT>
+LS_DEV void att_phase(const MegaArgs& a, const Lds& s, const CntLayout& cl, int l, Consumer<T, MT>& co,
+                      ConsBar& cb) {
+  constexpr int E = AttLane<T>::E, NU = 32 / E, QN = NU * E;   // head pieces are at most 512 bytes
+  const AttGeo ag = att_geo<T>(a, s.vgt[a.M]);
+  const int G = att_grid(ag.N), b = blockIdx.x;
+  if (b >= G) return;
+  const int T0 = (int)((long long)b * ag.N / G), T1 = (int)((long long)(b + 1) * ag.N / G);
+  int* C = a.cnt + (size_t)l * cl.per_layer;
+  const int lane = threadIdx.x & 63, jj = lane >> 5, kk = (lane >> 2) & 7, sub = lane & 3;
+  const int c = co.c, jh = c + 4 * jj;
+  const int hd = a.hd;
+  constexpr int esz = (int)sizeof(T);
+  const int nch = hd * esz / 16;                    // 16-byte chunks of one head's K (or V) piece
+  const float scale = 1.0f / sqrtf((float)hd);
+  const __amdgpu_buffer_rsrc_t Rq = rsrc_of(a.q, a.M * a.d * 4);
+  float q[NRA][QN], acc[NRA][QN], mrun[NRA], lsum[NRA];
+  int rows[NRA];
+  int nr = 0, hbn = 0, h0 = 0, blk = 0;
+  bool hv = false;
+  int seg = T0 / ag.n_kt, kt = T0 - seg * ag.n_kt;
+  int cur_seg = -1;
+
+  // end of this workgroup's part of segment sg: one partial per (row, head), then the merge if
+  // every other workgroup of the segment has left its partials
+  auto flush = [&](int sg) {
+#pragma unroll
+    for (int r = 0; r < NRA; ++r) {
+      if (r < nr) {
+#pragma unroll
+        for (int o = 4; o <= 16; o <<= 1) {
+          lsum[r] += __shfl_xor(lsum[r], o, 64);
+#pragma unroll
+          for (int x = 0; x < QN; ++x) acc[r][x] += __shfl_xor(acc[r][x], o, 64);
+        }
+      }
+    }
+    const int first = sg * ag.n_kt;
+    const int o0 = att_owner(first, ag.N, G);
+    const int np = att_owner(first + ag.n_kt - 1, ag.N, G) - o0 + 1;
+    if (kk == 0 && hv) {
+#pragma unroll
+      for (int r = 0; r < NRA; ++r) {
+        if (r >= nr) continue;
+        float* out = a.patt + (((size_t)rows[r] * a.nh + h0 + jh) * a.att_pmax + (b - o0)) * (hd + 2);
+        if (sub == 0) { stc(out, mrun[r]); stc(out + 1, lsum[r]); }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int ch = sub + 4 * u;
+          if (ch < nch) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) stc(out + 2 + ch * E + e, acc[r][u * E + e]);
+          }
+        }
+      }
+    }
+    drain();
+    cb.sync();
+    if (c == 0 && lane == 0) s.ints[2 * s.NS + 4] = atomicAdd(C + cl.o_fa + sg, 1);
+    cb.sync();
+    if (s.ints[2 * s.NS + 4] == np - 1) {
+      // this consumer merges its own heads (it has waited for their QKV tiles)
+      for (int r = 0; r < nr; ++r) {
+        if (c < hbn) att_merge_row<T>(a, s, l, blk, rows[r], h0 + c, np);
+        if (c + 4 < hbn) att_merge_row<T>(a, s, l, blk, rows[r], h0 + c + 4, np);
+      }
+    }
+  };
+
+  for (int t = T0; t < T1; ++t) {
+    if (seg != cur_seg) {
+      if (cur_seg >= 0) flush(cur_seg);
+      cur_seg = seg;
+      const int vg = seg / ag.n_hb, hb = seg - vg * ag.n_hb;
+      const int vt = s.vgt[vg], g = vt & 63, r0 = vt >> 6;
+      const int g0 = s.goff[g];
+      nr = min(NRA, s.goff[g + 1] - g0 - r0);
+#pragma unroll
+      for (int r = 0; r < NRA; ++r) rows[r] = s.grow[g0 + r0 + min(r, nr - 1)];
+      blk = (a.dep ? s.rdep[s.grow[g0]] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
+      h0 = hb * ag.HB;
+      hbn = min(ag.HB, a.nh - h0);
+      hv = jh < hbn;
+      // queries of the consumer's heads are complete once their q/k/v tiles have signalled
+      {
+        const int nf = 3 * (hd / 16);
+        bool done = true;
+        int fi = 0;
+        if (lane < nf) { done = c >= hbn; fi = (h0 + c) * nf + lane; }
+        else if (lane < 2 * nf) { done = c + 4 >= hbn; fi = (h0 + c + 4) * nf + lane - nf; }
+        int n = 0;
+        while (true) {
+          if (!done) done = ld_acq(C + cl.o_qkvh + (size_t)fi * PADC) >= 1;
+          if (__all(done)) break;
+          __builtin_amdgcn_s_sleep(POLL_SLEEP);
+          if (give_up(n, a.err)) break;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < NRA; ++r) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int ch = sub + 4 * u;
+          const bool ok = hv && r < nr && ch < nch;
+          const int off = ok ? (rows[r] * a.d + (h0 + jh) * hd + ch * E) * 4 : 0x7fffff00;
+#pragma unroll
+          for (int v = 0; v < E / 4; ++v) {
+            const u32x4_t w = ldc128(Rq, off + 16 * v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q[r][u * E + 4 * v + e] = __uint_as_float(w[e]) * scale;
+          }
+        }
+        mrun[r] = -INFINITY;
+        lsum[r] = 0.f;
+#pragma unroll
+        for (int x = 0; x < QN; ++x) acc[r][x] = 0.f;
+      }
+    }
+    // ---- one tile: keys [8kt, 8kt + 8), this lane's key kk
+    const bool kok = hv && kk < a.n_fin - 8 * kt;
+    const int ns = (hbn * hd * esz + 511) / 512;
+    {
+      // lane k < ns watches the tile's slab k
+      const int k = lane < ns ? lane : 0;
+      int sl = co.cslot + k, us = co.cuse;
+      if (sl >= s.NS) { sl -= s.NS; ++us; }
+      int n = 0;
+      while (!__all(lds_read_lane(s.ints + sl) >= us + 1)) {
+        __builtin_amdgcn_s_sleep(0);
+        if (give_up(n, a.err)) break;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" : : : "memory");
+    // LDS byte addresses of this lane's K and V chunks.  Chunks past the head read its chunk 0
+    // (finite data): their query entries are zero and their accumulators are never stored.
+    const unsigned ring0 = (unsigned)(size_t)(__attribute__((address_space(3))) char*)s.ring;
+    unsigned kp[NU], vp[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int ch = sub + 4 * u;
+      const int off = hv && ch < nch ? jh * hd * esz + ch * 16 : 0;
+      int sl = co.cslot + (off >> 9);
+      if (sl >= s.NS) sl -= s.NS;
+      const int pos = (off >> 4) & 31;
+      const unsigned row0 = ring0 + (unsigned)(sl * SLAB + (2 * kk) * 512);
+      kp[u] = row0 + ((pos ^ (2 * kk)) << 4);
+      vp[u] = row0 + 512 + ((pos ^ (2 * kk + 1)) << 4);
+    }
+    // K chunks (and for bf16 the V chunks too) are all requested before the first is used
+    u32x4_t kw[NU], vw[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      if (4 * u >= nch) break;
+      kw[u] = lds_ld128(kp[u]);
+      if constexpr (E == 8) vw[u] = lds_ld128(vp[u]);
+    }
+    float part[NRA];
+#pragma unroll
+    for (int r = 0; r < NRA; ++r) part[r] = 0.f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      if (4 * u >= nch) break;
+      float kf[E];
+      AttLane<T>::unpack(kw[u], kf);
+#pragma unroll
+      for (int r = 0; r < NRA; ++r) {
+        if (r >= nr) break;
+#pragma unroll
+        for (int e = 0; e < E; ++e) part[r] += q[r][u * E + e] * kf[e];
+      }
+    }
+    float p[NRA];
+#pragma unroll
+    for (int r = 0; r < NRA; ++r) {
+      p[r] = 0.f;
+      if (r >= nr) break;
+      float x = part[r];
+      x += dpp_f<0xB1>(x);                     // the four dims quarters of the key's score
+      x += dpp_f<0x4E>(x);
+      const float sc = kok ? x : -INFINITY;
+      float mx = fmaxf(sc, dpp_f<0x141>(sc));  // half-row mirror: key kk ^ 1 (quarters hold equal values)
+      mx = fmaxf(mx, dpp_f<0x140>(mx));        // row mirror: key kk ^ 3
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));  // keys kk ^ 4
+      // the state is rescaled only when the running maximum grows (rarely, after the first keys)
+      const bool up = mx > mrun[r];
+      if (__any(up)) {
+        const float al = !up ? 1.f : (mrun[r] == -INFINITY ? 0.f : __expf(mrun[r] - mx));
+        lsum[r] *= al;
+#pragma unroll
+        for (int x2 = 0; x2 < QN; ++x2) acc[r][x2] *= al;
+        if (up) mrun[r] = mx;
+      }
+      p[r] = sc == -INFINITY ? 0.f : __expf(sc - mrun[r]);
+      lsum[r] += p[r];
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      if (4 * u >= nch) break;
+      float vf[E];
+      if constexpr (E == 8) AttLane<T>::unpack(vw[u], vf);
+      else AttLane<T>::unpack(lds_ld128(vp[u]), vf);
+#pragma unroll
+      for (int r = 0; r < NRA; ++r) {
+        if (r >= nr) break;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[r][u * E + e] += p[r] * vf[e];
+      }
+    }
+    // this consumer is done with the tile's slabs (a slot is free once all four have released it)
+    if (lane < ns) {
+      int sl = co.cslot + lane;
+      if (sl >= s.NS) sl -= s.NS;
+      lds_add(s.ints + s.NS + sl, 1);
+    }
+    co.cslot += ns;
+    while (co.cslot >= s.NS) { co.cslot -= s.NS; ++co.cuse; }
+    if (++kt == ag.n_kt) { kt = 0; ++seg; }
+  }
+  flush(cur_seg);
 }
 
 // ---- init unit: embedding row or gathered hidden row into the working rows ---------------------------
@@ -1707,7 +1743,7 @@ LS_DEV Step step_of(const MegaArgs& a, int st) {
   return Step{k == 0 ? PH_QKV : (k == 1 ? PH_ATT : (k == 2 ? PH_O : (k == 3 ? PH_GU : PH_DOWN))), st / 5};
 }
 
-template <typename T, int MT, bool LONG>
+template <typename T, int MT>
 LS_DEV void mega_body(const MegaArgs& a) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   const Lds s = lds_carve<T>(smem_raw, a.M, a.d);
@@ -1742,10 +1778,13 @@ LS_DEV void mega_body(const MegaArgs& a) {
   if (wv >= NCONS) {
     // ------------------------------ producer waves ------------------------------
     Producer<T> pr(a, s, wv - NCONS);
+    AttWindow win;
+    win.tab = s.win + (wv - NCONS) * ATT_WPW;
 #pragma unroll 1
     for (int st = 0; st < n_steps; ++st) {
       const Step sp = step_of(a, st);
-      if (sp.ph != PH_ATT) walk_gemm<T, MT, true>(a, s, cl, sp.ph, sp.l, deal, &pr, nullptr, nullptr);
+      if (sp.ph == PH_ATT) walk_att_prod<T>(a, s, sp.l, pr, win);
+      else walk_gemm<T, MT, true>(a, s, cl, sp.ph, sp.l, deal, &pr, nullptr, nullptr);
     }
     pr.finish();
     return;
@@ -1755,24 +1794,12 @@ LS_DEV void mega_body(const MegaArgs& a) {
   Consumer<T, MT> co(a, s, cb, wv);
   if (a.init_mode)
     for (int u = b; u < a.M; u += G) init_unit<T>(a, cl, cb, u);
-  int att_deal = 0;
 #pragma unroll 1
   for (int st = 0; st < n_steps; ++st) {
     const Step sp = step_of(a, st);
     if (threadIdx.x == 0) tstamp(a, sp.l, sp.ph, 0);
     if (sp.ph == PH_ATT) {
-      const int nu = a.att_chunks;                 // prefix chunks per (group, head), >= 1
-      const int natt = s.goff[64] * a.nh * nu;
-      const Share sa = share_of(natt, att_deal, G, b);
-      att_deal = (att_deal + natt) % G;
-      // unit u runs on workgroup (u + att_deal) mod G, wave (u / G) mod 4: every unit gets a
-      // wave of its own before any wave takes a second one
-      for (int k = co.c; k < sa.count; k += NCONS) {
-        const int u = sa.first + k * G;
-        const int cch = u % nu, gh = u / nu;
-        if constexpr (LONG) att_unit_wave_long<T>(a, s, cl, sp.l, gh / a.nh, gh % a.nh, cch, nu);
-        else att_unit_wave<T>(a, s, cl, sp.l, gh / a.nh, gh % a.nh, cch, nu);
-      }
+      att_phase<T, MT>(a, s, cl, sp.l, co, cb);
     } else {
       walk_gemm<T, MT, false>(a, s, cl, sp.ph, sp.l, deal, nullptr, &co, &cb);
     }
@@ -1782,12 +1809,10 @@ LS_DEV void mega_body(const MegaArgs& a) {
 
 // Two entry symbols over the same body, so that profiles tell the loop block's launches
 // (ls_loop_step) apart from the prelude, coda and LM-head launches.
-// LONG: attention units of several sub-units (long prefixes), compiled separately so that the
-// short-prefix kernels keep their code size.
-template <typename T, int MT, bool LONG>
-__global__ __launch_bounds__(MEGA_THREADS) void k_mega(MegaArgs a) { mega_body<T, MT, LONG>(a); }
-template <typename T, int MT, bool LONG>
-__global__ __launch_bounds__(MEGA_THREADS) void k_mega_aux(MegaArgs a) { mega_body<T, MT, LONG>(a); }
+template <typename T, int MT>
+__global__ __launch_bounds__(MEGA_THREADS) void k_mega(MegaArgs a) { mega_body<T, MT>(a); }
+template <typename T, int MT>
+__global__ __launch_bounds__(MEGA_THREADS) void k_mega_aux(MegaArgs a) { mega_body<T, MT>(a); }
 
 // P of a model without prelude layers (LoopSpec page, section 2.1, eq. 1; here P is the
 // embedding row alone): one workgroup per row checks the row and copies its token's embedding
@@ -1819,12 +1844,16 @@ hipError_t launch_embed(bool bf16, const ValidateArgs& v, const int32_t* tokens,
 }
 
 // Set-up of one launch: counters to zero, this launch's polled buffers to SENT32, rotary
-// cos/sin of the rows' positions, and (first launch of a call) the row-descriptor check.
+// cos/sin of the rows' positions, the check of the finished prefix's slots (the attention
+// phase reads keys at slot 0 in place of an out-of-range slot), and (first launch of a call)
+// the row-descriptor check.
 __global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, const double* inv_freq, int M, int half,
                        unsigned* xs_fill, long long n_xs, unsigned* ys_fill, long long n_ys, unsigned* o_fill,
-                       long long n_o, ValidateArgs v) {
+                       long long n_o, ValidateArgs v, const int32_t* fin, int n_fin, long long S, int* err) {
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x, str = (long long)gridDim.x * blockDim.x;
   for (long long i = tid; i < v.n; i += str) check_row(v, (int)i);
+  for (long long i = tid; i < n_fin; i += str)
+    if (fin[i] < 0 || fin[i] >= S) ls_flag(err, 1);
   for (long long i = tid; i < n; i += str) cnt[i] = 0;
   for (long long i = tid; i < n_xs; i += str) xs_fill[i] = SENT32;
   for (long long i = tid; i < n_ys; i += str) ys_fill[i] = SENT32;
@@ -1838,30 +1867,29 @@ __global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, c
   }
 }
 
-template <typename T, bool LONG>
+template <typename T>
 static const void* pick_tl(int mt, bool loop) {
   if (loop) {
-    if (mt <= 1) return reinterpret_cast<const void*>(&k_mega<T, 1, LONG>);
-    if (mt <= 2) return reinterpret_cast<const void*>(&k_mega<T, 2, LONG>);
-    if (mt <= 4) return reinterpret_cast<const void*>(&k_mega<T, 4, LONG>);
-    return reinterpret_cast<const void*>(&k_mega<T, 8, LONG>);
+    if (mt <= 1) return reinterpret_cast<const void*>(&k_mega<T, 1>);
+    if (mt <= 2) return reinterpret_cast<const void*>(&k_mega<T, 2>);
+    if (mt <= 4) return reinterpret_cast<const void*>(&k_mega<T, 4>);
+    return reinterpret_cast<const void*>(&k_mega<T, 8>);
   }
-  if (mt <= 1) return reinterpret_cast<const void*>(&k_mega_aux<T, 1, LONG>);
-  if (mt <= 2) return reinterpret_cast<const void*>(&k_mega_aux<T, 2, LONG>);
-  if (mt <= 4) return reinterpret_cast<const void*>(&k_mega_aux<T, 4, LONG>);
-  return reinterpret_cast<const void*>(&k_mega_aux<T, 8, LONG>);
+  if (mt <= 1) return reinterpret_cast<const void*>(&k_mega_aux<T, 1>);
+  if (mt <= 2) return reinterpret_cast<const void*>(&k_mega_aux<T, 2>);
+  if (mt <= 4) return reinterpret_cast<const void*>(&k_mega_aux<T, 4>);
+  return reinterpret_cast<const void*>(&k_mega_aux<T, 8>);
 }
 
-static const void* pick(bool bf16, int M, bool loop = true, bool lng = false) {
+static const void* pick(bool bf16, int M, bool loop = true) {
   const int mt = (M + 15) / 16;
-  if (lng) return bf16 ? pick_tl<uint16_t, true>(mt, loop) : pick_tl<float, true>(mt, loop);
-  return bf16 ? pick_tl<uint16_t, false>(mt, loop) : pick_tl<float, false>(mt, loop);
+  return bf16 ? pick_tl<uint16_t>(mt, loop) : pick_tl<float>(mt, loop);
 }
 
-int mega_occupancy(bool bf16, int M, int d, bool loop_block, bool long_att) {
+int mega_occupancy(bool bf16, int M, int d, bool loop_block) {
   const size_t smem = mega_smem_bytes(bf16, M, d);
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick(bf16, M, loop_block, long_att), MEGA_THREADS, smem) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick(bf16, M, loop_block), MEGA_THREADS, smem) !=
       hipSuccess)
     return 0;
   return n;
@@ -1869,16 +1897,18 @@ int mega_occupancy(bool bf16, int M, int d, bool loop_block, bool long_att) {
 
 hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool loop_block, const ValidateArgs& v) {
   const CntLayout cl = cnt_layout(a.M, a.d, a.F, a.nh, x_chunk_for(a.M, bf16 ? 2 : 4, a.d), a.n_layers);
-  const long long n_prep = std::max<long long>(std::max<long long>(cl.total, (long long)a.M * (a.hd / 2)), v.n);
+  const long long n_prep = std::max<long long>(std::max<long long>(cl.total, (long long)a.M * (a.hd / 2)),
+                                               std::max<long long>(v.n, a.n_fin));
   const long long rows = (long long)a.M * a.d;   // one layer slice of Xs / Ys
   hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<long long>(1024, (n_prep + 255) / 256)), dim3(256), 0, s, a.cnt,
                      (long long)cl.total, a.rope, a.pos, a.inv_freq, a.M, a.hd / 2,
                      reinterpret_cast<unsigned*>(a.Xs + rows), (long long)a.n_layers * rows,
                      reinterpret_cast<unsigned*>(a.Ys), (long long)a.n_layers * rows,
-                     reinterpret_cast<unsigned*>(a.o), (long long)a.n_layers * rows * (bf16 ? 2 : 4) / 4, v);
+                     reinterpret_cast<unsigned*>(a.o), (long long)a.n_layers * rows * (bf16 ? 2 : 4) / 4, v, a.fin,
+                     a.n_fin, a.S, a.err);
   const size_t smem = mega_smem_bytes(bf16, a.M, a.d);
   void* args[] = {(void*)&a};
-  return hipLaunchCooperativeKernel(pick(bf16, a.M, loop_block, a.att_sub > 1), dim3(G), dim3(MEGA_THREADS), args,
+  return hipLaunchCooperativeKernel(pick(bf16, a.M, loop_block), dim3(G), dim3(MEGA_THREADS), args,
                                     (unsigned)smem, s);
 }
 

@@ -63,6 +63,9 @@ def test_static_loop_step_equals_loop_step(cfg):
 
 
 def test_static_loop_step_rejects_oversized_calls():
+    """Calls whose buffers exceed the static scratch (here the attention partials of
+    LS_MAX_ROWS rows over 10000 prefix keys), more rows than LS_MAX_ROWS, or more keys than
+    the kernels index come back as LS_ERR_CAPACITY before any device work."""
     from looped_transformer_self_amd import _lib as L
     from looped_transformer_self_amd.engine import Engine
     cfg = configs.MINI_OURO
@@ -70,10 +73,14 @@ def test_static_loop_step_rejects_oversized_calls():
     e = Engine(cfg, w, slot_capacity=64, max_rows=8, max_keys=64, max_jobs=4, prob_rows=4)
     fin_t = torch.zeros(64, dtype=torch.int32, device="cuda")
     rows = e.rows([1], [0], [1], 0, [[]], C.c_void_p(fin_t.data_ptr()))
-    rows.s.n_fin = 50_000_000                          # attention partials far beyond the scratch
+    rows.s.n = L.LS_MAX_ROWS
+    rows.s.n_fin = 10_000
     st = _static(e, rows, None)
     assert st == L.LS_ERR_CAPACITY and b"static scratch" in L.lib.ls_last_error()
-    rows.s.n_fin = 0
     rows.s.n = L.LS_MAX_ROWS + 1
+    rows.s.n_fin = 0
+    assert _static(e, rows, None) == L.LS_ERR_CAPACITY
+    rows.s.n = 1
+    rows.s.n_fin = (1 << 30) + 1
     assert _static(e, rows, None) == L.LS_ERR_CAPACITY
     e.close()
