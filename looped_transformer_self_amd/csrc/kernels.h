@@ -50,6 +50,7 @@ struct MegaArgs {
   float* logits;
   int ldo;
   float *patt, *ssq;
+  float* spart;                 // partial sums of split residual tiles: [workgroup][2][M][16]
   int* cnt;
   int* err;
   int init_mode;                // 0 none, 1 embedding rows of tokens, 2 gather Hg[gather[m]]

@@ -45,7 +45,7 @@ struct Workspace {
   void *o = nullptr, *act = nullptr;
   double* invf = nullptr;
   float* rope = nullptr;
-  float *patt = nullptr, *ssq = nullptr;
+  float *patt = nullptr, *ssq = nullptr, *spart = nullptr;
   int att_pmax = 0;                 // attention partials per (row, head) in patt
   int* cnt = nullptr;
   LayerW *tab_pre = nullptr, *tab_core = nullptr, *tab_coda = nullptr;
@@ -78,7 +78,7 @@ namespace {
 struct Carve {
   int max_rows, max_keys, max_jobs, att_pmax;
   size_t off_err, off_slot, off_dep, off_row, off_q, off_o, off_act, off_hc, off_logits;
-  size_t off_Xs, off_Ys, off_invf, off_rope, off_patt, off_ssq, off_cnt, off_tab, total;
+  size_t off_Xs, off_Ys, off_invf, off_rope, off_patt, off_ssq, off_spart, off_cnt, off_tab, total;
 };
 
 // Elements of one layer's slice of a per-layer activation buffer: rows x width, rounded up so
@@ -113,6 +113,7 @@ Carve carve(const ls_model* m, int max_rows, int max_keys, int max_jobs) {
   c.att_pmax = att_pmax_for(max_keys, d.n_heads, d.head_dim, (int)es);
   c.off_patt = take(R * d.n_heads * (size_t)c.att_pmax * (d.head_dim + 2) * 4);
   c.off_ssq = take(nl * 2 * (d.d / 16) * R * 4);
+  c.off_spart = take((size_t)MEGA_MAX_GRID * 2 * R * 16 * 4);
   c.off_cnt = take(mega_counter_ints(max_rows, d.d, d.F, d.n_heads, (int)nl) * 4);
   c.off_tab = take((size_t)(d.L + d.L_pre + d.L_coda) * sizeof(LayerW));
   c.total = off;
@@ -140,6 +141,7 @@ Workspace carve_into(const Carve& c, char* b) {
   w.patt = (float*)(b + c.off_patt);
   w.att_pmax = c.att_pmax;
   w.ssq = (float*)(b + c.off_ssq);
+  w.spart = (float*)(b + c.off_spart);
   w.cnt = (int*)(b + c.off_cnt);
   return w;
 }
@@ -319,7 +321,7 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
   a.logits = logits; a.ldo = d.V;
   a.inv_freq = m->w.invf;
   a.rope = m->w.rope;
-  a.patt = m->w.patt; a.ssq = m->w.ssq;
+  a.patt = m->w.patt; a.ssq = m->w.ssq; a.spart = m->w.spart;
   a.cnt = m->w.cnt; a.err = m->w.err;
   a.init_mode = init_mode; a.gather = gather ? gather + i0 : nullptr; a.Hg = Hg;
   a.do_head = logits != nullptr;

@@ -256,7 +256,7 @@ LS_DEV void wait_spread(const int* base, int lo, int hi, ConsBar& cb) {
 // ---- counter layout -----------------------------------------------------------------------------
 struct CntLayout {
   int per_layer, nchF;
-  int o_qkvh, o_o, o_gu, o_down, o_fa;
+  int o_qkvh, o_o, o_gu, o_down, o_fa, o_split;
   int o_init, total;
 };
 
@@ -271,6 +271,7 @@ __host__ __device__ inline CntLayout cnt_layout(int M, int d, int F, int nh, int
   c.o_gu = o; o += c.nchF * NSPREAD * PADC;
   c.o_down = o; o += NSPREAD * PADC;
   c.o_fa = o; o += M * nh;
+  c.o_split = o; o += 2 * (d / 16);        // arrivals at the split O and DOWN tiles
   o = (o + PADC - 1) / PADC * PADC;
   c.per_layer = o;
   c.o_init = n_layers * o;
@@ -285,9 +286,6 @@ struct LdsPlan {
   int NS, XC, nred;
 };
 constexpr int LDS_BUDGET = 160 * 1024 - 512;
-#ifndef LS_GU_AVOID
-#define LS_GU_AVOID 1
-#endif
 __host__ __device__ inline size_t x_region_bytes(int M, int esz, int XC) { return (size_t)M * (XC + 16 / esz) * esz; }
 // Per-launch row tables in LDS: rows by group [M], depth histogram [64], group offsets and
 // count [65], copies of the rows' slot [M], depth [M] and ancestor offsets [M + 1], and the
@@ -457,36 +455,58 @@ LS_DEV Share share_of(int n, int deal, int G, int b) {
   return s;
 }
 
-// A phase's tiles for workgroup b, in order.  Round-robin (tile first + i*G), except that the
-// gate/up phase deals its tiles beyond the last full round only to workgroups that will own
-// no down-projection tile (the down phase is dealt next, from deal + n): otherwise a quarter of
-// the workgroups would stream three gate/up tiles and then a 2.8x larger down tile while
-// others sit idle.
+// A phase's tiles for workgroup b, in order: tile first + i*G, i < count (round-robin).
 struct PhaseShare {
-  int first, count;   // round-robin part: tiles first + i*G, i < rounds
-  int rounds;
-  int rem0, nN, kN;   // extra tiles rem0 + kN + m*nN (m >= 0) of a workgroup outside the down set
-  LS_DEV int tile(int i, int G) const { return i < rounds ? first + i * G : rem0 + kN + (i - rounds) * nN; }
+  int first, count;
+  LS_DEV int tile(int i, int G) const { return first + i * G; }
 };
-LS_DEV PhaseShare phase_share(const MegaArgs& a, int ph, int n, int deal, int G, int b) {
-  PhaseShare p;
-  const Share s = share_of(n, deal, G, b);
-  p.first = s.first;
-  p.count = s.count;
-  p.rounds = s.count;
-  p.rem0 = 0; p.nN = 1; p.kN = 0;
-  const int nd = a.d / 16;                                  // down-projection tiles
-  if (LS_GU_AVOID && ph == PH_GU && nd < G && n % G != 0) {
-    const int full = n / G;                                 // complete rounds for everyone
-    const int jd = ((s.first - n) % G + G) % G;             // this workgroup's index in the down deal
-    p.rounds = full;
-    p.rem0 = full * G;
-    p.nN = G - nd;
-    p.kN = jd - nd;
-    const int rem = n - full * G;
-    p.count = full + (jd >= nd && p.kN < rem ? (rem - 1 - p.kN) / p.nN + 1 : 0);
+LS_DEV PhaseShare phase_share(int n, int deal, int G, int b) {
+  const Share sh = share_of(n, deal, G, b);
+  return PhaseShare{sh.first, sh.count};
+}
+
+// The residual phases (O, DOWN) have only d/16 tiles, often fewer than two per workgroup, so
+// they are dealt by slabs (stream-K): workgroup b < Gs = min(G, n * nk) takes the phase's slabs
+// [b * n * nk / Gs, (b + 1) * n * nk / Gs) in tile-major order, as units (tile, slabs
+// [k0, k1)).  A tile whose slabs span several (consecutive) workgroups is split: each leaves
+// its partial sum, and the last to arrive adds them in workgroup order and runs the epilogue.
+// Other phases deal whole tiles round-robin.
+LS_DEV bool split_phase(int ph) { return ph == PH_O || ph == PH_DOWN; }
+struct Units {
+  bool split;
+  PhaseShare sh;
+  int nk;                    // slabs per tile
+  int S0, S1, total, Gs;     // split phases: this workgroup's slabs, all slabs, workgroups used
+  LS_DEV int count() const {
+    if (!split) return sh.count;
+    return S1 > S0 ? (S1 - 1) / nk - S0 / nk + 1 : 0;
   }
-  return p;
+  LS_DEV void get(int i, int G, int& t, int& k0, int& k1) const {
+    if (!split) { t = sh.tile(i, G); k0 = 0; k1 = nk; return; }
+    t = S0 / nk + i;
+    k0 = max(S0 - t * nk, 0);
+    k1 = min(S1 - t * nk, nk);
+  }
+  LS_DEV int owner(int sl) const { return (int)(((long long)(sl + 1) * Gs - 1) / total); }
+  LS_DEV int first_tile(int b) const { return (int)((long long)b * total / Gs) / nk; }
+  // the partial slot of workgroup b for split tile t: 0 for its first unit, 1 for its last
+  LS_DEV int pslot(int b, int t) const { return t == first_tile(b) ? 0 : 1; }
+};
+LS_DEV Units units_of(int ph, int n_tiles, int nk, int deal, int G, int b) {
+  Units u;
+  u.split = split_phase(ph);
+  u.nk = nk;
+  u.sh = PhaseShare{0, 0};
+  u.S0 = u.S1 = 0;
+  u.total = n_tiles * nk;
+  u.Gs = min(G, u.total);
+  if (!u.split) {
+    u.sh = phase_share(n_tiles, deal, G, b);
+  } else if (b < u.Gs) {
+    u.S0 = (int)((long long)b * u.total / u.Gs);
+    u.S1 = (int)((long long)(b + 1) * u.total / u.Gs);
+  }
+  return u;
 }
 
 // Wait for this wave's LDS (and scalar memory) operations only.
@@ -1557,16 +1577,18 @@ LS_DEV void init_unit(const MegaArgs& a, const CntLayout& cl, ConsBar& cb, int m
 // staged, 4 first tile batch multiplied.  Producer wave 0: 5 first slab issued, 6 last issued.
 
 // ---- the walk: the same slab sequence for producers and consumers ----------------------------------
-// Phase ph of layer l: the workgroup's tiles one by one; within a tile, activation chunk by
-// chunk (XC columns), slab by slab.
+// Phase ph of layer l: the workgroup's units (whole tiles, or slab ranges of tiles in the
+// residual phases) one by one; within a unit, activation chunk by chunk (XC columns), slab by
+// slab.
 template <typename T, int MT, bool PROD>
 LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int ph, int l, int& deal,
                       Producer<T>* pr, Consumer<T, MT>* co, ConsBar* cb) {
   const int G = gridDim.x, b = blockIdx.x;
   const PhaseGeo g = phase_geo<T>(a, ph);
-  const PhaseShare sh = phase_share(a, ph, g.n_tiles, deal, G, b);
+  const Units un = units_of(ph, g.n_tiles, (g.K + g.sk - 1) / g.sk, deal, G, b);
   deal = (deal + g.n_tiles) % G;
-  if (sh.count == 0) return;
+  const int nun = un.count();
+  if (nun == 0) return;
   const LayerW lw = ph == PH_HEAD ? LayerW{} : a.layers[l];
   const int nchunk = (g.K + s.XC - 1) / s.XC;
 
@@ -1604,17 +1626,23 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
     if (threadIdx.x == 0) tstamp(a, l, ph, 2);
   }
 
-  // One tile at a time.  With one activation chunk (the usual case) the chunk is staged once
-  // for all of the workgroup's tiles; with several, every tile re-stages its chunks.
+  // One unit at a time.  With one activation chunk (the usual case) the chunk is staged once
+  // for all of the workgroup's units; with several, every unit re-stages the chunks it covers.
   const bool restage = nchunk > 1;
-  for (int i = 0; i < sh.count; ++i) {
-    const int t = sh.tile(i, G);
+  for (int i = 0; i < nun; ++i) {
+    int t, k0, k1;
+    un.get(i, G, t, k0, k1);
     f32x4_t acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bool began = false;
     for (int ch = 0; ch < nchunk; ++ch) {
       const int x0 = ch * s.XC;
       const int xn = min(s.XC, g.K - x0);
+      const int k_first = x0 / g.sk;
+      const int k_last = (x0 + xn + g.sk - 1) / g.sk;
+      const int ka = max(k_first, k0), kb = min(k_last, k1);
+      if (ka >= kb) continue;                 // the unit has no slab in this chunk
       if (!PROD && (restage || i == 0)) {
         const int* C = a.cnt + (size_t)l * cl.per_layer;
         if (ph == PH_DOWN) {
@@ -1627,16 +1655,14 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
         else co->stage_norm(nsrc, nvia, gain, x0, xn, fuse, poll);
         if (threadIdx.x == 0 && i == 0 && ch == 0) tstamp(a, l, ph, 3);
       }
-      const int k_first = x0 / g.sk;
-      const int k_last = (x0 + xn + g.sk - 1) / g.sk;
-      if (PROD && ch == 0) pr->begin_tile(lw, ph, t, g);
-      for (int k = k_first; k < k_last; ++k) {
-        if (PROD) {
-          if (threadIdx.x == 64 * NCONS && i == 0 && ch == 0 && k == k_first) tstamp(a, l, ph, 5);
-          pr->issue(k, g);
-        } else {
-          co->slab(k - k_first, min(g.sk, g.K - k * g.sk), acc);
-        }
+      if (PROD && !began) {
+        pr->begin_tile(lw, ph, t, g);
+        if (threadIdx.x == 64 * NCONS && i == 0) tstamp(a, l, ph, 5);
+      }
+      began = true;
+      for (int k = ka; k < kb; ++k) {
+        if (PROD) pr->issue(k, g);
+        else co->slab(k - k_first, min(g.sk, g.K - k * g.sk), acc);
       }
     }
     if (!PROD) {
@@ -1667,7 +1693,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
       // buffer the epilogue wave has not released, so buffer b's count covers one tile at a time.
       if (lane == 0) lds_bump(s.ints + 2 * s.NS + 1 + q % s.nred);   // after this wave's partial writes complete
     }
-    if (PROD && threadIdx.x == 64 * NCONS && i == sh.count - 1) tstamp(a, l, ph, 6);
+    if (PROD && threadIdx.x == 64 * NCONS && i == nun - 1) tstamp(a, l, ph, 6);
   }
 }
 
@@ -1676,31 +1702,46 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
 // epilogue and release the partial buffer.  Stores are drained, and the tiles' counters
 // bumped, once no further tile of the phase is ready, so a burst of tiles costs one drain.
 //
-// Residual inputs of the first O / DOWN tile are loaded when the walk starts if the workgroup
-// had tiles in the phase before (QKV / GU): their partials having arrived means the consumers
-// passed that phase's dependency wait, which implies the residual rows are complete (the
-// previous layer for O, the O phase for DOWN).  The loads then overlap the consumers' work.
+// Residual inputs of the first O / DOWN unit, when it is a whole tile, are loaded when the walk
+// starts if the workgroup had tiles in the phase before (QKV / GU): their partials having
+// arrived means the consumers passed that phase's dependency wait, which implies the residual
+// rows are complete (the previous layer for O, the O phase for DOWN).  The loads then overlap
+// the consumers' work.
+//
+// A unit that covers only part of a split tile stores its sum to the workgroup's partial slot
+// (spart: [workgroup][first / last unit][M x 16]) and counts itself on the tile's counter; the
+// last of the tile's workgroups adds every partial in workgroup order (its own from LDS) and
+// runs the epilogue.  The slots are reused from phase to phase: a residual phase starts only
+// after the previous one's tiles are complete.
 template <typename T>
 LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int ph, int l, int& deal, int& seq,
                      bool& had_tiles) {
   const int G = gridDim.x, b = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const PhaseGeo g = phase_geo<T>(a, ph);
-  const PhaseShare sh = phase_share(a, ph, g.n_tiles, deal, G, b);
+  const Units un = units_of(ph, g.n_tiles, (g.K + g.sk - 1) / g.sk, deal, G, b);
   deal = (deal + g.n_tiles) % G;
-  const bool pref = (ph == PH_O || ph == PH_DOWN) && had_tiles && sh.count > 0 && a.M <= 16;
+  const int nun = un.count();
+  int t0 = 0, k00 = 0, k10 = 0;
+  if (nun > 0) un.get(0, G, t0, k00, k10);
+  const bool pref = (ph == PH_O || ph == PH_DOWN) && had_tiles && nun > 0 && k00 == 0 && k10 == un.nk && a.M <= 16;
   // O / DOWN counts are waited for only when the next normalised phase cannot poll its input
   // (its row does not fit one fused staging pass); otherwise their drain and bump are skipped.
   const bool next_polls = a.d <= s.XC && a.d <= FUSE_MAX_K;
   const bool signals = ph != PH_HEAD && !((ph == PH_O || ph == PH_DOWN) && next_polls);
   float pre[4] = {0.f, 0.f, 0.f, 0.f};
-  if (pref) residual_load(a, s, ph, l, sh.tile(0, G), 0, lane, pre);
-  had_tiles = sh.count > 0;
-  int pend = 0;                            // first of this phase's tiles not yet signalled
-  for (int i = 0; i < sh.count; ++i) {
-    const int t = sh.tile(i, G);
+  if (pref) residual_load(a, s, ph, l, t0, 0, lane, pre);
+  had_tiles = nun > 0;
+  int* C = a.cnt + (size_t)l * cl.per_layer;
+  const int MS = a.M * 16;
+  constexpr int NPEND = 8;
+  int pend[NPEND];                         // finished tiles not yet signalled
+  int npend = 0;
+  for (int i = 0; i < nun; ++i) {
+    int t, k0, k1;
+    un.get(i, G, t, k0, k1);
     const int q = seq++;
-    float* buf = s.red + (size_t)(q % s.nred) * NCONS * a.M * 16;
+    float* buf = s.red + (size_t)(q % s.nred) * NCONS * MS;
     if (lane == 0) {
       int n = 0;
       while (lds_peek(s.ints + 2 * s.NS + 1 + q % s.nred) < NCONS * (q / s.nred + 1)) {
@@ -1710,25 +1751,47 @@ LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int p
     }
     __builtin_amdgcn_wave_barrier();
     asm volatile("" : : : "memory");
-    for (int idx = lane; idx < a.M * 16; idx += 64) {
+    for (int idx = lane; idx < MS; idx += 64) {
       float y = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < NCONS; ++cc) y += buf[(size_t)cc * a.M * 16 + idx];
-      buf[idx] = y;                        // consumer 0's slot now holds the tile sum
+      for (int cc = 0; cc < NCONS; ++cc) y += buf[(size_t)cc * MS + idx];
+      buf[idx] = y;                        // consumer 0's slot now holds the unit's sum
     }
     __builtin_amdgcn_wave_barrier();
     wait_lgkm0();                          // the sums are visible to every lane
-    epilogue<T>(a, cl, s, ph, l, t, buf, lane, pref && i == 0, pre);
+    bool run = k0 == 0 && k1 == un.nk;     // the unit is the whole tile
+    if (!run) {
+      float* mine = a.spart + ((size_t)b * 2 + un.pslot(b, t)) * MS;
+      for (int idx = lane; idx < MS; idx += 64) stc(mine + idx, buf[idx]);
+      drain();
+      int old = 0;
+      if (lane == 0) old = atomicAdd(C + cl.o_split + (ph == PH_DOWN ? g.n_tiles : 0) + t, 1);
+      old = __shfl(old, 0, 64);
+      const int o0 = un.owner(t * un.nk), o1 = un.owner(t * un.nk + un.nk - 1);
+      if (old == o1 - o0) {                // every other part has arrived: sum in workgroup order
+        for (int idx = lane; idx < MS; idx += 64) {
+          float y = 0.f;
+          for (int bb = o0; bb <= o1; ++bb)
+            y += bb == b ? buf[idx] : ldc(a.spart + ((size_t)bb * 2 + un.pslot(bb, t)) * MS + idx);
+          buf[idx] = y;
+        }
+        __builtin_amdgcn_wave_barrier();
+        wait_lgkm0();
+        run = true;
+      }
+    }
+    if (run) epilogue<T>(a, cl, s, ph, l, t, buf, lane, pref && i == 0, pre);
     wait_lgkm0();                          // the epilogue's reads of the buffer are complete
     if (lane == 0) lds_bump(s.ints + 2 * s.NS + 3);
     if (!signals) continue;
+    if (run) pend[npend++] = t;
     const bool next_ready =
-        i + 1 < sh.count && lds_peek(s.ints + 2 * s.NS + 1 + (q + 1) % s.nred) >= NCONS * ((q + 1) / s.nred + 1);
-    if (!next_ready) {
+        i + 1 < nun && lds_peek(s.ints + 2 * s.NS + 1 + (q + 1) % s.nred) >= NCONS * ((q + 1) / s.nred + 1);
+    if (npend > 0 && (!next_ready || npend == NPEND)) {
       drain();
       if (lane == 0)
-        for (int k = pend; k <= i; ++k) tile_signal(a, cl, ph, l, sh.tile(k, G), s.XC);
-      pend = i + 1;
+        for (int k = 0; k < npend; ++k) tile_signal(a, cl, ph, l, pend[k], s.XC);
+      npend = 0;
     }
   }
 }
