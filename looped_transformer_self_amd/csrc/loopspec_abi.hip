@@ -111,7 +111,7 @@ Carve carve(const ls_model* m, int max_rows, int max_keys, int max_jobs) {
   c.off_invf = take((size_t)d.head_dim / 2 * 8);
   c.off_rope = take(R * (size_t)d.head_dim * 4);
   c.att_pmax = att_pmax_for(max_keys, d.n_heads, d.head_dim, (int)es);
-  c.off_patt = take(R * d.n_heads * (size_t)c.att_pmax * (d.head_dim + 2) * 4);
+  c.off_patt = take(R * d.n_heads * (size_t)c.att_pmax * (d.head_dim + 4) * 4);
   c.off_ssq = take(nl * 2 * (d.d / 16) * R * 4);
   c.off_spart = take((size_t)MEGA_MAX_GRID * 2 * R * 16 * 4);
   c.off_cnt = take(mega_counter_ints(max_rows, d.d, d.F, d.n_heads, (int)nl) * 4);

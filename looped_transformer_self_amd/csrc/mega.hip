@@ -1195,101 +1195,133 @@ LS_DEV void walk_att_prod(const MegaArgs& a, const Lds& s, int l, Producer<T>& p
   if (threadIdx.x == 64 * NCONS) tstamp(a, l, PH_ATT, 6);
 }
 
-// Merge of head h for row i (by one wave; lane = dims 2*lane, 2*lane + 1): the np prefix
-// partials of the row's segment and the row's own keys (its speculative ancestors, then
-// itself, written by this launch), online log-sum-exp over batches of (16 partials, 8 own
-// keys); every load of a batch is issued before any is used, so a batch costs one memory
-// round trip.
+// Partial records of the attention phase: acc[hd], then max and sum (16-byte aligned rows).
+LS_DEV int att_rec(int hd) { return hd + 4; }
+
+// Four elements of a K / V entry written by this launch (agent-coherent load).
+template <typename T> LS_DEV void load4_coh(const T* p, float* f);
+template <> LS_DEV void load4_coh<uint16_t>(const uint16_t* p, float* f) {
+  const unsigned long long w = ldc64(p);
+  const unsigned lo = (unsigned)w, hi = (unsigned)(w >> 32);
+  f[0] = __uint_as_float(lo << 16); f[1] = __uint_as_float(lo & 0xffff0000u);
+  f[2] = __uint_as_float(hi << 16); f[3] = __uint_as_float(hi & 0xffff0000u);
+}
+template <> LS_DEV void load4_coh<float>(const float* p, float* f) {
+  const unsigned long long w0 = ldc64(p), w1 = ldc64(p + 2);
+  f[0] = __uint_as_float((unsigned)w0); f[1] = __uint_as_float((unsigned)(w0 >> 32));
+  f[2] = __uint_as_float((unsigned)w1); f[3] = __uint_as_float((unsigned)(w1 >> 32));
+}
+
+// Sum / maximum over the 32 lanes of each half of the wave (every lane gets its half's result).
+LS_DEV float half_sum(float v) {
+  v = row_sum16(v);
+  const float h0 = lane_f(v, 0) + lane_f(v, 16), h1 = lane_f(v, 32) + lane_f(v, 48);
+  return (threadIdx.x & 32) ? h1 : h0;
+}
+LS_DEV float half_max(float v) {
+  v = row_max16(v);
+  const float h0 = fmaxf(lane_f(v, 0), lane_f(v, 16)), h1 = fmaxf(lane_f(v, 32), lane_f(v, 48));
+  return (threadIdx.x & 32) ? h1 : h0;
+}
+
+// Merge of heads hA (lanes 0-31) and hB (lanes 32-63; hB < 0: none) for row i, by one wave;
+// lane = 4 dims of its half's head: the np prefix partials of the row's segment and the row's
+// own keys (its speculative ancestors, then itself, written by this launch), online
+// log-sum-exp over batches of (16 partials, 4 own keys); every load of a batch is issued before
+// any is used, so a batch costs one memory round trip.
 template <typename T>
-LS_DEV void att_merge_row(const MegaArgs& a, const Lds& s, int l, int blk, int i, int h, int np) {
-  const int lane = threadIdx.x & 63;
-  const int hd = a.hd;
-  const bool dok = 2 * lane < hd;
-  const T* cache = (const T*)a.kv + (size_t)blk * a.S * 2 * a.d;
+LS_DEV void att_merge2(const MegaArgs& a, const Lds& s, int l, int blk, int i, int hA, int hB, int np) {
+  const int lane = threadIdx.x & 63, half = lane >> 5, hl = lane & 31;
+  const int hd = a.hd, rec = att_rec(hd);
+  const int h = half ? hB : hA;
+  const bool hok = h >= 0;
+  const int hh = hok ? h : hA;
+  const bool dok = hok && 4 * hl < hd;
+  const int d0 = 4 * min(hl, hd / 4 - 1);           // this lane's dims (lanes past the head repeat)
+  const T* cache = (const T*)a.kv + (size_t)blk * a.S * 2 * a.d + hh * hd + d0;
   const float scale = 1.0f / sqrtf((float)hd);
-  T* orow = o_of<T>(a, l) + (size_t)i * a.d + h * hd;
+  T* orow = o_of<T>(a, l) + (size_t)i * a.d + hh * hd + d0;
   const int self = s.rslot[i];
-  if (self < 0) {                                  // rejected row: zero output
-    if (dok) store2_coh<T>(orow + 2 * lane, 0.f, 0.f);
+  if (self < 0) {                                    // rejected row: zero output
+    if (dok) { store2_coh<T>(orow, 0.f, 0.f); store2_coh<T>(orow + 2, 0.f, 0.f); }
     return;
   }
   const int a0 = s.raoff[i], na = s.raoff[i + 1] - a0;
-  const int nt = na + 1;                           // the row's own keys: ancestors, then itself
-  const float* base = a.patt + ((size_t)i * a.nh + h) * a.att_pmax * (hd + 2);
-  // the query joins the first batch's loads (it is converted where the scores are formed)
-  const unsigned long long qw = dok ? ldc64(a.q + (size_t)i * a.d + h * hd + 2 * lane) : 0ull;
-  float run_m = -INFINITY, den = 0.f, num0 = 0.f, num1 = 0.f;
-  const int nbat = max((np + 15) / 16, (nt + 7) / 8);
-  for (int bt = 0; bt < nbat; ++bt) {
-    const int c0 = bt * 16, j0 = bt * 8;
-    // ---- issue the batch's loads
-    const int cl_ = c0 + lane;                     // partial whose statistics this lane holds
-    float mxc = -INFINITY, smc = 0.f;
-    if (lane < 16 && cl_ < np) {
-      mxc = ldc(base + (size_t)cl_ * (hd + 2));
-      smc = ldc(base + (size_t)cl_ * (hd + 2) + 1);
-    }
-    float2 ac[16];
+  const int nt = na + 1;                             // the row's own keys: ancestors, then itself
+  const __amdgpu_buffer_rsrc_t Rp = rsrc_of(a.patt + (size_t)i * a.nh * a.att_pmax * rec, a.nh * a.att_pmax * rec * 4);
+  const int pbase = hh * a.att_pmax * rec;           // this half's head: its first partial record
+  float q[4];
+  {
+    const u32x4_t w = ldc128(rsrc_of(a.q, a.M * a.d * 4), (i * a.d + hh * hd + d0) * 4);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int cc = min(c0 + u, np - 1);
-      ac[u] = make_float2(0.f, 0.f);
-      if (dok && c0 + u < np) {
-        const unsigned long long w = ldc64(base + (size_t)cc * (hd + 2) + 2 + 2 * lane);
-        ac[u] = make_float2(__uint_as_float((unsigned)w), __uint_as_float((unsigned)(w >> 32)));
-      }
+    for (int e = 0; e < 4; ++e) q[e] = __uint_as_float(w[e]) * scale;
+  }
+  float run_m = -INFINITY, den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
+  constexpr int NK = 4;                             // own keys per batch
+  const int nbat = max((np + 15) / 16, (nt + NK - 1) / NK);
+  for (int bt = 0; bt < nbat; ++bt) {
+    const int c0 = bt * 16, j0 = bt * NK;
+    // ---- issue the batch's loads
+    float mxc = -INFINITY, smc = 0.f;                // statistics of partial c0 + hl (hl < 16)
+    if (hok && hl < 16 && c0 + hl < np) {
+      mxc = ldc(a.patt + (size_t)i * a.nh * a.att_pmax * rec + pbase + (size_t)(c0 + hl) * rec + hd);
+      smc = ldc(a.patt + (size_t)i * a.nh * a.att_pmax * rec + pbase + (size_t)(c0 + hl) * rec + hd + 1);
     }
-    float2 k2[8], v2[8];
-    int xs[8];
+    u32x4_t ac[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      ac[u] = ldc128(Rp, hok && c0 + u < np ? (pbase + (c0 + u) * rec + d0) * 4 : 0x7fffff00);
+    float kf[NK][4], vf[NK][4];
     bool bad = false;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < NK; ++u) {
       const int j = min(j0 + u, nt - 1);
-      xs[u] = j < na ? a.anc[a0 + j] : self;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (xs[u] < 0 || xs[u] >= a.S) { bad = bad || j0 + u < nt; xs[u] = self; }
-      const T* ent = cache + (size_t)xs[u] * 2 * a.d + h * hd + 2 * lane;
-      k2[u] = v2[u] = make_float2(0.f, 0.f);
-      if (dok && j0 + u < nt) {
-        k2[u] = load2_coh<T>(ent);
-        v2[u] = load2_coh<T>(ent + a.d);
-      }
+      int x = j < na ? a.anc[a0 + j] : self;
+      if (x < 0 || x >= a.S) { bad = bad || j0 + u < nt; x = self; }
+      load4_coh<T>(cache + (size_t)x * 2 * a.d, kf[u]);
+      load4_coh<T>(cache + (size_t)x * 2 * a.d + a.d, vf[u]);
     }
     if (bad) ls_flag(a.err, 1);
     // ---- the batch's scores and its maximum
-    const float q0 = __uint_as_float((unsigned)qw) * scale, q1 = __uint_as_float((unsigned)(qw >> 32)) * scale;
-    float sc[8];
-    float bm = wave_max(mxc);
+    float sc[NK];
+    float bm = half_max(mxc);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      sc[u] = wave_sum(q0 * k2[u].x + q1 * k2[u].y);
+    for (int u = 0; u < NK; ++u) {
+      const float part = dok ? (q[0] * kf[u][0] + q[1] * kf[u][1]) + (q[2] * kf[u][2] + q[3] * kf[u][3]) : 0.f;
+      sc[u] = half_sum(part);
       if (j0 + u < nt) bm = fmaxf(bm, sc[u]);
     }
     const float nm = fmaxf(run_m, bm);
-    if (nm == -INFINITY) continue;                 // nothing in this batch or before
+    if (__all(nm == -INFINITY)) continue;            // nothing in this batch or before
     const float rs = run_m == -INFINITY ? 0.f : __expf(run_m - nm);
-    den *= rs; num0 *= rs; num1 *= rs;
+    den *= rs;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) num[e] *= rs;
     run_m = nm;
-    // prefix partials: weight w_c = exp(mx_c - m) held by lane c - c0
+    // prefix partials: weight w_c = exp(mx_c - m) held by lane c - c0 of the half
     const float wl = mxc == -INFINITY ? 0.f : __expf(mxc - nm);
-    den += wave_sum(wl * smc);
+    den += half_sum(wl * smc);
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const float w = lane_f(wl, u);
-      num0 += w * ac[u].x;
-      num1 += w * ac[u].y;
+      const float w = half ? lane_f(wl, 32 + u) : lane_f(wl, u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] += w * __uint_as_float(ac[u][e]);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < NK; ++u) {
       const float w = j0 + u < nt ? __expf(sc[u] - nm) : 0.f;
       den += w;
-      num0 += w * v2[u].x;
-      num1 += w * v2[u].y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] += w * vf[u][e];
     }
   }
-  if (dok) store2_coh<T>(orow + 2 * lane, den > 0.f ? canon_nan(num0 / den) : 0.f, den > 0.f ? canon_nan(num1 / den) : 0.f);
+  if (dok) {
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = den > 0.f ? canon_nan(num[e] / den) : 0.f;
+    store2_coh<T>(orow, y[0], y[1]);
+    store2_coh<T>(orow + 2, y[2], y[3]);
+  }
 }
 
 // 16 bytes of LDS at byte address addr.
@@ -1370,14 +1402,14 @@ LS_DEV void att_phase(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
 #pragma unroll
       for (int r = 0; r < NRA; ++r) {
         if (r >= nr) continue;
-        float* out = a.patt + (((size_t)rows[r] * a.nh + h0 + jh) * a.att_pmax + (b - o0)) * (hd + 2);
-        if (sub == 0) { stc(out, mrun[r]); stc(out + 1, lsum[r]); }
+        float* out = a.patt + (((size_t)rows[r] * a.nh + h0 + jh) * a.att_pmax + (b - o0)) * att_rec(hd);
+        if (sub == 0) { stc(out + hd, mrun[r]); stc(out + hd + 1, lsum[r]); }
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
           const int ch = sub + 4 * u;
           if (ch < nch) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) stc(out + 2 + ch * E + e, acc[r][u * E + e]);
+            for (int e = 0; e < E; ++e) stc(out + ch * E + e, acc[r][u * E + e]);
           }
         }
       }
@@ -1388,10 +1420,8 @@ LS_DEV void att_phase(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
     cb.sync();
     if (s.ints[2 * s.NS + 4] == np - 1) {
       // this consumer merges its own heads (it has waited for their QKV tiles)
-      for (int r = 0; r < nr; ++r) {
-        if (c < hbn) att_merge_row<T>(a, s, l, blk, rows[r], h0 + c, np);
-        if (c + 4 < hbn) att_merge_row<T>(a, s, l, blk, rows[r], h0 + c + 4, np);
-      }
+      for (int r = 0; r < nr; ++r)
+        if (c < hbn) att_merge2<T>(a, s, l, blk, rows[r], h0 + c, c + 4 < hbn ? h0 + c + 4 : -1, np);
     }
   };
 
