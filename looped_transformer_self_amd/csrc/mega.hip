@@ -307,7 +307,10 @@ __host__ __device__ inline size_t lds_bytes_for(int M, int esz, int NS, int XC, 
 __host__ __device__ inline LdsPlan lds_plan(int M, int esz, int d) {
   const int sk = 512 / esz;
   const int xfull = (d + sk - 1) / sk * sk;
-  const int ns_opts[5] = {16, 14, 12, 10, 8};
+#ifndef LS_NS_MAX
+#define LS_NS_MAX 18
+#endif
+  const int ns_opts[5] = {LS_NS_MAX, LS_NS_MAX - 2, LS_NS_MAX - 4, LS_NS_MAX - 6, 8};
   for (int i = 0; i < 5; ++i)
     if (lds_bytes_for(M, esz, ns_opts[i], xfull, 2) <= LDS_BUDGET) return LdsPlan{ns_opts[i], xfull, 2};
   // many rows: narrower activation chunks first, then a shallower ring (down to 4 slabs, one
@@ -539,7 +542,7 @@ LS_DEV void wait_vm_le8(int n) { wait_vm_le8_impl<56>(__builtin_amdgcn_readfirst
 // so the per-slab instruction count is what bounds a wave's streaming rate: row addresses are
 // computed once per tile, and a slab costs a compare, eight address adds and eight loads.
 #ifndef LS_PFL
-#define LS_PFL 2
+#define LS_PFL 4
 #endif
 constexpr int PFL = LS_PFL;
 // Cache policy of the weight loads: non-temporal.  Every weight byte is read once per call, by
@@ -615,9 +618,8 @@ struct Producer {
         if (pub < mine) {
           wait_vm_le8(8 * (mine - pub - 1));
           publish_one();
-        } else {
-          __builtin_amdgcn_s_sleep(0);
-          if (give_up(n, a.err)) break;
+        } else if (give_up(n, a.err)) {
+          break;
         }
       }
     }
@@ -836,17 +838,18 @@ struct Consumer {
     cb.sync();
   }
 
-  // Pass one slab of the sequence; if it is this consumer's (q mod 4 == c), multiply it.
+  // Pass one slab of the sequence; if it is this consumer's, multiply it (q: the slab's index in
+  // the staged activation chunk).
   LS_DEV void slab(int q, int kn, f32x4_t* acc) {
     const int slot = cslot, use = cuse;
     if (++cslot == s.NS) { cslot = 0; ++cuse; }
-    if ((q & (NCONS - 1)) != c) return;
+    // slabs are dealt to the consumers by position in the workgroup's whole sequence, so the
+    // four share every phase's slabs evenly whatever the slabs per tile
+    if (((use * s.NS + slot) & (NCONS - 1)) != c) return;
     if (lane == 0) {
       int n = 0;
-      while (lds_peek(s.ints + slot) < use + 1) {
-        __builtin_amdgcn_s_sleep(0);
+      while (lds_peek(s.ints + slot) < use + 1)     // tight poll: the slab is usually close
         if (give_up(n, a.err)) break;
-      }
     }
     __builtin_amdgcn_wave_barrier();
     asm volatile("" : : : "memory");
