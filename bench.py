@@ -255,8 +255,10 @@ def microbench(workload, Ms=(1, 2, 3, 4, 8, 16, 128), reps=10):
     spread over 1..R, each attending to a finished prefix of the workload's full context
     (prompt + new tokens), inputs resident in HBM (seeded synthetic hidden rows and KV
     entries).  Per M: event-timed microseconds per call, algorithmic bytes per call, GB/s and
-    the fraction of 8 TB/s.  Also a streaming-read reference: PyTorch's sum over a 4 GiB
-    bf16 tensor (reads only), the rate a plain library kernel sustains on this device."""
+    the fraction of 8 TB/s.  Also two streaming-read references over a 4 GiB buffer:
+    ls_measure_stream_read (the loads ls_loop_step's producer waves issue, with no consumers:
+    the achievable rate of that load pattern on this device) and PyTorch's sum (reads only, a
+    plain library kernel)."""
     import ctypes
 
     import torch
@@ -303,7 +305,24 @@ def microbench(workload, Ms=(1, 2, 3, 4, 8, 16, 128), reps=10):
         print(f"[microbench] {wl.key} M={M}: {us:.1f} us, {by / 1e9:.3f} GB, {by / us / 1e3:.0f} GB/s", file=sys.stderr,
               flush=True)
     e.close()
+    from looped_transformer_self_amd import _lib as L
     x = torch.empty(1 << 31, dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+    n_wg = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def stream_read():
+        L.check(L.lib.ls_measure_stream_read(ctypes.c_void_p(x.data_ptr()), x.numel() * 2, n_wg, stream),
+                "ls_measure_stream_read")
+    for _ in range(2):
+        stream_read()
+    torch.cuda.synchronize()
+    b, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b.record()
+    for _ in range(reps):
+        stream_read()
+    en.record()
+    torch.cuda.synchronize()
+    slab_gbs = x.numel() * 2 / (b.elapsed_time(en) / reps * 1e-3) / 1e9
     for _ in range(2):
         x.sum(dtype=torch.float32)
     torch.cuda.synchronize()
@@ -315,7 +334,9 @@ def microbench(workload, Ms=(1, 2, 3, 4, 8, 16, 128), reps=10):
     torch.cuda.synchronize()
     read_gbs = x.numel() * 2 / (b.elapsed_time(en) / reps * 1e-3) / 1e9
     out = {"workload": f"{wl.key}: {wl.description}", "prefix_keys": n_fin, "loop_step": res,
-           "streaming_read_GB_s": round(read_gbs, 1), "streaming_read_note": "torch sum over a 4 GiB bf16 tensor"}
+           "streaming_read_GB_s": round(slab_gbs, 1),
+           "streaming_read_note": "ls_measure_stream_read over 4 GiB: the producer waves' load pattern, no consumers",
+           "torch_sum_GB_s": round(read_gbs, 1)}
     print(json.dumps(out), flush=True)
 
 

@@ -263,6 +263,15 @@ ls_status ls_set_wait_limit(ls_model *m, double seconds);
  * Pass NULL to stop.  Not needed for decoding. */
 ls_status ls_debug_trace(ls_model *m, long long *dev_buf, int *grid_out);
 
+/* Measurement aid (not part of decoding): reads bytes of device memory at src with the loads
+ * the layer kernel's producer waves use (16-byte direct-to-LDS, non-temporal, 1 KB per wave
+ * instruction, 16 in flight per wave, two waves per workgroup), n_workgroups workgroups (one per
+ * CU: the device's multiprocessor count), asynchronously on stream; time it with events to get
+ * the streaming-read rate that ls_loop_step's HBM roofline is compared against.  bytes must be
+ * a positive multiple of n_workgroups * 2 KiB (else LS_ERR_INVALID); LS_ERR_HIP if the launch
+ * fails.  No workspace, no model. */
+ls_status ls_measure_stream_read(const void *src, size_t bytes, int n_workgroups, hipStream_t stream);
+
 /* Host-side Philox4x32-10 (Salmon et al., SC'11): word 0 of the block for key
  * (seed mod 2^32, seed >> 32) and counter (pos, purpose, 0, 0).  Fills out[i] for
  * purposes purposes[i]; used by the scheduler to build the uniform rows of ls_verify. */
