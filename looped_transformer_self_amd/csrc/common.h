@@ -9,6 +9,7 @@
 typedef short bf16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
 typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // bf16 <-> fp32 (bf16 held as uint16 bit patterns).
 LS_DEV float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

@@ -286,7 +286,19 @@ struct LdsPlan {
   int NS, XC, nred;
 };
 constexpr int LDS_BUDGET = 160 * 1024 - 512;
-__host__ __device__ inline size_t x_region_bytes(int M, int esz, int XC) { return (size_t)M * (XC + 16 / esz) * esz; }
+// Rows of the attention phase's virtual groups (see the attention section).
+constexpr int NRA = 1;
+// The attention phase reuses the activation region for the consumer waves' softmax states:
+// consumers 1..3 x NRA rows x (a head block's accumulators, HB * hd <= min(2048 / esz, d)
+// floats, and the block's maxima and sums, 2 x HB <= 16).
+__host__ __device__ inline size_t att_cmb_bytes(int esz, int d) {
+  const int hbhd = 2048 / esz < d ? 2048 / esz : d;
+  return (size_t)(NCONS - 1) * NRA * (hbhd + 16) * 4;
+}
+__host__ __device__ inline size_t x_region_bytes(int M, int esz, int XC, int d) {
+  const size_t x = (size_t)M * (XC + 16 / esz) * esz, c = att_cmb_bytes(esz, d);
+  return x > c ? x : c;
+}
 // Per-launch row tables in LDS: rows by group [M], depth histogram [64], group offsets and
 // count [65], copies of the rows' slot [M], depth [M] and ancestor offsets [M + 1], and the
 // virtual groups of the attention phase [M + 1].
@@ -294,9 +306,9 @@ __host__ __device__ inline int row_table_ints(int M) { return M + 64 + 65 + M + 
 // Key-slot windows of the producer waves (ATT_WPW slots each).
 constexpr int ATT_WPW = 256;
 constexpr int ATT_WIN = 2 * ATT_WPW;
-__host__ __device__ inline size_t lds_bytes_for(int M, int esz, int NS, int XC, int nred) {
+__host__ __device__ inline size_t lds_bytes_for(int M, int esz, int NS, int XC, int nred, int d) {
   size_t off = (size_t)NS * SLAB + ATT_WIN * 4;
-  off = (off + x_region_bytes(M, esz, XC) + 15) & ~(size_t)15;
+  off = (off + x_region_bytes(M, esz, XC, d) + 15) & ~(size_t)15;
   off = (off + (size_t)row_table_ints(M) * 4 + 15) & ~(size_t)15;
   off = (off + (size_t)nred * NCONS * M * 16 * 4 + 15) & ~(size_t)15;
   off = (off + (size_t)M * 4 + 15) & ~(size_t)15;
@@ -312,12 +324,12 @@ __host__ __device__ inline LdsPlan lds_plan(int M, int esz, int d) {
 #endif
   const int ns_opts[5] = {LS_NS_MAX, LS_NS_MAX - 2, LS_NS_MAX - 4, LS_NS_MAX - 6, 8};
   for (int i = 0; i < 5; ++i)
-    if (lds_bytes_for(M, esz, ns_opts[i], xfull, 2) <= LDS_BUDGET) return LdsPlan{ns_opts[i], xfull, 2};
+    if (lds_bytes_for(M, esz, ns_opts[i], xfull, 2, d) <= LDS_BUDGET) return LdsPlan{ns_opts[i], xfull, 2};
   // many rows: narrower activation chunks first, then a shallower ring (down to 4 slabs, one
   // per consumer), so every row count up to the workspace maximum fits
   LdsPlan p{8, xfull, M <= 64 ? 2 : 1};
-  while (p.XC > sk && lds_bytes_for(M, esz, p.NS, p.XC, p.nred) > LDS_BUDGET) p.XC = (p.XC / 2 + sk - 1) / sk * sk;
-  while (p.NS > NCONS && lds_bytes_for(M, esz, p.NS, p.XC, p.nred) > LDS_BUDGET) p.NS -= 2;
+  while (p.XC > sk && lds_bytes_for(M, esz, p.NS, p.XC, p.nred, d) > LDS_BUDGET) p.XC = (p.XC / 2 + sk - 1) / sk * sk;
+  while (p.NS > NCONS && lds_bytes_for(M, esz, p.NS, p.XC, p.nred, d) > LDS_BUDGET) p.NS -= 2;
   return p;
 }
 __host__ __device__ inline int x_chunk_for(int M, int esz, int d) { return lds_plan(M, esz, d).XC; }
@@ -363,7 +375,7 @@ LS_DEV Lds lds_carve(char* base, int M, int d) {
   size_t off = 0;
   s.ring = base; off += (size_t)s.NS * SLAB;
   s.win = (int*)(base + off); off += ATT_WIN * 4;
-  s.X = base + off; off = align16(off + x_region_bytes(M, (int)sizeof(T), s.XC));
+  s.X = base + off; off = align16(off + x_region_bytes(M, (int)sizeof(T), s.XC, d));
   s.grow = (int*)(base + off);
   s.goff = s.grow + M + 64;
   s.rslot = s.goff + 65;
@@ -381,7 +393,7 @@ LS_DEV Lds lds_carve(char* base, int M, int d) {
 size_t mega_smem_bytes(bool bf16, int M, int d) {
   const int esz = bf16 ? 2 : 4;
   const LdsPlan p = lds_plan(M, esz, d);
-  return lds_bytes_for(M, esz, p.NS, p.XC, p.nred);
+  return lds_bytes_for(M, esz, p.NS, p.XC, p.nred, d);
 }
 
 // ---- phase geometry -------------------------------------------------------------------------------
@@ -594,14 +606,14 @@ struct Producer {
 
   // Row addresses of an attention tile: row 2i (lanes 0-31) is key i's K piece, row 2i + 1
   // (lanes 32-63) its V piece, `hoff` bytes into the cache entries of slots sl[0..7] of the
-  // cache block at `cache`.
+  // cache block at `cache`.  Unlike weight rows these are not swizzled: the attention
+  // consumers read a row's 8-byte units at consecutive addresses.
   LS_DEV void begin_kv_tile(const char* cache, const int (&sl)[8], int hoff) {
     const size_t ent = (size_t)2 * a.d * sizeof(T);
     const int vo = (lane >> 5) * a.d * (int)sizeof(T) + hoff;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int rho = 2 * i + (lane >> 5);
-      co[i] = ((lane & 31) ^ rho) * 16;
+      co[i] = (lane & 31) * 16;
       rp[i] = cache + (size_t)sl[i] * ent + vo + co[i];
     }
   }
@@ -1021,7 +1033,6 @@ LS_DEV void tile_signal(const MegaArgs& a, const CntLayout& cl, int ph, int l, i
 //  2. the last workgroup of a segment to finish merges, per (row, head), those partials with
 //     the row's own keys (its speculative ancestors and itself, written by this launch) and
 //     stores o[l][row][h].
-constexpr int NRA = 1;
 struct AttGeo {
   int HB, n_hb, n_kt, n_vg;
   int N;                    // tiles: (vg * n_hb + hb) * n_kt + kt
@@ -1327,56 +1338,183 @@ LS_DEV void att_merge2(const MegaArgs& a, const Lds& s, int l, int blk, int i, i
   }
 }
 
-// 16 bytes of LDS at byte address addr.
-LS_DEV u32x4_t lds_ld128(unsigned addr) {
-  return *(const __attribute__((address_space(3))) u32x4_t*)(size_t)addr;
+// 8 bytes of LDS at byte address addr.
+LS_DEV u32x2_t lds_ld64(unsigned addr) {
+  return *(const __attribute__((address_space(3))) u32x2_t*)(size_t)addr;
 }
 
-// 16 ring bytes as E floats.
-template <typename T> struct AttLane;
-template <> struct AttLane<uint16_t> {
-  static constexpr int E = 8;
-  LS_DEV static void unpack(const u32x4_t& w, float* f) {
+// Agent-coherent stores of 16 / 8 bytes through a buffer descriptor (the store side of ldc128).
+LS_DEV void stc128(__amdgpu_buffer_rsrc_t r, int byte_off, const u32x4_t& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, CPOL_SC1);
+}
+
+// A lane's share of a head's K or V piece in the attention phase: 8-byte units u = g, g + 8,
+// ... (g: the lane's place among the head's eight lanes), D elements each.  UMAX units cover a
+// 128-dim head; KG keys' K units are held in registers at once.
+template <typename T> struct AttUnit;
+template <> struct AttUnit<uint16_t> {
+  static constexpr int D = 4, UMAX = 4, KG = 4;
+  LS_DEV static void unpack(const u32x2_t& w, float* f) {
+    f[0] = __uint_as_float(w[0] << 16);
+    f[1] = __uint_as_float(w[0] & 0xffff0000u);
+    f[2] = __uint_as_float(w[1] << 16);
+    f[3] = __uint_as_float(w[1] & 0xffff0000u);
+  }
+  // D fp32 elements at byte offset off of r (zeros out of range)
+  LS_DEV static void load(__amdgpu_buffer_rsrc_t r, int off, float* f) {
+    const u32x4_t w = ldc128(r, off);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      f[2 * k] = __uint_as_float(w[k] << 16);
-      f[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-    }
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(w[e]);
+  }
+  LS_DEV static void store(__amdgpu_buffer_rsrc_t r, int off, const float* f) {
+    stc128(r, off, u32x4_t{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])});
   }
 };
-template <> struct AttLane<float> {
-  static constexpr int E = 4;
-  LS_DEV static void unpack(const u32x4_t& w, float* f) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(w[k]);
+template <> struct AttUnit<float> {
+  static constexpr int D = 2, UMAX = 8, KG = 2;
+  LS_DEV static void unpack(const u32x2_t& w, float* f) {
+    f[0] = __uint_as_float(w[0]);
+    f[1] = __uint_as_float(w[1]);
+  }
+  LS_DEV static void load(__amdgpu_buffer_rsrc_t r, int off, float* f) {
+    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CPOL_SC1);
+    f[0] = __uint_as_float(w[0]);
+    f[1] = __uint_as_float(w[1]);
+  }
+  LS_DEV static void store(__amdgpu_buffer_rsrc_t r, int off, const float* f) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(f[0]), __float_as_uint(f[1])}, r, off, 0, CPOL_SC1);
   }
 };
 
-// The consumer waves' part of the attention phase.  All four consumers read every tile of the
-// workgroup's share; consumer c owns heads c and c + 4 of the block, lane = (head jj of the two,
-// key kk, dims quarter sub): lane sub holds the 16-byte chunks sub, sub + 4, ... of the head's K
-// and V pieces.  Per row (up to NRA, the rows of the segment's virtual group) a lane keeps the
-// query chunks and a partial softmax state over the keys it has seen (its own key position kk
-// in every tile; running maximum shared by the head's lanes), so a tile costs the 16-byte LDS
-// reads of one K and one V pass, two DPP steps for the score, three for the tile maximum.  At
-// the end of its part of a segment the workgroup sums the state over the key lanes, leaves one
-// partial per (row, head), and the last workgroup of the segment merges.
+// One tile for one consumer: the eight keys' K units (LDS addresses ua[j] + 1024 i, V units
+// 512 further) against the lane's query elements, the scores summed over the head's eight lanes,
+// the online-softmax update of the state, and the weighted V units into the accumulators.  JN
+// units per lane (a compile-time count, so the loops carry no guards); kn valid keys.
+template <typename T, int JN>
+LS_DEV void att_tile(const unsigned (&ua)[AttUnit<T>::UMAX], float (&q)[NRA][AttUnit<T>::UMAX * AttUnit<T>::D],
+                     float (&acc)[NRA][AttUnit<T>::UMAX * AttUnit<T>::D], float (&mrun)[NRA], float (&lsum)[NRA],
+                     int kn) {
+  using U = AttUnit<T>;
+  constexpr int D = U::D, KG = U::KG;
+  float sc[NRA][8];
+#pragma unroll
+  for (int k0 = 0; k0 < 8; k0 += KG) {
+    u32x2_t kw[KG][JN];
+#pragma unroll
+    for (int i = 0; i < KG; ++i)
+#pragma unroll
+      for (int j = 0; j < JN; ++j) kw[i][j] = lds_ld64(ua[j] + 1024 * (k0 + i));
+#pragma unroll
+    for (int i = 0; i < KG; ++i) {
+#pragma unroll
+      for (int r = 0; r < NRA; ++r) sc[r][k0 + i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < JN; ++j) {
+        float f[D];
+        U::unpack(kw[i][j], f);
+#pragma unroll
+        for (int r = 0; r < NRA; ++r)
+#pragma unroll
+          for (int e = 0; e < D; ++e) sc[r][k0 + i] += q[r][j * D + e] * f[e];
+      }
+    }
+  }
+  float p[NRA][8];
+#pragma unroll
+  for (int r = 0; r < NRA; ++r) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float x = sc[r][i];
+      x += dpp_f<0xB1>(x);                          // the head's eight lanes: quads, then halves
+      x += dpp_f<0x4E>(x);
+      x += dpp_f<0x141>(x);
+      sc[r][i] = i < kn ? x : -INFINITY;
+      mx = fmaxf(mx, sc[r][i]);
+    }
+    // the state is rescaled only when the running maximum grows
+    const bool up = mx > mrun[r];
+    if (__any(up)) {
+      const float al = !up ? 1.f : (mrun[r] == -INFINITY ? 0.f : __expf(mrun[r] - mx));
+      lsum[r] *= al;
+#pragma unroll
+      for (int x2 = 0; x2 < JN * D; ++x2) acc[r][x2] *= al;
+      if (up) mrun[r] = mx;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[r][i] = sc[r][i] == -INFINITY ? 0.f : __expf(sc[r][i] - mrun[r]);
+      lsum[r] += p[r][i];
+    }
+  }
+#pragma unroll
+  for (int k0 = 0; k0 < 8; k0 += KG) {
+    u32x2_t vw[KG][JN];
+#pragma unroll
+    for (int i = 0; i < KG; ++i)
+#pragma unroll
+      for (int j = 0; j < JN; ++j) vw[i][j] = lds_ld64(ua[j] + 1024 * (k0 + i) + 512);
+#pragma unroll
+    for (int i = 0; i < KG; ++i) {
+#pragma unroll
+      for (int j = 0; j < JN; ++j) {
+        float f[D];
+        U::unpack(vw[i][j], f);
+#pragma unroll
+        for (int r = 0; r < NRA; ++r)
+#pragma unroll
+          for (int e = 0; e < D; ++e) acc[r][j * D + e] += p[r][k0 + i] * f[e];
+      }
+    }
+  }
+}
+// att_tile with JN = jn (1 <= jn <= JMAX)
+template <typename T, int JMAX>
+LS_DEV void att_tile_jn(int jn, const unsigned (&ua)[AttUnit<T>::UMAX],
+                        float (&q)[NRA][AttUnit<T>::UMAX * AttUnit<T>::D],
+                        float (&acc)[NRA][AttUnit<T>::UMAX * AttUnit<T>::D], float (&mrun)[NRA], float (&lsum)[NRA],
+                        int kn) {
+  if constexpr (JMAX > 1) {
+    if (jn < JMAX) {
+      att_tile_jn<T, JMAX - 1>(jn, ua, q, acc, mrun, lsum, kn);
+      return;
+    }
+  }
+  att_tile<T, JMAX>(ua, q, acc, mrun, lsum, kn);
+}
+
+// The consumer waves' part of the attention phase.  The workgroup's tiles are dealt to the four
+// consumers in turn (tile i of the share to consumer i mod 4), and a consumer reads its tiles'
+// slabs alone.  Lane = (head hi of the block, place g among the head's eight lanes): the lane
+// holds units g, g + 8, ... of the head's K and V pieces, so a key's score is a partial dot
+// product per lane that three DPP steps sum over the head's lanes; every lane of the head then
+// holds the tile's eight scores, its maximum and the weights.  Per row (up to NRA, the rows of
+// the segment's virtual group) a lane keeps its query elements and a softmax state over its
+// consumer's keys: running maximum and sum (equal on the head's lanes) and the accumulator of
+// its elements.  At the end of its part of a segment the workgroup combines the four consumers'
+// states in LDS, consumer 0 leaves one partial per (row, head), and the last workgroup of the
+// segment merges.
 template <typename T, int MT>
 LS_DEV void att_phase(const MegaArgs& a, const Lds& s, const CntLayout& cl, int l, Consumer<T, MT>& co,
                       ConsBar& cb) {
-  constexpr int E = AttLane<T>::E, NU = 32 / E, QN = NU * E;   // head pieces are at most 512 bytes
+  using U = AttUnit<T>;
+  constexpr int D = U::D, UMAX = U::UMAX, KG = U::KG, QN = UMAX * D;
   const AttGeo ag = att_geo<T>(a, s.vgt[a.M]);
   const int G = att_grid(ag.N), b = blockIdx.x;
   if (b >= G) return;
   const int T0 = (int)((long long)b * ag.N / G), T1 = (int)((long long)(b + 1) * ag.N / G);
   int* C = a.cnt + (size_t)l * cl.per_layer;
-  const int lane = threadIdx.x & 63, jj = lane >> 5, kk = (lane >> 2) & 7, sub = lane & 3;
-  const int c = co.c, jh = c + 4 * jj;
+  const int lane = threadIdx.x & 63, hi = lane >> 3, g = lane & 7;
+  const int c = co.c;
   const int hd = a.hd;
   constexpr int esz = (int)sizeof(T);
-  const int nch = hd * esz / 16;                    // 16-byte chunks of one head's K (or V) piece
+  const int nu = hd * esz / 8;                      // units of one head's piece
+  const int jn = (nu + 7) / 8;                      // units per lane (the last ones ragged)
   const float scale = 1.0f / sqrtf((float)hd);
   const __amdgpu_buffer_rsrc_t Rq = rsrc_of(a.q, a.M * a.d * 4);
+  // softmax states of consumers 1..3: [consumer][row][HB x hd accumulators, HB maxima, HB sums]
+  float* const cmb = (float*)s.X;
+  const int cst = ag.HB * (hd + 2);
   float q[NRA][QN], acc[NRA][QN], mrun[NRA], lsum[NRA];
   int rows[NRA];
   int nr = 0, hbn = 0, h0 = 0, blk = 0;
@@ -1387,62 +1525,104 @@ LS_DEV void att_phase(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
   // end of this workgroup's part of segment sg: one partial per (row, head), then the merge if
   // every other workgroup of the segment has left its partials
   auto flush = [&](int sg) {
-#pragma unroll
-    for (int r = 0; r < NRA; ++r) {
-      if (r < nr) {
-#pragma unroll
-        for (int o = 4; o <= 16; o <<= 1) {
-          lsum[r] += __shfl_xor(lsum[r], o, 64);
-#pragma unroll
-          for (int x = 0; x < QN; ++x) acc[r][x] += __shfl_xor(acc[r][x], o, 64);
-        }
-      }
-    }
     const int first = sg * ag.n_kt;
     const int o0 = att_owner(first, ag.N, G);
     const int np = att_owner(first + ag.n_kt - 1, ag.N, G) - o0 + 1;
-    if (kk == 0 && hv) {
+    if (c > 0 && hv) {
 #pragma unroll
       for (int r = 0; r < NRA; ++r) {
-        if (r >= nr) continue;
-        float* out = a.patt + (((size_t)rows[r] * a.nh + h0 + jh) * a.att_pmax + (b - o0)) * att_rec(hd);
-        if (sub == 0) { stc(out + hd, mrun[r]); stc(out + hd + 1, lsum[r]); }
+        if (r >= nr) break;
+        float* cs = cmb + (size_t)((c - 1) * NRA + r) * cst;
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const int ch = sub + 4 * u;
-          if (ch < nch) {
+        for (int j = 0; j < UMAX; ++j) {
+          const int u = g + 8 * j;
+          if (j < jn && u < nu) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) stc(out + ch * E + e, acc[r][u * E + e]);
+            for (int e = 0; e < D; ++e) cs[hi * hd + D * u + e] = acc[r][j * D + e];
           }
+        }
+        if (g == 0) {
+          cs[ag.HB * hd + hi] = mrun[r];
+          cs[ag.HB * hd + ag.HB + hi] = lsum[r];
         }
       }
     }
-    drain();
     cb.sync();
-    if (c == 0 && lane == 0) s.ints[2 * s.NS + 4] = atomicAdd(C + cl.o_fa + sg, 1);
+    if (c == 0) {
+      if (hv) {
+#pragma unroll
+        for (int r = 0; r < NRA; ++r) {
+          if (r >= nr) break;
+          float mo[NCONS - 1], so[NCONS - 1];
+          float mx = mrun[r];
+#pragma unroll
+          for (int k = 0; k < NCONS - 1; ++k) {
+            const float* cs = cmb + (size_t)(k * NRA + r) * cst;
+            mo[k] = cs[ag.HB * hd + hi];
+            so[k] = cs[ag.HB * hd + ag.HB + hi];
+            mx = fmaxf(mx, mo[k]);
+          }
+          float wk[NCONS - 1];
+          const float w0 = mrun[r] == -INFINITY ? 0.f : __expf(mrun[r] - mx);
+          float sum = w0 * lsum[r];
+#pragma unroll
+          for (int k = 0; k < NCONS - 1; ++k) {
+            wk[k] = mo[k] == -INFINITY ? 0.f : __expf(mo[k] - mx);
+            sum += wk[k] * so[k];
+          }
+          // partial record of (row, head h0 + hi) from this workgroup
+          float* const prow = a.patt + (size_t)rows[r] * a.nh * a.att_pmax * att_rec(hd);
+          const __amdgpu_buffer_rsrc_t Rp = rsrc_of(prow, a.nh * a.att_pmax * att_rec(hd) * 4);
+          const int rec0 = ((h0 + hi) * a.att_pmax + (b - o0)) * att_rec(hd);
+#pragma unroll
+          for (int j = 0; j < UMAX; ++j) {
+            const int u = g + 8 * j;
+            if (j < jn && u < nu) {
+              float y[D];
+#pragma unroll
+              for (int e = 0; e < D; ++e) {
+                y[e] = w0 * acc[r][j * D + e];
+#pragma unroll
+                for (int k = 0; k < NCONS - 1; ++k)
+                  y[e] += wk[k] * cmb[(size_t)(k * NRA + r) * cst + hi * hd + D * u + e];
+              }
+              U::store(Rp, (rec0 + D * u) * 4, y);
+            }
+          }
+          if (g == 0) {
+            stc(prow + rec0 + hd, mx);
+            stc(prow + rec0 + hd + 1, sum);
+          }
+        }
+      }
+      drain();
+      if (lane == 0) s.ints[2 * s.NS + 4] = atomicAdd(C + cl.o_fa + sg, 1);
+    }
     cb.sync();
     if (s.ints[2 * s.NS + 4] == np - 1) {
-      // this consumer merges its own heads (it has waited for their QKV tiles)
+      // consumer c merges heads c and c + 4 (it has waited for their QKV tiles)
       for (int r = 0; r < nr; ++r)
         if (c < hbn) att_merge2<T>(a, s, l, blk, rows[r], h0 + c, c + 4 < hbn ? h0 + c + 4 : -1, np);
     }
   };
 
+  const unsigned ring0 = (unsigned)(size_t)(__attribute__((address_space(3))) char*)s.ring;
   for (int t = T0; t < T1; ++t) {
     if (seg != cur_seg) {
       if (cur_seg >= 0) flush(cur_seg);
       cur_seg = seg;
       const int vg = seg / ag.n_hb, hb = seg - vg * ag.n_hb;
-      const int vt = s.vgt[vg], g = vt & 63, r0 = vt >> 6;
-      const int g0 = s.goff[g];
-      nr = min(NRA, s.goff[g + 1] - g0 - r0);
+      const int vt = s.vgt[vg], gr = vt & 63, r0 = vt >> 6;
+      const int g0 = s.goff[gr];
+      nr = min(NRA, s.goff[gr + 1] - g0 - r0);
 #pragma unroll
       for (int r = 0; r < NRA; ++r) rows[r] = s.grow[g0 + r0 + min(r, nr - 1)];
       blk = (a.dep ? s.rdep[s.grow[g0]] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
       h0 = hb * ag.HB;
       hbn = min(ag.HB, a.nh - h0);
-      hv = jh < hbn;
-      // queries of the consumer's heads are complete once their q/k/v tiles have signalled
+      hv = hi < hbn;
+      // queries of the block's heads are complete once their q/k/v tiles have signalled:
+      // consumer c waits for heads c and c + 4 (whose merge it may run), then all four meet
       {
         const int nf = 3 * (hd / 16);
         bool done = true;
@@ -1457,19 +1637,16 @@ LS_DEV void att_phase(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
           if (give_up(n, a.err)) break;
         }
       }
+      cb.sync();
 #pragma unroll
       for (int r = 0; r < NRA; ++r) {
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const int ch = sub + 4 * u;
-          const bool ok = hv && r < nr && ch < nch;
-          const int off = ok ? (rows[r] * a.d + (h0 + jh) * hd + ch * E) * 4 : 0x7fffff00;
+        for (int j = 0; j < UMAX; ++j) {
+          const int u = g + 8 * j;
+          const bool ok = hv && r < nr && j < jn && u < nu;
+          U::load(Rq, ok ? (rows[r] * a.d + (h0 + hi) * hd + D * u) * 4 : 0x7fffff00, q[r] + j * D);
 #pragma unroll
-          for (int v = 0; v < E / 4; ++v) {
-            const u32x4_t w = ldc128(Rq, off + 16 * v);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) q[r][u * E + 4 * v + e] = __uint_as_float(w[e]) * scale;
-          }
+          for (int e = 0; e < D; ++e) q[r][j * D + e] *= scale;
         }
         mrun[r] = -INFINITY;
         lsum[r] = 0.f;
@@ -1477,102 +1654,39 @@ LS_DEV void att_phase(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
         for (int x = 0; x < QN; ++x) acc[r][x] = 0.f;
       }
     }
-    // ---- one tile: keys [8kt, 8kt + 8), this lane's key kk
-    const bool kok = hv && kk < a.n_fin - 8 * kt;
     const int ns = (hbn * hd * esz + 511) / 512;
-    {
-      // lane k < ns watches the tile's slab k
-      const int k = lane < ns ? lane : 0;
-      int sl = co.cslot + k, us = co.cuse;
-      if (sl >= s.NS) { sl -= s.NS; ++us; }
-      int n = 0;
-      while (!__all(lds_read_lane(s.ints + sl) >= us + 1)) {
-        __builtin_amdgcn_s_sleep(0);
-        if (give_up(n, a.err)) break;
+    if (((t - T0) & (NCONS - 1)) == c) {
+      // ---- one tile of this consumer: keys [8kt, 8kt + 8)
+      {
+        // lane k < ns watches the tile's slab k
+        const int k = lane < ns ? lane : 0;
+        int sl = co.cslot + k, us = co.cuse;
+        if (sl >= s.NS) { sl -= s.NS; ++us; }
+        int n = 0;
+        while (!__all(lds_read_lane(s.ints + sl) >= us + 1))   // tight poll: the slabs are usually close
+          if (give_up(n, a.err)) break;
       }
-    }
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("" : : : "memory");
-    // LDS byte addresses of this lane's K and V chunks.  Chunks past the head read its chunk 0
-    // (finite data): their query entries are zero and their accumulators are never stored.
-    const unsigned ring0 = (unsigned)(size_t)(__attribute__((address_space(3))) char*)s.ring;
-    unsigned kp[NU], vp[NU];
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" : : : "memory");
+      // LDS address of each unit in key 0's K row; key i's K row is 1024 i further, its V row
+      // 512 beyond that.  Units past the head (and lanes past the block) read the head's (the
+      // block's) first unit, finite data whose query elements are zero.
+      unsigned ua[UMAX];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int ch = sub + 4 * u;
-      const int off = hv && ch < nch ? jh * hd * esz + ch * 16 : 0;
-      int sl = co.cslot + (off >> 9);
-      if (sl >= s.NS) sl -= s.NS;
-      const int pos = (off >> 4) & 31;
-      const unsigned row0 = ring0 + (unsigned)(sl * SLAB + (2 * kk) * 512);
-      kp[u] = row0 + ((pos ^ (2 * kk)) << 4);
-      vp[u] = row0 + 512 + ((pos ^ (2 * kk + 1)) << 4);
-    }
-    // K chunks (and for bf16 the V chunks too) are all requested before the first is used
-    u32x4_t kw[NU], vw[NU];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      if (4 * u >= nch) break;
-      kw[u] = lds_ld128(kp[u]);
-      if constexpr (E == 8) vw[u] = lds_ld128(vp[u]);
-    }
-    float part[NRA];
-#pragma unroll
-    for (int r = 0; r < NRA; ++r) part[r] = 0.f;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      if (4 * u >= nch) break;
-      float kf[E];
-      AttLane<T>::unpack(kw[u], kf);
-#pragma unroll
-      for (int r = 0; r < NRA; ++r) {
-        if (r >= nr) break;
-#pragma unroll
-        for (int e = 0; e < E; ++e) part[r] += q[r][u * E + e] * kf[e];
+      for (int j = 0; j < UMAX; ++j) {
+        const int u = g + 8 * j;
+        const int off = hv ? hi * hd * esz + (u < nu ? 8 * u : 0) : 0;
+        int sl = co.cslot + (off >> 9);
+        if (sl >= s.NS) sl -= s.NS;
+        ua[j] = ring0 + (unsigned)(sl * SLAB + (off & 511));
       }
-    }
-    float p[NRA];
-#pragma unroll
-    for (int r = 0; r < NRA; ++r) {
-      p[r] = 0.f;
-      if (r >= nr) break;
-      float x = part[r];
-      x += dpp_f<0xB1>(x);                     // the four dims quarters of the key's score
-      x += dpp_f<0x4E>(x);
-      const float sc = kok ? x : -INFINITY;
-      float mx = fmaxf(sc, dpp_f<0x141>(sc));  // half-row mirror: key kk ^ 1 (quarters hold equal values)
-      mx = fmaxf(mx, dpp_f<0x140>(mx));        // row mirror: key kk ^ 3
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));  // keys kk ^ 4
-      // the state is rescaled only when the running maximum grows (rarely, after the first keys)
-      const bool up = mx > mrun[r];
-      if (__any(up)) {
-        const float al = !up ? 1.f : (mrun[r] == -INFINITY ? 0.f : __expf(mrun[r] - mx));
-        lsum[r] *= al;
-#pragma unroll
-        for (int x2 = 0; x2 < QN; ++x2) acc[r][x2] *= al;
-        if (up) mrun[r] = mx;
+      att_tile_jn<T, UMAX>(jn, ua, q, acc, mrun, lsum, a.n_fin - 8 * kt);
+      // the tile's slots are free again (a whole release per slab: no other consumer reads them)
+      if (lane < ns) {
+        int sl = co.cslot + lane;
+        if (sl >= s.NS) sl -= s.NS;
+        lds_add(s.ints + s.NS + sl, NCONS);
       }
-      p[r] = sc == -INFINITY ? 0.f : __expf(sc - mrun[r]);
-      lsum[r] += p[r];
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      if (4 * u >= nch) break;
-      float vf[E];
-      if constexpr (E == 8) AttLane<T>::unpack(vw[u], vf);
-      else AttLane<T>::unpack(lds_ld128(vp[u]), vf);
-#pragma unroll
-      for (int r = 0; r < NRA; ++r) {
-        if (r >= nr) break;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[r][u * E + e] += p[r] * vf[e];
-      }
-    }
-    // this consumer is done with the tile's slabs (a slot is free once all four have released it)
-    if (lane < ns) {
-      int sl = co.cslot + lane;
-      if (sl >= s.NS) sl -= s.NS;
-      lds_add(s.ints + s.NS + sl, 1);
     }
     co.cslot += ns;
     while (co.cslot >= s.NS) { co.cslot -= s.NS; ++co.cuse; }
