@@ -85,7 +85,8 @@ LS_DEV u32x4_t ld128(__amdgpu_buffer_rsrc_t r, int byte_off) {
 // The attention outputs o[l] are polled the same way by the O phase (all-ones words: 0xFFFF
 // halves in bf16, also a NaN pattern no merge stores), so the merge signals nothing.
 constexpr unsigned SENT32 = 0xFFFFFFFFu;
-// Rows up to this many columns are staged, normalised and (for Xs / Ys) polled in one pass.
+// Rows up to this many columns are staged, normalised and (for Xs / Ys) polled in one pass of
+// one wave; rows up to NCONS times as wide in one pass of the consumer waves together.
 constexpr int FUSE_MAX_K = 2048;
 
 // Per-layer activation buffers of one launch (rows m < M):
@@ -306,12 +307,19 @@ __host__ __device__ inline int row_table_ints(int M) { return M + 64 + 65 + M + 
 // Key-slot windows of the producer waves (ATT_WPW slots each).
 constexpr int ATT_WPW = 256;
 constexpr int ATT_WIN = 2 * ATT_WPW;
+// Row-normalisation scratch: the factor of each row, or (staging of rows split over the
+// consumer waves) two buffers of up to SRG rows' NCONS quarter sums of squares.
+constexpr int SRG = 2;
+__host__ __device__ inline int norm_floats(int M) {
+  const int g = M < SRG ? M : SRG;
+  return 2 * g * NCONS > M ? 2 * g * NCONS : M;
+}
 __host__ __device__ inline size_t lds_bytes_for(int M, int esz, int NS, int XC, int nred, int d) {
   size_t off = (size_t)NS * SLAB + ATT_WIN * 4;
   off = (off + x_region_bytes(M, esz, XC, d) + 15) & ~(size_t)15;
   off = (off + (size_t)row_table_ints(M) * 4 + 15) & ~(size_t)15;
   off = (off + (size_t)nred * NCONS * M * 16 * 4 + 15) & ~(size_t)15;
-  off = (off + (size_t)M * 4 + 15) & ~(size_t)15;
+  off = (off + (size_t)norm_floats(M) * 4 + 15) & ~(size_t)15;
   off = (off + (size_t)M * 4 + 15) & ~(size_t)15;
   off += (2 * NS + 8) * 4;
   return off;
@@ -349,7 +357,7 @@ struct Lds {
   int* win;          // key-slot windows of the producer waves, ATT_WPW each
   char* X;           // M x (XC + pad) elements
   float* red;        // nred x NCONS x M x 16: per-tile partials of the consumer waves
-  float* rinv;       // M
+  float* rinv;       // norm_floats(M): row factors, or the split staging's quarter sums
   int* hx;           // M: hidden-state row of each working row (-1: none)
   int* grow;         // M: rows ordered by KV depth group (attention shares a group's keys)
   int* goff;         // group g's rows: grow[goff[g] .. goff[g+1]); goff[64] = group count
@@ -384,7 +392,7 @@ LS_DEV Lds lds_carve(char* base, int M, int d) {
   s.vgt = s.raoff + M + 1;
   off = align16(off + (size_t)row_table_ints(M) * 4);
   s.red = (float*)(base + off); off = align16(off + (size_t)s.nred * NCONS * M * 16 * 4);
-  s.rinv = (float*)(base + off); off = align16(off + (size_t)M * 4);
+  s.rinv = (float*)(base + off); off = align16(off + (size_t)norm_floats(M) * 4);
   s.hx = (int*)(base + off); off = align16(off + (size_t)M * 4);
   s.ints = (int*)(base + off);
   return s;
@@ -733,6 +741,12 @@ struct Consumer {
   static_assert(64 * 4 * NVF == FUSE_MAX_K, "fused staging covers FUSE_MAX_K columns");
   LS_DEV void stage_norm(const float* src, bool via_hidx, const float* gain, int x0, int xn, bool fuse,
                          bool poll) {
+    if (fuse && xn > FUSE_MAX_K) {
+      // a quarter of qw <= FUSE_MAX_K columns is ceil(qw / 256) float4 per lane
+      const int qw = (xn + 4 * NCONS - 1) / (4 * NCONS) * 4;
+      stage_split_nv<8>((qw + 255) / 256, src, via_hidx, gain, xn, poll);
+      return;
+    }
     T* X = (T*)s.X;
     const __amdgpu_buffer_rsrc_t Rg = rsrc_of(gain + x0, xn * 4);
     for (int m = c; m < a.M; m += NCONS) {
@@ -799,6 +813,98 @@ struct Consumer {
       }
     }
     cb.sync();
+  }
+
+  // Whole rows wider than one wave's fused pass (FUSE_MAX_K < xn <= NCONS * FUSE_MAX_K): consumer
+  // wave c takes quarter c of every row, NV float4 per lane.  Rows go SRG at a time: the waves
+  // load (or poll) their quarters of the group's rows and the gains at once, leave each
+  // quarter's sum of squares in LDS, meet, and normalise from registers; the row's factor adds
+  // the four quarter sums in wave order.
+  template <int NV>
+  LS_DEV void stage_norm_split(const float* src, bool via_hidx, const float* gain, int xn, bool poll) {
+    T* X = (T*)s.X;
+    const int qw = (xn + 4 * NCONS - 1) / (4 * NCONS) * 4;     // columns per quarter
+    const int q0 = min(c * qw, xn), qn = min(qw, xn - q0);
+    const __amdgpu_buffer_rsrc_t Rg = rsrc_of(gain + q0, qn * 4);
+    u32x4_t gv[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) gv[u] = ld128(Rg, (4 * (lane + 64 * u)) * 4);
+    const int gmax = min(SRG, a.M);
+    int grp = 0;
+    for (int m0 = 0; m0 < a.M; m0 += SRG, ++grp) {
+      const int gn = min(SRG, a.M - m0);
+      __amdgpu_buffer_rsrc_t R[SRG];
+#pragma unroll
+      for (int r = 0; r < SRG; ++r) {
+        const int m = m0 + min(r, gn - 1);
+        const int hv = __builtin_amdgcn_readfirstlane(s.hx[m]);   // negative: rejected row, stages zeros
+        const int hr = via_hidx ? hv : m;
+        R[r] = rsrc_of(src + (size_t)(hv >= 0 ? hr : 0) * a.d + q0, r < gn && hv >= 0 ? qn * 4 : 0);
+      }
+      u32x4_t v[SRG][NV];
+      if (poll) {
+        // a quarter is complete once none of its elements holds the fill pattern
+        int n = 0;
+        while (true) {
+#pragma unroll
+          for (int r = 0; r < SRG; ++r)
+#pragma unroll
+            for (int u = 0; u < NV; ++u) v[r][u] = ldc128(R[r], (4 * (lane + 64 * u)) * 4);
+          bool ok = true;
+#pragma unroll
+          for (int r = 0; r < SRG; ++r)
+#pragma unroll
+            for (int u = 0; u < NV; ++u)
+              ok = ok && v[r][u].x != SENT32 && v[r][u].y != SENT32 && v[r][u].z != SENT32 && v[r][u].w != SENT32;
+          if (__all(ok)) break;
+          __builtin_amdgcn_s_sleep(POLL_SLEEP);
+          if (give_up(n, a.err)) break;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < SRG; ++r)
+#pragma unroll
+          for (int u = 0; u < NV; ++u) v[r][u] = ld128(R[r], (4 * (lane + 64 * u)) * 4);
+      }
+      float* sp = s.rinv + (grp & 1) * gmax * NCONS;   // alternate buffers: one meeting per group
+#pragma unroll
+      for (int r = 0; r < SRG; ++r) {
+        float ss = 0.f;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const float f0 = __uint_as_float(v[r][u].x), f1 = __uint_as_float(v[r][u].y);
+          const float f2 = __uint_as_float(v[r][u].z), f3 = __uint_as_float(v[r][u].w);
+          ss += (f0 * f0 + f1 * f1) + (f2 * f2 + f3 * f3);
+        }
+        ss = wave_sum(ss);
+        if (lane == 0 && r < gn) sp[r * NCONS + c] = ss;
+      }
+      cb.sync();
+#pragma unroll
+      for (int r = 0; r < SRG; ++r) {
+        if (r >= gn) break;
+        const float tot = (sp[r * NCONS] + sp[r * NCONS + 1]) + (sp[r * NCONS + 2] + sp[r * NCONS + 3]);
+        const float ri = 1.0f / sqrtf(tot / (float)a.d + a.eps);
+        T* xr = X + (size_t)(m0 + r) * s.xstride + q0;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int k = 4 * (lane + 64 * u);
+          if (k < qn) put4(xr + k, v[r][u], ri, gv[u]);
+        }
+      }
+    }
+    cb.sync();
+  }
+  // stage_norm_split with NV = nv (3 <= nv <= NVMAX: quarters wider than FUSE_MAX_K / NCONS)
+  template <int NVMAX>
+  LS_DEV void stage_split_nv(int nv, const float* src, bool via_hidx, const float* gain, int xn, bool poll) {
+    if constexpr (NVMAX > 3) {
+      if (nv < NVMAX) {
+        stage_split_nv<NVMAX - 1>(nv, src, via_hidx, gain, xn, poll);
+        return;
+      }
+    }
+    stage_norm_split<NVMAX>(src, via_hidx, gain, xn, poll);
   }
 
   LS_DEV static void put4(T* dst, const u32x4_t& v, float ri, const u32x4_t& g) {
@@ -1272,18 +1378,19 @@ LS_DEV void att_merge2(const MegaArgs& a, const Lds& s, int l, int blk, int i, i
   }
   float run_m = -INFINITY, den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
   constexpr int NK = 4;                             // own keys per batch
-  const int nbat = max((np + 15) / 16, (nt + NK - 1) / NK);
+  constexpr int NPB = 16;                           // prefix partials per batch (at most 32)
+  const int nbat = max((np + NPB - 1) / NPB, (nt + NK - 1) / NK);
   for (int bt = 0; bt < nbat; ++bt) {
-    const int c0 = bt * 16, j0 = bt * NK;
+    const int c0 = bt * NPB, j0 = bt * NK;
     // ---- issue the batch's loads
-    float mxc = -INFINITY, smc = 0.f;                // statistics of partial c0 + hl (hl < 16)
-    if (hok && hl < 16 && c0 + hl < np) {
+    float mxc = -INFINITY, smc = 0.f;                // statistics of partial c0 + hl (hl < NPB)
+    if (hok && hl < NPB && c0 + hl < np) {
       mxc = ldc(a.patt + (size_t)i * a.nh * a.att_pmax * rec + pbase + (size_t)(c0 + hl) * rec + hd);
       smc = ldc(a.patt + (size_t)i * a.nh * a.att_pmax * rec + pbase + (size_t)(c0 + hl) * rec + hd + 1);
     }
-    u32x4_t ac[16];
+    u32x4_t ac[NPB];
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
+    for (int u = 0; u < NPB; ++u)
       ac[u] = ldc128(Rp, hok && c0 + u < np ? (pbase + (c0 + u) * rec + d0) * 4 : 0x7fffff00);
     float kf[NK][4], vf[NK][4];
     bool bad = false;
@@ -1316,7 +1423,7 @@ LS_DEV void att_merge2(const MegaArgs& a, const Lds& s, int l, int blk, int i, i
     const float wl = mxc == -INFINITY ? 0.f : __expf(mxc - nm);
     den += half_sum(wl * smc);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < NPB; ++u) {
       const float w = half ? lane_f(wl, 32 + u) : lane_f(wl, u);
 #pragma unroll
       for (int e = 0; e < 4; ++e) num[e] += w * __uint_as_float(ac[u][e]);
@@ -1386,16 +1493,47 @@ template <> struct AttUnit<float> {
   }
 };
 
+// Release of a tile's ns ring slots from slot first on (a whole release per slab: the tile's
+// consumer is its only reader).
+struct SlotRelease {
+  int* empty;
+  int first, ns, NS;
+  LS_DEV void operator()() const {
+    const int lane = threadIdx.x & 63;
+    if (lane < ns) {
+      int sl = first + lane;
+      if (sl >= NS) sl -= NS;
+      lds_add(empty + sl, NCONS);
+    }
+  }
+};
+
 // One tile for one consumer: the eight keys' K units (LDS addresses ua[j] + 1024 i, V units
 // 512 further) against the lane's query elements, the scores summed over the head's eight lanes,
 // the online-softmax update of the state, and the weighted V units into the accumulators.  JN
-// units per lane (a compile-time count, so the loops carry no guards); kn valid keys.
-template <typename T, int JN>
+// units per lane (a compile-time count, so the loops carry no guards); kn valid keys.  With
+// bf16 pieces all of the tile's units are read into registers first and the slots released
+// (`release`) before any arithmetic, so that a consumer holds ring slots only for the reads;
+// fp32 pieces (twice the registers) are read KG keys at a time and released at the end.
+template <typename T, int JN, typename Rel>
 LS_DEV void att_tile(const unsigned (&ua)[AttUnit<T>::UMAX], float (&q)[NRA][AttUnit<T>::UMAX * AttUnit<T>::D],
                      float (&acc)[NRA][AttUnit<T>::UMAX * AttUnit<T>::D], float (&mrun)[NRA], float (&lsum)[NRA],
-                     int kn) {
+                     int kn, const Rel& release) {
   using U = AttUnit<T>;
-  constexpr int D = U::D, KG = U::KG;
+  constexpr int D = U::D;
+  constexpr bool EARLY = sizeof(T) == 2 && JN <= 3;
+  constexpr int KG = EARLY ? 8 : U::KG;
+  u32x2_t ke[EARLY ? 8 : 1][JN], vw[EARLY ? 8 : 1][JN];
+  if constexpr (EARLY) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < JN; ++j) {
+        ke[i][j] = lds_ld64(ua[j] + 1024 * i);
+        vw[i][j] = lds_ld64(ua[j] + 1024 * i + 512);
+      }
+    release();
+  }
   float sc[NRA][8];
 #pragma unroll
   for (int k0 = 0; k0 < 8; k0 += KG) {
@@ -1403,7 +1541,10 @@ LS_DEV void att_tile(const unsigned (&ua)[AttUnit<T>::UMAX], float (&q)[NRA][Att
 #pragma unroll
     for (int i = 0; i < KG; ++i)
 #pragma unroll
-      for (int j = 0; j < JN; ++j) kw[i][j] = lds_ld64(ua[j] + 1024 * (k0 + i));
+      for (int j = 0; j < JN; ++j) {
+        if constexpr (EARLY) kw[i][j] = ke[k0 + i][j];
+        else kw[i][j] = lds_ld64(ua[j] + 1024 * (k0 + i));
+      }
 #pragma unroll
     for (int i = 0; i < KG; ++i) {
 #pragma unroll
@@ -1449,17 +1590,20 @@ LS_DEV void att_tile(const unsigned (&ua)[AttUnit<T>::UMAX], float (&q)[NRA][Att
   }
 #pragma unroll
   for (int k0 = 0; k0 < 8; k0 += KG) {
-    u32x2_t vw[KG][JN];
+    u32x2_t vg[KG][JN];
 #pragma unroll
     for (int i = 0; i < KG; ++i)
 #pragma unroll
-      for (int j = 0; j < JN; ++j) vw[i][j] = lds_ld64(ua[j] + 1024 * (k0 + i) + 512);
+      for (int j = 0; j < JN; ++j) {
+        if constexpr (EARLY) vg[i][j] = vw[k0 + i][j];
+        else vg[i][j] = lds_ld64(ua[j] + 1024 * (k0 + i) + 512);
+      }
 #pragma unroll
     for (int i = 0; i < KG; ++i) {
 #pragma unroll
       for (int j = 0; j < JN; ++j) {
         float f[D];
-        U::unpack(vw[i][j], f);
+        U::unpack(vg[i][j], f);
 #pragma unroll
         for (int r = 0; r < NRA; ++r)
 #pragma unroll
@@ -1467,20 +1611,21 @@ LS_DEV void att_tile(const unsigned (&ua)[AttUnit<T>::UMAX], float (&q)[NRA][Att
       }
     }
   }
+  if constexpr (!EARLY) release();
 }
 // att_tile with JN = jn (1 <= jn <= JMAX)
-template <typename T, int JMAX>
+template <typename T, int JMAX, typename Rel>
 LS_DEV void att_tile_jn(int jn, const unsigned (&ua)[AttUnit<T>::UMAX],
                         float (&q)[NRA][AttUnit<T>::UMAX * AttUnit<T>::D],
                         float (&acc)[NRA][AttUnit<T>::UMAX * AttUnit<T>::D], float (&mrun)[NRA], float (&lsum)[NRA],
-                        int kn) {
+                        int kn, const Rel& release) {
   if constexpr (JMAX > 1) {
     if (jn < JMAX) {
-      att_tile_jn<T, JMAX - 1>(jn, ua, q, acc, mrun, lsum, kn);
+      att_tile_jn<T, JMAX - 1>(jn, ua, q, acc, mrun, lsum, kn, release);
       return;
     }
   }
-  att_tile<T, JMAX>(ua, q, acc, mrun, lsum, kn);
+  att_tile<T, JMAX>(ua, q, acc, mrun, lsum, kn, release);
 }
 
 // The consumer waves' part of the attention phase.  The workgroup's tiles are dealt to the four
@@ -1680,13 +1825,7 @@ LS_DEV void att_phase(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
         if (sl >= s.NS) sl -= s.NS;
         ua[j] = ring0 + (unsigned)(sl * SLAB + (off & 511));
       }
-      att_tile_jn<T, UMAX>(jn, ua, q, acc, mrun, lsum, a.n_fin - 8 * kt);
-      // the tile's slots are free again (a whole release per slab: no other consumer reads them)
-      if (lane < ns) {
-        int sl = co.cslot + lane;
-        if (sl >= s.NS) sl -= s.NS;
-        lds_add(s.ints + s.NS + sl, NCONS);
-      }
+      att_tile_jn<T, UMAX>(jn, ua, q, acc, mrun, lsum, a.n_fin - 8 * kt, SlotRelease{s.ints + s.NS, co.cslot, ns, s.NS});
     }
     co.cslot += ns;
     while (co.cslot >= s.NS) { co.cslot -= s.NS; ++co.cuse; }
@@ -1741,7 +1880,7 @@ LS_DEV void walk_gemm(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
 
   // normalised phases (QKV, GU, HEAD) read a whole row when one activation chunk covers it and
   // then take the RMSNorm factor from the same loads; otherwise from the per-tile sums of squares
-  const bool fuse = nchunk == 1 && g.K <= FUSE_MAX_K;
+  const bool fuse = nchunk == 1 && g.K <= NCONS * FUSE_MAX_K;
   const int lin = ph == PH_HEAD ? a.n_layers : l;              // layer whose input a normalised phase reads
   const float* nsrc = ph == PH_GU ? ys_of(a, l) : layer_in(a, lin);
   const bool nvia = ph != PH_GU && lin == 0;                   // rows addressed through hidx
@@ -1874,7 +2013,7 @@ LS_DEV void epi_walk(const MegaArgs& a, const Lds& s, const CntLayout& cl, int p
   const bool pref = (ph == PH_O || ph == PH_DOWN) && had_tiles && nun > 0 && k00 == 0 && k10 == un.nk && a.M <= 16;
   // O / DOWN counts are waited for only when the next normalised phase cannot poll its input
   // (its row does not fit one fused staging pass); otherwise their drain and bump are skipped.
-  const bool next_polls = a.d <= s.XC && a.d <= FUSE_MAX_K;
+  const bool next_polls = a.d <= s.XC && a.d <= NCONS * FUSE_MAX_K;
   const bool signals = ph != PH_HEAD && !((ph == PH_O || ph == PH_DOWN) && next_polls);
   float pre[4] = {0.f, 0.f, 0.f, 0.f};
   if (pref) residual_load(a, s, ph, l, t0, 0, lane, pre);
