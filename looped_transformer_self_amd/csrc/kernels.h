@@ -40,6 +40,7 @@ struct MegaArgs {
   const int32_t *slot, *pos, *dep, *fin, *anc_off, *anc, *tokens;
   int n_fin;
   int att_pmax;                 // attention partials per (row, head) that patt holds (att_pmax_for)
+  int att_npf;                  // partial records per (row, head) this launch fills and its mergers poll
   void* kv;                     // cache tensor; block(i, l) = (dep[i] + dep_off) * blk_mul + layer0 + l
   int dep_off, blk_mul, layer0;
   long long S;

@@ -111,7 +111,7 @@ Carve carve(const ls_model* m, int max_rows, int max_keys, int max_jobs) {
   c.off_invf = take((size_t)d.head_dim / 2 * 8);
   c.off_rope = take(R * (size_t)d.head_dim * 4);
   c.att_pmax = att_pmax_for(max_keys, d.n_heads, d.head_dim, (int)es);
-  c.off_patt = take(R * d.n_heads * (size_t)c.att_pmax * (d.head_dim + 4) * 4);
+  c.off_patt = take(nl * R * d.n_heads * (size_t)c.att_pmax * (d.head_dim + 4) * 4);   // per layer: the records are polled
   c.off_ssq = take(nl * 2 * (d.d / 16) * R * 4);
   c.off_spart = take((size_t)MEGA_MAX_GRID * 2 * R * 16 * 4);
   c.off_cnt = take(mega_counter_ints(max_rows, d.d, d.F, d.n_heads, (int)nl) * 4);
@@ -340,6 +340,17 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
     if (G > MEGA_MAX_GRID || need > m->w.att_pmax)
       return fail(LS_ERR_UNSUPPORTED, "persistent kernel: %d workgroups need %d attention partials, workspace holds %d",
                   G, need, m->w.att_pmax);
+    // partials of the launch's segments (one row per virtual group): the workgroups that hold
+    // tiles of a segment, by the same contiguous deal as the kernel's
+    const long long N = (long long)mc * n_hb * n_kt, Ga = std::min<long long>(G, N);
+    auto owner = [&](long long t) { return ((t + 1) * Ga - 1) / N; };
+    int npf = 1;
+    for (long long sg = 0; sg < (long long)mc * n_hb; ++sg)
+      npf = std::max(npf, (int)(owner(sg * n_kt + n_kt - 1) - owner(sg * n_kt) + 1));
+    if (npf > m->w.att_pmax)
+      return fail(LS_ERR_UNSUPPORTED, "persistent kernel: %d attention partials per head, workspace holds %d", npf,
+                  m->w.att_pmax);
+    a.att_npf = npf;
   }
   a.att_pmax = m->w.att_pmax;
   a.wait_ticks = (long long)(m->wait_seconds * 1e3 * (double)m->clock_khz);

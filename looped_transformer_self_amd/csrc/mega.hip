@@ -257,7 +257,7 @@ LS_DEV void wait_spread(const int* base, int lo, int hi, ConsBar& cb) {
 // ---- counter layout -----------------------------------------------------------------------------
 struct CntLayout {
   int per_layer, nchF;
-  int o_qkvh, o_o, o_gu, o_down, o_fa, o_split;
+  int o_qkvh, o_o, o_gu, o_down, o_split;
   int o_init, total;
 };
 
@@ -271,7 +271,6 @@ __host__ __device__ inline CntLayout cnt_layout(int M, int d, int F, int nh, int
   c.o_o = o; o += NSPREAD * PADC;
   c.o_gu = o; o += c.nchF * NSPREAD * PADC;
   c.o_down = o; o += NSPREAD * PADC;
-  c.o_fa = o; o += M * nh;
   c.o_split = o; o += 2 * (d / 16);        // arrivals at the split O and DOWN tiles
   o = (o + PADC - 1) / PADC * PADC;
   c.per_layer = o;
@@ -1315,8 +1314,12 @@ LS_DEV void walk_att_prod(const MegaArgs& a, const Lds& s, int l, Producer<T>& p
   if (threadIdx.x == 64 * NCONS) tstamp(a, l, PH_ATT, 6);
 }
 
-// Partial records of the attention phase: acc[hd], then max and sum (16-byte aligned rows).
+// Partial records of the attention phase: acc[hd], then max and sum (16-byte aligned rows);
+// layer l's records [row][head][partial] of a launch.  Each layer has records of its own: they
+// carry no completion signal, so a reader tells this layer's records from an earlier layer's
+// only by the fill pattern they start the launch with.
 LS_DEV int att_rec(int hd) { return hd + 4; }
+LS_DEV float* patt_of(const MegaArgs& a, int l) { return a.patt + (size_t)l * a.M * a.nh * a.att_pmax * att_rec(a.hd); }
 
 // Four elements of a K / V entry written by this launch (agent-coherent load).
 template <typename T> LS_DEV void load4_coh(const T* p, float* f);
@@ -1348,7 +1351,9 @@ LS_DEV float half_max(float v) {
 // lane = 4 dims of its half's head: the np prefix partials of the row's segment and the row's
 // own keys (its speculative ancestors, then itself, written by this launch), online
 // log-sum-exp over batches of (16 partials, 4 own keys); every load of a batch is issued before
-// any is used, so a batch costs one memory round trip.
+// any is used, so a batch costs one memory round trip.  The partial records start the launch
+// filled with SENT32 and are written without a completion signal, so a batch is re-read until
+// none of its words holds the fill pattern.
 template <typename T>
 LS_DEV void att_merge2(const MegaArgs& a, const Lds& s, int l, int blk, int i, int hA, int hB, int np) {
   const int lane = threadIdx.x & 63, half = lane >> 5, hl = lane & 31;
@@ -1368,7 +1373,8 @@ LS_DEV void att_merge2(const MegaArgs& a, const Lds& s, int l, int blk, int i, i
   }
   const int a0 = s.raoff[i], na = s.raoff[i + 1] - a0;
   const int nt = na + 1;                             // the row's own keys: ancestors, then itself
-  const __amdgpu_buffer_rsrc_t Rp = rsrc_of(a.patt + (size_t)i * a.nh * a.att_pmax * rec, a.nh * a.att_pmax * rec * 4);
+  const float* const prow = patt_of(a, l) + (size_t)i * a.nh * a.att_pmax * rec;
+  const __amdgpu_buffer_rsrc_t Rp = rsrc_of(prow, a.nh * a.att_pmax * rec * 4);
   const int pbase = hh * a.att_pmax * rec;           // this half's head: its first partial record
   float q[4];
   {
@@ -1382,16 +1388,7 @@ LS_DEV void att_merge2(const MegaArgs& a, const Lds& s, int l, int blk, int i, i
   const int nbat = max((np + NPB - 1) / NPB, (nt + NK - 1) / NK);
   for (int bt = 0; bt < nbat; ++bt) {
     const int c0 = bt * NPB, j0 = bt * NK;
-    // ---- issue the batch's loads
-    float mxc = -INFINITY, smc = 0.f;                // statistics of partial c0 + hl (hl < NPB)
-    if (hok && hl < NPB && c0 + hl < np) {
-      mxc = ldc(a.patt + (size_t)i * a.nh * a.att_pmax * rec + pbase + (size_t)(c0 + hl) * rec + hd);
-      smc = ldc(a.patt + (size_t)i * a.nh * a.att_pmax * rec + pbase + (size_t)(c0 + hl) * rec + hd + 1);
-    }
-    u32x4_t ac[NPB];
-#pragma unroll
-    for (int u = 0; u < NPB; ++u)
-      ac[u] = ldc128(Rp, hok && c0 + u < np ? (pbase + (c0 + u) * rec + d0) * 4 : 0x7fffff00);
+    // ---- the batch's own keys, then its partials, re-read until none holds the fill pattern
     float kf[NK][4], vf[NK][4];
     bool bad = false;
 #pragma unroll
@@ -1401,6 +1398,25 @@ LS_DEV void att_merge2(const MegaArgs& a, const Lds& s, int l, int blk, int i, i
       if (x < 0 || x >= a.S) { bad = bad || j0 + u < nt; x = self; }
       load4_coh<T>(cache + (size_t)x * 2 * a.d, kf[u]);
       load4_coh<T>(cache + (size_t)x * 2 * a.d + a.d, vf[u]);
+    }
+    float mxc, smc;                                  // statistics of partial c0 + hl (hl < NPB)
+    u32x4_t ac[NPB];
+    for (int n = 0;;) {
+      mxc = -INFINITY;
+      smc = 0.f;
+      if (hok && hl < NPB && c0 + hl < np) {
+        mxc = ldc(prow + pbase + (size_t)(c0 + hl) * rec + hd);
+        smc = ldc(prow + pbase + (size_t)(c0 + hl) * rec + hd + 1);
+      }
+#pragma unroll
+      for (int u = 0; u < NPB; ++u)
+        ac[u] = ldc128(Rp, hok && c0 + u < np ? (pbase + (c0 + u) * rec + d0) * 4 : 0x7fffff00);
+      bool ok = __float_as_uint(mxc) != SENT32 && __float_as_uint(smc) != SENT32;
+#pragma unroll
+      for (int u = 0; u < NPB; ++u) ok = ok && ac[u].x != SENT32 && ac[u].y != SENT32 && ac[u].z != SENT32 && ac[u].w != SENT32;
+      if (__all(ok)) break;
+      __builtin_amdgcn_s_sleep(POLL_SLEEP);
+      if (give_up(n, a.err)) break;
     }
     if (bad) ls_flag(a.err, 1);
     // ---- the batch's scores and its maximum
@@ -1492,6 +1508,20 @@ template <> struct AttUnit<float> {
     __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(f[0]), __float_as_uint(f[1])}, r, off, 0, CPOL_SC1);
   }
 };
+
+// Rows (up to NRA), cache block and head block of attention segment sg of layer l.
+LS_DEV void att_segment(const MegaArgs& a, const Lds& s, const AttGeo& ag, int l, int sg, int (&rows)[NRA], int& nr,
+                        int& blk, int& h0, int& hbn) {
+  const int vg = sg / ag.n_hb, hb = sg - vg * ag.n_hb;
+  const int vt = s.vgt[vg], gr = vt & 63, r0 = vt >> 6;
+  const int g0 = s.goff[gr];
+  nr = min(NRA, s.goff[gr + 1] - g0 - r0);
+#pragma unroll
+  for (int r = 0; r < NRA; ++r) rows[r] = s.grow[g0 + r0 + min(r, nr - 1)];
+  blk = (a.dep ? s.rdep[s.grow[g0]] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
+  h0 = hb * ag.HB;
+  hbn = min(ag.HB, a.nh - h0);
+}
 
 // Release of a tile's ns ring slots from slot first on (a whole release per slab: the tile's
 // consumer is its only reader).
@@ -1667,12 +1697,10 @@ LS_DEV void att_phase(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
   int seg = T0 / ag.n_kt, kt = T0 - seg * ag.n_kt;
   int cur_seg = -1;
 
-  // end of this workgroup's part of segment sg: one partial per (row, head), then the merge if
-  // every other workgroup of the segment has left its partials
+  // end of this workgroup's part of segment sg: one partial per (row, head), written without a
+  // completion signal (the segment's merger polls the records)
   auto flush = [&](int sg) {
-    const int first = sg * ag.n_kt;
-    const int o0 = att_owner(first, ag.N, G);
-    const int np = att_owner(first + ag.n_kt - 1, ag.N, G) - o0 + 1;
+    const int o0 = att_owner(sg * ag.n_kt, ag.N, G);
     if (c > 0 && hv) {
 #pragma unroll
       for (int r = 0; r < NRA; ++r) {
@@ -1716,7 +1744,7 @@ LS_DEV void att_phase(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
             sum += wk[k] * so[k];
           }
           // partial record of (row, head h0 + hi) from this workgroup
-          float* const prow = a.patt + (size_t)rows[r] * a.nh * a.att_pmax * att_rec(hd);
+          float* const prow = patt_of(a, l) + (size_t)rows[r] * a.nh * a.att_pmax * att_rec(hd);
           const __amdgpu_buffer_rsrc_t Rp = rsrc_of(prow, a.nh * a.att_pmax * att_rec(hd) * 4);
           const int rec0 = ((h0 + hi) * a.att_pmax + (b - o0)) * att_rec(hd);
 #pragma unroll
@@ -1740,15 +1768,9 @@ LS_DEV void att_phase(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
           }
         }
       }
-      drain();
-      if (lane == 0) s.ints[2 * s.NS + 4] = atomicAdd(C + cl.o_fa + sg, 1);
     }
-    cb.sync();
-    if (s.ints[2 * s.NS + 4] == np - 1) {
-      // consumer c merges heads c and c + 4 (it has waited for their QKV tiles)
-      for (int r = 0; r < nr; ++r)
-        if (c < hbn) att_merge2<T>(a, s, l, blk, rows[r], h0 + c, c + 4 < hbn ? h0 + c + 4 : -1, np);
-    }
+    // consumers 1..3 write the next segment's states only after the sync of its set-up, which
+    // consumer 0 reaches once it has read these
   };
 
   const unsigned ring0 = (unsigned)(size_t)(__attribute__((address_space(3))) char*)s.ring;
@@ -1756,15 +1778,7 @@ LS_DEV void att_phase(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
     if (seg != cur_seg) {
       if (cur_seg >= 0) flush(cur_seg);
       cur_seg = seg;
-      const int vg = seg / ag.n_hb, hb = seg - vg * ag.n_hb;
-      const int vt = s.vgt[vg], gr = vt & 63, r0 = vt >> 6;
-      const int g0 = s.goff[gr];
-      nr = min(NRA, s.goff[gr + 1] - g0 - r0);
-#pragma unroll
-      for (int r = 0; r < NRA; ++r) rows[r] = s.grow[g0 + r0 + min(r, nr - 1)];
-      blk = (a.dep ? s.rdep[s.grow[g0]] + a.dep_off : 0) * a.blk_mul + a.layer0 + l;
-      h0 = hb * ag.HB;
-      hbn = min(ag.HB, a.nh - h0);
+      att_segment(a, s, ag, l, seg, rows, nr, blk, h0, hbn);
       hv = hi < hbn;
       // queries of the block's heads are complete once their q/k/v tiles have signalled:
       // consumer c waits for heads c and c + 4 (whose merge it may run), then all four meet
@@ -1832,6 +1846,17 @@ LS_DEV void att_phase(const MegaArgs& a, const Lds& s, const CntLayout& cl, int 
     if (++kt == ag.n_kt) { kt = 0; ++seg; }
   }
   flush(cur_seg);
+  // Merges of the segments whose last tile this workgroup holds, after all of its own tiles:
+  // consumer c takes heads c and c + 4 (it waited for their QKV tiles at the segment's set-up)
+  // and polls the other workgroups' partials.
+  for (int sg = T0 / ag.n_kt; sg <= (T1 - 1) / ag.n_kt; ++sg) {
+    const int last = sg * ag.n_kt + ag.n_kt - 1;
+    if (att_owner(last, ag.N, G) != b) continue;
+    const int np = b - att_owner(sg * ag.n_kt, ag.N, G) + 1;
+    att_segment(a, s, ag, l, sg, rows, nr, blk, h0, hbn);
+    for (int r = 0; r < nr; ++r)
+      if (c < hbn) att_merge2<T>(a, s, l, blk, rows[r], h0 + c, c + 4 < hbn ? h0 + c + 4 : -1, np);
+  }
 }
 
 // ---- init unit: embedding row or gathered hidden row into the working rows ---------------------------
@@ -2198,7 +2223,8 @@ hipError_t launch_embed(bool bf16, const ValidateArgs& v, const int32_t* tokens,
 // the row-descriptor check.
 __global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, const double* inv_freq, int M, int half,
                        unsigned* xs_fill, long long n_xs, unsigned* ys_fill, long long n_ys, unsigned* o_fill,
-                       long long n_o, ValidateArgs v, const int32_t* fin, int n_fin, long long S, int* err) {
+                       long long n_o, unsigned* p_fill, int p_rows, int p_max, int p_n, int p_rec, ValidateArgs v,
+                       const int32_t* fin, int n_fin, long long S, int* err) {
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x, str = (long long)gridDim.x * blockDim.x;
   for (long long i = tid; i < v.n; i += str) check_row(v, (int)i);
   for (long long i = tid; i < n_fin; i += str)
@@ -2207,6 +2233,12 @@ __global__ void k_prep(int* cnt, long long n, float* rope, const int32_t* pos, c
   for (long long i = tid; i < n_xs; i += str) xs_fill[i] = SENT32;
   for (long long i = tid; i < n_ys; i += str) ys_fill[i] = SENT32;
   for (long long i = tid; i < n_o; i += str) o_fill[i] = 0xffffffffu;
+  // the first p_n partial records of each of p_rows (layer, row, head) triples
+  const long long per = (long long)p_n * p_rec;
+  for (long long i = tid; i < (long long)p_rows * per; i += str) {
+    const long long rh = i / per, k = i - rh * per;
+    p_fill[rh * p_max * p_rec + k] = SENT32;
+  }
   for (long long i = tid; i < (long long)M * half; i += str) {
     const int m = (int)(i / half), f = (int)(i % half);
     double sn, cs;
@@ -2246,14 +2278,17 @@ int mega_occupancy(bool bf16, int M, int d, bool loop_block) {
 
 hipError_t launch_mega(bool bf16, const MegaArgs& a, int G, hipStream_t s, bool loop_block, const ValidateArgs& v) {
   const CntLayout cl = cnt_layout(a.M, a.d, a.F, a.nh, x_chunk_for(a.M, bf16 ? 2 : 4, a.d), a.n_layers);
-  const long long n_prep = std::max<long long>(std::max<long long>(cl.total, (long long)a.M * (a.hd / 2)),
-                                               std::max<long long>(v.n, a.n_fin));
+  const long long n_patt = (long long)a.n_layers * a.M * a.nh * a.att_npf * (a.hd + 4);
+  const long long n_prep = std::max<long long>(std::max<long long>(std::max<long long>(cl.total, (long long)a.M * (a.hd / 2)),
+                                                                   std::max<long long>(v.n, a.n_fin)),
+                                               n_patt);
   const long long rows = (long long)a.M * a.d;   // one layer slice of Xs / Ys
   hipLaunchKernelGGL(k_prep, dim3((unsigned)std::min<long long>(1024, (n_prep + 255) / 256)), dim3(256), 0, s, a.cnt,
                      (long long)cl.total, a.rope, a.pos, a.inv_freq, a.M, a.hd / 2,
                      reinterpret_cast<unsigned*>(a.Xs + rows), (long long)a.n_layers * rows,
                      reinterpret_cast<unsigned*>(a.Ys), (long long)a.n_layers * rows,
-                     reinterpret_cast<unsigned*>(a.o), (long long)a.n_layers * rows * (bf16 ? 2 : 4) / 4, v, a.fin,
+                     reinterpret_cast<unsigned*>(a.o), (long long)a.n_layers * rows * (bf16 ? 2 : 4) / 4,
+                     reinterpret_cast<unsigned*>(a.patt), a.n_layers * a.M * a.nh, a.att_pmax, a.att_npf, a.hd + 4, v, a.fin,
                      a.n_fin, a.S, a.err);
   const size_t smem = mega_smem_bytes(bf16, a.M, a.d);
   void* args[] = {(void*)&a};
