@@ -77,6 +77,25 @@ def _cpu_model():
     return "unknown"
 
 
+def prefill_report(cfg, dec, mode, seconds):
+    """Prefill (untimed in the decode metric, LoopSpec page section 3.1): wall time of
+    Decoder.prefill for the workload prompt (ls_prefill chunks plus the last position's
+    readout), and the rate of its matrix products against the dense bf16 matrix-core peak.
+    Matrix flops: 2 * positions * (layer weights of P, of R loop iterations of B and of the
+    coda at every readout depth whose caches are filled) plus the causal attention products
+    (4 * d per (query, key) pair per layer)."""
+    T0, d, F = dec.prompt_len, cfg.d, cfg.F
+    per_layer = 4 * d * d + 3 * F * d
+    n_coda = len(cfg.readout_depths) if mode == "spec" else 1
+    layers = cfg.L_pre + cfg.R * cfg.L + (n_coda * cfg.L_coda if cfg.L_coda else 0)
+    flops = 2.0 * T0 * per_layer * layers + 4.0 * d * (T0 * (T0 + 1) / 2) * layers
+    peak = 2500.0 if cfg.dtype == "bf16" else 157.3
+    tf = flops / seconds / 1e12
+    return {"tokens": T0, "seconds": round(seconds, 3), "tokens_per_s": round(T0 / seconds, 1),
+            "matrix_tflops": round(tf, 1), "peak_tflops": peak, "frac": round(tf / peak, 4),
+            "note": "ls_prefill: every layer of every depth as matrix products over 2048-position chunks"}
+
+
 COPY_BYTES = 1 << 30            # size of the plain device copy that calibrates the HBM byte counters
 LOOP_KERNEL = "void ls::k_mega<"  # profile name prefix of the loop-block launches (ls_loop_step)
 TRAFFIC_SOURCES = ["mega.hip", "common.h", "kernels.h", "loopspec_abi.hip"]
@@ -447,9 +466,12 @@ def main():
                prob_rows=4 * dec.max_branches + 16)
     d = Decoder(e, dec, args.mode)
     print("[bench] prefill", file=sys.stderr, flush=True)
-    d.prefill(prompt, progress=_Progress("prefill"))
-    snap = d.snapshot()
     torch.cuda.synchronize()
+    tp = time.perf_counter()
+    d.prefill(prompt, progress=_Progress("prefill"))
+    torch.cuda.synchronize()
+    t_pre = time.perf_counter() - tp
+    snap = d.snapshot()
     run = SliceRunner(d, snap, n_new)
     for i in range(args.warmup):
         run.step()
@@ -507,6 +529,7 @@ def main():
         "decode_stats": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in _merge_stats(
             run.finished, (dec.screen_depth if dec.copy else dec.d1, dec.d2 or cfg.R, cfg.R)).items()},
     }
+    out["prefill"] = prefill_report(cfg, dec, args.mode, t_pre)
     if traffic and "mfma_util_percent" in traffic:
         # matrix-core use of the same kernel from the committed counter summary
         out["roofline"]["mfma_util_percent"] = traffic["mfma_util_percent"]

@@ -210,6 +210,28 @@ ls_status ls_readout(ls_model *m, const ls_rows *rows, const float *H, const ls_
                      float *probs, const int32_t *out_rows, int n_prob_rows, int32_t *argmax, float *logits,
                      const ls_kv *kv, hipStream_t stream);
 
+/* Prefill of a chunk of prompt positions (the step before decoding: section 2.1, eq. 1
+ * applied to the prompt; section 2.4 for the prelude, loop and coda caches; section 3.1
+ * excludes it from decode timing).  Row i is position n_fin + i of the sequence whose first
+ * n_fin positions are committed with their slots in fin_slots[0..n_fin) (device int32, every
+ * cache already filled for them).  For every row the call runs P (embedding, prelude layers
+ * writing the prelude cache at slots[i]), every loop iteration k = 1..R of B (writing the
+ * cache of depth k at slots[i]; causal attention over the committed prefix and rows 0..i of
+ * the chunk), and, for each readout depth index j with bit j of coda_mask set, the coda
+ * layers on H^(D[j]) (writing the coda cache of that readout depth; their outputs are not
+ * kept), and leaves H[slots[i]] = H^(R).  The readout of the last position (its distribution
+ * at R) is an ls_readout call afterwards.  Each layer runs as matrix products with the
+ * chunk's n rows as M (the weights are streamed once per layer per depth for the chunk).
+ * tokens, slots: device int32 [n].  pws: device scratch of ls_prefill_workspace_bytes(m, n)
+ * bytes or more, 256-byte aligned, caller-owned (LS_ERR_CAPACITY if smaller).  Requires a
+ * bound workspace (its error word and rotary table).  A token outside [0, V) or a slot outside
+ * [0, S) raises LS_ERR_INVALID in the error word: such a row's embedding is zero, an invalid
+ * row slot stores nothing, an invalid prefix slot is read as slot 0. */
+size_t ls_prefill_workspace_bytes(const ls_model *m, int max_n);
+ls_status ls_prefill(ls_model *m, const int32_t *tokens, const int32_t *slots, int n, const int32_t *fin_slots,
+                     int n_fin, unsigned coda_mask, float *H, const ls_kv *kv, void *pws, size_t pws_bytes,
+                     hipStream_t stream);
+
 /* Lossless verification jobs (section 2.2-2.3), one integer pass over V per job; results
  * are bit-identical for identical inputs.  jobs: [n_jobs]; probs: fp32
  * [n_prob_rows][V], each row a probability vector (entries in [0, 1], sum <= ~1; a row whose

@@ -23,7 +23,8 @@ LS_OUT_ACC1, LS_OUT_ACC2, LS_OUT_RESAMPLED, LS_OUT_DRAWN, LS_OUT_ACC_COPY, LS_OU
 
 EXPORTS = ("ls_last_error", "ls_model_create", "ls_model_destroy", "ls_workspace_bytes", "ls_bind_workspace",
            "ls_prelude", "ls_loop_step", "ls_readout", "ls_verify", "ls_sync_status", "ls_philox_uniforms",
-           "ls_debug_trace", "ls_set_wait_limit", "ls_loop_step_static", "ls_measure_stream_read")
+           "ls_debug_trace", "ls_set_wait_limit", "ls_loop_step_static", "ls_measure_stream_read",
+           "ls_prefill_workspace_bytes", "ls_prefill")
 
 
 class ls_model_desc(C.Structure):
@@ -93,6 +94,8 @@ def _load():
         "ls_set_wait_limit": (C.c_int, [P, C.c_double]),
         "ls_loop_step_static": (C.c_int, [P, C.POINTER(ls_rows), P, C.POINTER(ls_kv), P, P]),
         "ls_measure_stream_read": (C.c_int, [P, C.c_size_t, C.c_int, P]),
+        "ls_prefill_workspace_bytes": (C.c_size_t, [P, C.c_int]),
+        "ls_prefill": (C.c_int, [P, P, P, C.c_int, P, C.c_int, C.c_uint, P, C.POINTER(ls_kv), P, C.c_size_t, P]),
         "ls_philox_uniforms": (None, [C.c_uint64, C.c_int64, C.POINTER(C.c_int32), C.c_int,
                                       C.POINTER(C.c_uint32)]),
     }

@@ -7,7 +7,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libloopspec.so")
-SOURCES = ["mega.hip", "readout.hip", "verify.hip", "misc.hip", "loopspec_abi.hip", "stream.hip"]
+SOURCES = ["mega.hip", "readout.hip", "verify.hip", "misc.hip", "loopspec_abi.hip", "stream.hip", "prefill.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # packed fp32 arithmetic stays off: hipcc must not emit packed-fp32 instructions
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -101,4 +101,31 @@ void launch_dist(const float* logits, int M, int V, int greedy, float T, float t
 void launch_verify(const void* jobs, int n_jobs, const float* probs, int V, int n_rows, int32_t* cands, int n_cands,
                    const uint32_t* uniforms, void* out, int* err, hipStream_t s);
 
+// Prefill of a chunk of prompt positions (prefill.hip): buffers carved from the caller's
+// prefill workspace, n rows each.
+struct PrefillBufs {
+  float *X = nullptr, *Xc = nullptr;   // residual stream of the chunk and its coda copy [n][d]
+  void* A = nullptr;                   // normalised rows [n][d] (model dtype)
+  float* QKV = nullptr;                // q | k | v [n][3d]; q rotated in place
+  void *O = nullptr, *ACT = nullptr;   // attention outputs [n][d], SwiGLU outputs [n][F]
+};
+struct PrefillArgs {
+  int n, n_fin, d, F, hd, nh, V, L, L_pre, L_coda, R, n_readout;
+  int readout_depths[8];
+  unsigned coda_mask;                  // bit j: fill the coda caches of readout depth index j
+  float eps;
+  long long S;
+  const int32_t *tokens, *slots, *fin;
+  const void* emb;
+  const LayerW *pre, *core, *coda;     // host arrays of device weight pointers
+  void *kv_pre, *kv_core, *kv_coda;
+  const double* invf;                  // device rotary frequencies
+  float* H;
+  int* err;
+  PrefillBufs b;
+};
+size_t prefill_bytes(int n, int d, int F, bool bf16);
+PrefillBufs prefill_carve(void* base, int n, int d, int F, bool bf16);
+hipError_t launch_prefill(bool bf16, const PrefillArgs& a, hipStream_t s);
+
 }  // namespace ls

@@ -510,6 +510,49 @@ ls_status ls_readout(ls_model* m, const ls_rows* r, const float* H, const ls_sam
   return check_hip("ls_readout");
 }
 
+size_t ls_prefill_workspace_bytes(const ls_model* m, int max_n) {
+  if (!m || max_n < 0) return 0;
+  return prefill_bytes(max_n, m->d.d, m->d.F, m->bf16());
+}
+
+ls_status ls_prefill(ls_model* m, const int32_t* tokens, const int32_t* slots, int n, const int32_t* fin_slots, int n_fin,
+                     unsigned coda_mask, float* H, const ls_kv* kv, void* pws, size_t pws_bytes, hipStream_t s) {
+  if (!m || !m->w.base) return fail(LS_ERR_INVALID, "ls_prefill: null model or no workspace bound");
+  if (n < 0 || n_fin < 0) return fail(LS_ERR_INVALID, "ls_prefill: negative sizes");
+  if (n == 0) return LS_OK;
+  const ls_model_desc& d = m->d;
+  if (!tokens || !slots || !H || !kv || !kv->core || !pws || (n_fin && !fin_slots))
+    return fail(LS_ERR_INVALID, "ls_prefill: null argument");
+  if (d.L_pre && !kv->pre) return fail(LS_ERR_INVALID, "ls_prefill: prelude layers need kv->pre");
+  const unsigned mask = coda_mask & ((1u << d.n_readout) - 1u);
+  if (d.L_coda && mask && !kv->coda) return fail(LS_ERR_INVALID, "ls_prefill: coda layers need kv->coda");
+  if ((long long)n_fin + n > 0x7fffffffLL) return fail(LS_ERR_INVALID, "ls_prefill: positions overflow");
+  const size_t need = prefill_bytes(n, d.d, d.F, m->bf16());
+  if (pws_bytes < need)
+    return fail(LS_ERR_CAPACITY, "ls_prefill: %d rows need %zu workspace bytes, %zu given", n, need, pws_bytes);
+  if ((uintptr_t)pws % 256) return fail(LS_ERR_INVALID, "ls_prefill: workspace must be 256-byte aligned");
+  PrefillArgs a{};
+  a.n = n; a.n_fin = n_fin; a.d = d.d; a.F = d.F; a.hd = d.head_dim; a.nh = d.n_heads; a.V = d.V;
+  a.L = d.L; a.L_pre = d.L_pre; a.L_coda = d.L_coda; a.R = d.R; a.n_readout = d.n_readout;
+  for (int i = 0; i < d.n_readout; ++i) a.readout_depths[i] = d.readout_depths[i];
+  a.coda_mask = mask;
+  a.eps = d.norm_eps;
+  a.S = d.slot_capacity;
+  a.tokens = tokens; a.slots = slots; a.fin = fin_slots;
+  a.emb = m->emb;
+  a.pre = m->host_tab.data();
+  a.core = a.pre + m->pre.size();
+  a.coda = a.core + m->core.size();
+  a.kv_pre = kv->pre; a.kv_core = kv->core; a.kv_coda = kv->coda;
+  a.invf = m->w.invf;
+  a.H = H;
+  a.err = m->w.err;
+  a.b = prefill_carve(pws, n, d.d, d.F, m->bf16());
+  hipError_t e = launch_prefill(m->bf16(), a, s);
+  if (e != hipSuccess) return fail(LS_ERR_HIP, "ls_prefill: launch: %s", hipGetErrorString(e));
+  return LS_OK;
+}
+
 ls_status ls_verify(ls_model* m, const ls_verify_job* jobs, int n_jobs, const float* probs, int n_prob_rows,
                     int32_t* cands, int n_cands, const uint32_t* uniforms, ls_verify_out* out, hipStream_t s) {
   if (!m || !m->w.base) return fail(LS_ERR_INVALID, "ls_verify: null model or no workspace");

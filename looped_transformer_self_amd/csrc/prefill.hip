@@ -1,0 +1,508 @@
+// Prefill of a chunk of prompt positions as large-M matrix products.
+//
+// The prompt runs through P, every loop iteration 1..R of B and the coda layers at the
+// readout depths before decoding starts (LoopSpec page, section 2.1, eq. 1: the same P/B/C
+// map, applied to all prompt positions at once; section 2.4: prelude, loop and coda caches
+// indexed by depth; section 3.1 leaves prefill out of the decode timing).  A chunk of n
+// consecutive positions follows the n_fin committed ones; each layer of each depth is
+//   RMSNorm -> [q k v] = a W^T -> RoPE, K/V into the depth's cache -> causal attention over
+//   the committed prefix and the chunk -> h += o Wo^T -> RMSNorm -> silu(b Wg^T) * (b Wu^T)
+//   -> h += act Wd^T,
+// with the chunk's rows as the M dimension of every product, so the weights are streamed
+// once per layer for the whole chunk and the products run on the matrix cores.
+//
+// Storage precision is the decode path's: weights, normalised activations, attention
+// outputs, SwiGLU outputs and the K/V cache in the model dtype; residual stream, queries,
+// scores and softmax in fp32.
+#include <math.h>
+
+#include <utility>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace ls {
+
+namespace {
+
+// ---- matrix product C = X W^T over 128 x 128 tiles -------------------------------------------
+// X: activation rows [M][K] (model dtype); W: weight rows [N][K].  A workgroup of 4 waves
+// computes 128 weight rows x 128 activation rows; wave (wn, wx) a 64 x 64 quarter as 4 x 4
+// MFMA blocks of 16 x 16 (A = 16 weight rows, B = 16 activation rows; lane l holds weight
+// rows 4*(l/16) + j of activation row l%16 of a block).  K advances 128 bytes per stage
+// (64 bf16 or 32 fp32); a stage of both operands (2 x 16 KB) sits in LDS as rows of eight
+// 16-byte chunks, chunk c of row r at c ^ (r & 7) so the 16 rows an MFMA operand read touches
+// fall on distinct banks.  Two LDS stages: the next stage's global loads are in flight while
+// the current one is multiplied.
+constexpr int GT = 128;              // tile rows (both operands)
+constexpr int GCH = 8;               // 16-byte chunks per tile row per stage
+constexpr int GTHREADS = 256;
+
+enum PfMode { PF_STORE = 0, PF_ADD = 1, PF_SWIGLU = 2 };
+
+struct GemmArgs {
+  const void* X;                     // [M][K], row stride K
+  int M, K;
+  const void* W[3];                  // nmat weight matrices [Nb][K]; SWIGLU: W[0] = gate, W[1] = up
+  int Nb, nmat;
+  int n_wt, n_xt;                    // weight tiles (over all matrices), activation tiles
+  float* out;                        // STORE: out[m][mat*Nb + n]; ADD: out[m][n] += (row stride ldo)
+  int ldo;
+  void* act;                         // SWIGLU: act[m][n] (model dtype, row stride Nb)
+};
+
+template <typename T> struct PfMma;
+template <> struct PfMma<uint16_t> {
+  LS_DEV static void run(f32x4_t& c, const u32x4_t& a, const u32x4_t& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0,
+                                                0, 0);
+  }
+};
+template <> struct PfMma<float> {
+  LS_DEV static void run(f32x4_t& c, const u32x4_t& a, const u32x4_t& b) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(b[e]), c, 0, 0, 0);
+  }
+};
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(GTHREADS) void k_pf_gemm(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) char gsm[];
+  u32x4_t* const Ws = reinterpret_cast<u32x4_t*>(gsm);                  // [2][GT][GCH]
+  u32x4_t* const Xs = Ws + 2 * GT * GCH;                                // [2][GT][GCH]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // tile of this workgroup: workgroups are placed on the 8 XCDs round-robin; consecutive tile
+  // numbers (which share a weight tile) go to one XCD so its L2 serves their weight reads
+  const int nt = g.n_wt * g.n_xt, gid = blockIdx.x;
+  const int q8 = nt >> 3, r8 = nt & 7, x8 = gid & 7;
+  const int t = x8 * q8 + min(x8, r8) + (gid >> 3);
+  const int wt = t / g.n_xt, xt = t - wt * g.n_xt;
+  const size_t rb = (size_t)g.K * sizeof(T);                            // bytes per row
+  const int nst = (int)((rb + 16 * GCH - 1) / (16 * GCH));              // stages
+
+  // this thread's load rows: r = tid/8 + 32 i, chunk tid % 8
+  const int lch = tid & 7;
+  const char* wp[4];
+  const char* xp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    int mat, n;
+    if (MODE == PF_SWIGLU) {
+      const int b = r >> 4;
+      mat = b & 1;
+      n = wt * 64 + (b >> 1) * 16 + (r & 15);
+    } else {
+      const int tpm = (g.Nb + GT - 1) / GT;
+      mat = wt / tpm;
+      n = (wt - mat * tpm) * GT + r;
+    }
+    wp[i] = static_cast<const char*>(g.W[mat]) + (size_t)min(n, g.Nb - 1) * rb + 16 * lch;
+    xp[i] = static_cast<const char*>(g.X) + (size_t)min(xt * GT + r, g.M - 1) * rb + 16 * lch;
+  }
+  u32x4_t wv[4], xv[4];
+  auto gload = [&](int st) {
+    const size_t off = (size_t)st * 16 * GCH;
+    const bool ok = off + 16 * lch < rb;                                // K tail: zeros
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wv[i] = ok ? *reinterpret_cast<const u32x4_t*>(wp[i] + off) : u32x4_t{0u, 0u, 0u, 0u};
+      xv[i] = ok ? *reinterpret_cast<const u32x4_t*>(xp[i] + off) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid >> 3) + 32 * i;
+      const int c = (buf * GT + r) * GCH + (lch ^ (r & 7));
+      Ws[c] = wv[i];
+      Xs[c] = xv[i];
+    }
+  };
+
+  const int wn = w & 1, wx = w >> 1;
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int fr = lane & 15, fq = lane >> 4;
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) gload(st + 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4_t af[4], bf[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int r = wn * 64 + a * 16 + fr;
+        af[a] = Ws[(buf * GT + r) * GCH + ((s * 4 + fq) ^ (r & 7))];
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int r = wx * 64 + b * 16 + fr;
+        bf[b] = Xs[(buf * GT + r) * GCH + ((s * 4 + fq) ^ (r & 7))];
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) PfMma<T>::run(acc[a][b], af[a], bf[b]);
+    }
+    if (st + 1 < nst) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: block (a, b) holds weight rows wn*64 + a*16 + 4*fq + j of activation row
+  // wx*64 + b*16 + fr
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int m = xt * GT + wx * 64 + b * 16 + fr;
+    if (m >= g.M) continue;
+    if (MODE == PF_SWIGLU) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int f = wt * 64 + (wn * 2 + p) * 16 + 4 * fq;
+        if (f >= g.Nb) continue;
+        T* dst = static_cast<T*>(g.act) + (size_t)m * g.Nb + f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float gt = acc[2 * p][b][j], up = acc[2 * p + 1][b][j];
+          Elem<T>::store(dst + j, gt / (1.0f + expf(-gt)) * up);
+        }
+      }
+    } else {
+      const int tpm = (g.Nb + GT - 1) / GT;
+      const int mat = wt / tpm, n0 = (wt - mat * tpm) * GT;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int n = n0 + wn * 64 + a * 16 + 4 * fq;
+        if (n >= g.Nb) continue;
+        float4* dst = reinterpret_cast<float4*>(g.out + (size_t)m * g.ldo + (size_t)mat * g.Nb + n);
+        float4 v = make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+        if (MODE == PF_ADD) {
+          const float4 h = *dst;
+          v = make_float4(h.x + v.x, h.y + v.y, h.z + v.z, h.w + v.w);
+        }
+        *dst = v;
+      }
+    }
+  }
+}
+
+template <typename T, int MODE>
+void gemm(const void* X, int M, int K, const void* W0, const void* W1, const void* W2, int Nb, int nmat, float* out,
+          int ldo, void* act, hipStream_t s) {
+  GemmArgs g{};
+  g.X = X; g.M = M; g.K = K;
+  g.W[0] = W0; g.W[1] = W1; g.W[2] = W2;
+  g.Nb = Nb; g.nmat = nmat;
+  g.n_wt = MODE == PF_SWIGLU ? (Nb + 63) / 64 : nmat * ((Nb + GT - 1) / GT);
+  g.n_xt = (M + GT - 1) / GT;
+  g.out = out; g.ldo = ldo; g.act = act;
+  const size_t smem = (size_t)4 * GT * GCH * 16;
+  hipLaunchKernelGGL((k_pf_gemm<T, MODE>), dim3(g.n_wt * g.n_xt), dim3(GTHREADS), smem, s, g);
+}
+
+// ---- row kernels --------------------------------------------------------------------------------
+// Row check and embedding gather: X[i] = E[tokens[i]] (P without prelude layers, the first
+// step of P with them).  Tokens outside [0, V), slots outside [0, S) and committed-prefix
+// slots outside [0, S) raise the error word; such a row's embedding is zero.
+template <typename T>
+__global__ void k_pf_embed(const int32_t* tokens, const int32_t* slots, int n, const int32_t* fin, int n_fin, long long S,
+                           const T* emb, int V, int d, float* X, int* err) {
+  const int i = blockIdx.x;
+  if (i < n) {
+    const int tok = tokens[i], sl = slots[i];
+    const bool ok = tok >= 0 && tok < V;
+    if (threadIdx.x == 0 && (!ok || sl < 0 || sl >= S)) ls_flag(err, 1);
+    const T* e = emb + (size_t)(ok ? tok : 0) * d;
+    for (int k = threadIdx.x; k < d; k += blockDim.x) X[(size_t)i * d + k] = ok ? Elem<T>::load(e + k) : 0.f;
+  }
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n_fin; j += gridDim.x * blockDim.x)
+    if (fin[j] < 0 || fin[j] >= S) ls_flag(err, 1);
+}
+
+// A[i] = RMSNorm(X[i]) * g in the model dtype (one workgroup per row).
+template <typename T>
+__global__ __launch_bounds__(256) void k_pf_norm(const float* X, const float* g, T* A, int d, float eps) {
+  __shared__ float red[4];
+  const float* x = X + (size_t)blockIdx.x * d;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < d; k += 256) ss += x[k] * x[k];
+  const float ri = 1.0f / sqrtf(block_sum(ss, red) / (float)d + eps);
+  T* a = A + (size_t)blockIdx.x * d;
+  for (int k = threadIdx.x; k < d; k += 256) Elem<T>::store(a + k, x[k] * ri * g[k]);
+}
+
+// Rotary embedding of q and k (rotate-half pairs (f, f + hd/2) of every head, angle
+// pos * theta^(-2f/hd) evaluated in double), q kept in fp32 in place, k and v stored into the
+// cache entry of the row's slot (rows with an invalid slot store nothing).
+template <typename T>
+__global__ void k_pf_rope(float* QKV, int n, int d, int hd, int pos0, const double* invf, const int32_t* slots,
+                          long long S, T* kv) {
+  const int i = blockIdx.x, half = hd / 2;
+  float* row = QKV + (size_t)i * 3 * d;
+  const int sl = slots[i];
+  const bool st = sl >= 0 && sl < S;
+  T* ent = kv + (size_t)(st ? sl : 0) * 2 * d;
+  for (int p = threadIdx.x; p < d / 2; p += blockDim.x) {
+    const int h = p / half, f = p - h * half;
+    const int c0 = h * hd + f, c1 = c0 + half;
+    double sd, cd;
+    sincos((double)(pos0 + i) * invf[f], &sd, &cd);
+    const float c = (float)cd, s = (float)sd;
+    const float q0 = row[c0], q1 = row[c1];
+    row[c0] = q0 * c - q1 * s;
+    row[c1] = q1 * c + q0 * s;
+    const float k0 = row[d + c0], k1 = row[d + c1];
+    if (st) {
+      Elem<T>::store(ent + c0, k0 * c - k1 * s);
+      Elem<T>::store(ent + c1, k1 * c + k0 * s);
+      Elem<T>::store(ent + d + c0, row[2 * d + c0]);
+      Elem<T>::store(ent + d + c1, row[2 * d + c1]);
+    }
+  }
+}
+
+// H[slots[i]] = X[i] (rows with an invalid slot are skipped).
+__global__ void k_pf_scatter(const float* X, const int32_t* slots, long long S, int d, float* H) {
+  const int sl = slots[blockIdx.x];
+  if (sl < 0 || sl >= S) return;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) H[(size_t)sl * d + k] = X[(size_t)blockIdx.x * d + k];
+}
+
+// ---- causal attention of the chunk ----------------------------------------------------------
+// Workgroup (query block of 64 rows, head): keys of the committed prefix (slots fin[0..n_fin))
+// and of the chunk (slots[0..n)) in blocks of 64, row i seeing keys t <= n_fin + i; online
+// softmax in fp32.  Thread t: queries 4*(t/16) + i (i < 4); scores of keys t%16 + 16 j (j < 4);
+// output dims (t%16)*HD/16 + e.  Q, the key block's K and V (converted to fp32) and the
+// probabilities sit in LDS.
+constexpr int AQ = 64;
+
+template <int HD> struct AttLds {
+  static constexpr int ST = HD + 4;                                      // row stride (floats)
+  static constexpr size_t bytes = (size_t)(3 * AQ * ST + AQ * (AQ + 4)) * 4 + AQ * 4;
+};
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void k_pf_attn(const float* Q, int ldq, int n, int n_fin, const int32_t* fin,
+                                                 const int32_t* slots, long long S, const T* kv, int d, T* O,
+                                                 float scale) {
+  extern __shared__ __attribute__((aligned(16))) char asm_[];
+  constexpr int ST = AttLds<HD>::ST, DPT = HD / 16;
+  float* const Qs = reinterpret_cast<float*>(asm_);
+  float* const Ks = Qs + AQ * ST;
+  float* const Vs = Ks + AQ * ST;
+  float* const Ps = Vs + AQ * ST;                                       // [AQ][AQ + 4]
+  int* const ksl = reinterpret_cast<int*>(Ps + AQ * (AQ + 4));
+  const int tid = threadIdx.x, qg = tid >> 4, kg = tid & 15;
+  const int q0 = blockIdx.x * AQ, h = blockIdx.y;
+  const int qlast = min(q0 + AQ, n) - 1;
+  const int tmax = n_fin + qlast;                                        // last key any row sees
+
+  for (int e = tid; e < AQ * HD; e += 256) {
+    const int r = e / HD, c = e - r * HD;
+    Qs[r * ST + c] = q0 + r < n ? Q[(size_t)(q0 + r) * ldq + h * HD + c] * scale : 0.f;
+  }
+  float mrun[4], lsum[4], acc[4][DPT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mrun[i] = -INFINITY;
+    lsum[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) acc[i][e] = 0.f;
+  }
+
+  for (int k0 = 0; k0 <= tmax; k0 += AQ) {
+    __syncthreads();                                                     // previous block's reads done
+    if (tid < AQ) {
+      const int t = k0 + tid;
+      int sl = t < n_fin ? fin[t] : (t < n_fin + n ? slots[t - n_fin] : 0);
+      ksl[tid] = sl >= 0 && sl < S ? sl : 0;
+    }
+    __syncthreads();
+    for (int e = tid; e < AQ * HD; e += 256) {
+      const int r = e / HD, c = e - r * HD;
+      const T* ent = kv + (size_t)ksl[r] * 2 * d + h * HD + c;
+      Ks[r * ST + c] = Elem<T>::load(ent);
+      Vs[r * ST + c] = Elem<T>::load(ent + d);
+    }
+    __syncthreads();
+    float sc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[i][j] = 0.f;
+    for (int c = 0; c < HD; c += 4) {
+      float4 qv[4], kk[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[i] = *reinterpret_cast<const float4*>(Qs + (4 * qg + i) * ST + c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kk[j] = *reinterpret_cast<const float4*>(Ks + (kg + 16 * j) * ST + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sc[i][j] += qv[i].x * kk[j].x + qv[i].y * kk[j].y + qv[i].z * kk[j].z + qv[i].w * kk[j].w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = n_fin + q0 + 4 * qg + i;                             // this query's position
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = k0 + kg + 16 * j;
+        if (t > p || t >= n_fin + n) sc[i][j] = -INFINITY;
+        mx = fmaxf(mx, sc[i][j]);
+      }
+      mx = row_max16(mx);
+      const float mnew = fmaxf(mrun[i], mx);                             // finite: key 0 <= p
+      const float al = expf(mrun[i] - mnew);
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e = expf(sc[i][j] - mnew);
+        Ps[(4 * qg + i) * (AQ + 4) + kg + 16 * j] = e;
+        ps += e;
+      }
+      lsum[i] = lsum[i] * al + row_sum16(ps);
+      mrun[i] = mnew;
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) acc[i][e] *= al;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < AQ; kk += 4) {
+      float4 pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = *reinterpret_cast<const float4*>(Ps + (4 * qg + i) * (AQ + 4) + kk);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float vv[DPT];
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) vv[e] = Vs[(kk + u) * ST + kg * DPT + e];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pw = u == 0 ? pv[i].x : (u == 1 ? pv[i].y : (u == 2 ? pv[i].z : pv[i].w));
+#pragma unroll
+          for (int e = 0; e < DPT; ++e) acc[i][e] += pw * vv[e];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = q0 + 4 * qg + i;
+    if (r >= n) continue;
+    const float inv = 1.0f / lsum[i];
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) Elem<T>::store(O + (size_t)r * d + h * HD + kg * DPT + e, acc[i][e] * inv);
+  }
+}
+
+template <typename T, int HD>
+void attn_hd(const float* Q, int n, int n_fin, const int32_t* fin, const int32_t* slots, long long S, const T* kv, int d,
+             int nh, T* O, hipStream_t s) {
+  hipLaunchKernelGGL((k_pf_attn<T, HD>), dim3((n + AQ - 1) / AQ, nh), dim3(256), AttLds<HD>::bytes, s, Q, 3 * d, n,
+                     n_fin, fin, slots, S, kv, d, O, 1.0f / sqrtf((float)HD));
+}
+
+template <typename T>
+void attn(int hd, const float* Q, int n, int n_fin, const int32_t* fin, const int32_t* slots, long long S, const T* kv,
+          int d, int nh, T* O, hipStream_t s) {
+  switch (hd) {
+    case 16: attn_hd<T, 16>(Q, n, n_fin, fin, slots, S, kv, d, nh, O, s); break;
+    case 32: attn_hd<T, 32>(Q, n, n_fin, fin, slots, S, kv, d, nh, O, s); break;
+    case 48: attn_hd<T, 48>(Q, n, n_fin, fin, slots, S, kv, d, nh, O, s); break;
+    case 64: attn_hd<T, 64>(Q, n, n_fin, fin, slots, S, kv, d, nh, O, s); break;
+    case 80: attn_hd<T, 80>(Q, n, n_fin, fin, slots, S, kv, d, nh, O, s); break;
+    case 96: attn_hd<T, 96>(Q, n, n_fin, fin, slots, S, kv, d, nh, O, s); break;
+    case 112: attn_hd<T, 112>(Q, n, n_fin, fin, slots, S, kv, d, nh, O, s); break;
+    default: attn_hd<T, 128>(Q, n, n_fin, fin, slots, S, kv, d, nh, O, s); break;
+  }
+}
+
+// One pre-norm layer on the chunk: X (fp32 [n][d]) updated in place; K/V of the chunk stored
+// into kv (the layer's cache block [S][2][d]).  kv_only: stop after the K/V store (the last
+// coda layer, whose output no later computation reads during prefill).
+template <typename T>
+void layer(const PrefillArgs& a, const LayerW& lw, T* kv, bool kv_only, hipStream_t s) {
+  const int n = a.n, d = a.d, F = a.F;
+  const PrefillBufs& b = a.b;
+  T* A = static_cast<T*>(b.A);
+  const float* g1 = lw.g1;
+  hipLaunchKernelGGL(k_pf_norm<T>, dim3(n), dim3(256), 0, s, b.X, g1, A, d, a.eps);
+  gemm<T, PF_STORE>(A, n, d, lw.Wq, lw.Wk, lw.Wv, d, 3, b.QKV, 3 * d, nullptr, s);
+  hipLaunchKernelGGL(k_pf_rope<T>, dim3(n), dim3(256), 0, s, b.QKV, n, d, a.hd, a.n_fin, a.invf, a.slots, a.S, kv);
+  if (kv_only) return;
+  attn<T>(a.hd, b.QKV, n, a.n_fin, a.fin, a.slots, a.S, kv, d, a.nh, static_cast<T*>(b.O), s);
+  gemm<T, PF_ADD>(b.O, n, d, lw.Wo, nullptr, nullptr, d, 1, b.X, d, nullptr, s);
+  hipLaunchKernelGGL(k_pf_norm<T>, dim3(n), dim3(256), 0, s, b.X, lw.g2, A, d, a.eps);
+  gemm<T, PF_SWIGLU>(A, n, d, lw.Wg, lw.Wu, nullptr, F, 2, nullptr, 0, b.ACT, s);
+  gemm<T, PF_ADD>(b.ACT, n, F, lw.Wd, nullptr, nullptr, d, 1, b.X, d, nullptr, s);
+}
+
+template <typename T>
+hipError_t run(const PrefillArgs& a, hipStream_t s) {
+  const size_t ent = (size_t)2 * a.d;                                    // elements per cache entry
+  const size_t blk = (size_t)a.S * ent;                                  // elements per cache block
+  hipLaunchKernelGGL(k_pf_embed<T>, dim3(a.n), dim3(256), 0, s, a.tokens, a.slots, a.n, a.fin, a.n_fin, a.S,
+                     static_cast<const T*>(a.emb), a.V, a.d, a.b.X, a.err);
+  for (int l = 0; l < a.L_pre; ++l)
+    layer<T>(a, a.pre[l], static_cast<T*>(a.kv_pre) + l * blk, false, s);
+  for (int k = 1; k <= a.R; ++k) {
+    for (int l = 0; l < a.L; ++l)
+      layer<T>(a, a.core[l], static_cast<T*>(a.kv_core) + ((size_t)(k - 1) * a.L + l) * blk, false, s);
+    // coda caches at readout depth k (index ri): the coda layers on a copy of H^(k)
+    int ri = -1;
+    for (int j = 0; j < a.n_readout; ++j)
+      if (a.readout_depths[j] == k) ri = j;
+    if (ri >= 0 && a.L_coda && (a.coda_mask >> ri & 1)) {
+      const hipError_t e = hipMemcpyAsync(a.b.Xc, a.b.X, (size_t)a.n * a.d * 4, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return e;
+      PrefillArgs c = a;
+      std::swap(c.b.X, c.b.Xc);
+      for (int l = 0; l < a.L_coda; ++l)
+        layer<T>(c, a.coda[l], static_cast<T*>(a.kv_coda) + ((size_t)ri * a.L_coda + l) * blk,
+                 l == a.L_coda - 1, s);
+    }
+  }
+  hipLaunchKernelGGL(k_pf_scatter, dim3(a.n), dim3(256), 0, s, a.b.X, a.slots, a.S, a.d, a.H);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t prefill_bytes(int n, int d, int F, bool bf16) {
+  const size_t es = bf16 ? 2 : 4;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return al((size_t)n * d * 4) * 2                                       // X, Xc
+         + al((size_t)n * d * es)                                         // A
+         + al((size_t)n * 3 * d * 4)                                      // QKV
+         + al((size_t)n * d * es)                                         // O
+         + al((size_t)n * F * es);                                        // ACT
+}
+
+PrefillBufs prefill_carve(void* base, int n, int d, int F, bool bf16) {
+  const size_t es = bf16 ? 2 : 4;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  char* p = static_cast<char*>(base);
+  PrefillBufs b;
+  b.X = reinterpret_cast<float*>(p); p += al((size_t)n * d * 4);
+  b.Xc = reinterpret_cast<float*>(p); p += al((size_t)n * d * 4);
+  b.A = p; p += al((size_t)n * d * es);
+  b.QKV = reinterpret_cast<float*>(p); p += al((size_t)n * 3 * d * 4);
+  b.O = p; p += al((size_t)n * d * es);
+  b.ACT = p;
+  return b;
+}
+
+hipError_t launch_prefill(bool bf16, const PrefillArgs& a, hipStream_t s) {
+  return bf16 ? run<uint16_t>(a, s) : run<float>(a, s);
+}
+
+}  // namespace ls

@@ -171,13 +171,20 @@ class Decoder:
         return [(lg[i].copy(), pr[j].copy()) for i, j in zip(rows, prob_rows)]
 
     # ---- prefill ----------------------------------------------------------------------
-    def prefill(self, prompt, chunk=None, progress=None):
+    def prefill(self, prompt, chunk=None, progress=None, fast=None):
         """Run the prompt through P, all R loops and the readouts, then commit the first new
         token from p_R of the last prompt position.  Not part of the timed decode.
-        `progress(done, total)`, if given, is called after each chunk of prompt positions."""
+        `progress(done, total)`, if given, is called after each chunk of prompt positions.
+        fast (default: whenever the engine offers it): ls_prefill per chunk of prompt
+        positions (every depth as large-M matrix products), then one readout of the last
+        position; otherwise chunks of at most max_rows positions through the decode calls."""
         cfg, e = self.cfg, self.e
         prompt = [int(t) for t in prompt]
         T0 = len(prompt)
+        if fast is None:
+            fast = hasattr(e, "prefill")
+        if fast:
+            return self._prefill_fast(prompt, chunk or e.prefill_chunk, progress)
         chunk = chunk or e.max_rows
         last_row = -1
         for c0 in range(0, T0, chunk):
@@ -208,6 +215,34 @@ class Decoder:
             self._fin_append(slots)
             if progress is not None:
                 progress(c0 + n, T0)
+        return self._first_token(prompt, last_row)
+
+    def _prefill_fast(self, prompt, chunk, progress):
+        cfg, e = self.cfg, self.e
+        T0 = len(prompt)
+        # coda caches: every readout depth a later decode step may read (spec), R only (AR)
+        mask = (1 << len(self.D)) - 1 if self.mode == "spec" else 1 << self.didx[cfg.R]
+        slots = []
+        for c0 in range(0, T0, chunk):
+            toks = prompt[c0:c0 + chunk]
+            slots = [self._slot() for _ in toks]
+            e.prefill(toks, slots, c0, self.fin_ptr, mask)
+            self._fin_append(slots)
+            if progress is not None:
+                progress(c0 + len(toks), T0)
+        # p_R of the last position: its readout over the committed prefix before it
+        last_row = self._prob()
+        rr = e.rows([slots[-1]], [T0 - 1], [self.didx[cfg.R]], T0 - 1, [[]], self.fin_ptr,
+                    extra=[np.asarray([last_row], np.int32)])
+        e.readout(rr, self.dec.greedy, self.dec.T, self.dec.top_p, rr.extra[0], **self._trace_args(1))
+        if self.trace:
+            self.prefill_trace = {cfg.R: self._trace_rows([0], [last_row])[0]}
+        return self._first_token(prompt, last_row)
+
+    def _first_token(self, prompt, last_row):
+        """Commit the first new token, drawn from the prefill's p_R row."""
+        e = self.e
+        T0 = len(prompt)
         self.prompt_len = T0
         self.tokens = list(prompt)
         job = np.zeros((1, 10), np.int32)

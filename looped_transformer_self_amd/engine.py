@@ -207,6 +207,9 @@ class Engine:
         self._vin_jobs = max_jobs
         self.vin_host = torch.zeros(max_jobs * (10 + 24 + 16), dtype=torch.int32, pin_memory=True)
         self.vin_np = self.vin_host.numpy()
+        self.pws = None           # prefill scratch (allocated at the first prefill, sized for its chunk)
+        self.pws_bytes = 0
+        self.prefill_chunk = 2048 # prompt positions per ls_prefill call
         self.prof = None          # list of (start event, end event, row metadata) when profiling
         self.n_loop_calls = 0     # ls_loop_step launches with at least one row, since creation
 
@@ -221,7 +224,8 @@ class Engine:
         L.lib.ls_model_destroy(self.h)
         self.h = None
         self.up.close()
-        for name in ("kv_core", "kv_pre", "kv_coda", "H", "probs", "ws", "w", "layers", "vout_host", "vin_host"):
+        for name in ("kv_core", "kv_pre", "kv_coda", "H", "probs", "ws", "pws", "w", "layers", "vout_host",
+                     "vin_host"):
             setattr(self, name, None)
         self.vin_np = None
 
@@ -307,6 +311,20 @@ class Engine:
     def prelude(self, rows, tokens_ptr):
         L.check(L.lib.ls_prelude(self.h, C.byref(rows.s), tokens_ptr, _ptr(self.H), C.byref(self.kv),
                                  self.stream_ptr()), "ls_prelude")
+
+    def prefill(self, tokens, slots, n_fin, fin_ptr, coda_mask):
+        """ls_prefill of one chunk of prompt positions n_fin .. n_fin + len(tokens) - 1 into
+        `slots` (the committed prefix's slot table at fin_ptr), H[slots] = H^(R) afterwards."""
+        n = len(tokens)
+        need = int(L.lib.ls_prefill_workspace_bytes(self.h, n))
+        if self.pws is None or self.pws_bytes < need:
+            self.pws = None
+            self.pws = torch.empty(need + 256, dtype=torch.uint8, device=self.dev)
+            self.pws_bytes = need
+        ptr = self.pws.data_ptr() + (-self.pws.data_ptr()) % 256
+        arrs, _keep = self.up.pack([np.asarray(tokens, np.int32), np.asarray(slots, np.int32)])
+        L.check(L.lib.ls_prefill(self.h, arrs[0], arrs[1], n, fin_ptr, int(n_fin), int(coda_mask), _ptr(self.H),
+                                 C.byref(self.kv), C.c_void_p(ptr), self.pws_bytes, self.stream_ptr()), "ls_prefill")
 
     def loop_step(self, rows):
         if self.prof is not None and rows.n:
