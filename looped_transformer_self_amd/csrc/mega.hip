@@ -329,8 +329,8 @@ __host__ __device__ inline LdsPlan lds_plan(int M, int esz, int d) {
 #ifndef LS_NS_MAX
 #define LS_NS_MAX 18
 #endif
-  const int ns_opts[5] = {LS_NS_MAX, LS_NS_MAX - 2, LS_NS_MAX - 4, LS_NS_MAX - 6, 8};
-  for (int i = 0; i < 5; ++i)
+  const int ns_opts[6] = {LS_NS_MAX, LS_NS_MAX - 2, LS_NS_MAX - 4, LS_NS_MAX - 6, LS_NS_MAX - 8, 8};
+  for (int i = 0; i < 6; ++i)
     if (lds_bytes_for(M, esz, ns_opts[i], xfull, 2, d) <= LDS_BUDGET) return LdsPlan{ns_opts[i], xfull, 2};
   // many rows: narrower activation chunks first, then a shallower ring (down to 4 slabs, one
   // per consumer), so every row count up to the workspace maximum fits

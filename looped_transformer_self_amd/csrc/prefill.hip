@@ -26,17 +26,25 @@ namespace ls {
 namespace {
 
 // ---- matrix product C = X W^T over 128 x 128 tiles -------------------------------------------
-// X: activation rows [M][K] (model dtype); W: weight rows [N][K].  A workgroup of 4 waves
-// computes 128 weight rows x 128 activation rows; wave (wn, wx) a 64 x 64 quarter as 4 x 4
-// MFMA blocks of 16 x 16 (A = 16 weight rows, B = 16 activation rows; lane l holds weight
-// rows 4*(l/16) + j of activation row l%16 of a block).  K advances 128 bytes per stage
-// (64 bf16 or 32 fp32); a stage of both operands (2 x 16 KB) sits in LDS as rows of eight
-// 16-byte chunks, chunk c of row r at c ^ (r & 7) so the 16 rows an MFMA operand read touches
-// fall on distinct banks.  Two LDS stages: the next stage's global loads are in flight while
-// the current one is multiplied.
+// X: activation rows [M][K] (model dtype); W: weight rows [N][K].  A workgroup computes 128
+// weight rows x 128 activation rows.  Two producer waves stream the operands into a ring of
+// GNST LDS stages with direct-to-LDS 16-byte loads (producer 0 the weight tile, producer 1 the
+// activation tile; 128 bytes of K per row per stage), keeping GNST - 1 stages in flight; four
+// consumer waves multiply: consumer (wn, wx) a 64 x 64 quarter as 4 x 4 MFMA blocks of 16 x 16
+// (A = 16 weight rows, B = 16 activation rows; lane l holds weight rows 4*(l/16) + j of
+// activation row l%16 of a block).  A stage holds each tile as rows of eight 16-byte chunks,
+// chunk c of row r at c ^ (r & 7) (the producers pick each lane's source chunk so the loads
+// land that way), so the 16 rows an MFMA operand read touches fall on distinct banks.  One
+// workgroup barrier per stage: a producer passes it once its loads of that stage have landed,
+// and issues the stage GNST - 1 ahead only after it, when every consumer is done with the
+// buffer that stage reuses.
 constexpr int GT = 128;              // tile rows (both operands)
 constexpr int GCH = 8;               // 16-byte chunks per tile row per stage
-constexpr int GTHREADS = 256;
+constexpr int GNST = 4;              // LDS stages
+constexpr int GCONS = 4, GPROD = 2;
+constexpr int GTHREADS = 64 * (GCONS + GPROD);
+constexpr int GSTAGE = 2 * GT * GCH * 16;   // bytes of one stage: weight tile, then activation tile
+constexpr int GLOADS = GT / 8;       // load instructions per producer wave per stage (8 rows each)
 
 enum PfMode { PF_STORE = 0, PF_ADD = 1, PF_SWIGLU = 2 };
 
@@ -66,95 +74,105 @@ template <> struct PfMma<float> {
   }
 };
 
+// Wait until at most N vector memory instructions of this wave are outstanding.
+template <int N>
+LS_DEV void vm_wait() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 template <typename T, int MODE>
 __global__ __launch_bounds__(GTHREADS) void k_pf_gemm(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) char gsm[];
-  u32x4_t* const Ws = reinterpret_cast<u32x4_t*>(gsm);                  // [2][GT][GCH]
-  u32x4_t* const Xs = Ws + 2 * GT * GCH;                                // [2][GT][GCH]
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // tile of this workgroup: workgroups are placed on the 8 XCDs round-robin; consecutive tile
   // numbers (which share a weight tile) go to one XCD so its L2 serves their weight reads
   const int nt = g.n_wt * g.n_xt, gid = blockIdx.x;
   const int q8 = nt >> 3, r8 = nt & 7, x8 = gid & 7;
   const int t = x8 * q8 + min(x8, r8) + (gid >> 3);
   const int wt = t / g.n_xt, xt = t - wt * g.n_xt;
-  const size_t rb = (size_t)g.K * sizeof(T);                            // bytes per row
-  const int nst = (int)((rb + 16 * GCH - 1) / (16 * GCH));              // stages
+  const int rb = g.K * (int)sizeof(T);                                  // bytes per row
+  const int nst = (rb + 16 * GCH - 1) / (16 * GCH);                     // stages
+  const bool tail = rb % (16 * GCH) != 0;                               // last stage: one 64-byte k-step
 
-  // this thread's load rows: r = tid/8 + 32 i, chunk tid % 8
-  const int lch = tid & 7;
-  const char* wp[4];
-  const char* xp[4];
+  if (w >= GCONS) {
+    // ------------------------------ producer waves ------------------------------
+    const int p = w - GCONS, pos = lane & 7;
+    const char* src[GLOADS];
+    int cb[GLOADS];                                                     // byte offset of the lane's chunk
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    int mat, n;
-    if (MODE == PF_SWIGLU) {
-      const int b = r >> 4;
-      mat = b & 1;
-      n = wt * 64 + (b >> 1) * 16 + (r & 15);
-    } else {
-      const int tpm = (g.Nb + GT - 1) / GT;
-      mat = wt / tpm;
-      n = (wt - mat * tpm) * GT + r;
+    for (int i = 0; i < GLOADS; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      cb[i] = 16 * (pos ^ (r & 7));
+      if (p == 0) {
+        int mat, n;
+        if (MODE == PF_SWIGLU) {                                        // 16-row blocks alternate gate / up
+          const int blk = r >> 4;
+          mat = blk & 1;
+          n = wt * 64 + (blk >> 1) * 16 + (r & 15);
+        } else {
+          const int tpm = (g.Nb + GT - 1) / GT;
+          mat = wt / tpm;
+          n = (wt - mat * tpm) * GT + r;
+        }
+        src[i] = static_cast<const char*>(g.W[mat]) + (size_t)min(n, g.Nb - 1) * rb;   // rows past Nb: never stored
+      } else {
+        src[i] = static_cast<const char*>(g.X) + (size_t)min(xt * GT + r, g.M - 1) * rb;  // rows past M: never stored
+      }
     }
-    wp[i] = static_cast<const char*>(g.W[mat]) + (size_t)min(n, g.Nb - 1) * rb + 16 * lch;
-    xp[i] = static_cast<const char*>(g.X) + (size_t)min(xt * GT + r, g.M - 1) * rb + 16 * lch;
+    auto issue = [&](int st) {
+      char* dst = gsm + (st % GNST) * GSTAGE + p * (GSTAGE / 2);
+      const int off = st * 16 * GCH;
+#pragma unroll
+      for (int i = 0; i < GLOADS; ++i) {
+        // a chunk past the row end (second half of a ragged last stage, never multiplied):
+        // load the row's first chunk instead, so every address stays inside the row
+        const int o = off + cb[i] < rb ? off + cb[i] : 0;
+        __builtin_amdgcn_global_load_lds(src[i] + o, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+      }
+    };
+    for (int st = 0; st < GNST - 1 && st < nst; ++st) issue(st);
+    for (int st = 0; st < nst; ++st) {
+      const int newer = min(nst, st + GNST - 1) - st - 1;               // stages issued after st
+      if (newer >= 2) vm_wait<2 * GLOADS>();
+      else if (newer == 1) vm_wait<GLOADS>();
+      else vm_wait<0>();
+      asm volatile("s_barrier" ::: "memory");                           // stage st is in LDS
+      if (st + GNST - 1 < nst) issue(st + GNST - 1);
+    }
+    return;
   }
-  u32x4_t wv[4], xv[4];
-  auto gload = [&](int st) {
-    const size_t off = (size_t)st * 16 * GCH;
-    const bool ok = off + 16 * lch < rb;                                // K tail: zeros
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wv[i] = ok ? *reinterpret_cast<const u32x4_t*>(wp[i] + off) : u32x4_t{0u, 0u, 0u, 0u};
-      xv[i] = ok ? *reinterpret_cast<const u32x4_t*>(xp[i] + off) : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      const int c = (buf * GT + r) * GCH + (lch ^ (r & 7));
-      Ws[c] = wv[i];
-      Xs[c] = xv[i];
-    }
-  };
 
+  // ------------------------------ consumer waves ------------------------------
   const int wn = w & 1, wx = w >> 1;
   f32x4_t acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
   const int fr = lane & 15, fq = lane >> 4;
   for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) gload(st + 1);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    __syncthreads();
+    const u32x4_t* const Ws = reinterpret_cast<const u32x4_t*>(gsm + (st % GNST) * GSTAGE);
+    const u32x4_t* const Xs = Ws + GT * GCH;
+    const int nk = tail && st == nst - 1 ? 1 : 2;
+    for (int s = 0; s < nk; ++s) {
       u32x4_t af[4], bf[4];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int r = wn * 64 + a * 16 + fr;
-        af[a] = Ws[(buf * GT + r) * GCH + ((s * 4 + fq) ^ (r & 7))];
+        af[a] = Ws[r * GCH + ((s * 4 + fq) ^ (r & 7))];
       }
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int r = wx * 64 + b * 16 + fr;
-        bf[b] = Xs[(buf * GT + r) * GCH + ((s * 4 + fq) ^ (r & 7))];
+        bf[b] = Xs[r * GCH + ((s * 4 + fq) ^ (r & 7))];
       }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) PfMma<T>::run(acc[a][b], af[a], bf[b]);
     }
-    if (st + 1 < nst) sstore(buf ^ 1);
-    __syncthreads();
   }
 
   // epilogue: block (a, b) holds weight rows wn*64 + a*16 + 4*fq + j of activation row
@@ -204,8 +222,7 @@ void gemm(const void* X, int M, int K, const void* W0, const void* W1, const voi
   g.n_wt = MODE == PF_SWIGLU ? (Nb + 63) / 64 : nmat * ((Nb + GT - 1) / GT);
   g.n_xt = (M + GT - 1) / GT;
   g.out = out; g.ldo = ldo; g.act = act;
-  const size_t smem = (size_t)4 * GT * GCH * 16;
-  hipLaunchKernelGGL((k_pf_gemm<T, MODE>), dim3(g.n_wt * g.n_xt), dim3(GTHREADS), smem, s, g);
+  hipLaunchKernelGGL((k_pf_gemm<T, MODE>), dim3(g.n_wt * g.n_xt), dim3(GTHREADS), (size_t)GNST * GSTAGE, s, g);
 }
 
 // ---- row kernels --------------------------------------------------------------------------------
@@ -404,6 +421,184 @@ __global__ __launch_bounds__(256) void k_pf_attn(const float* Q, int ldq, int n,
   }
 }
 
+// ---- causal attention of the chunk on the matrix cores (bf16 caches) -------------------------
+// Workgroup (query block of 64 rows, head); wave w takes queries 16w .. 16w + 15 of the block.
+// Keys arrive in blocks of 64: K rows [key][hd] and V transposed [hd][key] in LDS (bf16, as
+// cached).  Scores S = K q^T come out of v_mfma_f32_16x16x32_bf16 with A = 16 keys x 32 dims
+// of K and B = 32 dims x 16 queries; the fp32 query (scaled by 1/sqrt(hd)) enters as two bf16
+// terms, q = hi + lo with lo the rounding residual, so the products keep ~16 significant
+// bits of q (the key is exactly bf16) and accumulate in fp32.  Lane l then holds the scores
+// of query l%16 for keys 16b + 4(l/16) + j; the four lanes of a query meet by shuffles for the
+// online-softmax maximum and sum (fp32).  The same lane's eight weights of keys
+// {32c + 4(l/16) + j, 32c + 16 + 4(l/16) + j} are its B operand of O^T += V^T P^T (again as
+// hi + lo bf16 terms), with A = 16 dims x those 8 keys read from the transposed V: no
+// exchange of weights between lanes.  Lane l accumulates dims 16e + 4(l/16) + j of query l%16.
+constexpr int AKB = 64;                                  // keys per block
+
+template <int HD> struct MAttLds {
+  static constexpr int KS = HD + 8;                      // K row stride (elements)
+  static constexpr int VS = AKB + 4;                     // V^T row stride (elements)
+  static constexpr size_t bytes = (size_t)(AKB * KS + HD * VS) * 2;
+};
+
+LS_DEV void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - bf2f(hi));
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_pf_attn_mfma(const float* Q, int ldq, int n, int n_fin, const int32_t* fin,
+                                                      const int32_t* slots, long long S, const uint16_t* kv, int d,
+                                                      uint16_t* O, float scale) {
+  constexpr int NC = HD / 32, NE = HD / 16, CPR = HD / 8;   // dim chunks, dim blocks, 16-byte chunks per row
+  constexpr int LPT = (AKB * CPR + 255) / 256;               // 16-byte loads per thread per operand
+  extern __shared__ __attribute__((aligned(16))) char msm[];
+  uint16_t* const Ks = reinterpret_cast<uint16_t*>(msm);
+  uint16_t* const Vt = Ks + AKB * MAttLds<HD>::KS;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int qn = lane & 15, g = lane >> 4;
+  const int q0 = blockIdx.x * AKB, h = blockIdx.y;
+  const int qlast = min(q0 + AKB, n) - 1;
+  const int tmax = n_fin + qlast;
+  const int qrow = q0 + 16 * w + qn;                          // this lane's query (chunk row)
+  const int qpos = n_fin + qrow;                              // its position
+
+  // the query's B fragments: dims 32c + 8g .. +7, hi and lo terms
+  u32x4_t qh[NC], ql[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    uint16_t hv[8], lv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = qrow < n ? Q[(size_t)qrow * ldq + h * HD + 32 * c + 8 * g + i] * scale : 0.f;
+      split_bf16(x, hv[i], lv[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qh[c][i] = (unsigned)hv[2 * i] | ((unsigned)hv[2 * i + 1] << 16);
+      ql[c][i] = (unsigned)lv[2 * i] | ((unsigned)lv[2 * i + 1] << 16);
+    }
+  }
+  f32x4_t acc[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lsum = 0.f;
+
+  // this thread's 16-byte pieces of a key block: key r = idx / CPR, chunk idx % CPR
+  u32x4_t kr[LPT], vr[LPT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int idx = tid + 256 * u;
+      if (idx < AKB * CPR) {
+        const int r = idx / CPR, ch = idx - r * CPR;
+        const int t = k0 + r;
+        int sl = t < n_fin ? fin[t] : (t < n_fin + n ? slots[t - n_fin] : 0);
+        sl = sl >= 0 && sl < S ? sl : 0;
+        const uint16_t* ent = kv + (size_t)sl * 2 * d + h * HD + 8 * ch;
+        kr[u] = *reinterpret_cast<const u32x4_t*>(ent);
+        vr[u] = *reinterpret_cast<const u32x4_t*>(ent + d);
+      }
+    }
+  };
+  gload(0);
+  for (int k0 = 0; k0 <= tmax; k0 += AKB) {
+    __syncthreads();                                            // previous block's reads done
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int idx = tid + 256 * u;
+      if (idx < AKB * CPR) {
+        const int r = idx / CPR, ch = idx - r * CPR;
+        *reinterpret_cast<u32x4_t*>(Ks + r * MAttLds<HD>::KS + 8 * ch) = kr[u];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Vt[(8 * ch + 2 * i) * MAttLds<HD>::VS + r] = (uint16_t)(vr[u][i] & 0xffffu);
+          Vt[(8 * ch + 2 * i + 1) * MAttLds<HD>::VS + r] = (uint16_t)(vr[u][i] >> 16);
+        }
+      }
+    }
+    __syncthreads();
+    if (k0 + AKB <= tmax) gload(k0 + AKB);                      // next block in flight meanwhile
+
+    // scores of this lane's query for keys k0 + 16b + 4g + j
+    f32x4_t sc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      sc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(Ks + (16 * b + qn) * MAttLds<HD>::KS + 32 * c + 8 * g);
+        PfMma<uint16_t>::run(sc[b], ka, qh[c]);
+        PfMma<uint16_t>::run(sc[b], ka, ql[c]);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = k0 + 16 * b + 4 * g + j;
+        if (t > qpos || t >= n_fin + n) sc[b][j] = -INFINITY;
+        mx = fmaxf(mx, sc[b][j]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(mrun, mx);                         // finite: key 0 <= every position
+    const float al = expf(mrun - mnew);
+    float ps = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sc[b][j] = expf(sc[b][j] - mnew);
+        ps += sc[b][j];
+      }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    lsum = lsum * al + ps;
+    mrun = mnew;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[e][j] *= al;
+    // O^T += V^T P^T over the two 32-key chunks
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint16_t ph[8], pl[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        split_bf16(sc[2 * c][j], ph[j], pl[j]);
+        split_bf16(sc[2 * c + 1][j], ph[4 + j], pl[4 + j]);
+      }
+      u32x4_t pbh, pbl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pbh[i] = (unsigned)ph[2 * i] | ((unsigned)ph[2 * i + 1] << 16);
+        pbl[i] = (unsigned)pl[2 * i] | ((unsigned)pl[2 * i + 1] << 16);
+      }
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const uint16_t* vrow = Vt + (16 * e + qn) * MAttLds<HD>::VS + 32 * c + 4 * g;
+        const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
+        const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
+        const u32x4_t va = u32x4_t{v0.x, v0.y, v1.x, v1.y};
+        PfMma<uint16_t>::run(acc[e], va, pbh);
+        PfMma<uint16_t>::run(acc[e], va, pbl);
+      }
+    }
+  }
+  if (qrow < n) {
+    const float inv = 1.0f / lsum;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      uint16_t* dst = O + (size_t)qrow * d + h * HD + 16 * e + 4 * g;
+      const unsigned lo = (unsigned)f2bf(acc[e][0] * inv) | ((unsigned)f2bf(acc[e][1] * inv) << 16);
+      const unsigned hi = (unsigned)f2bf(acc[e][2] * inv) | ((unsigned)f2bf(acc[e][3] * inv) << 16);
+      *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{lo, hi};
+    }
+  }
+}
+
 template <typename T, int HD>
 void attn_hd(const float* Q, int n, int n_fin, const int32_t* fin, const int32_t* slots, long long S, const T* kv, int d,
              int nh, T* O, hipStream_t s) {
@@ -411,9 +606,28 @@ void attn_hd(const float* Q, int n, int n_fin, const int32_t* fin, const int32_t
                      n_fin, fin, slots, S, kv, d, O, 1.0f / sqrtf((float)HD));
 }
 
+template <int HD>
+void attn_mfma(const float* Q, int n, int n_fin, const int32_t* fin, const int32_t* slots, long long S,
+               const uint16_t* kv, int d, int nh, uint16_t* O, hipStream_t s) {
+  hipLaunchKernelGGL((k_pf_attn_mfma<HD>), dim3((n + AKB - 1) / AKB, nh), dim3(256), MAttLds<HD>::bytes, s, Q, 3 * d,
+                     n, n_fin, fin, slots, S, kv, d, O, 1.0f / sqrtf((float)HD));
+}
+
 template <typename T>
 void attn(int hd, const float* Q, int n, int n_fin, const int32_t* fin, const int32_t* slots, long long S, const T* kv,
           int d, int nh, T* O, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    // bf16 caches: the matrix-core kernel for head dims it tiles (multiples of 32)
+    const uint16_t* k16 = reinterpret_cast<const uint16_t*>(kv);
+    uint16_t* o16 = reinterpret_cast<uint16_t*>(O);
+    switch (hd) {
+      case 32: return attn_mfma<32>(Q, n, n_fin, fin, slots, S, k16, d, nh, o16, s);
+      case 64: return attn_mfma<64>(Q, n, n_fin, fin, slots, S, k16, d, nh, o16, s);
+      case 96: return attn_mfma<96>(Q, n, n_fin, fin, slots, S, k16, d, nh, o16, s);
+      case 128: return attn_mfma<128>(Q, n, n_fin, fin, slots, S, k16, d, nh, o16, s);
+      default: break;
+    }
+  }
   switch (hd) {
     case 16: attn_hd<T, 16>(Q, n, n_fin, fin, slots, S, kv, d, nh, O, s); break;
     case 32: attn_hd<T, 32>(Q, n, n_fin, fin, slots, S, kv, d, nh, O, s); break;

@@ -147,6 +147,31 @@ def test_prefill_full_size_ouro():
     print(f"[prefill] C2 shape: H^(R) worst rel {worst:.2e}", flush=True)
 
 
+def test_prefill_full_size_huginn_depth_R():
+    """Huginn-3.5B shape, 48 positions: H^(R) after all 32 loop iterations and the loop
+    caches of every depth against the reference, bounded by the float32-products reference's
+    own distance (32 iterations of a random-init block carry rounding-level differences to a
+    few per cent)."""
+    wl = configs.get("C4")
+    cfg = wl.model
+    w = weights.make_weights(cfg, seed=wl.decode.seed_w)
+    prompt = [int(t) for t in inputs.prompt(cfg.V, 48, seed=1)]
+    slots, H, kv = _gpu_prefill(cfg, w, prompt, (48,), 1 << (len(cfg.readout_depths) - 1), S=64)
+    print("[prefill] C4 shape, depth R: GPU done; reference passes", flush=True)
+    seqs = []
+    for products in ("f64", "f32"):
+        s = Model(cfg, w, products=products).new_seq()
+        _, hid = s.extend(prompt, depths=(cfg.R,), last_only=False, keep_hidden=True)
+        seqs.append((s, hid))
+        gc.collect()
+    (seq, hid), (alt, hid_alt) = seqs
+    worst = _rows_close(H, hid[cfg.R], hid_alt[cfg.R], tol(cfg), "H^(R)")
+    n = _check_caches(cfg, kv, slots, seq, alt, 1 << (len(cfg.readout_depths) - 1), range(1, cfg.R + 1))
+    alt_d = max(rel_l2(hid_alt[cfg.R][i], hid[cfg.R][i]) for i in range(len(prompt)))
+    print(f"[prefill] C4 shape: H^(R) worst rel {worst:.2e} (float32-products reference {alt_d:.2e}); "
+          f"{n} caches checked", flush=True)
+
+
 def test_prefill_full_size_huginn():
     """Huginn-3.5B shape (d 5280 = 41 x 128 + 32, 55 x 96 heads, F 17920, prelude 2, core 4),
     140 positions in chunks of 130 and 10: the prelude caches and the loop caches of depths
