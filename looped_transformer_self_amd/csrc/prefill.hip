@@ -40,7 +40,10 @@ namespace {
 // buffer that stage reuses.
 constexpr int GT = 128;              // tile rows (both operands)
 constexpr int GCH = 8;               // 16-byte chunks per tile row per stage
-constexpr int GNST = 4;              // LDS stages
+#ifndef LS_PF_STAGES
+#define LS_PF_STAGES 4
+#endif
+constexpr int GNST = LS_PF_STAGES;   // LDS stages
 constexpr int GCONS = 4, GPROD = 2;
 constexpr int GTHREADS = 64 * (GCONS + GPROD);
 constexpr int GSTAGE = 2 * GT * GCH * 16;   // bytes of one stage: weight tile, then activation tile
