@@ -74,6 +74,17 @@ __host__ __device__ inline int att_heads_per_block(int nh, int hd, int esz) {
   h = h < 1 ? 1 : (h > 8 ? 8 : h);
   return h < nh ? h : nh;
 }
+// Workgroups of a G-workgroup launch that take the N attention tiles of a layer: each takes at
+// least LS_ATT_TMIN tiles (a segment's partials are merged by one workgroup, a memory round trip
+// per 16 of them, so spreading few tiles over many workgroups lengthens the merge).
+#ifndef LS_ATT_TMIN
+#define LS_ATT_TMIN 3
+#endif
+__host__ __device__ inline int att_workgroups(int G, int N) {
+  int g = N / LS_ATT_TMIN;
+  g = g < 1 ? 1 : g;
+  return g < G ? g : G;
+}
 // Most workgroups a launch of the layer kernel uses (4 per CU on 256 CUs).
 constexpr int MEGA_MAX_GRID = 1024;
 // Partials per (row, head) that a workspace for keys up to max_keys holds: the workgroups that

@@ -342,7 +342,7 @@ ls_status run_mega(ls_model* m, const ls_rows* r, int i0, int mc, float* H, cons
                   G, need, m->w.att_pmax);
     // partials of the launch's segments (one row per virtual group): the workgroups that hold
     // tiles of a segment, by the same contiguous deal as the kernel's
-    const long long N = (long long)mc * n_hb * n_kt, Ga = std::min<long long>(G, N);
+    const long long N = (long long)mc * n_hb * n_kt, Ga = att_workgroups(G, (int)N);
     auto owner = [&](long long t) { return ((t + 1) * Ga - 1) / N; };
     int npf = 1;
     for (long long sg = 0; sg < (long long)mc * n_hb; ++sg)

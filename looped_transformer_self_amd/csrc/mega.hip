@@ -487,8 +487,10 @@ LS_DEV PhaseShare phase_share(int n, int deal, int G, int b) {
   return PhaseShare{sh.first, sh.count};
 }
 
-// The residual phases (O, DOWN) have only d/16 tiles, often fewer than two per workgroup, so
-// they are dealt by slabs (stream-K): workgroup b < Gs = min(G, n * nk) takes the phase's slabs
+// The residual phases (O, DOWN) have only d/16 tiles, often between one and two per workgroup,
+// so when there are more tiles than workgroups they are dealt by slabs (stream-K; with at most
+// one tile per workgroup whole tiles are balanced already and need no combining of partial
+// sums): workgroup b < Gs = min(G, n * nk) takes the phase's slabs
 // [b * n * nk / Gs, (b + 1) * n * nk / Gs) in tile-major order, as units (tile, slabs
 // [k0, k1)).  A tile whose slabs span several (consecutive) workgroups is split: each leaves
 // its partial sum, and the last to arrive adds them in workgroup order and runs the epilogue.
@@ -516,7 +518,7 @@ struct Units {
 };
 LS_DEV Units units_of(int ph, int n_tiles, int nk, int deal, int G, int b) {
   Units u;
-  u.split = split_phase(ph);
+  u.split = split_phase(ph) && n_tiles > G;   // at most one tile per workgroup: whole tiles
   u.nk = nk;
   u.sh = PhaseShare{0, 0};
   u.S0 = u.S1 = 0;
@@ -1152,9 +1154,9 @@ LS_DEV AttGeo att_geo(const MegaArgs& a, int n_vg) {
   g.N = n_vg * g.n_hb * g.n_kt;
   return g;
 }
-// Workgroup b < Ga = min(G, N) takes tiles [b*N/Ga, (b+1)*N/Ga) (a share of at least one tile, so
-// that the workgroups holding a segment's tiles are consecutive); the owner of tile t.
-LS_DEV int att_grid(int N) { return min((int)gridDim.x, N); }
+// Workgroup b < Ga = att_workgroups(G, N) takes tiles [b*N/Ga, (b+1)*N/Ga) (a share of at least
+// one tile, so that the workgroups holding a segment's tiles are consecutive); the owner of tile t.
+LS_DEV int att_grid(int N) { return att_workgroups((int)gridDim.x, N); }
 LS_DEV int att_owner(int t, int N, int Ga) { return (int)(((long long)(t + 1) * Ga - 1) / N); }
 
 // Two adjacent elements of a K/V entry written by this launch (agent-coherent load).
@@ -1384,7 +1386,10 @@ LS_DEV void att_merge2(const MegaArgs& a, const Lds& s, int l, int blk, int i, i
   }
   float run_m = -INFINITY, den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
   constexpr int NK = 4;                             // own keys per batch
-  constexpr int NPB = 16;                           // prefix partials per batch (at most 32)
+#ifndef LS_ATT_NPB
+#define LS_ATT_NPB 16
+#endif
+  constexpr int NPB = LS_ATT_NPB;                   // prefix partials per batch (at most 32)
   const int nbat = max((np + NPB - 1) / NPB, (nt + NK - 1) / NK);
   for (int bt = 0; bt < nbat; ++bt) {
     const int c0 = bt * NPB, j0 = bt * NK;

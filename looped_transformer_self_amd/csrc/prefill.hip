@@ -13,7 +13,9 @@
 //
 // Storage precision is the decode path's: weights, normalised activations, attention
 // outputs, SwiGLU outputs and the K/V cache in the model dtype; residual stream, queries,
-// scores and softmax in fp32.
+// scores and softmax in fp32 (the matrix-core attention of bf16 models feeds the fp32 query
+// and softmax weights to bf16 MFMAs as hi + lo pairs, ~16 significant bits, and accumulates in
+// fp32).
 #include <math.h>
 
 #include <utility>
@@ -651,8 +653,7 @@ void layer(const PrefillArgs& a, const LayerW& lw, T* kv, bool kv_only, hipStrea
   const int n = a.n, d = a.d, F = a.F;
   const PrefillBufs& b = a.b;
   T* A = static_cast<T*>(b.A);
-  const float* g1 = lw.g1;
-  hipLaunchKernelGGL(k_pf_norm<T>, dim3(n), dim3(256), 0, s, b.X, g1, A, d, a.eps);
+  hipLaunchKernelGGL(k_pf_norm<T>, dim3(n), dim3(256), 0, s, b.X, lw.g1, A, d, a.eps);
   gemm<T, PF_STORE>(A, n, d, lw.Wq, lw.Wk, lw.Wv, d, 3, b.QKV, 3 * d, nullptr, s);
   hipLaunchKernelGGL(k_pf_rope<T>, dim3(n), dim3(256), 0, s, b.QKV, n, d, a.hd, a.n_fin, a.invf, a.slots, a.S, kv);
   if (kv_only) return;
