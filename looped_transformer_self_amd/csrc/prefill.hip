@@ -27,29 +27,34 @@ namespace ls {
 
 namespace {
 
-// ---- matrix product C = X W^T over 128 x 128 tiles -------------------------------------------
-// X: activation rows [M][K] (model dtype); W: weight rows [N][K].  A workgroup computes 128
-// weight rows x 128 activation rows.  Two producer waves stream the operands into a ring of
-// GNST LDS stages with direct-to-LDS 16-byte loads (producer 0 the weight tile, producer 1 the
-// activation tile; 128 bytes of K per row per stage), keeping GNST - 1 stages in flight; four
-// consumer waves multiply: consumer (wn, wx) a 64 x 64 quarter as 4 x 4 MFMA blocks of 16 x 16
-// (A = 16 weight rows, B = 16 activation rows; lane l holds weight rows 4*(l/16) + j of
-// activation row l%16 of a block).  A stage holds each tile as rows of eight 16-byte chunks,
-// chunk c of row r at c ^ (r & 7) (the producers pick each lane's source chunk so the loads
-// land that way), so the 16 rows an MFMA operand read touches fall on distinct banks.  One
-// workgroup barrier per stage: a producer passes it once its loads of that stage have landed,
-// and issues the stage GNST - 1 ahead only after it, when every consumer is done with the
-// buffer that stage reuses.
-constexpr int GT = 128;              // tile rows (both operands)
+// ---- matrix product C = X W^T over 256 x 128 tiles -------------------------------------------
+// X: activation rows [M][K] (model dtype); W: weight rows [N][K].  A workgroup computes 256
+// weight rows x 128 activation rows.  Three producer waves stream the operands into a ring of
+// GNST LDS stages with direct-to-LDS 16-byte loads (each producer 128 of the stage's 384 rows,
+// weight rows first; 128 bytes of K per row per stage), keeping GNST - 1 stages in flight;
+// four consumer waves multiply: consumer (wn, wx) a 128 x 64 part as 8 x 4 MFMA blocks of
+// 16 x 16 (A = 16 weight rows, B = 16 activation rows; lane l holds weight rows 4*(l/16) + j
+// of activation row l%16 of a block), so a k-step reads 12 operand fragments from LDS for 32
+// MFMAs.  A stage holds each tile as rows of eight 16-byte chunks, chunk c of row r at
+// c ^ (r & 7) (the producers pick each lane's source chunk so the loads land that way), so the
+// 16 rows an MFMA operand read touches fall on distinct banks.  One workgroup barrier per
+// stage: a producer passes it once its loads of that stage have landed, and issues the stage
+// GNST - 1 ahead only after it, when every consumer is done with the buffer that stage reuses.
+#ifndef LS_PF_WTILE
+#define LS_PF_WTILE 256
+#endif
+constexpr int GWT = LS_PF_WTILE;     // weight rows per tile (128 or 256)
+constexpr int GT = 128;              // activation rows per tile
 constexpr int GCH = 8;               // 16-byte chunks per tile row per stage
+constexpr int GWB = GWT / 32;        // 16-row weight blocks per consumer wave
 #ifndef LS_PF_STAGES
-#define LS_PF_STAGES 4
+#define LS_PF_STAGES (GWT == 128 ? 4 : 3)
 #endif
 constexpr int GNST = LS_PF_STAGES;   // LDS stages
-constexpr int GCONS = 4, GPROD = 2;
+constexpr int GLOADS = 16;           // load instructions per producer wave per stage (8 rows each)
+constexpr int GCONS = 4, GPROD = (GWT + GT) / (8 * GLOADS);
 constexpr int GTHREADS = 64 * (GCONS + GPROD);
-constexpr int GSTAGE = 2 * GT * GCH * 16;   // bytes of one stage: weight tile, then activation tile
-constexpr int GLOADS = GT / 8;       // load instructions per producer wave per stage (8 rows each)
+constexpr int GSTAGE = (GWT + GT) * GCH * 16;   // bytes of one stage: weight tile, then activation tile
 
 enum PfMode { PF_STORE = 0, PF_ADD = 1, PF_SWIGLU = 2 };
 
@@ -102,31 +107,32 @@ __global__ __launch_bounds__(GTHREADS) void k_pf_gemm(GemmArgs g) {
 
   if (w >= GCONS) {
     // ------------------------------ producer waves ------------------------------
+    // producer p loads stage rows [128p, 128p + 128): weight rows first, then activation rows
     const int p = w - GCONS, pos = lane & 7;
     const char* src[GLOADS];
     int cb[GLOADS];                                                     // byte offset of the lane's chunk
 #pragma unroll
     for (int i = 0; i < GLOADS; ++i) {
-      const int r = 8 * i + (lane >> 3);
+      const int r = 128 * p + 8 * i + (lane >> 3);                      // row within the stage
       cb[i] = 16 * (pos ^ (r & 7));
-      if (p == 0) {
+      if (r < GWT) {
         int mat, n;
         if (MODE == PF_SWIGLU) {                                        // 16-row blocks alternate gate / up
           const int blk = r >> 4;
           mat = blk & 1;
-          n = wt * 64 + (blk >> 1) * 16 + (r & 15);
+          n = wt * (GWT / 2) + (blk >> 1) * 16 + (r & 15);
         } else {
-          const int tpm = (g.Nb + GT - 1) / GT;
+          const int tpm = (g.Nb + GWT - 1) / GWT;
           mat = wt / tpm;
-          n = (wt - mat * tpm) * GT + r;
+          n = (wt - mat * tpm) * GWT + r;
         }
         src[i] = static_cast<const char*>(g.W[mat]) + (size_t)min(n, g.Nb - 1) * rb;   // rows past Nb: never stored
       } else {
-        src[i] = static_cast<const char*>(g.X) + (size_t)min(xt * GT + r, g.M - 1) * rb;  // rows past M: never stored
+        src[i] = static_cast<const char*>(g.X) + (size_t)min(xt * GT + r - GWT, g.M - 1) * rb;  // rows past M: never stored
       }
     }
     auto issue = [&](int st) {
-      char* dst = gsm + (st % GNST) * GSTAGE + p * (GSTAGE / 2);
+      char* dst = gsm + (st % GNST) * GSTAGE + p * (128 * GCH * 16);
       const int off = st * 16 * GCH;
 #pragma unroll
       for (int i = 0; i < GLOADS; ++i) {
@@ -150,22 +156,22 @@ __global__ __launch_bounds__(GTHREADS) void k_pf_gemm(GemmArgs g) {
 
   // ------------------------------ consumer waves ------------------------------
   const int wn = w & 1, wx = w >> 1;
-  f32x4_t acc[4][4];
+  f32x4_t acc[GWB][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < GWB; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15, fq = lane >> 4;
   for (int st = 0; st < nst; ++st) {
     __syncthreads();
     const u32x4_t* const Ws = reinterpret_cast<const u32x4_t*>(gsm + (st % GNST) * GSTAGE);
-    const u32x4_t* const Xs = Ws + GT * GCH;
+    const u32x4_t* const Xs = Ws + GWT * GCH;
     const int nk = tail && st == nst - 1 ? 1 : 2;
     for (int s = 0; s < nk; ++s) {
-      u32x4_t af[4], bf[4];
+      u32x4_t af[GWB], bf[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int r = wn * 64 + a * 16 + fr;
+      for (int a = 0; a < GWB; ++a) {
+        const int r = wn * (GWT / 2) + a * 16 + fr;
         af[a] = Ws[r * GCH + ((s * 4 + fq) ^ (r & 7))];
       }
 #pragma unroll
@@ -174,13 +180,13 @@ __global__ __launch_bounds__(GTHREADS) void k_pf_gemm(GemmArgs g) {
         bf[b] = Xs[r * GCH + ((s * 4 + fq) ^ (r & 7))];
       }
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < GWB; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) PfMma<T>::run(acc[a][b], af[a], bf[b]);
     }
   }
 
-  // epilogue: block (a, b) holds weight rows wn*64 + a*16 + 4*fq + j of activation row
+  // epilogue: block (a, b) holds weight rows wn*GWT/2 + a*16 + 4*fq + j of activation row
   // wx*64 + b*16 + fr
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -188,8 +194,8 @@ __global__ __launch_bounds__(GTHREADS) void k_pf_gemm(GemmArgs g) {
     if (m >= g.M) continue;
     if (MODE == PF_SWIGLU) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int f = wt * 64 + (wn * 2 + p) * 16 + 4 * fq;
+      for (int p = 0; p < GWB / 2; ++p) {
+        const int f = wt * (GWT / 2) + (wn * GWB / 2 + p) * 16 + 4 * fq;
         if (f >= g.Nb) continue;
         T* dst = static_cast<T*>(g.act) + (size_t)m * g.Nb + f;
 #pragma unroll
@@ -199,11 +205,11 @@ __global__ __launch_bounds__(GTHREADS) void k_pf_gemm(GemmArgs g) {
         }
       }
     } else {
-      const int tpm = (g.Nb + GT - 1) / GT;
-      const int mat = wt / tpm, n0 = (wt - mat * tpm) * GT;
+      const int tpm = (g.Nb + GWT - 1) / GWT;
+      const int mat = wt / tpm, n0 = (wt - mat * tpm) * GWT;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int n = n0 + wn * 64 + a * 16 + 4 * fq;
+      for (int a = 0; a < GWB; ++a) {
+        const int n = n0 + wn * (GWT / 2) + a * 16 + 4 * fq;
         if (n >= g.Nb) continue;
         float4* dst = reinterpret_cast<float4*>(g.out + (size_t)m * g.ldo + (size_t)mat * g.Nb + n);
         float4 v = make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
@@ -224,7 +230,7 @@ void gemm(const void* X, int M, int K, const void* W0, const void* W1, const voi
   g.X = X; g.M = M; g.K = K;
   g.W[0] = W0; g.W[1] = W1; g.W[2] = W2;
   g.Nb = Nb; g.nmat = nmat;
-  g.n_wt = MODE == PF_SWIGLU ? (Nb + 63) / 64 : nmat * ((Nb + GT - 1) / GT);
+  g.n_wt = MODE == PF_SWIGLU ? (Nb + GWT / 2 - 1) / (GWT / 2) : nmat * ((Nb + GWT - 1) / GWT);
   g.n_xt = (M + GT - 1) / GT;
   g.out = out; g.ldo = ldo; g.act = act;
   hipLaunchKernelGGL((k_pf_gemm<T, MODE>), dim3(g.n_wt * g.n_xt), dim3(GTHREADS), (size_t)GNST * GSTAGE, s, g);
