@@ -96,3 +96,39 @@ def test_model_create_rejects_unsupported_shapes(fields, status):
     st = lib.ls_model_create(C.byref(d), C.byref(w), C.byref(out))
     assert st == status, (st, lib.ls_last_error())
     assert lib.ls_last_error()
+
+
+def test_prefill_host_contract():
+    """ls_prefill's host-side checks and scratch size need no GPU: the scratch holds the
+    chunk's residual stream and its coda copy (fp32), the normalised rows, attention outputs
+    and SwiGLU outputs (model dtype) and q|k|v (fp32), each 256-byte aligned; a call without
+    a bound workspace, with negative sizes or without a model is rejected before any device
+    work, and n = 0 is a no-op."""
+    from looped_transformer_self_amd import _lib as binding
+    lib = _lib()
+    lib.ls_model_create.restype = C.c_int
+    lib.ls_prefill_workspace_bytes.restype = C.c_size_t
+    lib.ls_prefill_workspace_bytes.argtypes = [C.c_void_p, C.c_int]
+    lib.ls_prefill.restype = C.c_int
+    lib.ls_prefill.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_uint,
+                               C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    assert lib.ls_prefill_workspace_bytes(None, 16) == 0
+    assert lib.ls_prefill(None, None, None, 4, None, 0, 1, None, None, None, 0, None) == binding.LS_ERR_INVALID
+    d = _desc()
+    fake = 0x1000                                  # pointers are only stored at creation
+    lay = (binding.ls_layer_ptrs * d.L)(*[binding.ls_layer_ptrs(*([fake] * 9)) for _ in range(d.L)])
+    w = binding.ls_weight_ptrs(fake, fake, None, lay, None)
+    m = C.c_void_p()
+    assert lib.ls_model_create(C.byref(d), C.byref(w), C.byref(m)) == binding.LS_OK
+    try:
+        al = lambda x: (x + 255) // 256 * 256
+        for n in (1, 130, 2048):
+            want = 2 * al(n * d.d * 4) + al(n * d.d * 2) + al(n * 3 * d.d * 4) + al(n * d.d * 2) + al(n * d.F * 2)
+            assert lib.ls_prefill_workspace_bytes(m, n) == want, n
+        kv = binding.ls_kv(fake, None, None)
+        args = (fake, fake, 4, None, 0, 1, fake, C.addressof(kv), fake, 1 << 30, None)
+        assert lib.ls_prefill(m, *args) == binding.LS_ERR_INVALID          # no workspace bound
+        assert lib.ls_prefill(m, fake, fake, -1, None, 0, 1, fake, C.addressof(kv), fake, 1 << 30,
+                              None) == binding.LS_ERR_INVALID
+    finally:
+        lib.ls_model_destroy(m)
