@@ -181,6 +181,8 @@ class Decoder:
         cfg, e = self.cfg, self.e
         prompt = [int(t) for t in prompt]
         T0 = len(prompt)
+        if T0 == 0:
+            raise ValueError("prefill needs at least one prompt token")
         if fast is None:
             fast = hasattr(e, "prefill")
         if fast:
