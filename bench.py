@@ -359,6 +359,76 @@ def microbench(workload, Ms=(1, 2, 3, 4, 8, 16, 128), reps=10):
     print(json.dumps(out), flush=True)
 
 
+def phase_stamps(workload, Ms=(1, 4, 7)):
+    """Per-phase timeline of one ls_loop_step launch at fixed row counts M (rows at distinct
+    depths, the workload's full context, synthetic hidden rows and KV as in the
+    microbenchmark): ls_debug_trace's wall-clock stamps (100 MHz) of phase begin and end per
+    workgroup, for the first four layers, as medians (and the maximum end) over workgroups in
+    microseconds from the launch's first stamp.  Prints a markdown table."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from looped_transformer_self_amd import _lib as L
+    from looped_transformer_self_amd.engine import Engine
+    from synth import configs, weights
+
+    wl = configs.get(workload)
+    cfg, dec = wl.model, wl.decode
+    n_fin = dec.prompt_len + dec.new_tokens
+    S = n_fin + max(Ms) + 8
+    w = weights.make_weights(cfg, seed=dec.seed_w)
+    e = Engine(cfg, w, slot_capacity=S, max_rows=max(Ms), max_keys=S, max_jobs=4, prob_rows=4)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    kv = e.kv_core.view(torch.bfloat16) if cfg.dtype == "bf16" else e.kv_core
+    for i in range(0, kv.numel(), 1 << 28):
+        n = min(1 << 28, kv.numel() - i)
+        kv[i:i + n] = torch.randn(n, generator=g, device="cuda", dtype=torch.float32).to(kv.dtype)
+    e.H.copy_(torch.randn(e.H.shape, generator=g, device="cuda"))
+    fin = torch.arange(S, dtype=torch.int32, device="cuda")
+    fin_ptr = ctypes.c_void_p(fin.data_ptr())
+    buf = torch.zeros(1024 * (4 * 8 * 8 + 32), dtype=torch.int64, device="cuda")
+    names = ["QKV", "attention", "O", "GU", "DOWN"]
+    out = [f"# ls_loop_step phase timeline on workload {wl.key} ({wl.description}), {n_fin} prefix keys", "",
+           f"Command (repo root, MI355X, one GPU): python3 bench.py --phase-stamps --workload {wl.key}", "",
+           "Microseconds from the launch's first stamp; each cell is begin / median end / latest end of the "
+           "phase over workgroups (ls_debug_trace wall-clock stamps).", ""]
+    for M in Ms:
+        slots = list(range(n_fin, n_fin + M))
+        depth = [1 + (cfg.R - 1 - (i * cfg.R) // M) % cfg.R for i in range(M)]
+        rows = e.rows(slots, [n_fin] * M, depth, n_fin, [[]] * M, fin_ptr)
+        for _ in range(3):
+            e.loop_step(rows)
+        torch.cuda.synchronize()
+        grid = ctypes.c_int()
+        buf.zero_()
+        L.check(L.lib.ls_debug_trace(e.h, ctypes.c_void_p(buf.data_ptr()), ctypes.byref(grid)), "ls_debug_trace")
+        b, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record()
+        e.loop_step(rows)
+        en.record()
+        torch.cuda.synchronize()
+        L.check(L.lib.ls_debug_trace(e.h, None, ctypes.byref(grid)), "ls_debug_trace")
+        assert e.sync_status() == 0
+        G = grid.value
+        st = buf[:G * 256].cpu().numpy().reshape(G, 4, 8, 8).astype(np.float64)
+        us = (st - st[st > 0].min()) / 100.0
+        out += [f"## M = {M} (distinct depths {len(set(depth))}), grid {G}, event-timed "
+                f"{b.elapsed_time(en) * 1e3:.0f} us", "", "| layer | " + " | ".join(names) + " |",
+                "|---|" + "---|" * len(names)]
+        for l in range(min(4, cfg.L)):
+            cells = []
+            for ph in range(1, 6):
+                ok = st[:, l, ph, 1] > 0
+                cells.append(f"{np.median(us[ok, l, ph, 0]):.0f} / {np.median(us[ok, l, ph, 1]):.0f} / "
+                             f"{us[ok, l, ph, 1].max():.0f}" if ok.any() else "-")
+            out.append(f"| {l} | " + " | ".join(cells) + " |")
+        out.append("")
+    e.close()
+    print("\n".join(out), flush=True)
+
+
 SLICE = 32                      # committed tokens per benchmark step
 AR_SLICES = 2                   # slices decoded again in plain full-depth mode
 
@@ -421,6 +491,8 @@ def main():
     ap.add_argument("--no-ar", action="store_true", help="skip the plain full-depth comparison")
     ap.add_argument("--microbench", action="store_true",
                     help="ls_loop_step at fixed row counts on the workload's shape, and a streaming-read reference")
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="per-phase timeline of ls_loop_step at 1, 4 and 7 rows (markdown)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run one plain device copy of 1 GiB (byte-counter calibration)")
     ap.add_argument("--pmc-summary", action="store_true",
@@ -447,6 +519,9 @@ def main():
         return
     if args.microbench:
         microbench(args.workload)
+        return
+    if args.phase_stamps:
+        phase_stamps(args.workload)
         return
 
     import torch
